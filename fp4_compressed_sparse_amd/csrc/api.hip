@@ -1,0 +1,483 @@
+// Host side of the CSA2 C ABI: validation, workspace layout, launches and
+// the layer-stack driver.  The kernel sources are compiled in this single
+// translation unit so the device flag word has one definition.
+//
+// Modes and the hierarchical pool follow rebasdaily.com "DeepSeek-V4.1-Flash
+// KV compression", section "same notes, many layers" (Full / Reindex /
+// Reuse; the first Full layer scans everything into a pool that later layers
+// search) and the mode table of ailily.cc "890 bytes per token", section 二.
+#include "quantize.hip"
+#include "index.hip"
+#include "attend.hip"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "csa2.h"
+
+using namespace csa2;
+
+namespace {
+
+thread_local std::string t_last_error;
+
+csa2_status fail(csa2_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  t_last_error = buf;
+  return s;
+}
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+csa2_status launched(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CSA2_E_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return CSA2_OK;
+}
+
+// One-time per-device setup: architecture check and LDS limits.
+csa2_status device_ready() {
+  static std::mutex mu;
+  static int state[64] = {0};   // 0 unknown, 1 ok, 2 unsupported
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(CSA2_E_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(CSA2_E_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(CSA2_E_HIP, "hipGetDeviceProperties failed");
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      state[dev] = 2;
+    } else {
+      const int big = 160 * 1024 - 16 * 1024;
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel<1>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel<2>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel<4>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&rescore_kernel<true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
+      (void)hipGetLastError();
+      state[dev] = 1;
+    }
+  }
+  if (state[dev] == 2) return fail(CSA2_E_UNSUPPORTED, "device %d is not gfx950", dev);
+  return CSA2_OK;
+}
+
+// ---- workspace layout ----------------------------------------------------
+
+int att_positions_per_stage(int heads) { return heads == 16 ? 128 : 64; }
+
+int att_splits(int batch, int n_stages) {
+  int want = (int)ceil_div(512, batch);
+  if (want < 1) want = 1;
+  return n_stages < want ? n_stages : want;
+}
+
+struct Layout {
+  size_t ctrl, hist, scores, bitmap, cands, part_o, part_ml, total;
+  int64_t score_stride, cand_stride;
+  int32_t nwords;
+  int32_t att_stages, att_splits;
+};
+
+bool make_layout(int32_t batch, int32_t heads, int64_t max_len, int32_t pool, int32_t topk, Layout *L) {
+  if (batch < 1 || max_len < 0 || topk < 1 || topk > CSA2_MAX_TOPK || pool < 0 || pool > CSA2_MAX_POOL)
+    return false;
+  if (heads < 1 || heads > CSA2_MAX_HEADS) return false;
+  const int64_t nblk = ceil_div(max_len, BLOCK);
+  L->score_stride = ceil_div(nblk > CSA2_MAX_POOL ? nblk : CSA2_MAX_POOL, 64) * 64;
+  L->nwords = (int32_t)(ceil_div(nblk > 0 ? nblk : 1, 64) * 2);
+  L->cand_stride = nblk > 0 ? nblk : 1;
+  size_t off = 0;
+  L->ctrl = off;   off = align256(off + sizeof(Ctrl) * batch);
+  L->hist = off;   off = align256(off + sizeof(uint32_t) * HIST_BINS * (size_t)batch);
+  L->scores = off; off = align256(off + sizeof(float) * (size_t)L->score_stride * batch);
+  L->bitmap = off; off = align256(off + sizeof(uint32_t) * (size_t)L->nwords * batch);
+  L->cands = off;  off = align256(off + sizeof(uint64_t) * (size_t)L->cand_stride * batch);
+  L->att_stages = L->att_splits = 0;
+  L->part_o = L->part_ml = off;
+  if (heads == 16 || heads == 32 || heads == 64) {
+    L->att_stages = (int32_t)ceil_div((int64_t)topk * BLOCK, att_positions_per_stage(heads));
+    L->att_splits = att_splits(batch, L->att_stages);
+    const size_t slots = (size_t)batch * L->att_splits * 4 * 16;
+    L->part_o = off;  off = align256(off + sizeof(float) * slots * D);
+    L->part_ml = off; off = align256(off + sizeof(float) * slots * 2);
+  }
+  L->total = off;
+  return true;
+}
+
+csa2_status check_kv(const csa2_kv *kv) {
+  if (!kv) return fail(CSA2_E_ARG, "kv is NULL");
+  if (!kv->codes || !kv->scales || !kv->seq_len) return fail(CSA2_E_ARG, "kv has a NULL pointer");
+  if (!aligned(kv->codes, 256) || !aligned(kv->scales, 256))
+    return fail(CSA2_E_ARG, "kv codes/scales must be 256-byte aligned");
+  if (!aligned(kv->seq_len, 8)) return fail(CSA2_E_ARG, "kv seq_len must be 8-byte aligned");
+  if (kv->batch < 1 || kv->batch > 65535) return fail(CSA2_E_ARG, "kv batch %d out of range", kv->batch);
+  if (kv->capacity < BLOCK || kv->capacity % BLOCK)
+    return fail(CSA2_E_SHAPE, "kv capacity %lld must be a positive multiple of 8", (long long)kv->capacity);
+  if (kv->max_len < 0 || kv->max_len > kv->capacity)
+    return fail(CSA2_E_CAPACITY, "kv max_len %lld outside [0, capacity %lld]", (long long)kv->max_len,
+                (long long)kv->capacity);
+  return CSA2_OK;
+}
+
+csa2_status check_ws(void *ws, size_t ws_bytes, const Layout &L) {
+  if (!ws) return fail(CSA2_E_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(CSA2_E_ARG, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(CSA2_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  return CSA2_OK;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+int grid_for(int64_t items, int batch, int target) {
+  int64_t want = ceil_div(target, batch);
+  if (want < 1) want = 1;
+  if (items < want) want = items;
+  return (int)(want < 1 ? 1 : want);
+}
+
+// ---- launches (arguments already validated) -----------------------------
+
+csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, int32_t R,
+                            int32_t *first_out, int32_t topk2, int32_t *idx_out, void *ws,
+                            const Layout &L, hipStream_t s) {
+  const int B = kv->batch;
+  const int64_t nblk_grid = ceil_div(kv->max_len, BLOCK);
+  ScanArgs sa;
+  sa.codes = kv->codes; sa.scales = kv->scales; sa.seq_len = kv->seq_len; sa.capacity = kv->capacity;
+  sa.limit = kv->max_len;
+  sa.q = q; sa.heads = heads; sa.nblk_grid = (int32_t)nblk_grid;
+  sa.scores = at<float>(ws, L.scores); sa.score_stride = L.score_stride;
+  sa.ctrl = at<Ctrl>(ws, L.ctrl); sa.hist = at<uint32_t>(ws, L.hist);
+  sa.R = R; sa.fill_invalid = 0;
+  const int iters = (int)ceil_div(nblk_grid > 0 ? nblk_grid : 1, BLOCKS_PER_ITER);
+  dim3 g1(grid_for(iters, B, 512), B);
+  scan_kernel<true><<<g1, SCAN_THREADS, 0, s>>>(sa);
+  if (csa2_status st = launched("scan")) return st;
+  SelectArgs se;
+  se.seq_len = kv->seq_len; se.limit = kv->max_len; se.scores = sa.scores; se.score_stride = L.score_stride;
+  se.ctrl = sa.ctrl; se.bitmap = at<uint32_t>(ws, L.bitmap); se.nwords = L.nwords;
+  se.cands = at<uint64_t>(ws, L.cands); se.cand_stride = L.cand_stride;
+  se.R = R; se.first_out = first_out; se.topk = topk2; se.idx_out = idx_out;
+  int lk = R > 4096 ? R : 4096;
+  se.lds_keys = lk;
+  dim3 g2(grid_for(ceil_div(L.nwords / 2, 4), B, 256), B);
+  select_kernel<<<g2, SCAN_THREADS, (size_t)lk * sizeof(uint64_t), s>>>(se);
+  return launched("select");
+}
+
+csa2_status run_rescore(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *cand,
+                        int32_t n_cand, int32_t topk, int32_t *idx_out, float *scores,
+                        int64_t score_stride, Ctrl *ctrl, hipStream_t s) {
+  const int B = kv->batch;
+  RescoreArgs ra;
+  ra.codes = kv->codes; ra.scales = kv->scales; ra.seq_len = kv->seq_len; ra.capacity = kv->capacity;
+  ra.limit = kv->max_len;
+  ra.q = q; ra.heads = heads; ra.cand = cand; ra.n_cand = n_cand;
+  ra.scores = scores; ra.score_stride = score_stride; ra.ctrl = ctrl;
+  ra.topk = topk; ra.idx_out = idx_out;
+  dim3 g(grid_for(ceil_div(n_cand, BLOCKS_PER_ITER), B, 512), B);
+  if (idx_out) {
+    rescore_kernel<true><<<g, SCAN_THREADS, (size_t)n_cand * sizeof(uint64_t), s>>>(ra);
+  } else {
+    rescore_kernel<false><<<g, SCAN_THREADS, 0, s>>>(ra);
+  }
+  return launched("rescore");
+}
+
+csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *idx,
+                       int32_t topk, float scale, float *out, void *ws, const Layout &L,
+                       hipStream_t s) {
+  const int B = kv->batch;
+  AttendArgs aa;
+  aa.codes = kv->codes; aa.scales = kv->scales; aa.seq_len = kv->seq_len; aa.capacity = kv->capacity;
+  aa.limit = kv->max_len;
+  aa.q = q; aa.idx = idx; aa.topk = topk;
+  aa.scale_log2 = scale * 1.4426950408889634f;
+  aa.n_stages = L.att_stages; aa.splits = L.att_splits;
+  aa.part_o = at<float>(ws, L.part_o); aa.part_ml = at<float>(ws, L.part_ml);
+  dim3 g(L.att_splits, B);
+  const size_t lds = (size_t)att_positions_per_stage(heads) * ROW_HALVES * sizeof(_Float16);
+  if (heads == 16) attend_partial_kernel<1><<<g, ATT_THREADS, lds, s>>>(aa);
+  else if (heads == 32) attend_partial_kernel<2><<<g, ATT_THREADS, lds, s>>>(aa);
+  else attend_partial_kernel<4><<<g, ATT_THREADS, lds, s>>>(aa);
+  if (csa2_status st = launched("attend")) return st;
+  CombineArgs ca;
+  ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = L.att_splits; ca.heads = heads; ca.out = out;
+  attend_combine_kernel<<<dim3(heads, B), 128, 0, s>>>(ca);
+  return launched("combine");
+}
+
+csa2_status check_select_args(int32_t topk, int32_t pool) {
+  if (topk < 1 || topk > CSA2_MAX_TOPK) return fail(CSA2_E_SHAPE, "topk %d outside [1, %d]", topk, CSA2_MAX_TOPK);
+  if (pool < 0 || pool > CSA2_MAX_POOL) return fail(CSA2_E_SHAPE, "pool %d outside [0, %d]", pool, CSA2_MAX_POOL);
+  if (pool > 0 && pool < topk) return fail(CSA2_E_ARG, "pool %d < topk %d", pool, topk);
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *csa2_status_string(csa2_status s) {
+  switch (s) {
+    case CSA2_OK: return "ok";
+    case CSA2_E_ARG: return "invalid argument";
+    case CSA2_E_SHAPE: return "unsupported shape";
+    case CSA2_E_WORKSPACE: return "workspace too small";
+    case CSA2_E_CAPACITY: return "capacity exceeded";
+    case CSA2_E_HIP: return "HIP error";
+    case CSA2_E_UNSUPPORTED: return "unsupported device";
+    default: return "unknown status";
+  }
+}
+
+const char *csa2_last_error(void) { return t_last_error.c_str(); }
+
+size_t csa2_workspace_bytes(int32_t batch, int32_t heads, int64_t max_len, int32_t pool, int32_t topk) {
+  Layout L;
+  if (!make_layout(batch, heads, max_len, pool, topk, &L)) return 0;
+  return L.total;
+}
+
+csa2_status csa2_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  t_last_error.clear();
+  if (!ws || !aligned(ws, 256) || ws_bytes % 4) return fail(CSA2_E_ARG, "workspace must be non-NULL, 256-byte aligned, size a multiple of 4");
+  if (csa2_status st = device_ready()) return st;
+  if (ws_bytes == 0) return CSA2_OK;
+  const int64_t words = (int64_t)(ws_bytes / 4);
+  const int grid = (int)(ceil_div(words, 256) < 2048 ? ceil_div(words, 256) : 2048);
+  zero_kernel<<<grid, 256, 0, as_stream(stream)>>>(static_cast<uint32_t *>(ws), words);
+  return launched("workspace_init");
+}
+
+csa2_status fp4_quantize_kv(const float *x, int64_t rows, const int64_t *dst_row, int64_t dst_rows,
+                            uint8_t *codes, uint8_t *scales, void *stream) {
+  t_last_error.clear();
+  if (rows < 0) return fail(CSA2_E_ARG, "rows %lld < 0", (long long)rows);
+  if (rows == 0) return CSA2_OK;
+  if (!x || !codes || !scales) return fail(CSA2_E_ARG, "NULL pointer");
+  if (!aligned(x, 16)) return fail(CSA2_E_ARG, "x must be 16-byte aligned");
+  if (!aligned(codes, 4) || !aligned(scales, 1)) return fail(CSA2_E_ARG, "codes must be 4-byte aligned");
+  if (dst_row && !aligned(dst_row, 8)) return fail(CSA2_E_ARG, "dst_row must be 8-byte aligned");
+  if (dst_rows < 0 || (!dst_row && dst_rows < rows))
+    return fail(CSA2_E_CAPACITY, "dst_rows %lld too small for %lld rows", (long long)dst_rows, (long long)rows);
+  if (csa2_status st = device_ready()) return st;
+  const int64_t quads = rows * 128;
+  const int grid = (int)(ceil_div(quads, 256) < 4096 ? ceil_div(quads, 256) : 4096);
+  quantize_rows_kernel<<<grid, 256, 0, as_stream(stream)>>>(x, rows, dst_row, dst_rows, codes, scales);
+  return launched("quantize");
+}
+
+csa2_status csa2_append_kv(const csa2_kv *kv, const float *x, void *stream) {
+  t_last_error.clear();
+  if (csa2_status st = check_kv(kv)) return st;
+  if (!x || !aligned(x, 16)) return fail(CSA2_E_ARG, "x must be non-NULL and 16-byte aligned");
+  if (csa2_status st = device_ready()) return st;
+  AppendArgs aa;
+  memset(&aa, 0, sizeof aa);
+  aa.codes[0] = kv->codes; aa.scales[0] = kv->scales; aa.seq_len[0] = kv->seq_len; aa.capacity[0] = kv->capacity;
+  append_kernel<<<dim3(kv->batch, 1), 128, 0, as_stream(stream)>>>(aa, x, kv->batch);
+  return launched("append");
+}
+
+csa2_status csa2_index_topk(int32_t mode, const csa2_kv *kv, const float *q, int32_t heads,
+                            const int32_t *cand, int32_t n_cand, int32_t topk, int32_t *idx_out,
+                            int32_t pool, int32_t *pool_out, const int32_t *prior_idx, void *ws,
+                            size_t ws_bytes, void *stream) {
+  t_last_error.clear();
+  if (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)
+    return fail(CSA2_E_ARG, "mode %d is not Full/Reindex/Reuse", mode);
+  if (!idx_out || !aligned(idx_out, 4)) return fail(CSA2_E_ARG, "idx_out must be non-NULL");
+  if (topk < 1 || topk > CSA2_MAX_TOPK) return fail(CSA2_E_SHAPE, "topk %d outside [1, %d]", topk, CSA2_MAX_TOPK);
+  hipStream_t s = as_stream(stream);
+  if (mode == CSA2_REUSE) {
+    if (!prior_idx) return fail(CSA2_E_ARG, "Reuse needs prior_idx");
+    if (!kv || kv->batch < 1) return fail(CSA2_E_ARG, "Reuse needs kv for the batch size");
+    if (csa2_status st = device_ready()) return st;
+    if (prior_idx == idx_out) return CSA2_OK;
+    const int64_t nidx = (int64_t)kv->batch * topk;
+    copy_idx_kernel<<<(int)ceil_div(nidx, 256), 256, 0, s>>>(prior_idx, idx_out, nidx);
+    return launched("reuse copy");
+  }
+  if (csa2_status st = check_kv(kv)) return st;
+  if (!q || !aligned(q, 16)) return fail(CSA2_E_ARG, "q must be non-NULL and 16-byte aligned");
+  if (heads < 1 || heads > CSA2_MAX_HEADS) return fail(CSA2_E_SHAPE, "heads %d outside [1, 64]", heads);
+  if (csa2_status st = check_select_args(topk, pool)) return st;
+  Layout L;
+  if (!make_layout(kv->batch, heads, kv->max_len, pool, topk, &L)) return fail(CSA2_E_SHAPE, "bad sizes");
+  if (csa2_status st = check_ws(ws, ws_bytes, L)) return st;
+  if (csa2_status st = device_ready()) return st;
+  if (cand) {
+    if (pool != 0) return fail(CSA2_E_ARG, "pool must be 0 with a candidate list");
+    if (n_cand < 1 || n_cand > CSA2_MAX_POOL) return fail(CSA2_E_SHAPE, "n_cand %d outside [1, %d]", n_cand, CSA2_MAX_POOL);
+    if (!aligned(cand, 4)) return fail(CSA2_E_ARG, "cand misaligned");
+    return run_rescore(kv, q, heads, cand, n_cand, topk, idx_out, at<float>(ws, L.scores),
+                       L.score_stride, at<Ctrl>(ws, L.ctrl), s);
+  }
+  if (pool > 0) {
+    if (!pool_out || !aligned(pool_out, 4)) return fail(CSA2_E_ARG, "pool > 0 needs pool_out");
+    return run_scan_select(kv, q, heads, pool, pool_out, topk, idx_out, ws, L, s);
+  }
+  return run_scan_select(kv, q, heads, topk, idx_out, 0, nullptr, ws, L, s);
+}
+
+csa2_status csa2_sparse_attend(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *idx,
+                               int32_t topk, float scale, float *out, void *ws, size_t ws_bytes,
+                               void *stream) {
+  t_last_error.clear();
+  if (csa2_status st = check_kv(kv)) return st;
+  if (!q || !aligned(q, 16) || !out || !aligned(out, 16))
+    return fail(CSA2_E_ARG, "q/out must be non-NULL and 16-byte aligned");
+  if (!idx || !aligned(idx, 4)) return fail(CSA2_E_ARG, "idx must be non-NULL");
+  if (heads != 16 && heads != 32 && heads != 64)
+    return fail(CSA2_E_SHAPE, "attention heads must be 16, 32 or 64 (got %d)", heads);
+  if (topk < 1 || topk > CSA2_MAX_TOPK) return fail(CSA2_E_SHAPE, "topk %d outside [1, %d]", topk, CSA2_MAX_TOPK);
+  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
+    return fail(CSA2_E_ARG, "scale must be finite");
+  Layout L;
+  if (!make_layout(kv->batch, heads, kv->max_len, 0, topk, &L)) return fail(CSA2_E_SHAPE, "bad sizes");
+  if (csa2_status st = check_ws(ws, ws_bytes, L)) return st;
+  if (csa2_status st = device_ready()) return st;
+  return run_attend(kv, q, heads, idx, topk, scale, out, ws, L, as_stream(stream));
+}
+
+csa2_status csa2_block_scores(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *cand,
+                              int32_t n_cand, float *scores, void *stream) {
+  t_last_error.clear();
+  if (csa2_status st = check_kv(kv)) return st;
+  if (!q || !aligned(q, 16) || !scores || !aligned(scores, 4))
+    return fail(CSA2_E_ARG, "q/scores must be non-NULL and aligned");
+  if (heads < 1 || heads > CSA2_MAX_HEADS) return fail(CSA2_E_SHAPE, "heads %d outside [1, 64]", heads);
+  if (csa2_status st = device_ready()) return st;
+  hipStream_t s = as_stream(stream);
+  if (cand) {
+    if (n_cand < 1 || n_cand > CSA2_MAX_POOL) return fail(CSA2_E_SHAPE, "n_cand %d outside [1, %d]", n_cand, CSA2_MAX_POOL);
+    return run_rescore(kv, q, heads, cand, n_cand, 0, nullptr, scores, n_cand, nullptr, s);
+  }
+  const int64_t nblk_grid = ceil_div(kv->max_len, BLOCK);
+  if (nblk_grid == 0) return CSA2_OK;
+  ScanArgs sa;
+  sa.codes = kv->codes; sa.scales = kv->scales; sa.seq_len = kv->seq_len; sa.capacity = kv->capacity;
+  sa.limit = kv->max_len;
+  sa.q = q; sa.heads = heads; sa.nblk_grid = (int32_t)nblk_grid;
+  sa.scores = scores; sa.score_stride = nblk_grid; sa.ctrl = nullptr; sa.hist = nullptr;
+  sa.R = 0; sa.fill_invalid = 1;
+  dim3 g(grid_for(ceil_div(nblk_grid, BLOCKS_PER_ITER), kv->batch, 512), kv->batch);
+  scan_kernel<false><<<g, SCAN_THREADS, 0, s>>>(sa);
+  return launched("scores");
+}
+
+csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
+  t_last_error.clear();
+  if (!st) return fail(CSA2_E_ARG, "step is NULL");
+  if (!st->caches || st->n_caches < 1 || st->n_caches > CSA2_MAX_CACHES)
+    return fail(CSA2_E_ARG, "n_caches %d outside [1, %d]", st->n_caches, CSA2_MAX_CACHES);
+  if (!st->layers || st->n_layers < 1) return fail(CSA2_E_ARG, "no layers");
+  const int B = st->caches[0].batch;
+  int64_t max_len = 0;
+  for (int c = 0; c < st->n_caches; ++c) {
+    if (csa2_status e = check_kv(&st->caches[c])) return e;
+    if (st->caches[c].batch != B) return fail(CSA2_E_ARG, "caches differ in batch");
+    if (st->caches[c].max_len > max_len) max_len = st->caches[c].max_len;
+  }
+  if (st->heads != 16 && st->heads != 32 && st->heads != 64)
+    return fail(CSA2_E_SHAPE, "heads must be 16, 32 or 64");
+  if (csa2_status e = check_select_args(st->topk, st->pool)) return e;
+  if (st->pool > 0 && (!st->pool_out || !aligned(st->pool_out, 4))) return fail(CSA2_E_ARG, "pool > 0 needs pool_out");
+  if (st->new_rows && !aligned(st->new_rows, 16)) return fail(CSA2_E_ARG, "new_rows misaligned");
+  // mode pattern: layer 0 Full; Reindex/Reuse use the latest Full cache
+  int latest = -1;
+  for (int l = 0; l < st->n_layers; ++l) {
+    const csa2_layer &ly = st->layers[l];
+    if (ly.mode != CSA2_FULL && ly.mode != CSA2_REINDEX && ly.mode != CSA2_REUSE)
+      return fail(CSA2_E_ARG, "layer %d: bad mode %d", l, ly.mode);
+    if (ly.cache < 0 || ly.cache >= st->n_caches) return fail(CSA2_E_ARG, "layer %d: cache %d out of range", l, ly.cache);
+    if (ly.mode == CSA2_FULL) latest = ly.cache;
+    else if (latest < 0) return fail(CSA2_E_ARG, "layer %d: no earlier Full layer", l);
+    else if (ly.cache != latest) return fail(CSA2_E_ARG, "layer %d: must use the latest Full cache %d", l, latest);
+    if (!ly.q || !aligned(ly.q, 16) || !ly.out || !aligned(ly.out, 16) || !ly.idx || !aligned(ly.idx, 4))
+      return fail(CSA2_E_ARG, "layer %d: q/out/idx missing or misaligned", l);
+  }
+  Layout L;
+  if (!make_layout(B, st->heads, max_len, st->pool, st->topk, &L)) return fail(CSA2_E_SHAPE, "bad sizes");
+  if (csa2_status e = check_ws(st->ws, st->ws_bytes, L)) return e;
+  if (csa2_status e = device_ready()) return e;
+  hipStream_t s = as_stream(stream);
+
+  if (st->new_rows) {
+    AppendArgs aa;
+    memset(&aa, 0, sizeof aa);
+    for (int c = 0; c < st->n_caches; ++c) {
+      aa.codes[c] = st->caches[c].codes; aa.scales[c] = st->caches[c].scales;
+      aa.seq_len[c] = st->caches[c].seq_len; aa.capacity[c] = st->caches[c].capacity;
+    }
+    append_kernel<<<dim3(B, st->n_caches), 128, 0, s>>>(aa, st->new_rows, B);
+    if (csa2_status e = launched("append")) return e;
+  }
+  bool pool_built = false;
+  const int32_t *prev_idx = nullptr;
+  for (int l = 0; l < st->n_layers; ++l) {
+    const csa2_layer &ly = st->layers[l];
+    const csa2_kv *kv = &st->caches[ly.cache];
+    csa2_status e = CSA2_OK;
+    if (ly.mode == CSA2_REUSE) {
+      if (!prev_idx) return fail(CSA2_E_ARG, "layer %d: Reuse with no earlier selection", l);
+      if (prev_idx != ly.idx) {
+        const int64_t nidx = (int64_t)B * st->topk;
+        copy_idx_kernel<<<(int)ceil_div(nidx, 256), 256, 0, s>>>(prev_idx, ly.idx, nidx);
+        e = launched("reuse copy");
+      }
+    } else if (st->pool > 0 && !pool_built) {
+      e = run_scan_select(kv, ly.q, st->heads, st->pool, st->pool_out, st->topk, ly.idx, st->ws, L, s);
+      pool_built = true;
+    } else if (st->pool > 0) {
+      e = run_rescore(kv, ly.q, st->heads, st->pool_out, st->pool, st->topk, ly.idx,
+                      at<float>(st->ws, L.scores), L.score_stride, at<Ctrl>(st->ws, L.ctrl), s);
+    } else {
+      e = run_scan_select(kv, ly.q, st->heads, st->topk, ly.idx, 0, nullptr, st->ws, L, s);
+    }
+    if (e) return e;
+    e = run_attend(kv, ly.q, st->heads, ly.idx, st->topk, st->scale, ly.out, st->ws, L, s);
+    if (e) return e;
+    prev_idx = ly.idx;
+  }
+  return CSA2_OK;
+}
+
+csa2_status csa2_device_error(int32_t *flags_host, void *stream) {
+  t_last_error.clear();
+  if (!flags_host) return fail(CSA2_E_ARG, "flags_host is NULL");
+  if (csa2_status st = device_ready()) return st;
+  hipError_t e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return fail(CSA2_E_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  uint32_t v = 0;
+  e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_flags), sizeof v, 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(CSA2_E_HIP, "read flags: %s", hipGetErrorString(e));
+  const uint32_t zero = 0;
+  e = hipMemcpyToSymbol(HIP_SYMBOL(g_flags), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(CSA2_E_HIP, "clear flags: %s", hipGetErrorString(e));
+  *flags_host = (int32_t)v;
+  return CSA2_OK;
+}
+
+}  // extern "C"

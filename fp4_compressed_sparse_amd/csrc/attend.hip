@@ -1,0 +1,271 @@
+// Sparse softmax attention over the selected FP4 positions (gfx950).
+//
+// CSA2 attends only to the positions of the selected blocks (rebasdaily.com
+// "DeepSeek-V4.1-Flash KV compression", section "same notes, many layers");
+// the FP4 rows are dequantised inside the kernel from a fixed-stride layout
+// (yomxxx.com long-form post, section 五).  Keys and values are both the
+// 512-channel latent (ailily.cc "890 bytes per token", section 三), shared
+// by all heads.
+//
+// Design (matrix cores, fp16 operands, fp32 accumulation):
+//  * A workgroup (4 waves) takes a range of "stages" of SP gathered
+//    positions.  Per stage the 256 threads load the FP4 codes and E4M3
+//    scales of the SP positions and write code*scale as fp16 rows into LDS
+//    (exact: at most 6 significant bits, range 2^-10..2688).
+//  * Each wave owns 16 heads (one MFMA tile) and 32-position sub-tiles:
+//      S^T = K Q^T   v_mfma_f32_16x16x32_f16, K rows read from LDS (b128),
+//                    Q in registers (fp16), 16 k-steps over 512 channels;
+//      online softmax in registers (exp2 domain);
+//      O^T += V^T P^T  32 channel tiles, V^T read straight from the
+//                    row-major LDS tile with ds_read_b64_tr_b16, P^T from
+//                    the S^T accumulators (lane layout already matches).
+//  * Each wave writes its (max, sum, O) partial; a combine kernel merges the
+//    partials of every head (split-K over positions).
+//
+// MFMA 16x16x32 f16 lane layout (checked on gfx950): A row = lane%16 with
+// k = 8*(lane/16)..+7; B column = lane%16, same k; C column = lane%16,
+// rows 4*(lane/16)..+3.  ds_read_b64_tr_b16: within each 16-lane group,
+// result lane i, element r comes from element i%4 of the 8 bytes addressed
+// by lane 4r + i/4.
+#include "common.hpp"
+
+namespace csa2 {
+
+constexpr int ATT_THREADS = 256;
+constexpr int ROW_HALVES = D + 8;                 // LDS row stride: 1040 bytes
+
+struct AttendArgs {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const int64_t *seq_len;
+  int64_t capacity;
+  int64_t limit;            // min(capacity, max_len)
+  const float *q;           // [batch][heads][512]
+  const int32_t *idx;       // [batch][topk]
+  int32_t topk;
+  float scale_log2;         // scale * log2(e)
+  int32_t n_stages;         // ceil(topk*8 / SP)
+  int32_t splits;           // workgroups per sequence
+  float *part_o;            // [batch][splits][4][16][512]
+  float *part_ml;           // [batch][splits][4][16][2]
+};
+
+// Channel of row m of O^T tile ct (see the V^T read pattern below).
+__device__ __forceinline__ int tile_channel(int ct, int m) {
+  return 128 * (ct >> 3) + 4 * (ct & 7) + 32 * (m >> 2) + (m & 3);
+}
+
+template <int HT>   // head tiles of 16: 1, 2 or 4
+__global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs a) {
+  constexpr int WPT = 4 / HT;                     // waves per head tile
+  constexpr int NSUB = (HT == 4) ? 2 : 1;         // 32-position sub-tiles per wave per stage
+  constexpr int SP = 32 * NSUB * WPT;             // positions per stage: 64, 64, 128
+  extern __shared__ _Float16 s_v[];               // [SP][ROW_HALVES]
+  __shared__ uint8_t s_ok[SP];
+
+  const int b = blockIdx.y, split = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ht = wv % HT, wsub = wv / HT;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int64_t n = clamp_len(a.seq_len[b], a.limit);
+  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  const int32_t *idx = a.idx + (int64_t)b * a.topk;
+  const uint8_t *codes = a.codes + (int64_t)b * a.capacity * CODE_BYTES;
+  const uint8_t *scales = a.scales + (int64_t)b * a.capacity * SCALE_BYTES;
+  const int total_pos = a.topk * BLOCK;
+
+  // stage range of this workgroup
+  const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
+  const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
+
+  // Q^T operand: head ht*16 + n16, channels 32*kc + 8*g + 0..7
+  f16x8 qop[16];
+  {
+    const int heads = 16 * HT;
+    const float *qh = a.q + ((int64_t)b * heads + ht * 16 + n16) * D + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < 16; ++kc) {
+      float4 lo = *reinterpret_cast<const float4 *>(qh + 32 * kc);
+      float4 hi = *reinterpret_cast<const float4 *>(qh + 32 * kc + 4);
+      qop[kc] = f16x8{(_Float16)lo.x, (_Float16)lo.y, (_Float16)lo.z, (_Float16)lo.w,
+                      (_Float16)hi.x, (_Float16)hi.y, (_Float16)hi.z, (_Float16)hi.w};
+    }
+  }
+
+  f32x4 acc[32];
+#pragma unroll
+  for (int ct = 0; ct < 32; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_huge_valf();   // running max of this lane's head (log2 domain)
+  float l_run = 0.f;                      // this lane's share of the softmax sum
+
+  for (int st = st0; st < st1; ++st) {
+    __syncthreads();                      // previous stage fully consumed
+    // ---- load + dequantise SP positions into LDS (16 threads per row) ----
+    for (int pp = tid >> 4; pp < SP; pp += ATT_THREADS / 16) {
+      const int i = tid & 15;
+      const int j = st * SP + pp;
+      bool ok = false;
+      int64_t pos = 0;
+      if (j < total_pos) {
+        const int32_t blk = idx[j >> 3];
+        pos = (int64_t)blk * BLOCK + (j & 7);
+        ok = blk >= 0 && blk < nblk && pos < n;
+        if (blk >= nblk && i == 0 && (j & 7) == 0) raise_flag(FLAG_BAD_INDEX);
+      }
+      u32x4 out[4];
+      if (ok) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(codes + pos * CODE_BYTES + 16 * i);
+        const uint32_t sc = *reinterpret_cast<const uint16_t *>(scales + pos * SCALE_BYTES + 2 * i);
+        const _Float16 s0 = (_Float16)e4m3_to_f32(sc & 0xffu);
+        const _Float16 s1 = (_Float16)e4m3_to_f32(sc >> 8);
+        const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
+#pragma unroll
+        for (int dw = 0; dw < 4; ++dw) {
+          const f16x2 sv = dw < 2 ? sv0 : sv1;
+          f16x2 h0 = e2m1x2_to_f16<0>(w[dw]) * sv;
+          f16x2 h1 = e2m1x2_to_f16<1>(w[dw]) * sv;
+          f16x2 h2 = e2m1x2_to_f16<2>(w[dw]) * sv;
+          f16x2 h3 = e2m1x2_to_f16<3>(w[dw]) * sv;
+          out[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                          __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
+        }
+      } else {
+#pragma unroll
+        for (int dw = 0; dw < 4; ++dw) out[dw] = u32x4{0u, 0u, 0u, 0u};
+      }
+      u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i);
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) dst[dw] = out[dw];
+      if (i == 0) s_ok[pp] = ok ? 1 : 0;
+    }
+    __syncthreads();
+
+    // ---- this wave's 32-position sub-tiles of the stage ----
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const int base = 32 * (wsub * NSUB + sub);          // first row of the sub-tile
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const _Float16 *krow = s_v + (base + 16 * t + n16) * ROW_HALVES + 8 * g;
+#pragma unroll
+        for (int kc = 0; kc < 16; ++kc) {
+          f16x8 kop = *reinterpret_cast<const f16x8 *>(krow + 32 * kc);
+          sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kc], sacc[t], 0, 0, 0);
+        }
+      }
+      // lane (head n16, group g) holds logits of rows 4g..4g+3 of tiles 0 and 1:
+      // positions base + 4g + r and base + 16 + 4g + r
+      float z[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        z[r] = s_ok[base + 4 * g + r] ? sacc[0][r] * a.scale_log2 : -__builtin_huge_valf();
+        z[4 + r] = s_ok[base + 16 + 4 * g + r] ? sacc[1][r] * a.scale_log2 : -__builtin_huge_valf();
+      }
+      float mx = z[0];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) mx = fmaxf(mx, z[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      float corr = 1.f;
+      _Float16 ph[8];
+      if (m_new == -__builtin_huge_valf()) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) ph[r] = (_Float16)0.f;
+      } else {
+        corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          ph[r] = (_Float16)__builtin_amdgcn_exp2f(z[r] - m_new);
+          psum += (float)ph[r];
+        }
+        l_run = l_run * corr + psum;
+        m_run = m_new;
+      }
+      if (corr != 1.f) {
+#pragma unroll
+        for (int ct = 0; ct < 32; ++ct) acc[ct] *= corr;
+      }
+      const f16x8 pop = {ph[0], ph[1], ph[2], ph[3], ph[4], ph[5], ph[6], ph[7]};
+      // V^T operand rows (k) = positions base + 4g + 0..3 then base + 16 + 4g + 0..3;
+      // source lane s = 4r + q points at row k0 + r, channel n0 + 32q
+      const int r_src = n16 >> 2, q_src = n16 & 3;
+      const _Float16 *v0 = s_v + (base + 4 * g + r_src) * ROW_HALVES + 32 * q_src;
+      const _Float16 *v1 = v0 + 16 * ROW_HALVES;
+#pragma unroll
+      for (int ct = 0; ct < 32; ++ct) {
+        const int n0 = 128 * (ct >> 3) + 4 * (ct & 7);
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(v0 + n0));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(v1 + n0));
+        f16x8 vop = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, acc[ct], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- write this wave's partial: O^T rows 4g..4g+3 of every tile ----
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const int64_t slot = ((int64_t)b * a.splits + split) * 4 + wv;
+  float *po = a.part_o + (slot * 16 + n16) * D;
+#pragma unroll
+  for (int ct = 0; ct < 32; ++ct) {
+    const int c = tile_channel(ct, 4 * g);
+    *reinterpret_cast<f32x4 *>(po + c) = acc[ct];
+  }
+  if (g == 0) {
+    float *pm = a.part_ml + (slot * 16 + n16) * 2;
+    pm[0] = m_run;
+    pm[1] = l_tot;
+  }
+}
+
+struct CombineArgs {
+  const float *part_o;
+  const float *part_ml;
+  int32_t splits;
+  int32_t heads;
+  float *out;               // [batch][heads][512]
+};
+
+// grid (heads, batch), 128 threads x 4 channels: merge every partial of a head.
+__global__ void __launch_bounds__(128) attend_combine_kernel(CombineArgs a) {
+  const int hh = blockIdx.x, b = blockIdx.y;
+  const int HT = a.heads / 16, ht = hh / 16, n16 = hh % 16;
+  const int WPT = 4 / HT;
+  const int nslots = a.splits * WPT;
+  float M = -__builtin_huge_valf();
+  for (int s = 0; s < nslots; ++s) {
+    const int split = s / WPT, w = ht + HT * (s % WPT);
+    const int64_t slot = ((int64_t)b * a.splits + split) * 4 + w;
+    M = fmaxf(M, a.part_ml[(slot * 16 + n16) * 2]);
+  }
+  float4 o = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != -__builtin_huge_valf()) {
+    for (int s = 0; s < nslots; ++s) {
+      const int split = s / WPT, w = ht + HT * (s % WPT);
+      const int64_t slot = ((int64_t)b * a.splits + split) * 4 + w;
+      const float m = a.part_ml[(slot * 16 + n16) * 2];
+      if (m == -__builtin_huge_valf()) continue;
+      const float e = __builtin_amdgcn_exp2f(m - M);
+      L += e * a.part_ml[(slot * 16 + n16) * 2 + 1];
+      const float4 v = reinterpret_cast<const float4 *>(a.part_o + (slot * 16 + n16) * D)[threadIdx.x];
+      o.x += e * v.x; o.y += e * v.y; o.z += e * v.z; o.w += e * v.w;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+  reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.heads + hh) * D)[threadIdx.x] = o;
+}
+
+template __global__ void attend_partial_kernel<1>(AttendArgs);
+template __global__ void attend_partial_kernel<2>(AttendArgs);
+template __global__ void attend_partial_kernel<4>(AttendArgs);
+
+}  // namespace csa2

@@ -1,0 +1,118 @@
+// Device-side helpers shared by the CSA2 kernels (gfx950, wave64).
+//
+// Format facts used here: FP4 E2M1 element codes with one E4M3 scale per 16
+// channels of the 512-channel latent (ailily.cc "890 bytes per token",
+// section 二 and 三); fixed-stride rows addressed by position index
+// (yomxxx.com long-form post, section 五).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int D = 512;            // latent channels
+constexpr int BLOCK = 8;          // positions per block
+constexpr int CODE_BYTES = 256;   // FP4 bytes per position
+constexpr int SCALE_BYTES = 32;   // E4M3 scales per position
+constexpr int GROUP = 16;         // channels per scale
+constexpr int NGROUPS = 32;
+constexpr int WAVE = 64;
+
+constexpr int HIST_BINS = 4096;   // first radix digit: top 12 bits of the score key
+constexpr int HIST_SHIFT = 20;
+
+// Device flag bits (mirrors include/csa2.h).
+constexpr uint32_t FLAG_NONFINITE_KV = 1, FLAG_CAPACITY = 2, FLAG_NONFINITE_Q = 4,
+                   FLAG_BAD_INDEX = 8;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Per-row control words of a workspace (one 64-byte line per sequence).
+struct Ctrl {
+  uint32_t arrive_scan;    // scan workgroups finished
+  uint32_t arrive_sel;     // select / rescore workgroups finished
+  uint32_t ncand;          // tie-bucket candidates collected
+  uint32_t thr_digit;      // top-12-bit digit holding the R-th largest key
+  uint32_t need;           // keys still to take from that digit
+  uint32_t all;            // 1: every block is selected (nblk <= R)
+  uint32_t pad[10];
+};
+
+// E4M3FN byte -> float (exact).  gfx950 decodes the OCP FN variant.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// Two E2M1 codes of byte `sel` (0..3) of w -> floats, low nibble first.
+// The hardware applies only the exponent of its scale operand, so it is
+// always called with 1.0 and the E4M3 scale is applied by the caller.
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+template <int SEL>
+__device__ __forceinline__ f16x2 e2m1x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// Valid positions of a sequence: seq_len clamped to [0, limit], where
+// limit = min(capacity, host max_len), so a bad length can never move an
+// access outside the cache.
+__device__ __forceinline__ int64_t clamp_len(int64_t n, int64_t limit) {
+  return n < 0 ? 0 : (n > limit ? limit : n);
+}
+
+// Order-preserving map of a float (no NaN) onto uint32.
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Device-wide flag word; read and cleared by csa2_device_error.
+extern __device__ uint32_t g_flags;
+__device__ __forceinline__ void raise_flag(uint32_t bit) {
+  __hip_atomic_fetch_or(&g_flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Load of a value another workgroup of the same kernel wrote (after the
+// arrive_last hand-off): agent-scope atomic load, coherent across XCDs.
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// "Last workgroup" hand-off: every workgroup of a grid row calls this once
+// after its global writes; exactly one (the last to arrive) gets true and,
+// after the acquire fence, sees every other workgroup's writes.  The caller
+// must be all threads of the workgroup.
+__device__ __forceinline__ bool arrive_last(uint32_t *counter, uint32_t expected) {
+  __shared__ uint32_t s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev + 1 == expected) ? 1u : 0u;
+  }
+  __syncthreads();
+  bool last = s_last != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+}  // namespace csa2

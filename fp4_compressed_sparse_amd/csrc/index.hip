@@ -1,0 +1,591 @@
+// Hierarchical sparse indexer of CSA2 (gfx950).
+//
+// Method: each layer picks the top-k most relevant blocks of 8 positions;
+// the first Full layer scans the whole range into a candidate pool
+// (2,048 blocks x 8 = 16,384 positions in the example) and later layers
+// search only the pool (rebasdaily.com "DeepSeek-V4.1-Flash KV
+// compression", section "same notes, many layers").  The cache rows are FP4
+// E2M1 codes with an E4M3 scale per 16 channels (ailily.cc "890 bytes per
+// token", section 二), read at a fixed stride and dequantised inside the
+// kernel (yomxxx.com long-form post, section 五).
+//
+// Score definition (the pages give none; this fixes one so that indices are
+// reproducible bit for bit):
+//   key[c]  = (rows of the block added in ascending position order, float32)
+//             / row count   (x 0.125 for a full block: exact)
+//   Qbar    = q_0 + q_1 + ... + q_{H-1}, float32, heads in order
+//   p_c     = fl(Qbar[c] * key[c])                  (never fused)
+//   g_j     = p_{16j} + ... + p_{16j+15}            left to right
+//   score   = adjacent-pair tree over g_0..g_31, plus 0.0 (no -0)
+// The row sum uses FMA: each dequantised value code*scale is exact in
+// float32, so fma(code, scale, acc) == fl(acc + code*scale).
+//
+// Work layout of the scan: 16 lanes per block, lane i owns channels
+// 32i..32i+31 (16 code bytes and 2 scale bytes of each of the 8 rows), so
+// every load instruction of a wave covers 4 blocks x 8 rows of 256-byte
+// contiguous runs; the two 16-channel groups of a lane are summed in-lane
+// and the tree's levels 2..5 are lane butterflies (xor 1, 2, 4, 8).
+//
+// Selection: keys are (order-preserving score bits << 32) | ~block_id, so
+// all keys differ and ties go to the lowest id.  The scan adds the top 12
+// key bits of every block to a histogram; the last scan workgroup finds the
+// digit that holds the R-th largest key.  The select kernel marks every
+// block above that digit in a bitmap and collects the digit's blocks; its
+// last workgroup finishes the choice among them with an LDS radix select,
+// then writes the chosen ids in ascending order by compacting the bitmap.
+#include "common.hpp"
+
+namespace csa2 {
+
+constexpr int SCAN_THREADS = 256;
+constexpr int BLOCKS_PER_ITER = 16;      // 4 waves x 4 blocks
+constexpr int LDS_KEYS = 8192;           // finisher key capacity (64 KB)
+
+struct ScanArgs {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const int64_t *seq_len;
+  int64_t capacity;
+  int64_t limit;            // min(capacity, max_len)
+  const float *q;
+  int32_t heads;
+  int32_t nblk_grid;        // blocks covered by the grid: ceil(max_len / 8)
+  float *scores;            // [batch][score_stride]
+  int64_t score_stride;
+  Ctrl *ctrl;               // [batch]
+  uint32_t *hist;           // [batch][HIST_BINS]
+  int32_t R;                // keys to select (pool or topk)
+  int32_t fill_invalid;     // write -inf for blocks >= nblk (export only)
+};
+
+// Qbar of sequence b into LDS (all threads call).
+__device__ __forceinline__ void compute_qbar(const float *__restrict__ q, int heads, int b,
+                                             float *s_qbar) {
+  const int t = threadIdx.x;
+  if (t < D / 4) {
+    const float4 *qp = reinterpret_cast<const float4 *>(q + (int64_t)b * heads * D) + t;
+    float4 acc = qp[0];
+    for (int h = 1; h < heads; ++h) {
+      float4 v = qp[(int64_t)h * (D / 4)];
+      acc.x = acc.x + v.x; acc.y = acc.y + v.y; acc.z = acc.z + v.z; acc.w = acc.w + v.w;
+    }
+    bool ok = __builtin_isfinite(acc.x) && __builtin_isfinite(acc.y) &&
+              __builtin_isfinite(acc.z) && __builtin_isfinite(acc.w);
+    if (!ok) raise_flag(FLAG_NONFINITE_Q);
+    reinterpret_cast<float4 *>(s_qbar)[t] = acc;
+  }
+  __syncthreads();
+}
+
+// Score of one block; the 16 lanes of a slot call it together (lane16 = i).
+// rowbase: address of the block's first row (codes), srow: its first scale
+// row.  cnt: rows present (1..8).  qb: this lane's 32 Qbar values.
+__device__ __forceinline__ float block_score(const uint8_t *__restrict__ rowbase,
+                                             const uint8_t *__restrict__ srow, int cnt, int i,
+                                             const float *qb) {
+  u32x4 w[BLOCK];
+  uint32_t sc[BLOCK];
+#pragma unroll
+  for (int t = 0; t < BLOCK; ++t) {
+    w[t] = *reinterpret_cast<const u32x4 *>(rowbase + (int64_t)t * CODE_BYTES + 16 * i);
+    sc[t] = *reinterpret_cast<const uint16_t *>(srow + (int64_t)t * SCALE_BYTES + 2 * i);
+  }
+  float S[32];
+#pragma unroll
+  for (int t = 0; t < BLOCK; ++t) {
+    if (t < cnt) {
+      const float s0 = e4m3_to_f32(sc[t] & 0xffu), s1 = e4m3_to_f32(sc[t] >> 8);
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) {
+        const float s = dw < 2 ? s0 : s1;
+        f32x2 v0 = e2m1x2_to_f32<0>(w[t][dw]);
+        f32x2 v1 = e2m1x2_to_f32<1>(w[t][dw]);
+        f32x2 v2 = e2m1x2_to_f32<2>(w[t][dw]);
+        f32x2 v3 = e2m1x2_to_f32<3>(w[t][dw]);
+        float *o = S + 8 * dw;
+        if (t == 0) {
+          o[0] = v0.x * s; o[1] = v0.y * s; o[2] = v1.x * s; o[3] = v1.y * s;
+          o[4] = v2.x * s; o[5] = v2.y * s; o[6] = v3.x * s; o[7] = v3.y * s;
+        } else {
+          o[0] = __builtin_fmaf(v0.x, s, o[0]); o[1] = __builtin_fmaf(v0.y, s, o[1]);
+          o[2] = __builtin_fmaf(v1.x, s, o[2]); o[3] = __builtin_fmaf(v1.y, s, o[3]);
+          o[4] = __builtin_fmaf(v2.x, s, o[4]); o[5] = __builtin_fmaf(v2.y, s, o[5]);
+          o[6] = __builtin_fmaf(v3.x, s, o[6]); o[7] = __builtin_fmaf(v3.y, s, o[7]);
+        }
+      }
+    }
+  }
+  float g0, g1;
+  if (cnt == BLOCK) {
+    g0 = qb[0] * (S[0] * 0.125f);
+#pragma unroll
+    for (int c = 1; c < 16; ++c) g0 = g0 + qb[c] * (S[c] * 0.125f);
+    g1 = qb[16] * (S[16] * 0.125f);
+#pragma unroll
+    for (int c = 17; c < 32; ++c) g1 = g1 + qb[c] * (S[c] * 0.125f);
+  } else {
+    const float fc = (float)cnt;
+    g0 = qb[0] * __fdiv_rn(S[0], fc);
+    for (int c = 1; c < 16; ++c) g0 = g0 + qb[c] * __fdiv_rn(S[c], fc);
+    g1 = qb[16] * __fdiv_rn(S[16], fc);
+    for (int c = 17; c < 32; ++c) g1 = g1 + qb[c] * __fdiv_rn(S[c], fc);
+  }
+  float v = g0 + g1;                    // tree level 1: groups 2i, 2i+1
+  v = v + __shfl_xor(v, 1);             // level 2
+  v = v + __shfl_xor(v, 2);             // level 3
+  v = v + __shfl_xor(v, 4);             // level 4
+  v = v + __shfl_xor(v, 8);             // level 5
+  return v + 0.0f;
+}
+
+// ---- block-level helpers (256 threads) ---------------------------------
+
+// Exclusive prefix sum over the threads of a workgroup of `nthreads`
+// (multiple of 64, <= 1024); returns the total in *total.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *total,
+                                                         uint32_t *s_wave) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t x = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_wave[wv] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+  for (int j = 0; j < nw; ++j) {
+    uint32_t s = s_wave[j];
+    if (j < wv) before += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+// Among keys[0..m) with valid[j] (LDS), find the key T such that exactly r
+// valid keys are >= T (keys distinct, 1 <= r <= #valid).  8-bit digits from
+// the top; stops as soon as a digit bucket is taken whole.
+__device__ uint64_t radix_threshold(const uint64_t *keys, const uint8_t *valid, int m, int r,
+                                    uint32_t *s_hist /*256*/, uint64_t *s_state /*2*/) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  uint64_t prefix = 0, pmask = 0;
+  int remaining = r;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int j = t; j < 256; j += nt) s_hist[j] = 0;
+    __syncthreads();
+    for (int j = t; j < m; j += nt) {
+      uint64_t k = keys[j];
+      if (valid[j] && (k & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (t < 64) {
+      // bins 255..0 in descending order: lane owns 4 bins, top lane first
+      uint32_t c[4], sum = 0;
+      for (int j = 0; j < 4; ++j) { c[j] = s_hist[255 - (4 * t + j)]; sum += c[j]; }
+      uint32_t x = sum;
+      for (int d = 1; d < 64; d <<= 1) {
+        uint32_t y = __shfl_up(x, d);
+        if (t >= d) x += y;
+      }
+      uint32_t above = x - sum;   // keys in higher bins than this lane's
+      if (above < (uint32_t)remaining && (uint32_t)remaining <= x) {
+        uint32_t acc = above;
+        for (int j = 0; j < 4; ++j) {
+          if (acc + c[j] >= (uint32_t)remaining) {
+            uint32_t d = 255 - (4 * t + j);
+            s_state[0] = prefix | ((uint64_t)d << shift);
+            // state[1]: remaining after this digit, with bit 63 = bucket taken whole
+            uint32_t rem = (uint32_t)remaining - acc;
+            s_state[1] = (uint64_t)rem | ((rem == c[j]) ? (1ull << 63) : 0ull);
+            break;
+          }
+          acc += c[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix = s_state[0];
+    pmask |= 0xFFull << shift;
+    uint64_t st = s_state[1];
+    __syncthreads();
+    remaining = (int)(uint32_t)st;
+    if (st >> 63) return prefix;   // every key with this prefix is taken
+  }
+  return prefix;
+}
+
+// ---- full scan ----------------------------------------------------------
+
+template <bool HIST>
+__global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
+  __shared__ float s_qbar[D];
+  __shared__ uint32_t s_hist[HIST ? HIST_BINS : 1];
+  __shared__ uint32_t s_wave[16];
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int slot = lane >> 4, i = lane & 15;
+  const int64_t n = clamp_len(a.seq_len[b], a.limit);
+  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  if (HIST) {
+    for (int j = threadIdx.x; j < HIST_BINS; j += SCAN_THREADS) s_hist[j] = 0;
+  }
+  compute_qbar(a.q, a.heads, b, s_qbar);
+  float qb[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) qb[c] = s_qbar[32 * i + c];
+
+  const uint8_t *codes = a.codes + (int64_t)b * a.capacity * CODE_BYTES;
+  const uint8_t *scales = a.scales + (int64_t)b * a.capacity * SCALE_BYTES;
+  float *scores = a.scores + (int64_t)b * a.score_stride;
+  const int iters = (a.nblk_grid + BLOCKS_PER_ITER - 1) / BLOCKS_PER_ITER;
+  for (int it = blockIdx.x; it < iters; it += gridDim.x) {
+    const int64_t blk = (int64_t)it * BLOCKS_PER_ITER + wv * 4 + slot;
+    if (blk < nblk) {
+      const int cnt = (int)min((int64_t)BLOCK, n - blk * BLOCK);
+      float s = block_score(codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES,
+                            cnt, i, qb);
+      if (i == 0) {
+        scores[blk] = s;
+        if (HIST) atomicAdd(&s_hist[ord_key(s) >> HIST_SHIFT], 1u);
+      }
+    } else if (a.fill_invalid && i == 0 && blk < a.score_stride) {
+      scores[blk] = -__builtin_huge_valf();
+    }
+  }
+  if (!HIST) return;
+  __syncthreads();
+  Ctrl *ctrl = a.ctrl + b;
+  uint32_t *gh = a.hist + (int64_t)b * HIST_BINS;
+  for (int j = threadIdx.x; j < HIST_BINS; j += SCAN_THREADS) {
+    uint32_t c = s_hist[j];
+    if (c) atomic_add_agent(gh + j, c);
+  }
+  if (!arrive_last(&ctrl->arrive_scan, gridDim.x)) return;
+  // last workgroup: locate the digit of the R-th largest key
+  const int t = threadIdx.x;
+  if ((int64_t)a.R >= nblk) {
+    if (t == 0) { ctrl->all = 1; ctrl->thr_digit = 0; ctrl->need = 0; }
+  } else {
+    // thread t owns bins [4096-16(t+1), 4096-16t), top thread first
+    uint32_t c[16], sum = 0;
+    for (int j = 0; j < 16; ++j) {
+      c[j] = __hip_atomic_load(gh + (HIST_BINS - 1 - (16 * t + j)), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      sum += c[j];
+    }
+    uint32_t total;
+    uint32_t above = block_exclusive_scan(sum, &total, s_wave);
+    const uint32_t R = (uint32_t)a.R;
+    if (above < R && R <= above + sum) {
+      uint32_t acc = above;
+      for (int j = 0; j < 16; ++j) {
+        if (acc + c[j] >= R) {
+          ctrl->thr_digit = HIST_BINS - 1 - (16 * t + j);
+          ctrl->need = R - acc;
+          ctrl->all = 0;
+          break;
+        }
+        acc += c[j];
+      }
+    }
+  }
+  __syncthreads();
+  for (int j = t; j < HIST_BINS; j += SCAN_THREADS) gh[j] = 0;
+  if (t == 0) ctrl->arrive_scan = 0;
+}
+
+// ---- select (after a full scan) ------------------------------------------
+
+struct SelectArgs {
+  const int64_t *seq_len;
+  int64_t limit;
+  const float *scores;      // [batch][score_stride]
+  int64_t score_stride;
+  Ctrl *ctrl;
+  uint32_t *bitmap;         // [batch][nwords]
+  int32_t nwords;           // per row, even
+  uint64_t *cands;          // [batch][cand_stride]
+  int64_t cand_stride;
+  int32_t R;                // first-level count (pool or topk)
+  int32_t *first_out;       // [batch][R]: pool_out, or idx_out when no pool
+  int32_t topk;             // second level (pool > 0) or 0
+  int32_t *idx_out;         // [batch][topk] when topk > 0
+  int32_t lds_keys;         // dynamic LDS keys (>= R, <= LDS_KEYS)
+};
+
+__device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
+  return ((uint64_t)ord_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+
+// Writes the ids of the set bits of bitmap[0..nwords) in ascending order to
+// out[0..len), padding with -1.  All threads.
+__device__ void compact_bitmap(const uint32_t *bm, int nwords, int32_t *out, int len,
+                               uint32_t *s_wave) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int per = (nwords + nt - 1) / nt;
+  const int w0 = min(nwords, t * per), w1 = min(nwords, w0 + per);
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(ld_agent(bm + w));
+  uint32_t total;
+  uint32_t off = block_exclusive_scan(cnt, &total, s_wave);
+  for (int w = w0; w < w1 && off < (uint32_t)len; ++w) {
+    uint32_t bits = ld_agent(bm + w);
+    while (bits && off < (uint32_t)len) {
+      int bpos = __ffs(bits) - 1;
+      bits &= bits - 1;
+      out[off++] = w * 32 + bpos;
+    }
+  }
+  for (int j = (int)total + t; j < len; j += nt) out[j] = -1;
+}
+
+// Top r of the m keys in s_keys (LDS) by flag, compacting the corresponding
+// ids (in stored order) into out[0..len) with -1 padding.  All threads.
+__device__ void select_in_lds(uint64_t *s_keys, uint8_t *s_valid, const int32_t *ids, int m,
+                              int r, int32_t *out, int len, uint32_t *s_hist,
+                              uint64_t *s_state, uint32_t *s_wave) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  uint32_t nvalid_local = 0;
+  for (int j = t; j < m; j += nt) nvalid_local += s_valid[j];
+  uint32_t nvalid;
+  (void)block_exclusive_scan(nvalid_local, &nvalid, s_wave);
+  r = min(r, (int)nvalid);
+  uint64_t T = r > 0 ? radix_threshold(s_keys, s_valid, m, r, s_hist, s_state) : ~0ull;
+  // ordered compaction of the kept entries; each thread owns a contiguous run
+  const int per = (m + nt - 1) / nt;
+  const int j0 = min(m, t * per), j1 = min(m, j0 + per);
+  uint32_t cnt = 0;
+  for (int j = j0; j < j1; ++j) cnt += (r > 0 && s_valid[j] && s_keys[j] >= T) ? 1u : 0u;
+  uint32_t total;
+  uint32_t off = block_exclusive_scan(cnt, &total, s_wave);
+  for (int j = j0; j < j1; ++j)
+    if (r > 0 && s_valid[j] && s_keys[j] >= T && off < (uint32_t)len) out[off++] = ids[j];
+  for (int j = (int)total + t; j < len; j += nt) out[j] = -1;
+}
+
+__global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
+  extern __shared__ uint64_t s_keys[];                 // LDS_KEYS
+  __shared__ uint8_t s_valid[LDS_KEYS];
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint64_t s_state[2];
+  __shared__ uint32_t s_wave[16];
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  Ctrl *ctrl = a.ctrl + b;
+  const int64_t n = clamp_len(a.seq_len[b], a.limit);
+  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  const float *scores = a.scores + (int64_t)b * a.score_stride;
+  uint32_t *bm = a.bitmap + (int64_t)b * a.nwords;
+  uint64_t *cands = a.cands + (int64_t)b * a.cand_stride;
+  const bool all = ctrl->all != 0;
+  const uint32_t thr = ctrl->thr_digit;
+  // 64 ids per wave step: ballot into two bitmap words
+  const int chunks = a.nwords / 2;
+  for (int ch = blockIdx.x * 4 + wv; ch < chunks; ch += gridDim.x * 4) {
+    const int64_t id = (int64_t)ch * 64 + lane;
+    bool in = false, tie = false;
+    uint32_t key_hi = 0;
+    if (id < nblk) {
+      if (all) {
+        in = true;
+      } else {
+        float s = scores[id];
+        key_hi = ord_key(s);
+        uint32_t dg = key_hi >> HIST_SHIFT;
+        in = dg > thr;
+        tie = dg == thr;
+      }
+    }
+    uint64_t m_in = __ballot(in);
+    if (lane == 0) { bm[2 * ch] = (uint32_t)m_in; bm[2 * ch + 1] = (uint32_t)(m_in >> 32); }
+    uint64_t m_tie = __ballot(tie);
+    if (m_tie) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomic_add_agent(&ctrl->ncand, (uint32_t)__popcll(m_tie));
+      base = __shfl(base, 0);
+      if (tie) {
+        uint32_t rank = (uint32_t)__popcll(m_tie & ((1ull << lane) - 1));
+        cands[base + rank] = ((uint64_t)key_hi << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+      }
+    }
+  }
+  if (!arrive_last(&ctrl->arrive_sel, gridDim.x)) return;
+
+  // ---- finisher: one workgroup per sequence ----
+  const int t = threadIdx.x, nt = blockDim.x;
+  if (!all && nblk > 0) {
+    const int c = (int)__hip_atomic_load(&ctrl->ncand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int need = (int)ctrl->need;
+    if (c <= a.lds_keys) {
+      for (int j = t; j < c; j += nt) { s_keys[j] = ld_agent(cands + j); s_valid[j] = 1; }
+      __syncthreads();
+      uint64_t T = radix_threshold(s_keys, s_valid, c, need, s_hist, s_state);
+      for (int j = t; j < c; j += nt) {
+        uint64_t k = s_keys[j];
+        if (k >= T) {
+          uint32_t id = 0xFFFFFFFFu - (uint32_t)k;
+          atomicOr(&bm[id >> 5], 1u << (id & 31));
+        }
+      }
+    } else {
+      // rare: the tie digit holds more keys than LDS; select through global
+      // memory one 8-bit digit at a time (same rule, slower)
+      uint64_t prefix = 0, pmask = 0;
+      int remaining = need;
+      for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int j = t; j < 256; j += nt) s_hist[j] = 0;
+        __syncthreads();
+        for (int j = t; j < c; j += nt) {
+          uint64_t k = ld_agent(cands + j);
+          if ((k & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(k >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (t == 0) {
+          uint32_t acc = 0;
+          for (int d = 255; d >= 0; --d) {
+            if (acc + s_hist[d] >= (uint32_t)remaining) {
+              s_state[0] = prefix | ((uint64_t)d << shift);
+              uint32_t rem = (uint32_t)remaining - acc;
+              s_state[1] = (uint64_t)rem | ((rem == s_hist[d]) ? (1ull << 63) : 0ull);
+              break;
+            }
+            acc += s_hist[d];
+          }
+        }
+        __syncthreads();
+        prefix = s_state[0];
+        pmask |= 0xFFull << shift;
+        uint64_t st = s_state[1];
+        __syncthreads();
+        remaining = (int)(uint32_t)st;
+        if (st >> 63) break;
+      }
+      for (int j = t; j < c; j += nt) {
+        uint64_t k = ld_agent(cands + j);
+        if (k >= prefix) {
+          uint32_t id = 0xFFFFFFFFu - (uint32_t)k;
+          atomicOr(&bm[id >> 5], 1u << (id & 31));
+        }
+      }
+    }
+    __threadfence_block();
+    __syncthreads();
+  }
+  int32_t *first = a.first_out + (int64_t)b * a.R;
+  compact_bitmap(bm, a.nwords, first, a.R, s_wave);
+  __syncthreads();
+  if (a.topk > 0) {
+    // top-k inside the pool: keys of the pool members, in pool order
+    const int m = a.R;
+    for (int j = t; j < m; j += nt) {
+      int32_t id = first[j];
+      s_valid[j] = id >= 0;
+      s_keys[j] = id >= 0 ? make_key(scores[id], (uint32_t)id) : 0ull;
+    }
+    __syncthreads();
+    select_in_lds(s_keys, s_valid, first, m, a.topk, a.idx_out + (int64_t)b * a.topk, a.topk,
+                  s_hist, s_state, s_wave);
+  }
+  __syncthreads();
+  for (int j = t; j < a.nwords; j += nt) bm[j] = 0;
+  if (t == 0) {
+    ctrl->ncand = 0;
+    ctrl->all = 0;
+    ctrl->need = 0;
+    ctrl->thr_digit = 0;
+    ctrl->arrive_sel = 0;
+  }
+}
+
+// ---- rescoring of a candidate list (pool) + top-k --------------------------
+
+struct RescoreArgs {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const int64_t *seq_len;
+  int64_t capacity;
+  int64_t limit;
+  const float *q;
+  int32_t heads;
+  const int32_t *cand;      // [batch][n_cand]
+  int32_t n_cand;
+  float *scores;            // [batch][score_stride]
+  int64_t score_stride;
+  Ctrl *ctrl;
+  int32_t topk;
+  int32_t *idx_out;         // [batch][topk]; NULL = scores only
+};
+
+template <bool SELECT>
+__global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
+  extern __shared__ uint64_t s_keys[];
+  __shared__ float s_qbar[D];
+  __shared__ uint8_t s_valid[SELECT ? LDS_KEYS : 1];
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint64_t s_state[2];
+  __shared__ uint32_t s_wave[16];
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int slot = lane >> 4, i = lane & 15;
+  const int64_t n = clamp_len(a.seq_len[b], a.limit);
+  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  compute_qbar(a.q, a.heads, b, s_qbar);
+  float qb[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) qb[c] = s_qbar[32 * i + c];
+  const uint8_t *codes = a.codes + (int64_t)b * a.capacity * CODE_BYTES;
+  const uint8_t *scales = a.scales + (int64_t)b * a.capacity * SCALE_BYTES;
+  const int32_t *cand = a.cand + (int64_t)b * a.n_cand;
+  float *scores = a.scores + (int64_t)b * a.score_stride;
+  const int iters = (a.n_cand + BLOCKS_PER_ITER - 1) / BLOCKS_PER_ITER;
+  for (int it = blockIdx.x; it < iters; it += gridDim.x) {
+    const int j = it * BLOCKS_PER_ITER + wv * 4 + slot;
+    if (j < a.n_cand) {
+      const int32_t blk = cand[j];
+      if (blk >= 0 && blk < nblk) {
+        const int cnt = (int)min((int64_t)BLOCK, n - (int64_t)blk * BLOCK);
+        float s = block_score(codes + (int64_t)blk * BLOCK * CODE_BYTES,
+                              scales + (int64_t)blk * BLOCK * SCALE_BYTES, cnt, i, qb);
+        if (i == 0) scores[j] = s;
+      } else {
+        if (i == 0) {
+          scores[j] = -__builtin_huge_valf();
+          if (blk >= nblk) raise_flag(FLAG_BAD_INDEX);
+        }
+      }
+    }
+  }
+  if (!SELECT) return;
+  Ctrl *ctrl = a.ctrl + b;
+  if (!arrive_last(&ctrl->arrive_sel, gridDim.x)) return;
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int m = a.n_cand;
+  for (int j = t; j < m; j += nt) {
+    int32_t id = cand[j];
+    bool ok = id >= 0 && id < nblk;
+    s_valid[j] = ok;
+    s_keys[j] = ok ? make_key(ld_agent(scores + j), (uint32_t)id) : 0ull;
+  }
+  __syncthreads();
+  select_in_lds(s_keys, s_valid, cand, m, a.topk, a.idx_out + (int64_t)b * a.topk, a.topk,
+                s_hist, s_state, s_wave);
+  __syncthreads();
+  if (t == 0) ctrl->arrive_sel = 0;
+}
+
+// Reuse: idx_out = prior (grid-stride copy).
+__global__ void __launch_bounds__(256) copy_idx_kernel(const int32_t *__restrict__ src,
+                                                       int32_t *__restrict__ dst, int64_t n) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n;
+       j += (int64_t)gridDim.x * blockDim.x)
+    dst[j] = src[j];
+}
+
+// Explicit instantiations used by the host layer.
+template __global__ void scan_kernel<true>(ScanArgs);
+template __global__ void scan_kernel<false>(ScanArgs);
+template __global__ void rescore_kernel<true>(RescoreArgs);
+template __global__ void rescore_kernel<false>(RescoreArgs);
+
+}  // namespace csa2

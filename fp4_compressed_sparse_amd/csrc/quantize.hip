@@ -1,0 +1,157 @@
+// FP4 quantiser / packer of the global-KV cache (gfx950).
+//
+// One position is the 512-channel latent stored as E2M1 codes with one E4M3
+// scale per 16 channels (ailily.cc "890 bytes per token", section 二; the
+// representable maximum 448 x 6 = 2688 of section 三 leaves no room for a
+// second, per-tensor scale).  Rows sit at a fixed stride so a kernel finds
+// a position from its index (yomxxx.com long-form post, section 五).
+//
+// Rounding (the pages give none): scale = E4M3 nearest to amax/6, ties to
+// the even code, saturating at 448; code = E2M1 nearest to |x|/scale, ties
+// to even, saturating at 6; the sign bit is kept (-0 -> 0x8).  Both
+// decisions are made exactly by comparing against exact products:
+//   amax <> 6 * (midpoint of two E4M3 values)   (<= 8 significant bits)
+//   |x|  <> scale * (midpoint of two E2M1 values) (<= 7 significant bits)
+// so no division is ever rounded.
+//
+// Thread layout: 4 lanes per 16-channel group, 4 channels (one float4) per
+// lane, 128 lanes per row: loads of 1 KB per wave instruction, 128-byte
+// code stores, one scale byte per group.
+#include "common.hpp"
+
+namespace csa2 {
+
+__device__ uint32_t g_flags = 0;
+
+// E4M3 value of a non-negative code 0..126.
+__device__ __forceinline__ float e4m3_pos(uint32_t c) { return e4m3_to_f32(c); }
+
+// Exact E4M3 code of RNE(amax / 6), saturating.  amax >= 0, finite.
+__device__ __forceinline__ uint32_t scale_code(float amax) {
+  // 6 * midpoint(416, 448) = 2592: anything at or above rounds to 448 (0x7E, even)
+  if (amax >= 2592.0f) return 0x7Eu;
+  // estimate from y ~ amax/6 (at most one code off), then fix exactly
+  float y = amax * (1.0f / 6.0f);
+  uint32_t c;
+  if (y < 0.015625f) {
+    c = (uint32_t)__builtin_rintf(y * 512.0f);          // subnormal codes 0..8
+  } else {
+    uint32_t u = __float_as_uint(y);
+    int e = (int)(u >> 23) - 127;                        // -6 .. 8
+    c = (uint32_t)(((e + 7) << 3) | ((u >> 20) & 7u));
+    c = c > 126u ? 126u : c;
+  }
+  // threshold between codes k and k+1, times 6: 3 * (v_k + v_{k+1}), exact
+  while (c < 126u) {
+    float t = 3.0f * (e4m3_pos(c) + e4m3_pos(c + 1));
+    if (amax > t || (amax == t && ((c + 1) & 1u) == 0)) ++c; else break;
+  }
+  while (c > 0u) {
+    float t = 3.0f * (e4m3_pos(c - 1) + e4m3_pos(c));
+    if (amax < t || (amax == t && (c & 1u))) --c; else break;
+  }
+  return c;
+}
+
+// E2M1 magnitude code (0..7) of RNE(a / s) given t[k] = s * midpoint_k.
+__device__ __forceinline__ uint32_t mag_code(float a, const float *t) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) c += (a > t[k]) ? 1u : 0u;
+  // ties at the midpoints 0.75, 1.75, 3.5 (k odd) go up to the even code
+  c += (a == t[1] || a == t[3] || a == t[5]) ? 1u : 0u;
+  return c;
+}
+
+// Quantise one float4 (channels 4q..4q+3 of a row); all 4 lanes of a group
+// must call together.  Returns the 16-bit packed codes; *sbyte the scale.
+__device__ __forceinline__ uint32_t quantize_quad(float4 v, uint32_t *sbyte, bool *bad) {
+  float ax = fabsf(v.x), ay = fabsf(v.y), az = fabsf(v.z), aw = fabsf(v.w);
+  bool nf = !(__builtin_isfinite(v.x) && __builtin_isfinite(v.y) &&
+              __builtin_isfinite(v.z) && __builtin_isfinite(v.w));
+  float amax = fmaxf(fmaxf(ax, ay), fmaxf(az, aw));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  int nfi = nf ? 1 : 0;
+  nfi |= __shfl_xor(nfi, 1);
+  nfi |= __shfl_xor(nfi, 2);
+  *bad = nfi != 0;
+  if (nfi) { *sbyte = 0; return 0; }
+  uint32_t sc = scale_code(amax);
+  float s = e4m3_pos(sc);
+  *sbyte = sc;
+  if (s == 0.0f) {
+    // magnitudes all round to 0; keep the signs
+    return ((__float_as_uint(v.x) >> 31) << 3) | ((__float_as_uint(v.y) >> 31) << 7) |
+           ((__float_as_uint(v.z) >> 31) << 11) | ((__float_as_uint(v.w) >> 31) << 15);
+  }
+  float t[7] = {s * 0.25f, s * 0.75f, s * 1.25f, s * 1.75f, s * 2.5f, s * 3.5f, s * 5.0f};
+  uint32_t n0 = mag_code(ax, t) | ((__float_as_uint(v.x) >> 31) << 3);
+  uint32_t n1 = mag_code(ay, t) | ((__float_as_uint(v.y) >> 31) << 3);
+  uint32_t n2 = mag_code(az, t) | ((__float_as_uint(v.z) >> 31) << 3);
+  uint32_t n3 = mag_code(aw, t) | ((__float_as_uint(v.w) >> 31) << 3);
+  return n0 | (n1 << 4) | (n2 << 8) | (n3 << 12);
+}
+
+// rows x 512 floats -> codes/scales rows dst_row[r] (or r).
+__global__ void __launch_bounds__(256) quantize_rows_kernel(
+    const float *__restrict__ x, int64_t rows, const int64_t *__restrict__ dst_row,
+    int64_t dst_rows, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+  const int64_t total = rows * 128;  // a multiple of 64: whole waves stay together
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    int64_t r = i >> 7;
+    int q = (int)(i & 127);
+    float4 v = reinterpret_cast<const float4 *>(x)[i];
+    uint32_t sb;
+    bool bad;
+    uint32_t packed = quantize_quad(v, &sb, &bad);
+    int64_t d = dst_row ? dst_row[r] : r;
+    if (d < 0 || d >= dst_rows) {
+      if ((q & 127) == 0) raise_flag(FLAG_CAPACITY);
+      continue;
+    }
+    if (bad && (q & 3) == 0) raise_flag(FLAG_NONFINITE_KV);
+    reinterpret_cast<uint16_t *>(codes + d * CODE_BYTES)[q] = (uint16_t)packed;
+    if ((q & 3) == 0) scales[d * SCALE_BYTES + (q >> 2)] = (uint8_t)sb;
+  }
+}
+
+// Caches appended in one launch (decode step: one row per sequence each).
+struct AppendArgs {
+  uint8_t *codes[16];
+  uint8_t *scales[16];
+  int64_t *seq_len[16];
+  int64_t capacity[16];
+};
+
+// grid (batch, n_caches), 128 threads: x[c][b][512] -> position seq_len[b].
+__global__ void __launch_bounds__(128) append_kernel(AppendArgs a, const float *__restrict__ x,
+                                                     int32_t batch) {
+  const int b = blockIdx.x, c = blockIdx.y;
+  const int q = threadIdx.x;
+  int64_t *len = a.seq_len[c] + b;
+  const int64_t pos = *len;
+  float4 v = reinterpret_cast<const float4 *>(x + ((int64_t)c * batch + b) * D)[q];
+  uint32_t sb;
+  bool bad;
+  uint32_t packed = quantize_quad(v, &sb, &bad);
+  if (pos < 0 || pos >= a.capacity[c]) {
+    if (q == 0) raise_flag(FLAG_CAPACITY);
+    return;
+  }
+  if (bad && (q & 3) == 0) raise_flag(FLAG_NONFINITE_KV);
+  const int64_t row = (int64_t)b * a.capacity[c] + pos;
+  reinterpret_cast<uint16_t *>(a.codes[c] + row * CODE_BYTES)[q] = (uint16_t)packed;
+  if ((q & 3) == 0) a.scales[c][row * SCALE_BYTES + (q >> 2)] = (uint8_t)sb;
+  __syncthreads();
+  if (q == 0) *len = pos + 1;
+}
+
+// Zero fill (graph-safe replacement for memset).
+__global__ void __launch_bounds__(256) zero_kernel(uint32_t *__restrict__ p, int64_t words) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride) p[i] = 0;
+}
+
+}  // namespace csa2

@@ -103,17 +103,18 @@ def e2m1_magnitude_code(absx, s):
     """3-bit magnitude code of RNE(|x| / s), saturating at 6; 0 where s == 0.
 
     Compared as |x| <> s*mid: s has at most 4 significant bits and each
-    midpoint at most 3, so s*mid is exact.
+    midpoint at most 3, so s*mid is exact.  The code is the number of
+    midpoints strictly below |x|, plus one when |x| sits exactly on a
+    midpoint whose upper neighbour has the even code (0.75, 1.75, 3.5).
     """
     absx = np.asarray(absx, dtype=np.float64)
-    s = np.asarray(s, dtype=np.float64)
-    s_b = np.broadcast_to(s, absx.shape)
-    thr = s_b[..., None] * E2M1_MIDPOINTS            # [..., 7], exact
-    below = thr < absx[..., None]
-    k = below.sum(axis=-1)
-    kk = np.minimum(k, 6)
-    tie = (k < 7) & (np.take_along_axis(thr, kk[..., None], -1)[..., 0] == absx)
-    code = np.where(tie & (k % 2 == 1), k + 1, k)
+    s_b = np.broadcast_to(np.asarray(s, dtype=np.float64), absx.shape)
+    code = np.zeros(absx.shape, dtype=np.uint8)
+    for k, mid in enumerate(E2M1_MIDPOINTS):
+        thr = s_b * mid                                   # exact
+        code += (absx > thr)
+        if k % 2 == 1:                                    # tie between codes k and k+1, k+1 even
+            code += (absx == thr)
     return np.where(s_b == 0, 0, code).astype(np.uint8)
 
 

@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every entry point include/csa2.h
+declares, and rejects malformed arguments on the host before any launch.
+Runs without a GPU: nothing here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_compressed_sparse_amd as csa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(?:csa2_status|size_t|const char \*)\s*\*?\s*(\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(csa2.LIB_PATH):
+        pytest.fail("libcsa2.so is not built; run __graft_entry__.build()")
+    return csa2.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(csa2.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.csa2_status_string(0) == b"ok"
+    assert lib.csa2_status_string(3) == b"workspace too small"
+    assert lib.csa2_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes_host_only(lib):
+    n3 = lib.csa2_workspace_bytes(1, 64, (1 << 20) + 64, 2048, 256)
+    assert n3 > 0 and n3 % 256 == 0
+    # bigger bounds never need less
+    assert lib.csa2_workspace_bytes(2, 64, (1 << 20) + 64, 2048, 256) > n3
+    assert lib.csa2_workspace_bytes(1, 64, 4096, 0, 64) < n3
+    # unsupported bounds give 0
+    assert lib.csa2_workspace_bytes(0, 64, 4096, 0, 64) == 0
+    assert lib.csa2_workspace_bytes(1, 65, 4096, 0, 64) == 0
+    assert lib.csa2_workspace_bytes(1, 16, 4096, 0, 4096) == 0
+    assert lib.csa2_workspace_bytes(1, 16, 4096, 9000, 64) == 0
+
+
+def _err(lib):
+    return lib.csa2_last_error().decode()
+
+
+def test_quantize_argument_errors(lib):
+    assert lib.fp4_quantize_kv(None, 0, None, 0, None, None, None) == 0     # no-op
+    assert lib.fp4_quantize_kv(None, -1, None, 0, None, None, None) == 1
+    assert lib.fp4_quantize_kv(None, 4, None, 4, None, None, None) == 1
+    assert "NULL" in _err(lib)
+    assert lib.fp4_quantize_kv(ctypes.c_void_p(0x1004), 4, None, 4, ctypes.c_void_p(0x2000),
+                               ctypes.c_void_p(0x3000), None) == 1          # x misaligned
+    assert lib.fp4_quantize_kv(ctypes.c_void_p(0x1000), 4, None, 3, ctypes.c_void_p(0x2000),
+                               ctypes.c_void_p(0x3000), None) == 4          # too few rows
+
+
+def _kv(**kw):
+    base = dict(codes=0x10000, scales=0x20000, seq_len=0x30000, capacity=4096, max_len=4096, batch=1)
+    base.update(kw)
+    return csa2._Kv(base["codes"], base["scales"], base["seq_len"], base["capacity"],
+                    base["max_len"], base["batch"])
+
+
+def test_index_and_attend_argument_errors(lib):
+    idx = ctypes.c_void_p(0x40000)
+    q = ctypes.c_void_p(0x50000)
+    ws = ctypes.c_void_p(0x60000)
+    need = lib.csa2_workspace_bytes(1, 16, 4096, 0, 64)
+    call = lambda mode, kv, heads=16, topk=64, pool=0, wsb=need, cand=None, n_cand=0: lib.csa2_index_topk(
+        mode, ctypes.byref(kv), q, heads, cand, n_cand, topk, idx, pool, None, None, ws, wsb, None)
+    assert call(7, _kv()) == 1                                   # bad mode
+    assert call(0, _kv(codes=0x10010)) == 1                      # misaligned codes
+    assert call(0, _kv(capacity=4092)) == 2                      # capacity not a multiple of 8
+    assert call(0, _kv(max_len=5000)) == 4                       # max_len > capacity
+    assert call(0, _kv(), heads=0) == 2
+    assert call(0, _kv(), topk=0) == 2
+    assert call(0, _kv(), topk=128, pool=64) == 1                # pool < topk
+    assert call(0, _kv(), wsb=need - 1) == 3                     # workspace too small
+    assert "workspace" in _err(lib)
+    assert call(2, _kv()) == 1                                   # Reuse without prior_idx
+    out = ctypes.c_void_p(0x70000)
+    assert lib.csa2_sparse_attend(ctypes.byref(_kv()), q, 24, idx, 64, ctypes.c_float(0.04), out, ws,
+                                  need, None) == 2               # 24 heads unsupported
+    assert lib.csa2_sparse_attend(ctypes.byref(_kv()), q, 16, idx, 64, ctypes.c_float(float("nan")),
+                                  out, ws, need, None) == 1
+
+
+def test_decode_step_pattern_errors(lib):
+    kv = (csa2._Kv * 2)(_kv(), _kv())
+    q, out, idx = 0x50000, 0x70000, 0x40000
+    ws = 0x100000
+    need = lib.csa2_workspace_bytes(1, 16, 4096, 0, 64)
+
+    def step(layers, heads=16, pool=0):
+        arr = (csa2._Layer * len(layers))(*[csa2._Layer(m, c, q, out, idx) for m, c in layers])
+        st = csa2._Step(kv, 2, arr, len(layers), None, heads, 64, pool, 0.04, None, ws, need)
+        return lib.csa2_decode_step(ctypes.byref(st), None)
+
+    assert step([(1, 0)]) == 1                  # Reindex first
+    assert step([(2, 0)]) == 1                  # Reuse first
+    assert step([(0, 0), (1, 1)]) == 1          # Reindex on a stale cache
+    assert step([(0, 0), (0, 1), (1, 0)]) == 1  # Reindex must use the latest Full cache
+    assert step([(0, 0)], heads=48) == 2
+    assert step([(0, 0)], pool=64) == 1         # pool > 0 without pool_out

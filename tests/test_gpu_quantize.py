@@ -1,0 +1,141 @@
+"""GPU quantiser and append vs the oracle: codes and scales byte-equal."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_compressed_sparse_amd as csa2
+import workloads as W
+from oracle import formats as F
+from oracle import quantize as Q
+from tests._gpu import log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _edge_rows():
+    """Rows that sit on every rounding boundary of both formats."""
+    rows = []
+    e4 = F.E4M3_TABLE[:0x7F].astype(np.float64)
+    mids = (e4[:-1] + e4[1:]) / 2
+    # amax exactly on 6 * every E4M3 midpoint, and one float32 ulp either side
+    for k, m in enumerate(mids):
+        a = np.float32(6 * m)
+        for v in (a, np.nextafter(a, np.float32(0)), np.nextafter(a, np.float32(1e9))):
+            r = np.zeros(Q.D, dtype=np.float32)
+            r[(k % 32) * 16 + (k % 16)] = v if k % 3 else -v
+            rows.append(r)
+    # E2M1 ties: |x| = s * midpoint with s = 1 (amax = 6) and other scales
+    for sb in (0x01, 0x07, 0x08, 0x30, 0x38, 0x3B, 0x55, 0x7E):
+        s = F.e4m3_value(sb)
+        r = np.zeros(Q.D, dtype=np.float32)
+        for g in range(Q.NGROUPS):
+            r[16 * g] = 6 * s
+            for j, mid in enumerate(F.E2M1_MIDPOINTS):
+                r[16 * g + 1 + j] = np.float32(s * mid) * (1 if j % 2 else -1)
+                r[16 * g + 8 + j] = np.nextafter(np.float32(s * mid), np.float32(0))
+        rows.append(r)
+    # saturation, zeros, signed zeros, tiny values
+    rows.append(np.full(Q.D, 3000.0, dtype=np.float32))
+    rows.append(np.full(Q.D, -1e30, dtype=np.float32))
+    rows.append(np.zeros(Q.D, dtype=np.float32))
+    rows.append(-np.zeros(Q.D, dtype=np.float32))
+    rows.append(np.full(Q.D, 1e-30, dtype=np.float32))
+    rows.append(np.full(Q.D, 2.0 ** -10 * 6, dtype=np.float32))
+    rng = np.random.default_rng(7)
+    for _ in range(64):
+        rows.append((rng.standard_normal(Q.D) * 2.0 ** rng.uniform(-24, 14, Q.D)).astype(np.float32))
+    return np.stack(rows)
+
+
+def _gpu_quantize(x, dst_row=None, dst_rows=None):
+    n = dst_rows if dst_rows is not None else x.shape[0]
+    codes = torch.full((n, Q.CODE_BYTES), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((n, Q.SCALE_BYTES), 0xCD, dtype=torch.uint8, device="cuda")
+    xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    dr = None if dst_row is None else torch.from_numpy(dst_row).cuda()
+    csa2.fp4_quantize_kv(xt, codes, scales, dst_row=dr)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def test_edge_rows_bit_exact():
+    require_gpu()
+    x = _edge_rows()
+    log(f"quantize edge rows: {x.shape}")
+    c, s = _gpu_quantize(x)
+    oc, os_ = Q.quantize_rows(x)
+    assert np.array_equal(s, os_), np.argwhere(s != os_)[:5]
+    assert np.array_equal(c, oc), np.argwhere(c != oc)[:5]
+    assert csa2.device_error() == 0
+
+
+def test_workload_rows_bit_exact_and_ragged_count():
+    require_gpu()
+    x = W.kv_rows(4, 0, 3, 1000, 8191)          # odd row count: partial last workgroup
+    c, s = _gpu_quantize(x)
+    oc, os_ = Q.quantize_rows(x)
+    assert np.array_equal(c, oc) and np.array_equal(s, os_)
+
+
+def test_dst_rows_and_capacity_flag():
+    require_gpu()
+    x = W.kv_rows(4, 1, 0, 0, 64)
+    perm = np.random.default_rng(3).permutation(100)[:64].astype(np.int64)
+    perm[5] = 100          # out of range: skipped and flagged
+    c, s = _gpu_quantize(x, dst_row=perm, dst_rows=100)
+    oc, os_ = Q.quantize_rows(x)
+    for i, d in enumerate(perm):
+        if d < 100:
+            assert np.array_equal(c[d], oc[i]) and np.array_equal(s[d], os_[i])
+    untouched = sorted(set(range(100)) - set(perm.tolist()))
+    assert np.all(c[untouched] == 0xAB)
+    assert csa2.device_error() & csa2.FLAG_CAPACITY
+
+
+def test_non_finite_group_flagged():
+    require_gpu()
+    x = W.kv_rows(4, 1, 0, 0, 4)
+    x[1, 37] = np.inf
+    x[2, 300] = np.nan
+    c, s = _gpu_quantize(x)
+    assert csa2.device_error() & csa2.FLAG_NONFINITE_KV
+    assert np.all(c[1, 16:24] == 0) and s[1, 2] == 0
+    assert np.all(c[2, 144:152] == 0) and s[2, 18] == 0
+    oc, os_ = Q.quantize_rows(x[[0, 3]])
+    assert np.array_equal(c[[0, 3]], oc) and np.array_equal(s[[0, 3]], os_)
+
+
+def test_append_and_full_cache():
+    require_gpu()
+    cache = csa2.KVCache(3, 16)
+    cache.seq_len.copy_(torch.tensor([0, 7, 16]))
+    rows = W.append_rows(4, 0, 0, 3)
+    csa2.append_kv(cache, torch.from_numpy(rows).cuda())
+    torch.cuda.synchronize()
+    assert cache.seq_len.cpu().tolist() == [1, 8, 16]
+    assert csa2.device_error() & csa2.FLAG_CAPACITY
+    oc, os_ = Q.quantize_rows(rows)
+    codes, scales = cache.codes.cpu().numpy(), cache.scales.cpu().numpy()
+    assert np.array_equal(codes[0, 0], oc[0]) and np.array_equal(scales[0, 0], os_[0])
+    assert np.array_equal(codes[1, 7], oc[1]) and np.array_equal(scales[1, 7], os_[1])
+
+
+def test_prefill_write_full_size_sampled():
+    """The batch-64 prefill write: 16,384 fresh rows per sequence (1,048,576
+    rows); oracle on a sample of 4,096 rows spread over every sequence."""
+    require_gpu()
+    B, N = 64, W.PREFILL_WRITE_ROWS
+    cache = csa2.KVCache(B, N)
+    xs_all = W.kv_rows_threaded(4, 9, 0, B * N)          # sequence b = rows b*N .. b*N+N-1
+    log("prefill write: rows generated")
+    x = torch.from_numpy(xs_all).cuda()
+    csa2.fp4_quantize_kv(x, cache.codes.view(-1, Q.CODE_BYTES), cache.scales.view(-1, Q.SCALE_BYTES))
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(B * N, 4096, replace=False))
+    oc, os_ = Q.quantize_rows(xs_all[rows])
+    sel = torch.from_numpy(rows).cuda()
+    gc = cache.codes.view(-1, Q.CODE_BYTES)[sel].cpu().numpy()
+    gs = cache.scales.view(-1, Q.SCALE_BYTES)[sel].cpu().numpy()
+    assert np.array_equal(gc, oc) and np.array_equal(gs, os_)

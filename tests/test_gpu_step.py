@@ -1,0 +1,81 @@
+"""GPU layer-stack driver vs the oracle over whole decode steps: every
+layer's selection (and the pool) byte-equal, every output within 2e-3.
+The workloads keep their layer patterns, heads, top-k and pool; contexts
+are cut so the oracle finishes in seconds (full sizes: test_gpu_fullsize)."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_compressed_sparse_amd as csa2
+import workloads as W
+from oracle.step import decode_step as oracle_step
+from tests._gpu import ATT_TOL, cap_for, log, normwise_err, oracle_cache, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_compare(w, lengths, steps):
+    require_gpu()
+    lengths = np.asarray(lengths, dtype=np.int64)
+    B = len(lengths)
+    cap = cap_for(int(lengths.max()), steps if w.append else 0)
+    ocs = [oracle_cache(w.wid, c, lengths, cap) for c in range(w.n_caches)]
+    gcs = [to_device(oc) for oc in ocs]
+    caches_of = w.layer_caches()
+    L = len(w.pattern)
+    max_len = int(lengths.max()) + (steps if w.append else 0)
+    ws = csa2.workspace(B, w.heads, max_len, w.pool, w.topk)
+    pool_out = torch.zeros((B, w.pool), dtype=torch.int32, device="cuda") if w.pool else None
+    for step in range(steps):
+        qs = [W.queries(w.wid, l, step, B, w.heads) for l in range(L)]
+        new_rows = np.stack([W.append_rows(w.wid, c, step, B) for c in range(w.n_caches)]) if w.append else None
+        ref = oracle_step(ocs, [(m, caches_of[l], qs[l]) for l, m in enumerate(w.pattern)],
+                          new_rows, w.topk, w.pool, w.scale)
+        for g in gcs:
+            g.max_len = int(lengths.max()) + ((step + 1) if w.append else 0)
+        qt = [torch.from_numpy(q).cuda() for q in qs]
+        outs = [torch.zeros((B, w.heads, 512), dtype=torch.float32, device="cuda") for _ in range(L)]
+        idxs = [torch.full((B, w.topk), -9, dtype=torch.int32, device="cuda") for _ in range(L)]
+        layers = [(m, caches_of[l], qt[l], outs[l], idxs[l]) for l, m in enumerate(w.pattern)]
+        nr = torch.from_numpy(new_rows).cuda() if new_rows is not None else None
+        csa2.decode_step(gcs, layers, w.heads, w.topk, w.pool, w.scale, ws, pool_out=pool_out, new_rows=nr)
+        torch.cuda.synchronize()
+        assert csa2.device_error() == 0
+        for c, (g, oc) in enumerate(zip(gcs, ocs)):
+            assert np.array_equal(g.seq_len.cpu().numpy(), oc.seq_len)
+        if w.pool:
+            assert np.array_equal(pool_out.cpu().numpy(), ref["pool"]), step
+        worst = 0.0
+        for l in range(L):
+            gi = idxs[l].cpu().numpy()
+            assert np.array_equal(gi, ref["idx"][l]), (step, l, w.pattern[l])
+            err = normwise_err(outs[l].cpu().numpy(), ref["out"][l])
+            worst = max(worst, err)
+            assert err <= ATT_TOL, (step, l, err)
+        log(f"{w.name} step {step}: idx equal on {L} layers, worst attention error {worst:.2e}")
+
+
+def test_workload0_single_full_4k():
+    w = W.WORKLOADS[0]
+    run_and_compare(w, [w.context], 1)
+
+
+def test_workload1_full_reindex_reuse_b4():
+    w = W.scaled(W.WORKLOADS[1], context=8192)
+    run_and_compare(w, [8192] * 4, 1)
+
+
+def test_workload2_hierarchical_pool():
+    w = W.scaled(W.WORKLOADS[2], context=32768)
+    run_and_compare(w, [32768], 1)
+
+
+def test_workload3_twenty_layers_appending():
+    w = W.scaled(W.WORKLOADS[3], context=20000)
+    run_and_compare(w, [20000 - 3], 3)
+
+
+def test_workload4_ragged_batch_appending():
+    w = W.scaled(W.WORKLOADS[4], context=0, batch=6)
+    lengths = np.random.default_rng(4).integers(4000, 20000, 6)
+    run_and_compare(w, lengths, 2)

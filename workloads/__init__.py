@@ -133,6 +133,22 @@ def kv_chunks(wid, cache, seq, count):
         yield c * CHUNK, rows[:n]
 
 
+def kv_rows_threaded(wid, cache, seq, count, threads=8):
+    """kv_rows(wid, cache, seq, 0, count), chunks drawn on a thread pool
+    (each chunk has its own seed, so the result does not depend on threads)."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty((count, D), dtype=np.float32)
+    nchunk = (count + CHUNK - 1) // CHUNK
+
+    def one(c):
+        n = min(CHUNK, count - c * CHUNK)
+        out[c * CHUNK:c * CHUNK + n] = _kv_chunk(wid, cache, seq, c)[:n]
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, range(nchunk)))
+    return out
+
+
 def queries(wid, layer, step, batch, heads):
     """Query heads of one layer at one step -> float32 [B, H, 512]."""
     return _rng(wid, STREAM_Q, layer, step).standard_normal((batch, heads, D), dtype=np.float32)
