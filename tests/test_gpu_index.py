@@ -50,7 +50,7 @@ def test_block_scores_candidates():
     g = to_device(oc)
     q = W.queries(0, 6, 0, 2, 16)
     rng = np.random.default_rng(1)
-    cand = np.stack([rng.permutation(251)[:100], rng.permutation(376)[:100]]).astype(np.int32)
+    cand = np.stack([rng.permutation(250)[:100], rng.permutation(376)[:100]]).astype(np.int32)
     cand[0, 7] = -1
     got = _scores_gpu(g, q, cand)
     for b, n in enumerate(lengths):
