@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the CSA2 FP4 global-KV hot path on one MI355X.
+
+One step = one decode step of the whole hot path for the 20-layer decoder
+pattern [Full, Reindex, Reuse, Reuse, Reindex] x 4 at a 1,048,576-position
+context (batch 1, 64 heads, pool 2,048 blocks, top-256): append one
+quantised row to each of the 4 Full caches, full-range scan of the first Full
+layer into the pool, top-k, pool rescoring in the 11 later selecting layers,
+Reuse forwarding and sparse attention in all 20 layers.  Inputs (caches,
+queries, appended rows) are synthetic and resident in HBM before timing.
+
+Prints one JSON line (metric, value = decode tokens/s, roofline of the
+dominant kernel, CPU-oracle baseline).  Progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1]
+  python bench.py --copy-probe     (plain copy kernel for counter calibration)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+TOKEN_BYTES = 288              # 256 code bytes + 32 scale bytes per position
+BLOCK_BYTES = 8 * TOKEN_BYTES  # 2,304
+PMC_FILE = os.path.join(ROOT, "profiles", "scan_kernel_decoder20-1m_pmc.json")
+SCAN_SOURCES = [os.path.join(ROOT, "fp4_compressed_sparse_amd", "csrc", f)
+                for f in ("index.hip", "common.hpp")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def scan_source_sha():
+    h = hashlib.sha256()
+    for p in SCAN_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def step_bytes(w, n_tokens):
+    """Algorithmic KV bytes of one step: (unique, touched), per sequence
+    lengths n_tokens (after the append)."""
+    unique = touched = 0
+    for n in n_tokens:
+        nblk = (n + 7) // 8
+        first = True
+        pool_blocks = min(w.pool, nblk) if w.pool else 0
+        full_count = 0
+        for m in w.pattern:
+            if m != 2:                         # selecting layer
+                if first:
+                    touched += n * TOKEN_BYTES
+                    unique += n * TOKEN_BYTES
+                    first = False
+                elif w.pool:
+                    touched += pool_blocks * BLOCK_BYTES
+                    if m == 0:                 # a later Full layer reads its own cache's pool blocks
+                        unique += pool_blocks * BLOCK_BYTES
+                else:
+                    touched += n * TOKEN_BYTES
+                    if m == 0:
+                        unique += n * TOKEN_BYTES
+            if m == 0:
+                full_count += 1
+            touched += min(w.topk, nblk) * BLOCK_BYTES   # attention gather
+    return unique, touched
+
+
+def build_caches(w, lengths, capacity, log_every=8):
+    """GPU caches filled with the workload's rows, quantised on the GPU."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+
+    import fp4_compressed_sparse_amd as csa2
+    import workloads as W
+
+    caches = [csa2.KVCache(w.batch, capacity) for _ in range(w.n_caches)]
+    jobs = []
+    for c in range(w.n_caches):
+        for b, n in enumerate(lengths):
+            for k in range((int(n) + W.CHUNK - 1) // W.CHUNK):
+                jobs.append((c, b, k, min(W.CHUNK, int(n) - k * W.CHUNK)))
+
+    def gen(job):
+        c, b, k, cnt = job
+        return job, W._kv_chunk(w.wid, c, b, k)[:cnt]
+
+    done = 0
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+        for (c, b, k, cnt), rows in ex.map(gen, jobs):
+            x = torch.from_numpy(np.ascontiguousarray(rows)).cuda()
+            s0 = k * W.CHUNK
+            csa2.fp4_quantize_kv(x, caches[c].codes[b, s0:s0 + cnt], caches[c].scales[b, s0:s0 + cnt])
+            done += 1
+            if done % log_every == 0 or done == len(jobs):
+                log(f"caches: {done}/{len(jobs)} chunks")
+    for cache in caches:
+        cache.seq_len.copy_(torch.as_tensor(lengths, dtype=torch.int64))
+    torch.cuda.synchronize()
+    return caches
+
+
+def cpu_baseline(w):
+    """The oracle's decode step timed on the host (1 thread), on two bounded
+    contexts, extrapolated linearly in context to the workload's context."""
+    import numpy as np
+
+    import workloads as W
+    from oracle.step import Cache, decode_step
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                               # pragma: no cover
+        threadpool_limits = None
+    samples = (8192, 32768)
+    times = []
+    for n in samples:
+        caches = []
+        for c in range(w.n_caches):
+            oc = Cache(1, n + 8)
+            oc.write(0, 0, W.kv_rows(w.wid, c, 0, 0, n))
+            oc.seq_len[0] = n
+            caches.append(oc)
+        lc = w.layer_caches()
+        layers = [(m, lc[l], W.queries(w.wid, l, 0, 1, w.heads)) for l, m in enumerate(w.pattern)]
+        rows = np.stack([W.append_rows(w.wid, c, 0, 1) for c in range(w.n_caches)])
+        import contextlib
+        ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+        with ctx:
+            t0 = time.perf_counter()
+            decode_step(caches, layers, rows, w.topk, w.pool, w.scale)
+            times.append(time.perf_counter() - t0)
+        log(f"cpu oracle: context {n}: {times[-1]:.2f} s per step")
+    (n1, n2), (t1, t2) = samples, times
+    slope = (t2 - t1) / (n2 - n1)
+    t_full = t2 + slope * (w.context - n2)
+    return {
+        "value": round(w.batch / t_full, 6),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"one decode step of the same 20-layer pattern (64 heads, pool 2048, top-256, batch 1) "
+                   f"at contexts {n1} and {n2}: {t1:.2f} s and {t2:.2f} s on 1 host thread; "
+                   f"extrapolated linearly in context to {w.context} positions: {t_full:.1f} s per step"),
+    }
+
+
+def pmc_traffic(scan_launches_bytes):
+    """HBM bytes per scan launch from the committed rocprofv3 counter runs,
+    if they were taken on the current scan kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            p = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if p.get("source_sha") != scan_source_sha():
+        return None
+    return p.get("hbm_bytes_per_launch")
+
+
+class HipEvents:
+    """Raw HIP events (the library records them itself, so torch's Event
+    wrapper cannot be used to read them back)."""
+
+    def __init__(self):
+        import ctypes
+        for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+            try:
+                self.hip = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        self.ct = ctypes
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def copy_probe():
+    """A plain device copy of 1 GiB (read 1 GiB, write 1 GiB), repeated: the
+    reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, help="workload id (default 3: 20 layers at 1M)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(sequences shard by batch with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import numpy as np
+    import torch
+
+    import fp4_compressed_sparse_amd as csa2
+    import workloads as W
+
+    csa2.load()
+    torch.cuda.set_device(0)
+    w = W.WORKLOADS[args.workload]
+    K, WU = args.steps, args.warmup
+    total_steps = K + WU
+    lengths = W.lengths(w)
+    n_app = total_steps if w.append else 0
+    capacity = int((int(lengths.max()) + n_app + 7) // 8 * 8)
+    max_len = int(lengths.max()) + n_app
+    t0 = time.perf_counter()
+    caches = build_caches(w, lengths, capacity)
+    for c in caches:
+        c.max_len = max_len
+    log(f"caches built in {time.perf_counter() - t0:.1f} s: {w.n_caches} x {w.batch} x {capacity} positions")
+
+    B, H, L = w.batch, w.heads, len(w.pattern)
+    lc = w.layer_caches()
+    q_all = [[torch.from_numpy(W.queries(w.wid, l, s, B, H)).cuda() for l in range(L)]
+             for s in range(total_steps)]
+    rows_all = [torch.from_numpy(np.stack([W.append_rows(w.wid, c, s, B) for c in range(w.n_caches)])).cuda()
+                if w.append else None for s in range(total_steps)]
+    outs = [torch.zeros((B, H, 512), dtype=torch.float32, device="cuda") for _ in range(L)]
+    # a Reuse layer's selection is its predecessor's: the driver forwards it
+    # without a copy when both layers name the same buffer
+    idxs = []
+    for l, m in enumerate(w.pattern):
+        idxs.append(idxs[-1] if m == 2 else torch.zeros((B, w.topk), dtype=torch.int32, device="cuda"))
+    pool_out = torch.zeros((B, w.pool), dtype=torch.int32, device="cuda") if w.pool else None
+    ws = csa2.workspace(B, H, max_len, w.pool, w.topk)
+    plans = [csa2.StepPlan(caches, [(m, lc[l], q_all[s][l], outs[l], idxs[l]) for l, m in enumerate(w.pattern)],
+                           H, w.topk, w.pool, w.scale, ws, pool_out=pool_out, new_rows=rows_all[s])
+             for s in range(total_steps)]
+    stream = torch.cuda.current_stream()
+
+    for s in range(WU):
+        plans[s].run(stream)
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    hev = HipEvents()
+    sev = [(hev.create(), hev.create()) for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        csa2.set_scan_events(*sev[i])
+        ev[i][0].record(stream)
+        plans[WU + i].run(stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    csa2.set_scan_events(None, None)
+    flags = csa2.device_error()
+    if flags:
+        log(f"device flags raised: {flags}")
+        sys.exit(1)
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    scan_ms = [hev.elapsed_ms(a, b) for a, b in sev]
+    for a, b in sev:
+        hev.destroy(a)
+        hev.destroy(b)
+
+    ms_per_step = elapsed * 1e3 / K
+    n_mid = [int(n) + (WU + K // 2 + 1 if w.append else 0) for n in lengths]
+    uniq, touched = step_bytes(w, n_mid)
+    scan_bytes = sum(n * TOKEN_BYTES for n in n_mid)
+    scan_avg_s = float(np.mean(scan_ms)) * 1e-3
+    achieved = scan_bytes / scan_avg_s / 1e9
+    eff_gbs = uniq / (ms_per_step * 1e-3) / 1e9
+    log(f"step: wall {ms_per_step * 1e3:.1f} us, events median {np.median(step_ms) * 1e3:.1f} us; "
+        f"scan kernel avg {scan_avg_s * 1e6:.1f} us = {achieved:.0f} GB/s; "
+        f"unique {uniq / 1e6:.1f} MB -> {eff_gbs:.0f} GB/s ({eff_gbs / PEAK_HBM_GBS * 100:.1f}% of peak); "
+        f"touched {touched / 1e6:.1f} MB")
+
+    result = {
+        "metric": "CSA2 decode tokens/s + effective FP4 KV GB/s vs HBM peak (1M ctx, 1 GPU)",
+        "value": round(B * K / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": WU,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": B, "context": int(lengths.max()), "heads": H,
+            "topk_blocks": w.topk, "pool_blocks": w.pool, "layers": L,
+            "pattern": "[Full,Reindex,Reuse,Reuse,Reindex]x4" if w.wid == 3 else str(w.pattern),
+            "kv_format": "FP4 E2M1 + E4M3/16ch, 288 B/position",
+            "effective_kv_gbs": round(eff_gbs, 1),
+            "effective_kv_frac_of_peak": round(eff_gbs / PEAK_HBM_GBS, 4),
+            "unique_kv_bytes_per_step": uniq, "touched_kv_bytes_per_step": touched,
+            "median_event_step_us": round(float(np.median(step_ms)) * 1e3, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "scan_kernel (first Full layer full-range scan)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": pmc_traffic(scan_bytes),
+            "algorithmic_bytes_per_launch": scan_bytes,
+            "avg_launch_us": round(scan_avg_s * 1e6, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,7 @@ FLAG_NONFINITE_KV, FLAG_CAPACITY, FLAG_NONFINITE_Q, FLAG_BAD_INDEX = 1, 2, 4, 8
 
 EXPORTED = ("fp4_quantize_kv", "csa2_append_kv", "csa2_workspace_bytes", "csa2_workspace_init",
             "csa2_index_topk", "csa2_sparse_attend", "csa2_decode_step", "csa2_block_scores",
-            "csa2_device_error", "csa2_status_string", "csa2_last_error")
+            "csa2_device_error", "csa2_set_scan_events", "csa2_status_string", "csa2_last_error")
 
 
 class Csa2Error(RuntimeError):
@@ -72,6 +72,7 @@ def load():
         "csa2_decode_step": (i32, [ctypes.POINTER(_Step), vp]),
         "csa2_block_scores": (i32, [ctypes.POINTER(_Kv), vp, i32, vp, i32, vp, vp]),
         "csa2_device_error": (i32, [ctypes.POINTER(ctypes.c_int32), vp]),
+        "csa2_set_scan_events": (i32, [vp, vp]),
         "csa2_status_string": (ctypes.c_char_p, [i32]),
         "csa2_last_error": (ctypes.c_char_p, []),
     }
@@ -208,6 +209,12 @@ class StepPlan:
 
 def decode_step(caches, layers, heads, topk, pool, scale, ws, pool_out=None, new_rows=None, stream=None):
     StepPlan(caches, layers, heads, topk, pool, scale, ws, pool_out, new_rows).run(stream)
+
+
+def set_scan_events(before=None, after=None):
+    """Record hipEvent_t handles `before`/`after` (ctypes c_void_p) around
+    every full-scan kernel launched from this thread (None, None clears)."""
+    _check(load().csa2_set_scan_events(before, after))
 
 
 def device_error(stream=None):

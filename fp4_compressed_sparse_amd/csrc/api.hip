@@ -23,6 +23,7 @@ using namespace csa2;
 namespace {
 
 thread_local std::string t_last_error;
+thread_local hipEvent_t t_scan_before = nullptr, t_scan_after = nullptr;
 
 csa2_status fail(csa2_status s, const char *fmt, ...) {
   char buf[512];
@@ -170,9 +171,11 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
   sa.ctrl = at<Ctrl>(ws, L.ctrl); sa.hist = at<uint32_t>(ws, L.hist);
   sa.R = R; sa.fill_invalid = 0;
   const int iters = (int)ceil_div(nblk_grid > 0 ? nblk_grid : 1, BLOCKS_PER_ITER);
-  dim3 g1(grid_for(iters, B, 512), B);
+  dim3 g1(grid_for(iters, B, 1024), B);
+  if (t_scan_before) (void)hipEventRecord(t_scan_before, s);
   scan_kernel<true><<<g1, SCAN_THREADS, 0, s>>>(sa);
   if (csa2_status st = launched("scan")) return st;
+  if (t_scan_after) (void)hipEventRecord(t_scan_after, s);
   SelectArgs se;
   se.seq_len = kv->seq_len; se.limit = kv->max_len; se.scores = sa.scores; se.score_stride = L.score_stride;
   se.ctrl = sa.ctrl; se.bitmap = at<uint32_t>(ws, L.bitmap); se.nwords = L.nwords;
@@ -180,7 +183,7 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
   se.R = R; se.first_out = first_out; se.topk = topk2; se.idx_out = idx_out;
   int lk = R > 4096 ? R : 4096;
   se.lds_keys = lk;
-  dim3 g2(grid_for(ceil_div(L.nwords / 2, 4), B, 256), B);
+  dim3 g2(grid_for(ceil_div(L.nwords / 2, 4), B, 512), B);
   select_kernel<<<g2, SCAN_THREADS, (size_t)lk * sizeof(uint64_t), s>>>(se);
   return launched("select");
 }
@@ -252,6 +255,14 @@ const char *csa2_status_string(csa2_status s) {
 }
 
 const char *csa2_last_error(void) { return t_last_error.c_str(); }
+
+csa2_status csa2_set_scan_events(void *before, void *after) {
+  t_last_error.clear();
+  if ((before == nullptr) != (after == nullptr)) return fail(CSA2_E_ARG, "set both events or neither");
+  t_scan_before = reinterpret_cast<hipEvent_t>(before);
+  t_scan_after = reinterpret_cast<hipEvent_t>(after);
+  return CSA2_OK;
+}
 
 size_t csa2_workspace_bytes(int32_t batch, int32_t heads, int64_t max_len, int32_t pool, int32_t topk) {
   Layout L;

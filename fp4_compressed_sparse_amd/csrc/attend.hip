@@ -101,42 +101,53 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   for (int st = st0; st < st1; ++st) {
     __syncthreads();                      // previous stage fully consumed
     // ---- load + dequantise SP positions into LDS (16 threads per row) ----
-    for (int pp = tid >> 4; pp < SP; pp += ATT_THREADS / 16) {
+    // all block ids first, then all rows, then convert: two memory round
+    // trips per stage instead of two per row
+    {
+      constexpr int PASSES = SP / 16;
       const int i = tid & 15;
-      const int j = st * SP + pp;
-      bool ok = false;
-      int64_t pos = 0;
-      if (j < total_pos) {
-        const int32_t blk = idx[j >> 3];
-        pos = (int64_t)blk * BLOCK + (j & 7);
-        ok = blk >= 0 && blk < nblk && pos < n;
+      int64_t posv[PASSES];
+      bool okv[PASSES];
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) {
+        const int pp = (tid >> 4) + 16 * k;
+        const int j = st * SP + pp;
+        const int32_t blk = j < total_pos ? idx[j >> 3] : -1;
+        posv[k] = (int64_t)blk * BLOCK + (j & 7);
+        okv[k] = blk >= 0 && blk < nblk && posv[k] < n;
         if (blk >= nblk && i == 0 && (j & 7) == 0) raise_flag(FLAG_BAD_INDEX);
       }
-      u32x4 out[4];
-      if (ok) {
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(codes + pos * CODE_BYTES + 16 * i);
-        const uint32_t sc = *reinterpret_cast<const uint16_t *>(scales + pos * SCALE_BYTES + 2 * i);
-        const _Float16 s0 = (_Float16)e4m3_to_f32(sc & 0xffu);
-        const _Float16 s1 = (_Float16)e4m3_to_f32(sc >> 8);
+      u32x4 wr[PASSES];
+      uint32_t scr[PASSES];
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) {
+        if (okv[k]) {
+          wr[k] = *reinterpret_cast<const u32x4 *>(codes + posv[k] * CODE_BYTES + 16 * i);
+          scr[k] = *reinterpret_cast<const uint16_t *>(scales + posv[k] * SCALE_BYTES + 2 * i);
+        } else {
+          wr[k] = u32x4{0u, 0u, 0u, 0u};
+          scr[k] = 0u;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) {
+        const int pp = (tid >> 4) + 16 * k;
+        const _Float16 s0 = (_Float16)e4m3_to_f32(scr[k] & 0xffu);
+        const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
         const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
+        u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i);
 #pragma unroll
         for (int dw = 0; dw < 4; ++dw) {
           const f16x2 sv = dw < 2 ? sv0 : sv1;
-          f16x2 h0 = e2m1x2_to_f16<0>(w[dw]) * sv;
-          f16x2 h1 = e2m1x2_to_f16<1>(w[dw]) * sv;
-          f16x2 h2 = e2m1x2_to_f16<2>(w[dw]) * sv;
-          f16x2 h3 = e2m1x2_to_f16<3>(w[dw]) * sv;
-          out[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+          f16x2 h0 = e2m1x2_to_f16<0>(wr[k][dw]) * sv;
+          f16x2 h1 = e2m1x2_to_f16<1>(wr[k][dw]) * sv;
+          f16x2 h2 = e2m1x2_to_f16<2>(wr[k][dw]) * sv;
+          f16x2 h3 = e2m1x2_to_f16<3>(wr[k][dw]) * sv;
+          dst[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
                           __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
         }
-      } else {
-#pragma unroll
-        for (int dw = 0; dw < 4; ++dw) out[dw] = u32x4{0u, 0u, 0u, 0u};
+        if (i == 0) s_ok[pp] = okv[k] ? 1 : 0;
       }
-      u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i);
-#pragma unroll
-      for (int dw = 0; dw < 4; ++dw) dst[dw] = out[dw];
-      if (i == 0) s_ok[pp] = ok ? 1 : 0;
     }
     __syncthreads();
 
@@ -233,30 +244,52 @@ struct CombineArgs {
   float *out;               // [batch][heads][512]
 };
 
-// grid (heads, batch), 128 threads x 4 channels: merge every partial of a head.
+// grid (heads, batch), 128 threads x 4 channels: merge every partial of a
+// head.  Slot loads are issued 8 at a time.
 __global__ void __launch_bounds__(128) attend_combine_kernel(CombineArgs a) {
+  constexpr int U = 8;
   const int hh = blockIdx.x, b = blockIdx.y;
   const int HT = a.heads / 16, ht = hh / 16, n16 = hh % 16;
   const int WPT = 4 / HT;
   const int nslots = a.splits * WPT;
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < nslots; ++s) {
+  auto slot_of = [&](int s) -> int64_t {
     const int split = s / WPT, w = ht + HT * (s % WPT);
-    const int64_t slot = ((int64_t)b * a.splits + split) * 4 + w;
-    M = fmaxf(M, a.part_ml[(slot * 16 + n16) * 2]);
+    return (((int64_t)b * a.splits + split) * 4 + w) * 16 + n16;
+  };
+  float M = -__builtin_huge_valf();
+  for (int s0 = 0; s0 < nslots; s0 += U) {
+    float mv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mv[u] = s0 + u < nslots ? a.part_ml[slot_of(s0 + u) * 2] : -__builtin_huge_valf();
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, mv[u]);
   }
   float4 o = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -__builtin_huge_valf()) {
-    for (int s = 0; s < nslots; ++s) {
-      const int split = s / WPT, w = ht + HT * (s % WPT);
-      const int64_t slot = ((int64_t)b * a.splits + split) * 4 + w;
-      const float m = a.part_ml[(slot * 16 + n16) * 2];
-      if (m == -__builtin_huge_valf()) continue;
-      const float e = __builtin_amdgcn_exp2f(m - M);
-      L += e * a.part_ml[(slot * 16 + n16) * 2 + 1];
-      const float4 v = reinterpret_cast<const float4 *>(a.part_o + (slot * 16 + n16) * D)[threadIdx.x];
-      o.x += e * v.x; o.y += e * v.y; o.z += e * v.z; o.w += e * v.w;
+    for (int s0 = 0; s0 < nslots; s0 += U) {
+      float mv[U], lv[U];
+      float4 ov[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u < nslots) {
+          const int64_t sl = slot_of(s0 + u);
+          mv[u] = a.part_ml[sl * 2];
+          lv[u] = a.part_ml[sl * 2 + 1];
+          ov[u] = reinterpret_cast<const float4 *>(a.part_o + sl * D)[threadIdx.x];
+        } else {
+          mv[u] = -__builtin_huge_valf();
+          lv[u] = 0.f;
+          ov[u] = float4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (mv[u] == -__builtin_huge_valf()) continue;
+        const float e = __builtin_amdgcn_exp2f(mv[u] - M);
+        L += e * lv[u];
+        o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

@@ -58,38 +58,50 @@ struct ScanArgs {
   int32_t fill_invalid;     // write -inf for blocks >= nblk (export only)
 };
 
-// Qbar of sequence b into LDS (all threads call).
+// Qbar of sequence b into LDS; all 256 threads call.  Each thread owns two
+// channels and adds the heads in order; the loads of 16 heads are issued
+// together so the sum costs a few memory round trips, not one per head.
 __device__ __forceinline__ void compute_qbar(const float *__restrict__ q, int heads, int b,
                                              float *s_qbar) {
   const int t = threadIdx.x;
-  if (t < D / 4) {
-    const float4 *qp = reinterpret_cast<const float4 *>(q + (int64_t)b * heads * D) + t;
-    float4 acc = qp[0];
-    for (int h = 1; h < heads; ++h) {
-      float4 v = qp[(int64_t)h * (D / 4)];
-      acc.x = acc.x + v.x; acc.y = acc.y + v.y; acc.z = acc.z + v.z; acc.w = acc.w + v.w;
+  const float2 *qp = reinterpret_cast<const float2 *>(q + (int64_t)b * heads * D) + t;
+  float2 acc = qp[0];
+  for (int h0 = 1; h0 < heads; h0 += 16) {
+    float2 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      v[j] = (h0 + j < heads) ? qp[(int64_t)(h0 + j) * (D / 2)] : make_float2(0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (h0 + j < heads) { acc.x = acc.x + v[j].x; acc.y = acc.y + v[j].y; }
     }
-    bool ok = __builtin_isfinite(acc.x) && __builtin_isfinite(acc.y) &&
-              __builtin_isfinite(acc.z) && __builtin_isfinite(acc.w);
-    if (!ok) raise_flag(FLAG_NONFINITE_Q);
-    reinterpret_cast<float4 *>(s_qbar)[t] = acc;
   }
+  if (!(__builtin_isfinite(acc.x) && __builtin_isfinite(acc.y))) raise_flag(FLAG_NONFINITE_Q);
+  reinterpret_cast<float2 *>(s_qbar)[t] = acc;
   __syncthreads();
 }
 
-// Score of one block; the 16 lanes of a slot call it together (lane16 = i).
-// rowbase: address of the block's first row (codes), srow: its first scale
-// row.  cnt: rows present (1..8).  qb: this lane's 32 Qbar values.
-__device__ __forceinline__ float block_score(const uint8_t *__restrict__ rowbase,
-                                             const uint8_t *__restrict__ srow, int cnt, int i,
-                                             const float *qb) {
-  u32x4 w[BLOCK];
-  uint32_t sc[BLOCK];
+// The 8 rows of one block as one lane of its 16-lane slot sees them.
+struct BlockRows {
+  u32x4 w[BLOCK];       // code bytes 16i..16i+15 of each row
+  uint32_t sc[BLOCK];   // scale bytes 2i, 2i+1 of each row
+};
+
+__device__ __forceinline__ void load_block(BlockRows &r, const uint8_t *__restrict__ rowbase,
+                                           const uint8_t *__restrict__ srow, int i) {
 #pragma unroll
   for (int t = 0; t < BLOCK; ++t) {
-    w[t] = *reinterpret_cast<const u32x4 *>(rowbase + (int64_t)t * CODE_BYTES + 16 * i);
-    sc[t] = *reinterpret_cast<const uint16_t *>(srow + (int64_t)t * SCALE_BYTES + 2 * i);
+    r.w[t] = *reinterpret_cast<const u32x4 *>(rowbase + (int64_t)t * CODE_BYTES + 16 * i);
+    r.sc[t] = *reinterpret_cast<const uint16_t *>(srow + (int64_t)t * SCALE_BYTES + 2 * i);
   }
+}
+
+// Score of one block from its loaded rows; the 16 lanes of a slot call it
+// together (lane16 = i).  cnt: rows present (1..8).  qb: this lane's 32
+// Qbar values (LDS).
+__device__ __forceinline__ float block_score(const BlockRows &r, int cnt, const float *qb) {
+  const u32x4 *w = r.w;
+  const uint32_t *sc = r.sc;
   float S[32];
 #pragma unroll
   for (int t = 0; t < BLOCK; ++t) {
@@ -230,21 +242,23 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
   if (HIST) {
     for (int j = threadIdx.x; j < HIST_BINS; j += SCAN_THREADS) s_hist[j] = 0;
   }
-  compute_qbar(a.q, a.heads, b, s_qbar);
-  float qb[32];
-#pragma unroll
-  for (int c = 0; c < 32; ++c) qb[c] = s_qbar[32 * i + c];
-
   const uint8_t *codes = a.codes + (int64_t)b * a.capacity * CODE_BYTES;
   const uint8_t *scales = a.scales + (int64_t)b * a.capacity * SCALE_BYTES;
   float *scores = a.scores + (int64_t)b * a.score_stride;
   const int iters = (a.nblk_grid + BLOCKS_PER_ITER - 1) / BLOCKS_PER_ITER;
-  for (int it = blockIdx.x; it < iters; it += gridDim.x) {
-    const int64_t blk = (int64_t)it * BLOCKS_PER_ITER + wv * 4 + slot;
+  // Rows of the first block group are requested before the query sum so the
+  // two latencies overlap; afterwards the next group's rows are requested
+  // before the current group is scored.
+  int it = blockIdx.x;
+  int64_t blk = (int64_t)it * BLOCKS_PER_ITER + wv * 4 + slot;
+  BlockRows cur;
+  if (it < iters && blk < nblk) load_block(cur, codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES, i);
+  compute_qbar(a.q, a.heads, b, s_qbar);
+  const float *qb = s_qbar + 32 * i;
+  for (; it < iters; it += gridDim.x) {
     if (blk < nblk) {
       const int cnt = (int)min((int64_t)BLOCK, n - blk * BLOCK);
-      float s = block_score(codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES,
-                            cnt, i, qb);
+      float s = block_score(cur, cnt, qb);
       if (i == 0) {
         scores[blk] = s;
         if (HIST) atomicAdd(&s_hist[ord_key(s) >> HIST_SHIFT], 1u);
@@ -252,6 +266,11 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
     } else if (a.fill_invalid && i == 0 && blk < a.score_stride) {
       scores[blk] = -__builtin_huge_valf();
     }
+    // next group: one buffer of rows per wave; the other resident waves
+    // cover this wave's memory latency
+    blk = (int64_t)(it + gridDim.x) * BLOCKS_PER_ITER + wv * 4 + slot;
+    if (it + (int)gridDim.x < iters && blk < nblk)
+      load_block(cur, codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES, i);
   }
   if (!HIST) return;
   __syncthreads();
@@ -319,25 +338,46 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
 }
 
 // Writes the ids of the set bits of bitmap[0..nwords) in ascending order to
-// out[0..len), padding with -1.  All threads.
-__device__ void compact_bitmap(const uint32_t *bm, int nwords, int32_t *out, int len,
-                               uint32_t *s_wave) {
+// out[0..len) (and to s_out in LDS when given), padding with -1.  All
+// threads.  Each thread owns a contiguous run of words; the words of a run
+// are loaded 16 at a time so a pass costs a few memory round trips.
+__device__ void compact_bitmap(const uint32_t *bm, int nwords, int32_t *out, int32_t *s_out,
+                               int len, uint32_t *s_wave) {
+  constexpr int U = 16;
   const int t = threadIdx.x, nt = blockDim.x;
   const int per = (nwords + nt - 1) / nt;
   const int w0 = min(nwords, t * per), w1 = min(nwords, w0 + per);
   uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(ld_agent(bm + w));
+  for (int wb = w0; wb < w1; wb += U) {
+    uint32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = (wb + u < w1) ? ld_agent(bm + wb + u) : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) cnt += __popc(v[u]);
+  }
   uint32_t total;
   uint32_t off = block_exclusive_scan(cnt, &total, s_wave);
-  for (int w = w0; w < w1 && off < (uint32_t)len; ++w) {
-    uint32_t bits = ld_agent(bm + w);
-    while (bits && off < (uint32_t)len) {
-      int bpos = __ffs(bits) - 1;
-      bits &= bits - 1;
-      out[off++] = w * 32 + bpos;
+  for (int wb = w0; wb < w1 && off < (uint32_t)len; wb += U) {
+    uint32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = (wb + u < w1) ? ld_agent(bm + wb + u) : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t bits = v[u];
+      while (bits && off < (uint32_t)len) {
+        int bpos = __ffs(bits) - 1;
+        bits &= bits - 1;
+        const int32_t id = (wb + u) * 32 + bpos;
+        out[off] = id;
+        if (s_out) s_out[off] = id;
+        ++off;
+      }
     }
   }
-  for (int j = (int)total + t; j < len; j += nt) out[j] = -1;
+  for (int j = (int)total + t; j < len; j += nt) {
+    out[j] = -1;
+    if (s_out) s_out[j] = -1;
+  }
 }
 
 // Top r of the m keys in s_keys (LDS) by flag, compacting the corresponding
@@ -365,8 +405,9 @@ __device__ void select_in_lds(uint64_t *s_keys, uint8_t *s_valid, const int32_t 
 }
 
 __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
-  extern __shared__ uint64_t s_keys[];                 // LDS_KEYS
+  extern __shared__ uint64_t s_keys[];                 // lds_keys
   __shared__ uint8_t s_valid[LDS_KEYS];
+  __shared__ int32_t s_ids[LDS_KEYS];
   __shared__ uint32_t s_hist[256];
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
@@ -473,18 +514,32 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
     __syncthreads();
   }
   int32_t *first = a.first_out + (int64_t)b * a.R;
-  compact_bitmap(bm, a.nwords, first, a.R, s_wave);
+  compact_bitmap(bm, a.nwords, first, a.topk > 0 ? s_ids : nullptr, a.R, s_wave);
   __syncthreads();
   if (a.topk > 0) {
     // top-k inside the pool: keys of the pool members, in pool order
+    constexpr int U = 8;
     const int m = a.R;
-    for (int j = t; j < m; j += nt) {
-      int32_t id = first[j];
-      s_valid[j] = id >= 0;
-      s_keys[j] = id >= 0 ? make_key(scores[id], (uint32_t)id) : 0ull;
+    for (int j0 = t; j0 < m; j0 += nt * U) {
+      float sv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * nt;
+        const int32_t id = j < m ? s_ids[j] : -1;
+        sv[u] = id >= 0 ? scores[id] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * nt;
+        if (j < m) {
+          const int32_t id = s_ids[j];
+          s_valid[j] = id >= 0;
+          s_keys[j] = id >= 0 ? make_key(sv[u], (uint32_t)id) : 0ull;
+        }
+      }
     }
     __syncthreads();
-    select_in_lds(s_keys, s_valid, first, m, a.topk, a.idx_out + (int64_t)b * a.topk, a.topk,
+    select_in_lds(s_keys, s_valid, s_ids, m, a.topk, a.idx_out + (int64_t)b * a.topk, a.topk,
                   s_hist, s_state, s_wave);
   }
   __syncthreads();
@@ -530,42 +585,61 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   const int slot = lane >> 4, i = lane & 15;
   const int64_t n = clamp_len(a.seq_len[b], a.limit);
   const int64_t nblk = (n + BLOCK - 1) / BLOCK;
-  compute_qbar(a.q, a.heads, b, s_qbar);
-  float qb[32];
-#pragma unroll
-  for (int c = 0; c < 32; ++c) qb[c] = s_qbar[32 * i + c];
   const uint8_t *codes = a.codes + (int64_t)b * a.capacity * CODE_BYTES;
   const uint8_t *scales = a.scales + (int64_t)b * a.capacity * SCALE_BYTES;
   const int32_t *cand = a.cand + (int64_t)b * a.n_cand;
   float *scores = a.scores + (int64_t)b * a.score_stride;
   const int iters = (a.n_cand + BLOCKS_PER_ITER - 1) / BLOCKS_PER_ITER;
-  for (int it = blockIdx.x; it < iters; it += gridDim.x) {
-    const int j = it * BLOCKS_PER_ITER + wv * 4 + slot;
+  // first group's candidate ids and rows are requested before the query sum
+  int it = blockIdx.x;
+  int j = it * BLOCKS_PER_ITER + wv * 4 + slot;
+  int32_t blk = (it < iters && j < a.n_cand) ? cand[j] : -1;
+  BlockRows cur;
+  if (blk >= 0 && blk < nblk)
+    load_block(cur, codes + (int64_t)blk * BLOCK * CODE_BYTES, scales + (int64_t)blk * BLOCK * SCALE_BYTES, i);
+  compute_qbar(a.q, a.heads, b, s_qbar);
+  const float *qb = s_qbar + 32 * i;
+  for (; it < iters; it += gridDim.x) {
     if (j < a.n_cand) {
-      const int32_t blk = cand[j];
       if (blk >= 0 && blk < nblk) {
         const int cnt = (int)min((int64_t)BLOCK, n - (int64_t)blk * BLOCK);
-        float s = block_score(codes + (int64_t)blk * BLOCK * CODE_BYTES,
-                              scales + (int64_t)blk * BLOCK * SCALE_BYTES, cnt, i, qb);
+        float s = block_score(cur, cnt, qb);
         if (i == 0) scores[j] = s;
-      } else {
-        if (i == 0) {
-          scores[j] = -__builtin_huge_valf();
-          if (blk >= nblk) raise_flag(FLAG_BAD_INDEX);
-        }
+      } else if (i == 0) {
+        scores[j] = -__builtin_huge_valf();
+        if (blk >= nblk) raise_flag(FLAG_BAD_INDEX);
       }
     }
+    const int it_next = it + gridDim.x;
+    j = it_next * BLOCKS_PER_ITER + wv * 4 + slot;
+    blk = (it_next < iters && j < a.n_cand) ? cand[j] : -1;
+    if (blk >= 0 && blk < nblk)
+      load_block(cur, codes + (int64_t)blk * BLOCK * CODE_BYTES, scales + (int64_t)blk * BLOCK * SCALE_BYTES, i);
   }
   if (!SELECT) return;
   Ctrl *ctrl = a.ctrl + b;
   if (!arrive_last(&ctrl->arrive_sel, gridDim.x)) return;
   const int t = threadIdx.x, nt = blockDim.x;
   const int m = a.n_cand;
-  for (int j = t; j < m; j += nt) {
-    int32_t id = cand[j];
-    bool ok = id >= 0 && id < nblk;
-    s_valid[j] = ok;
-    s_keys[j] = ok ? make_key(ld_agent(scores + j), (uint32_t)id) : 0ull;
+  constexpr int U = 8;
+  for (int j0 = t; j0 < m; j0 += nt * U) {
+    int32_t idv[U];
+    float sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = j0 + u * nt;
+      idv[u] = jj < m ? cand[jj] : -1;
+      sv[u] = jj < m ? ld_agent(scores + jj) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = j0 + u * nt;
+      if (jj < m) {
+        const bool ok = idv[u] >= 0 && idv[u] < nblk;
+        s_valid[jj] = ok;
+        s_keys[jj] = ok ? make_key(sv[u], (uint32_t)idv[u]) : 0ull;
+      }
+    }
   }
   __syncthreads();
   select_in_lds(s_keys, s_valid, cand, m, a.topk, a.idx_out + (int64_t)b * a.topk, a.topk,

@@ -249,6 +249,14 @@ csa2_status csa2_block_scores(const csa2_kv *kv, const float *q, int32_t heads,
  */
 csa2_status csa2_device_error(int32_t *flags_host, void *stream);
 
+/*
+ * csa2_set_scan_events — diagnostic timing hook.  While set (on this host
+ * thread), every full-scan kernel launch records hipEvent_t `before` just
+ * before it and `after` just after it on the launch's stream, so a caller
+ * can time that kernel alone with hipEventElapsedTime.  NULL, NULL clears.
+ */
+csa2_status csa2_set_scan_events(void *before, void *after);
+
 const char *csa2_status_string(csa2_status s);
 /* Message of the last failing call on this thread ("" if none). */
 const char *csa2_last_error(void);
