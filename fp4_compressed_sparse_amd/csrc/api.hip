@@ -106,10 +106,10 @@ bool make_layout(int32_t batch, int32_t heads, int64_t max_len, int32_t pool, in
   L->cand_stride = nblk > 0 ? nblk : 1;
   size_t off = 0;
   L->ctrl = off;   off = align256(off + sizeof(Ctrl) * batch);
-  L->hist = off;   off = align256(off + sizeof(uint32_t) * HIST_BINS * (size_t)batch);
+  L->hist = off;   off = align256(off + sizeof(uint32_t) * HIST_COPIES * HIST_BINS * (size_t)batch);
   L->scores = off; off = align256(off + sizeof(float) * (size_t)L->score_stride * batch);
   L->bitmap = off; off = align256(off + sizeof(uint32_t) * (size_t)L->nwords * batch);
-  L->cands = off;  off = align256(off + sizeof(uint64_t) * (size_t)L->cand_stride * batch);
+  L->cands = off;  off = align256(off + sizeof(uint64_t) * CAND_COPIES * (size_t)L->cand_stride * batch);
   L->att_stages = L->att_splits = 0;
   L->part_o = L->part_ml = off;
   if (heads == 16 || heads == 32 || heads == 64) {
@@ -149,10 +149,13 @@ csa2_status check_ws(void *ws, size_t ws_bytes, const Layout &L) {
 template <typename T>
 T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
 
+// Workgroups per grid row: about `target` in total over the batch, at most
+// one per item and at most MAX_GRID_X (the hand-off counters' capacity).
 int grid_for(int64_t items, int batch, int target) {
   int64_t want = ceil_div(target, batch);
   if (want < 1) want = 1;
   if (items < want) want = items;
+  if (want > MAX_GRID_X) want = MAX_GRID_X;
   return (int)(want < 1 ? 1 : want);
 }
 

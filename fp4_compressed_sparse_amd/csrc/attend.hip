@@ -78,18 +78,32 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
   const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
 
-  // Q^T operand: head ht*16 + n16, channels 32*kc + 8*g + 0..7
+  // Q^T operand: head ht*16 + n16, channels 32*kc + 8*g + 0..7.  q is staged
+  // through LDS (coalesced float4 loads issued 16 per thread at a time,
+  // stored as fp16 rows in the space the stages use later), then each lane
+  // reads its 16 operand chunks.
   f16x8 qop[16];
   {
-    const int heads = 16 * HT;
-    const float *qh = a.q + ((int64_t)b * heads + ht * 16 + n16) * D + 8 * g;
+    constexpr int NV = 16 * HT * D / 4 / ATT_THREADS;       // float4 per thread: 8*HT
+    constexpr int BATCH = NV < 16 ? NV : 16;
+    const float4 *src = reinterpret_cast<const float4 *>(a.q + (int64_t)b * (16 * HT) * D);
 #pragma unroll
-    for (int kc = 0; kc < 16; ++kc) {
-      float4 lo = *reinterpret_cast<const float4 *>(qh + 32 * kc);
-      float4 hi = *reinterpret_cast<const float4 *>(qh + 32 * kc + 4);
-      qop[kc] = f16x8{(_Float16)lo.x, (_Float16)lo.y, (_Float16)lo.z, (_Float16)lo.w,
-                      (_Float16)hi.x, (_Float16)hi.y, (_Float16)hi.z, (_Float16)hi.w};
+    for (int u0 = 0; u0 < NV; u0 += BATCH) {
+      float4 v[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) v[u] = src[tid + (u0 + u) * ATT_THREADS];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int e = tid + (u0 + u) * ATT_THREADS;        // float4 index: head e/128, channels 4*(e%128)
+        f16x2 lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
+        *reinterpret_cast<u32x2 *>(s_v + (e >> 7) * ROW_HALVES + 4 * (e & 127)) =
+            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      }
     }
+    __syncthreads();
+    const _Float16 *qrow = s_v + (ht * 16 + n16) * ROW_HALVES + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < 16; ++kc) qop[kc] = *reinterpret_cast<const f16x8 *>(qrow + 32 * kc);
   }
 
   f32x4 acc[32];
@@ -245,51 +259,46 @@ struct CombineArgs {
 };
 
 // grid (heads, batch), 128 threads x 4 channels: merge every partial of a
-// head.  Slot loads are issued 8 at a time.
+// head.  Up to 32 slots are loaded in one batch (one memory round trip).
 __global__ void __launch_bounds__(128) attend_combine_kernel(CombineArgs a) {
-  constexpr int U = 8;
+  constexpr int U = 32;
   const int hh = blockIdx.x, b = blockIdx.y;
   const int HT = a.heads / 16, ht = hh / 16, n16 = hh % 16;
   const int WPT = 4 / HT;
   const int nslots = a.splits * WPT;
-  auto slot_of = [&](int s) -> int64_t {
-    const int split = s / WPT, w = ht + HT * (s % WPT);
-    return (((int64_t)b * a.splits + split) * 4 + w) * 16 + n16;
-  };
-  float M = -__builtin_huge_valf();
-  for (int s0 = 0; s0 < nslots; s0 += U) {
-    float mv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) mv[u] = s0 + u < nslots ? a.part_ml[slot_of(s0 + u) * 2] : -__builtin_huge_valf();
-#pragma unroll
-    for (int u = 0; u < U; ++u) M = fmaxf(M, mv[u]);
-  }
+  float M = -__builtin_huge_valf(), L = 0.f;
   float4 o = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M != -__builtin_huge_valf()) {
-    for (int s0 = 0; s0 < nslots; s0 += U) {
-      float mv[U], lv[U];
-      float4 ov[U];
+  for (int s0 = 0; s0 < nslots; s0 += U) {
+    float mv[U], lv[U];
+    float4 ov[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (s0 + u < nslots) {
-          const int64_t sl = slot_of(s0 + u);
-          mv[u] = a.part_ml[sl * 2];
-          lv[u] = a.part_ml[sl * 2 + 1];
-          ov[u] = reinterpret_cast<const float4 *>(a.part_o + sl * D)[threadIdx.x];
-        } else {
-          mv[u] = -__builtin_huge_valf();
-          lv[u] = 0.f;
-          ov[u] = float4{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < nslots) {
+        const int s = s0 + u;
+        const int split = s / WPT, w = ht + HT * (s % WPT);
+        const int64_t sl = (((int64_t)b * a.splits + split) * 4 + w) * 16 + n16;
+        mv[u] = a.part_ml[sl * 2];
+        lv[u] = a.part_ml[sl * 2 + 1];
+        ov[u] = reinterpret_cast<const float4 *>(a.part_o + sl * D)[threadIdx.x];
+      } else {
+        mv[u] = -__builtin_huge_valf();
+        lv[u] = 0.f;
+        ov[u] = float4{0.f, 0.f, 0.f, 0.f};
       }
+    }
+    float Mb = M;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (mv[u] == -__builtin_huge_valf()) continue;
-        const float e = __builtin_amdgcn_exp2f(mv[u] - M);
-        L += e * lv[u];
-        o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
-      }
+    for (int u = 0; u < U; ++u) Mb = fmaxf(Mb, mv[u]);
+    if (Mb == -__builtin_huge_valf()) continue;
+    const float r = __builtin_amdgcn_exp2f(M - Mb);     // rescale what was summed so far
+    L *= r; o.x *= r; o.y *= r; o.z *= r; o.w *= r;
+    M = Mb;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (mv[u] == -__builtin_huge_valf()) continue;
+      const float e = __builtin_amdgcn_exp2f(mv[u] - M);
+      L += e * lv[u];
+      o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

@@ -19,8 +19,11 @@ constexpr int GROUP = 16;         // channels per scale
 constexpr int NGROUPS = 32;
 constexpr int WAVE = 64;
 
-constexpr int HIST_BINS = 4096;   // first radix digit: top 12 bits of the score key
-constexpr int HIST_SHIFT = 20;
+constexpr int HIST_BINS = 1024;   // first radix digit: top 10 bits of the score key
+constexpr int HIST_SHIFT = 22;
+constexpr int HIST_COPIES = 8;    // histogram copies (workgroup x adds to copy x % 8)
+constexpr int CAND_COPIES = 8;    // tie-candidate lists, likewise
+constexpr int MAX_GRID_X = 2048;  // workgroups per grid row of a hand-off kernel
 
 // Device flag bits (mirrors include/csa2.h).
 constexpr uint32_t FLAG_NONFINITE_KV = 1, FLAG_CAPACITY = 2, FLAG_NONFINITE_Q = 4,
@@ -34,15 +37,17 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Per-row control words of a workspace (one 64-byte line per sequence).
+// Per-row control words of a workspace (1 KB per sequence).
 struct Ctrl {
-  uint32_t arrive_scan;    // scan workgroups finished
-  uint32_t arrive_sel;     // select / rescore workgroups finished
-  uint32_t ncand;          // tie-bucket candidates collected
-  uint32_t thr_digit;      // top-12-bit digit holding the R-th largest key
-  uint32_t need;           // keys still to take from that digit
-  uint32_t all;            // 1: every block is selected (nblk <= R)
-  uint32_t pad[10];
+  uint32_t scan_grp[MAX_GRID_X / 32];   // scan arrivals per group of 32 workgroups
+  uint32_t scan_top;                    // groups of the scan complete
+  uint32_t sel_grp[MAX_GRID_X / 32];    // select / rescore arrivals
+  uint32_t sel_top;
+  uint32_t ncand[CAND_COPIES];          // tie candidates collected per list
+  uint32_t thr_digit;                   // top-10-bit digit holding the R-th largest key
+  uint32_t need;                        // keys still to take from that digit
+  uint32_t all;                         // 1: every block is selected (nblk <= R)
+  uint32_t pad[256 - 2 * (MAX_GRID_X / 32) - 2 - CAND_COPIES - 3];
 };
 
 // E4M3FN byte -> float (exact).  gfx950 decodes the OCP FN variant.
@@ -92,22 +97,44 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// "Last workgroup" hand-off: every workgroup of a grid row calls this once
-// after its global writes; exactly one (the last to arrive) gets true and,
-// after the acquire fence, sees every other workgroup's writes.  The caller
-// must be all threads of the workgroup.
-__device__ __forceinline__ bool arrive_last(uint32_t *counter, uint32_t expected) {
+// "Last workgroup" hand-off without device-scope fences.
+//
+// On gfx950 a release fence per workgroup (an L2 write-back) followed by an
+// arrival on one counter costs about 75 ns per workgroup, serialised (77 us
+// for 1024 workgroups, measured), and same-address atomics serialise at
+// about 12 ns each.  So: every value the last workgroup reads is written
+// with a device-scope atomic (performed at the device coherence point, not
+// in an XCD's L2); each wave waits for all of its memory operations to
+// complete (s_waitcnt 0) before the workgroup barrier; the arrival counts on
+// two levels (groups of 32 workgroups, then groups), so no address sees more
+// than 64 contending atomics; the last workgroup reads with device-scope
+// atomic loads.  Counters reset themselves.  All threads of the workgroup
+// call this once; exactly one workgroup per grid row gets true.
+__device__ __forceinline__ bool arrive_last(uint32_t *grp, uint32_t *top, uint32_t nwg) {
   __shared__ uint32_t s_last;
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev + 1 == expected) ? 1u : 0u;
+    const uint32_t g = blockIdx.x >> 5;
+    const uint32_t gsize = min(32u, nwg - 32u * g);
+    const uint32_t ngroups = (nwg + 31) >> 5;
+    uint32_t last = 0;
+    if (__hip_atomic_fetch_add(grp + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gsize - 1) {
+      __hip_atomic_store(grp + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1) {
+        __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = 1;
+      }
+    }
+    s_last = last;
   }
   __syncthreads();
-  bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
+  return s_last != 0;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_agent(T *p, T v) {
+  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -275,22 +275,35 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
   if (!HIST) return;
   __syncthreads();
   Ctrl *ctrl = a.ctrl + b;
-  uint32_t *gh = a.hist + (int64_t)b * HIST_BINS;
-  for (int j = threadIdx.x; j < HIST_BINS; j += SCAN_THREADS) {
-    uint32_t c = s_hist[j];
-    if (c) atomic_add_agent(gh + j, c);
+  uint32_t *gh = a.hist + (int64_t)b * HIST_COPIES * HIST_BINS;
+  {
+    uint32_t *mine = gh + (blockIdx.x % HIST_COPIES) * HIST_BINS;
+    for (int j = threadIdx.x; j < HIST_BINS; j += SCAN_THREADS) {
+      uint32_t c = s_hist[j];
+      if (c) atomic_add_agent(mine + j, c);
+    }
   }
-  if (!arrive_last(&ctrl->arrive_scan, gridDim.x)) return;
+  if (!arrive_last(ctrl->scan_grp, &ctrl->scan_top, gridDim.x)) return;
   // last workgroup: locate the digit of the R-th largest key
   const int t = threadIdx.x;
   if ((int64_t)a.R >= nblk) {
     if (t == 0) { ctrl->all = 1; ctrl->thr_digit = 0; ctrl->need = 0; }
   } else {
-    // thread t owns bins [4096-16(t+1), 4096-16t), top thread first
-    uint32_t c[16], sum = 0;
-    for (int j = 0; j < 16; ++j) {
-      c[j] = __hip_atomic_load(gh + (HIST_BINS - 1 - (16 * t + j)), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    // thread t owns bins HIST_BINS-1-(4t+j), j = 0..3 (top thread first),
+    // summed over the copies
+    constexpr int PER = HIST_BINS / SCAN_THREADS;
+    uint32_t v[PER][HIST_COPIES];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+#pragma unroll
+      for (int k = 0; k < HIST_COPIES; ++k)
+        v[j][k] = ld_agent(gh + k * HIST_BINS + (HIST_BINS - 1 - (PER * t + j)));
+    uint32_t c[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      c[j] = 0;
+#pragma unroll
+      for (int k = 0; k < HIST_COPIES; ++k) c[j] += v[j][k];
       sum += c[j];
     }
     uint32_t total;
@@ -298,9 +311,9 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
     const uint32_t R = (uint32_t)a.R;
     if (above < R && R <= above + sum) {
       uint32_t acc = above;
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < PER; ++j) {
         if (acc + c[j] >= R) {
-          ctrl->thr_digit = HIST_BINS - 1 - (16 * t + j);
+          ctrl->thr_digit = HIST_BINS - 1 - (PER * t + j);
           ctrl->need = R - acc;
           ctrl->all = 0;
           break;
@@ -310,8 +323,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
     }
   }
   __syncthreads();
-  for (int j = t; j < HIST_BINS; j += SCAN_THREADS) gh[j] = 0;
-  if (t == 0) ctrl->arrive_scan = 0;
+  for (int j = t; j < HIST_COPIES * HIST_BINS; j += SCAN_THREADS) gh[j] = 0;
 }
 
 // ---- select (after a full scan) ------------------------------------------
@@ -324,7 +336,7 @@ struct SelectArgs {
   Ctrl *ctrl;
   uint32_t *bitmap;         // [batch][nwords]
   int32_t nwords;           // per row, even
-  uint64_t *cands;          // [batch][cand_stride]
+  uint64_t *cands;          // [batch][CAND_COPIES][cand_stride]
   int64_t cand_stride;
   int32_t R;                // first-level count (pool or topk)
   int32_t *first_out;       // [batch][R]: pool_out, or idx_out when no pool
@@ -418,10 +430,13 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   const int64_t nblk = (n + BLOCK - 1) / BLOCK;
   const float *scores = a.scores + (int64_t)b * a.score_stride;
   uint32_t *bm = a.bitmap + (int64_t)b * a.nwords;
-  uint64_t *cands = a.cands + (int64_t)b * a.cand_stride;
+  uint64_t *cands = a.cands + (int64_t)b * CAND_COPIES * a.cand_stride;
   const bool all = ctrl->all != 0;
   const uint32_t thr = ctrl->thr_digit;
-  // 64 ids per wave step: ballot into two bitmap words
+  // 64 ids per wave step: the ballot of ids above the tie digit is OR-ed
+  // into the (zeroed) bitmap; ids in the tie digit go to one of 8 lists
+  uint64_t *mylist = cands + (blockIdx.x % CAND_COPIES) * a.cand_stride;
+  uint32_t *mycount = &ctrl->ncand[blockIdx.x % CAND_COPIES];
   const int chunks = a.nwords / 2;
   for (int ch = blockIdx.x * 4 + wv; ch < chunks; ch += gridDim.x * 4) {
     const int64_t id = (int64_t)ch * 64 + lane;
@@ -439,27 +454,40 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
       }
     }
     uint64_t m_in = __ballot(in);
-    if (lane == 0) { bm[2 * ch] = (uint32_t)m_in; bm[2 * ch + 1] = (uint32_t)(m_in >> 32); }
+    if (lane == 0 && (uint32_t)m_in) atomicOr(bm + 2 * ch, (uint32_t)m_in);
+    if (lane == 1 && (uint32_t)(m_in >> 32)) atomicOr(bm + 2 * ch + 1, (uint32_t)(m_in >> 32));
     uint64_t m_tie = __ballot(tie);
     if (m_tie) {
       uint32_t base = 0;
-      if (lane == 0) base = atomic_add_agent(&ctrl->ncand, (uint32_t)__popcll(m_tie));
+      if (lane == 0) base = atomic_add_agent(mycount, (uint32_t)__popcll(m_tie));
       base = __shfl(base, 0);
       if (tie) {
         uint32_t rank = (uint32_t)__popcll(m_tie & ((1ull << lane) - 1));
-        cands[base + rank] = ((uint64_t)key_hi << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+        st_agent(mylist + base + rank, ((uint64_t)key_hi << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id));
       }
     }
   }
-  if (!arrive_last(&ctrl->arrive_sel, gridDim.x)) return;
+  if (!arrive_last(ctrl->sel_grp, &ctrl->sel_top, gridDim.x)) return;
 
   // ---- finisher: one workgroup per sequence ----
   const int t = threadIdx.x, nt = blockDim.x;
   if (!all && nblk > 0) {
-    const int c = (int)__hip_atomic_load(&ctrl->ncand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t cnt[CAND_COPIES], off[CAND_COPIES + 1];
+    off[0] = 0;
+#pragma unroll
+    for (int k = 0; k < CAND_COPIES; ++k) {
+      cnt[k] = ld_agent(&ctrl->ncand[k]);
+      off[k + 1] = off[k] + cnt[k];
+    }
+    const int c = (int)off[CAND_COPIES];
     const int need = (int)ctrl->need;
     if (c <= a.lds_keys) {
-      for (int j = t; j < c; j += nt) { s_keys[j] = ld_agent(cands + j); s_valid[j] = 1; }
+#pragma unroll
+      for (int k = 0; k < CAND_COPIES; ++k)
+        for (int j = t; j < (int)cnt[k]; j += nt) {
+          s_keys[off[k] + j] = ld_agent(cands + k * a.cand_stride + j);
+          s_valid[off[k] + j] = 1;
+        }
       __syncthreads();
       uint64_t T = radix_threshold(s_keys, s_valid, c, need, s_hist, s_state);
       for (int j = t; j < c; j += nt) {
@@ -477,10 +505,11 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
       for (int shift = 56; shift >= 0; shift -= 8) {
         for (int j = t; j < 256; j += nt) s_hist[j] = 0;
         __syncthreads();
-        for (int j = t; j < c; j += nt) {
-          uint64_t k = ld_agent(cands + j);
-          if ((k & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(k >> shift) & 255u], 1u);
-        }
+        for (int k = 0; k < CAND_COPIES; ++k)
+          for (int j = t; j < (int)cnt[k]; j += nt) {
+            uint64_t key = ld_agent(cands + k * a.cand_stride + j);
+            if ((key & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(key >> shift) & 255u], 1u);
+          }
         __syncthreads();
         if (t == 0) {
           uint32_t acc = 0;
@@ -502,15 +531,16 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
         remaining = (int)(uint32_t)st;
         if (st >> 63) break;
       }
-      for (int j = t; j < c; j += nt) {
-        uint64_t k = ld_agent(cands + j);
-        if (k >= prefix) {
-          uint32_t id = 0xFFFFFFFFu - (uint32_t)k;
-          atomicOr(&bm[id >> 5], 1u << (id & 31));
+      for (int k = 0; k < CAND_COPIES; ++k)
+        for (int j = t; j < (int)cnt[k]; j += nt) {
+          uint64_t key = ld_agent(cands + k * a.cand_stride + j);
+          if (key >= prefix) {
+            uint32_t id = 0xFFFFFFFFu - (uint32_t)key;
+            atomicOr(&bm[id >> 5], 1u << (id & 31));
+          }
         }
-      }
     }
-    __threadfence_block();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   int32_t *first = a.first_out + (int64_t)b * a.R;
@@ -543,13 +573,13 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
                   s_hist, s_state, s_wave);
   }
   __syncthreads();
+  // leave the row clean for the next call (read only by later kernels)
   for (int j = t; j < a.nwords; j += nt) bm[j] = 0;
+  if (t < CAND_COPIES) ctrl->ncand[t] = 0;
   if (t == 0) {
-    ctrl->ncand = 0;
     ctrl->all = 0;
     ctrl->need = 0;
     ctrl->thr_digit = 0;
-    ctrl->arrive_sel = 0;
   }
 }
 
@@ -604,9 +634,9 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
       if (blk >= 0 && blk < nblk) {
         const int cnt = (int)min((int64_t)BLOCK, n - (int64_t)blk * BLOCK);
         float s = block_score(cur, cnt, qb);
-        if (i == 0) scores[j] = s;
+        if (i == 0) { if (SELECT) st_agent(scores + j, s); else scores[j] = s; }
       } else if (i == 0) {
-        scores[j] = -__builtin_huge_valf();
+        if (SELECT) st_agent(scores + j, -__builtin_huge_valf()); else scores[j] = -__builtin_huge_valf();
         if (blk >= nblk) raise_flag(FLAG_BAD_INDEX);
       }
     }
@@ -618,7 +648,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   }
   if (!SELECT) return;
   Ctrl *ctrl = a.ctrl + b;
-  if (!arrive_last(&ctrl->arrive_sel, gridDim.x)) return;
+  if (!arrive_last(ctrl->sel_grp, &ctrl->sel_top, gridDim.x)) return;
   const int t = threadIdx.x, nt = blockDim.x;
   const int m = a.n_cand;
   constexpr int U = 8;
@@ -644,8 +674,6 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   __syncthreads();
   select_in_lds(s_keys, s_valid, cand, m, a.topk, a.idx_out + (int64_t)b * a.topk, a.topk,
                 s_hist, s_state, s_wave);
-  __syncthreads();
-  if (t == 0) ctrl->arrive_sel = 0;
 }
 
 // Reuse: idx_out = prior (grid-stride copy).
