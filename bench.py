@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 TOKEN_BYTES = 288              # 256 code bytes + 32 scale bytes per position
 BLOCK_BYTES = 8 * TOKEN_BYTES  # 2,304
-PMC_FILE = os.path.join(ROOT, "profiles", "scan_kernel_decoder20-1m_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "scan_kernel_decoder20-1m_pmc.txt")
 SCAN_SOURCES = [os.path.join(ROOT, "fp4_compressed_sparse_amd", "csrc", f)
                 for f in ("index.hip", "common.hpp")]
 
@@ -155,17 +155,22 @@ def cpu_baseline(w):
     }
 
 
-def pmc_traffic(scan_launches_bytes):
-    """HBM bytes per scan launch from the committed rocprofv3 counter runs,
-    if they were taken on the current scan kernel source."""
+def pmc_traffic():
+    """HBM bytes per scan launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), if they
+    were taken on the current scan kernel source; else None."""
     try:
         with open(PMC_FILE) as f:
-            p = json.load(f)
-    except (OSError, ValueError):
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
         return None
-    if p.get("source_sha") != scan_source_sha():
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha") != scan_source_sha():
         return None
-    return p.get("hbm_bytes_per_launch")
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 class HipEvents:
@@ -341,7 +346,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": pmc_traffic(scan_bytes),
+            "traffic": pmc_traffic(),
             "algorithmic_bytes_per_launch": scan_bytes,
             "avg_launch_us": round(scan_avg_s * 1e6, 2),
         },

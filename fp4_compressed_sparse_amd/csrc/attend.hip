@@ -46,14 +46,10 @@ struct AttendArgs {
   float scale_log2;         // scale * log2(e)
   int32_t n_stages;         // ceil(topk*8 / SP)
   int32_t splits;           // workgroups per sequence
-  float *part_o;            // [batch][splits][4][16][512]
-  float *part_ml;           // [batch][splits][4][16][2]
+  float *part_o;            // [batch][splits][4 waves][32 tiles][64 lanes][4]: the O^T
+                            // accumulators in lane order (contiguous stores)
+  float *part_ml;           // [batch][splits][4 waves][16 heads][2]
 };
-
-// Channel of row m of O^T tile ct (see the V^T read pattern below).
-__device__ __forceinline__ int tile_channel(int ct, int m) {
-  return 128 * (ct >> 3) + 4 * (ct & 7) + 32 * (m >> 2) + (m & 3);
-}
 
 template <int HT>   // head tiles of 16: 1, 2 or 4
 __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs a) {
@@ -77,6 +73,37 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   // stage range of this workgroup
   const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
   const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
+
+  // ---- gathered rows of a stage: block ids, then rows (two round trips) --
+  constexpr int PASSES = SP / 16;         // rows per thread per stage
+  const int i16 = tid & 15;               // this thread's 16-byte column of a row
+  int64_t posv[PASSES];
+  bool okv[PASSES];
+  u32x4 wr[PASSES];
+  uint32_t scr[PASSES];
+  auto fetch_stage = [&](int st) {
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      const int pp = (tid >> 4) + 16 * k;
+      const int j = st * SP + pp;
+      const int32_t blk = j < total_pos ? idx[j >> 3] : -1;
+      posv[k] = (int64_t)blk * BLOCK + (j & 7);
+      okv[k] = blk >= 0 && blk < nblk && posv[k] < n;
+      if (blk >= nblk && i16 == 0 && (j & 7) == 0) raise_flag(FLAG_BAD_INDEX);
+    }
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      if (okv[k]) {
+        wr[k] = *reinterpret_cast<const u32x4 *>(codes + posv[k] * CODE_BYTES + 16 * i16);
+        scr[k] = *reinterpret_cast<const uint16_t *>(scales + posv[k] * SCALE_BYTES + 2 * i16);
+      } else {
+        wr[k] = u32x4{0u, 0u, 0u, 0u};
+        scr[k] = 0u;
+      }
+    }
+  };
+  // the first stage's rows are requested before the query is staged
+  if (st0 < st1) fetch_stage(st0);
 
   // Q^T operand: head ht*16 + n16, channels 32*kc + 8*g + 0..7.  q is staged
   // through LDS (coalesced float4 loads issued 16 per thread at a time,
@@ -112,61 +139,35 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   float m_run = -__builtin_huge_valf();   // running max of this lane's head (log2 domain)
   float l_run = 0.f;                      // this lane's share of the softmax sum
 
+#pragma unroll 1
   for (int st = st0; st < st1; ++st) {
-    __syncthreads();                      // previous stage fully consumed
-    // ---- load + dequantise SP positions into LDS (16 threads per row) ----
-    // all block ids first, then all rows, then convert: two memory round
-    // trips per stage instead of two per row
-    {
-      constexpr int PASSES = SP / 16;
-      const int i = tid & 15;
-      int64_t posv[PASSES];
-      bool okv[PASSES];
+    __syncthreads();                      // query / previous stage fully consumed
+    if (st != st0) fetch_stage(st);
+    // ---- dequantise the stage's rows into LDS as fp16 (16 threads per row) ----
 #pragma unroll
-      for (int k = 0; k < PASSES; ++k) {
-        const int pp = (tid >> 4) + 16 * k;
-        const int j = st * SP + pp;
-        const int32_t blk = j < total_pos ? idx[j >> 3] : -1;
-        posv[k] = (int64_t)blk * BLOCK + (j & 7);
-        okv[k] = blk >= 0 && blk < nblk && posv[k] < n;
-        if (blk >= nblk && i == 0 && (j & 7) == 0) raise_flag(FLAG_BAD_INDEX);
+    for (int k = 0; k < PASSES; ++k) {
+      const int pp = (tid >> 4) + 16 * k;
+      const _Float16 s0 = (_Float16)e4m3_to_f32(scr[k] & 0xffu);
+      const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
+      const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
+      u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i16);
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) {
+        const f16x2 sv = dw < 2 ? sv0 : sv1;
+        f16x2 h0 = e2m1x2_to_f16<0>(wr[k][dw]) * sv;
+        f16x2 h1 = e2m1x2_to_f16<1>(wr[k][dw]) * sv;
+        f16x2 h2 = e2m1x2_to_f16<2>(wr[k][dw]) * sv;
+        f16x2 h3 = e2m1x2_to_f16<3>(wr[k][dw]) * sv;
+        dst[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                        __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
       }
-      u32x4 wr[PASSES];
-      uint32_t scr[PASSES];
-#pragma unroll
-      for (int k = 0; k < PASSES; ++k) {
-        if (okv[k]) {
-          wr[k] = *reinterpret_cast<const u32x4 *>(codes + posv[k] * CODE_BYTES + 16 * i);
-          scr[k] = *reinterpret_cast<const uint16_t *>(scales + posv[k] * SCALE_BYTES + 2 * i);
-        } else {
-          wr[k] = u32x4{0u, 0u, 0u, 0u};
-          scr[k] = 0u;
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < PASSES; ++k) {
-        const int pp = (tid >> 4) + 16 * k;
-        const _Float16 s0 = (_Float16)e4m3_to_f32(scr[k] & 0xffu);
-        const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
-        const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
-        u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i);
-#pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-          const f16x2 sv = dw < 2 ? sv0 : sv1;
-          f16x2 h0 = e2m1x2_to_f16<0>(wr[k][dw]) * sv;
-          f16x2 h1 = e2m1x2_to_f16<1>(wr[k][dw]) * sv;
-          f16x2 h2 = e2m1x2_to_f16<2>(wr[k][dw]) * sv;
-          f16x2 h3 = e2m1x2_to_f16<3>(wr[k][dw]) * sv;
-          dst[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
-                          __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
-        }
-        if (i == 0) s_ok[pp] = okv[k] ? 1 : 0;
-      }
+      if (i16 == 0) s_ok[pp] = okv[k] ? 1 : 0;
     }
     __syncthreads();
 
-    // ---- this wave's 32-position sub-tiles of the stage ----
-#pragma unroll
+    // ---- this wave's 32-position sub-tiles of the stage (kept as a loop:
+    // every dispatch starts with a cold instruction cache) ----
+#pragma unroll 1
     for (int sub = 0; sub < NSUB; ++sub) {
       const int base = 32 * (wsub * NSUB + sub);          // first row of the sub-tile
       f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -215,7 +216,9 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
       }
       const f16x8 pop = {ph[0], ph[1], ph[2], ph[3], ph[4], ph[5], ph[6], ph[7]};
       // V^T operand rows (k) = positions base + 4g + 0..3 then base + 16 + 4g + 0..3;
-      // source lane s = 4r + q points at row k0 + r, channel n0 + 32q
+      // source lane s = 4r + q points at row k0 + r, channel n0 + 32q, so row
+      // m of O^T tile ct holds channel 128*(ct/8) + 4*(ct%8) + 32*(m/4) + m%4
+      // (groups of 4 lanes read 8 bytes 64 bytes apart: no LDS bank conflict)
       const int r_src = n16 >> 2, q_src = n16 & 3;
       const _Float16 *v0 = s_v + (base + 4 * g + r_src) * ROW_HALVES + 32 * q_src;
       const _Float16 *v1 = v0 + 16 * ROW_HALVES;
@@ -237,12 +240,9 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   l_tot += __shfl_xor(l_tot, 16);
   l_tot += __shfl_xor(l_tot, 32);
   const int64_t slot = ((int64_t)b * a.splits + split) * 4 + wv;
-  float *po = a.part_o + (slot * 16 + n16) * D;
+  f32x4 *po = reinterpret_cast<f32x4 *>(a.part_o + slot * (16 * D)) + lane;
 #pragma unroll
-  for (int ct = 0; ct < 32; ++ct) {
-    const int c = tile_channel(ct, 4 * g);
-    *reinterpret_cast<f32x4 *>(po + c) = acc[ct];
-  }
+  for (int ct = 0; ct < 32; ++ct) po[ct * 64] = acc[ct];
   if (g == 0) {
     float *pm = a.part_ml + (slot * 16 + n16) * 2;
     pm[0] = m_run;
@@ -259,51 +259,55 @@ struct CombineArgs {
 };
 
 // grid (heads, batch), 128 threads x 4 channels: merge every partial of a
-// head.  Up to 32 slots are loaded in one batch (one memory round trip).
+// head.  The (max, sum) of every slot go through LDS first (vector loads;
+// uniform-address loads would become serialised scalar loads), then each
+// thread reads its 4 channels of every slot, 8 slots per batch.
+constexpr int MAX_SLOTS = 1024;
 __global__ void __launch_bounds__(128) attend_combine_kernel(CombineArgs a) {
-  constexpr int U = 32;
-  const int hh = blockIdx.x, b = blockIdx.y;
+  __shared__ float s_m[MAX_SLOTS], s_l[MAX_SLOTS];
+  constexpr int U = 8;
+  const int hh = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int HT = a.heads / 16, ht = hh / 16, n16 = hh % 16;
   const int WPT = 4 / HT;
   const int nslots = a.splits * WPT;
-  float M = -__builtin_huge_valf(), L = 0.f;
+  auto slot_of = [&](int s) -> int64_t {
+    return ((int64_t)b * a.splits + s / WPT) * 4 + ht + HT * (s % WPT);
+  };
+  float M = -__builtin_huge_valf();
+  for (int s = t; s < nslots; s += 128) {
+    const float2 ml = reinterpret_cast<const float2 *>(a.part_ml)[slot_of(s) * 16 + n16];
+    s_m[s] = ml.x;
+    s_l[s] = ml.y;
+  }
+  __syncthreads();
+  for (int s = 0; s < nslots; ++s) M = fmaxf(M, s_m[s]);
+  // channels 4t..4t+3 live in tile ct, lane 16g + n16 of the wave's partial
+  const int ct = 8 * (t >> 5) + (t & 7), g = (t >> 3) & 3;
+  const int64_t within = (int64_t)(ct * 64 + 16 * g + n16) * 4;
+  float L = 0.f;
   float4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nslots; s0 += U) {
-    float mv[U], lv[U];
-    float4 ov[U];
+  if (M != -__builtin_huge_valf()) {
+#pragma unroll 1
+    for (int s0 = 0; s0 < nslots; s0 += U) {
+      float4 ov[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (s0 + u < nslots) {
-        const int s = s0 + u;
-        const int split = s / WPT, w = ht + HT * (s % WPT);
-        const int64_t sl = (((int64_t)b * a.splits + split) * 4 + w) * 16 + n16;
-        mv[u] = a.part_ml[sl * 2];
-        lv[u] = a.part_ml[sl * 2 + 1];
-        ov[u] = reinterpret_cast<const float4 *>(a.part_o + sl * D)[threadIdx.x];
-      } else {
-        mv[u] = -__builtin_huge_valf();
-        lv[u] = 0.f;
-        ov[u] = float4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < U; ++u)
+        ov[u] = (s0 + u < nslots) ? *reinterpret_cast<const float4 *>(a.part_o + slot_of(s0 + u) * (16 * D) + within)
+                                  : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u >= nslots) break;
+        const float m = s_m[s0 + u];
+        if (m == -__builtin_huge_valf()) continue;
+        const float e = __builtin_amdgcn_exp2f(m - M);
+        L += e * s_l[s0 + u];
+        o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
       }
-    }
-    float Mb = M;
-#pragma unroll
-    for (int u = 0; u < U; ++u) Mb = fmaxf(Mb, mv[u]);
-    if (Mb == -__builtin_huge_valf()) continue;
-    const float r = __builtin_amdgcn_exp2f(M - Mb);     // rescale what was summed so far
-    L *= r; o.x *= r; o.y *= r; o.z *= r; o.w *= r;
-    M = Mb;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (mv[u] == -__builtin_huge_valf()) continue;
-      const float e = __builtin_amdgcn_exp2f(mv[u] - M);
-      L += e * lv[u];
-      o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
-  reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.heads + hh) * D)[threadIdx.x] = o;
+  reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.heads + hh) * D)[t] = o;
 }
 
 template __global__ void attend_partial_kernel<1>(AttendArgs);

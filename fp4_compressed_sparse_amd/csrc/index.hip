@@ -59,20 +59,22 @@ struct ScanArgs {
 };
 
 // Qbar of sequence b into LDS; all 256 threads call.  Each thread owns two
-// channels and adds the heads in order; the loads of 16 heads are issued
-// together so the sum costs a few memory round trips, not one per head.
+// channels and adds the heads in order; the loads of HB heads are issued
+// together so the sum costs 64/HB memory round trips, not one per head
+// (HB = 16 keeps the scan's register budget; the pool rescoring uses 64).
+template <int HB>
 __device__ __forceinline__ void compute_qbar(const float *__restrict__ q, int heads, int b,
                                              float *s_qbar) {
   const int t = threadIdx.x;
   const float2 *qp = reinterpret_cast<const float2 *>(q + (int64_t)b * heads * D) + t;
   float2 acc = qp[0];
-  for (int h0 = 1; h0 < heads; h0 += 16) {
-    float2 v[16];
+  for (int h0 = 1; h0 < heads; h0 += HB) {
+    float2 v[HB];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < HB; ++j)
       v[j] = (h0 + j < heads) ? qp[(int64_t)(h0 + j) * (D / 2)] : make_float2(0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < HB; ++j) {
       if (h0 + j < heads) { acc.x = acc.x + v[j].x; acc.y = acc.y + v[j].y; }
     }
   }
@@ -253,7 +255,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
   int64_t blk = (int64_t)it * BLOCKS_PER_ITER + wv * 4 + slot;
   BlockRows cur;
   if (it < iters && blk < nblk) load_block(cur, codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES, i);
-  compute_qbar(a.q, a.heads, b, s_qbar);
+  compute_qbar<16>(a.q, a.heads, b, s_qbar);
   const float *qb = s_qbar + 32 * i;
   for (; it < iters; it += gridDim.x) {
     if (blk < nblk) {
@@ -482,12 +484,24 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
     const int c = (int)off[CAND_COPIES];
     const int need = (int)ctrl->need;
     if (c <= a.lds_keys) {
+      // flat index over the 8 lists, 8 loads in flight per thread
+      constexpr int U = 8;
+      for (int j0 = t; j0 < c; j0 += nt * U) {
+        uint64_t kv[U];
 #pragma unroll
-      for (int k = 0; k < CAND_COPIES; ++k)
-        for (int j = t; j < (int)cnt[k]; j += nt) {
-          s_keys[off[k] + j] = ld_agent(cands + k * a.cand_stride + j);
-          s_valid[off[k] + j] = 1;
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * nt;
+          int k = 0;
+#pragma unroll
+          for (int kk = 1; kk < CAND_COPIES; ++kk) k += (j >= (int)off[kk]) ? 1 : 0;
+          kv[u] = j < c ? ld_agent(cands + k * a.cand_stride + (j - (int)off[k])) : 0ull;
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * nt;
+          if (j < c) { s_keys[j] = kv[u]; s_valid[j] = 1; }
+        }
+      }
       __syncthreads();
       uint64_t T = radix_threshold(s_keys, s_valid, c, need, s_hist, s_state);
       for (int j = t; j < c; j += nt) {
@@ -627,7 +641,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   BlockRows cur;
   if (blk >= 0 && blk < nblk)
     load_block(cur, codes + (int64_t)blk * BLOCK * CODE_BYTES, scales + (int64_t)blk * BLOCK * SCALE_BYTES, i);
-  compute_qbar(a.q, a.heads, b, s_qbar);
+  compute_qbar<64>(a.q, a.heads, b, s_qbar);
   const float *qb = s_qbar + 32 * i;
   for (; it < iters; it += gridDim.x) {
     if (j < a.n_cand) {
