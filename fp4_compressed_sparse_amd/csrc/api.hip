@@ -61,11 +61,7 @@ csa2_status device_ready() {
       state[dev] = 2;
     } else {
       const int big = 160 * 1024 - 16 * 1024;
-      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel<1>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
-      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel<2>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
-      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel<4>),
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, big);
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, big);
@@ -81,16 +77,15 @@ csa2_status device_ready() {
 
 // ---- workspace layout ----------------------------------------------------
 
-int att_positions_per_stage(int heads) { return heads == 16 ? 128 : 64; }
-
-int att_splits(int batch, int n_stages) {
-  int want = (int)ceil_div(512, batch);
+int att_splits(int workgroup_rows, int n_stages) {
+  int want = (int)ceil_div(512, workgroup_rows);
   if (want < 1) want = 1;
+  if (want > MAX_SPLITS) want = MAX_SPLITS;
   return n_stages < want ? n_stages : want;
 }
 
 struct Layout {
-  size_t ctrl, hist, scores, bitmap, cands, part_o, part_ml, total;
+  size_t ctrl, hist, scores, bitmap, cands, qbar, part_o, part_ml, total;
   int64_t score_stride, cand_stride;
   int32_t nwords;
   int32_t att_stages, att_splits;
@@ -110,12 +105,13 @@ bool make_layout(int32_t batch, int32_t heads, int64_t max_len, int32_t pool, in
   L->scores = off; off = align256(off + sizeof(float) * (size_t)L->score_stride * batch);
   L->bitmap = off; off = align256(off + sizeof(uint32_t) * (size_t)L->nwords * batch);
   L->cands = off;  off = align256(off + sizeof(uint64_t) * CAND_COPIES * (size_t)L->cand_stride * batch);
+  L->qbar = off;   off = align256(off + sizeof(float) * D * (size_t)batch);
   L->att_stages = L->att_splits = 0;
   L->part_o = L->part_ml = off;
   if (heads == 16 || heads == 32 || heads == 64) {
-    L->att_stages = (int32_t)ceil_div((int64_t)topk * BLOCK, att_positions_per_stage(heads));
-    L->att_splits = att_splits(batch, L->att_stages);
-    const size_t slots = (size_t)batch * L->att_splits * 4 * 16;
+    L->att_stages = (int32_t)ceil_div((int64_t)topk * BLOCK, ATT_SP);
+    L->att_splits = att_splits(batch * (heads / 16), L->att_stages);
+    const size_t slots = (size_t)batch * L->att_splits * (heads / 16) * 16;
     L->part_o = off;  off = align256(off + sizeof(float) * slots * D);
     L->part_ml = off; off = align256(off + sizeof(float) * slots * 2);
   }
@@ -173,6 +169,9 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
   sa.scores = at<float>(ws, L.scores); sa.score_stride = L.score_stride;
   sa.ctrl = at<Ctrl>(ws, L.ctrl); sa.hist = at<uint32_t>(ws, L.hist);
   sa.R = R; sa.fill_invalid = 0;
+  sa.qbar = at<float>(ws, L.qbar);
+  qbar_kernel<<<B, SCAN_THREADS, 0, s>>>(q, heads, at<float>(ws, L.qbar));
+  if (csa2_status st = launched("qbar")) return st;
   const int iters = (int)ceil_div(nblk_grid > 0 ? nblk_grid : 1, BLOCKS_PER_ITER);
   dim3 g1(grid_for(iters, B, 1024), B);
   if (t_scan_before) (void)hipEventRecord(t_scan_before, s);
@@ -186,7 +185,7 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
   se.R = R; se.first_out = first_out; se.topk = topk2; se.idx_out = idx_out;
   int lk = R > 4096 ? R : 4096;
   se.lds_keys = lk;
-  dim3 g2(grid_for(ceil_div(L.nwords / 2, 4), B, 512), B);
+  dim3 g2(grid_for(ceil_div(L.nwords / 2, 4), B, 256), B);
   select_kernel<<<g2, SCAN_THREADS, (size_t)lk * sizeof(uint64_t), s>>>(se);
   return launched("select");
 }
@@ -221,15 +220,14 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   aa.scale_log2 = scale * 1.4426950408889634f;
   aa.n_stages = L.att_stages; aa.splits = L.att_splits;
   aa.part_o = at<float>(ws, L.part_o); aa.part_ml = at<float>(ws, L.part_ml);
-  dim3 g(L.att_splits, B);
-  const size_t lds = (size_t)att_positions_per_stage(heads) * ROW_HALVES * sizeof(_Float16);
-  if (heads == 16) attend_partial_kernel<1><<<g, ATT_THREADS, lds, s>>>(aa);
-  else if (heads == 32) attend_partial_kernel<2><<<g, ATT_THREADS, lds, s>>>(aa);
-  else attend_partial_kernel<4><<<g, ATT_THREADS, lds, s>>>(aa);
+  aa.heads = heads;
+  dim3 g(L.att_splits * (heads / 16), B);
+  const size_t lds = (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16);
+  attend_partial_kernel<<<g, ATT_THREADS, lds, s>>>(aa);
   if (csa2_status st = launched("attend")) return st;
   CombineArgs ca;
   ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = L.att_splits; ca.heads = heads; ca.out = out;
-  attend_combine_kernel<<<dim3(heads, B), 128, 0, s>>>(ca);
+  attend_combine_kernel<<<dim3((heads / 16) * 8, B), 256, 0, s>>>(ca);
   return launched("combine");
 }
 
@@ -395,7 +393,7 @@ csa2_status csa2_block_scores(const csa2_kv *kv, const float *q, int32_t heads, 
   sa.limit = kv->max_len;
   sa.q = q; sa.heads = heads; sa.nblk_grid = (int32_t)nblk_grid;
   sa.scores = scores; sa.score_stride = nblk_grid; sa.ctrl = nullptr; sa.hist = nullptr;
-  sa.R = 0; sa.fill_invalid = 1;
+  sa.R = 0; sa.fill_invalid = 1; sa.qbar = nullptr;
   dim3 g(grid_for(ceil_div(nblk_grid, BLOCKS_PER_ITER), kv->batch, 512), kv->batch);
   scan_kernel<false><<<g, SCAN_THREADS, 0, s>>>(sa);
   return launched("scores");
@@ -477,6 +475,18 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
   }
   return CSA2_OK;
 }
+
+#ifdef CSA2_PHASE_TIMING
+// Profiling builds only: copy the phase timestamps to the host.
+int csa2_debug_phase_ts(void *host, size_t bytes) {
+  if (bytes > sizeof(g_phase_ts)) bytes = sizeof(g_phase_ts);
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_ts), bytes, 0, hipMemcpyDeviceToHost);
+}
+int csa2_debug_phase_clear(void) {
+  static unsigned long long zero[4096][TS_SLOTS];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_phase_ts), zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+}
+#endif
 
 csa2_status csa2_device_error(int32_t *flags_host, void *stream) {
   t_last_error.clear();

@@ -8,19 +8,18 @@
 // by all heads.
 //
 // Design (matrix cores, fp16 operands, fp32 accumulation):
-//  * A workgroup (4 waves) takes a range of "stages" of SP gathered
-//    positions.  Per stage the 256 threads load the FP4 codes and E4M3
-//    scales of the SP positions and write code*scale as fp16 rows into LDS
-//    (exact: at most 6 significant bits, range 2^-10..2688).
-//  * Each wave owns 16 heads (one MFMA tile) and 32-position sub-tiles:
-//      S^T = K Q^T   v_mfma_f32_16x16x32_f16, K rows read from LDS (b128),
-//                    Q in registers (fp16), 16 k-steps over 512 channels;
-//      online softmax in registers (exp2 domain);
-//      O^T += V^T P^T  32 channel tiles, V^T read straight from the
-//                    row-major LDS tile with ds_read_b64_tr_b16, P^T from
-//                    the S^T accumulators (lane layout already matches).
-//  * Each wave writes its (max, sum, O) partial; a combine kernel merges the
-//    partials of every head (split-K over positions).
+//  * A workgroup (4 waves) takes one 16-head tile and a range of "stages"
+//    of 64 gathered positions.  Per stage the 256 threads load the FP4 codes
+//    and E4M3 scales of the 64 positions and write code*scale as fp16 rows
+//    into LDS (exact: at most 6 significant bits, range 2^-10..2688).
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_f16 (K rows read from LDS with
+//    b128 reads, Q in registers as fp16), one 16-position tile per wave;
+//    online softmax in the exp2 domain with the stage's per-head max and
+//    sum exchanged through LDS; P stored to LDS as fp16;
+//    O^T += V^T P^T for 8 channel tiles per wave, V^T read straight from
+//    the row-major LDS tile with ds_read_b64_tr_b16.
+//  * Each workgroup writes its (max, sum, O) partial; a combine kernel
+//    merges the partials of every head (split-K over positions).
 //
 // MFMA 16x16x32 f16 lane layout (checked on gfx950): A row = lane%16 with
 // k = 8*(lane/16)..+7; B column = lane%16, same k; C column = lane%16,
@@ -32,7 +31,9 @@
 namespace csa2 {
 
 constexpr int ATT_THREADS = 256;
+constexpr int ATT_SP = 64;                        // gathered positions per stage
 constexpr int ROW_HALVES = D + 8;                 // LDS row stride: 1040 bytes
+constexpr int P_STRIDE = ATT_SP + 8;              // LDS P row stride (halves): no bank conflicts
 
 struct AttendArgs {
   const uint8_t *codes;
@@ -43,110 +44,128 @@ struct AttendArgs {
   const float *q;           // [batch][heads][512]
   const int32_t *idx;       // [batch][topk]
   int32_t topk;
+  int32_t heads;            // 16, 32 or 64
   float scale_log2;         // scale * log2(e)
-  int32_t n_stages;         // ceil(topk*8 / SP)
-  int32_t splits;           // workgroups per sequence
-  float *part_o;            // [batch][splits][4 waves][32 tiles][64 lanes][4]: the O^T
-                            // accumulators in lane order (contiguous stores)
-  float *part_ml;           // [batch][splits][4 waves][16 heads][2]
+  int32_t n_stages;         // ceil(topk*8 / ATT_SP)
+  int32_t splits;           // workgroups per (sequence, head tile)
+  float *part_o;            // [batch][splits][heads/16][32 tiles][64 lanes][4]: O^T accumulators
+                            // in lane order (contiguous stores)
+  float *part_ml;           // [batch][splits][heads/16][16 heads][2]: running max (log2) and sum
 };
 
-template <int HT>   // head tiles of 16: 1, 2 or 4
+// One workgroup = one 16-head tile x a range of stages of 64 gathered
+// positions.  Per stage: the 256 threads dequantise the 64 rows into LDS as
+// fp16; wave w computes S^T for positions 16w..16w+15 (16 MFMA k-steps);
+// the per-head max and sum of the stage are exchanged through LDS; P is
+// written to LDS as fp16; wave w then accumulates O^T for channel tiles
+// 8w..8w+7 over all 64 positions.
 __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs a) {
-  constexpr int WPT = 4 / HT;                     // waves per head tile
-  constexpr int NSUB = (HT == 4) ? 2 : 1;         // 32-position sub-tiles per wave per stage
-  constexpr int SP = 32 * NSUB * WPT;             // positions per stage: 64, 64, 128
-  extern __shared__ _Float16 s_v[];               // [SP][ROW_HALVES]
-  __shared__ uint8_t s_ok[SP];
+  extern __shared__ _Float16 s_v[];               // [ATT_SP][ROW_HALVES]; first holds q
+  __shared__ _Float16 s_p[16 * P_STRIDE];         // P: [16 heads][64 positions]
+  __shared__ float s_max[4][16], s_sum[4][16];
+  __shared__ uint8_t s_ok[ATT_SP];
 
-  const int b = blockIdx.y, split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int HT = a.heads >> 4;
+  const int ht = blockIdx.x % HT, split = blockIdx.x / HT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int ht = wv % HT, wsub = wv / HT;
   const int n16 = lane & 15, g = lane >> 4;
-  const int64_t n = clamp_len(a.seq_len[b], a.limit);
-  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  // The sequence length is only needed to mask positions: loads are bounded
+  // by the cache capacity, so they are issued without waiting for it.
+  const int64_t cap_blocks = a.capacity / BLOCK;  // blocks a load may touch
   const int32_t *idx = a.idx + (int64_t)b * a.topk;
   const uint8_t *codes = a.codes + (int64_t)b * a.capacity * CODE_BYTES;
   const uint8_t *scales = a.scales + (int64_t)b * a.capacity * SCALE_BYTES;
   const int total_pos = a.topk * BLOCK;
-
-  // stage range of this workgroup
   const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
   const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
 
   // ---- gathered rows of a stage: block ids, then rows (two round trips) --
-  constexpr int PASSES = SP / 16;         // rows per thread per stage
+  constexpr int PASSES = ATT_SP / 16;     // rows per thread per stage
   const int i16 = tid & 15;               // this thread's 16-byte column of a row
-  int64_t posv[PASSES];
+  int32_t blkv[PASSES];
   bool okv[PASSES];
   u32x4 wr[PASSES];
   uint32_t scr[PASSES];
-  auto fetch_stage = [&](int st) {
+  auto fetch_ids = [&](int st) {
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      const int pp = (tid >> 4) + 16 * k;
-      const int j = st * SP + pp;
-      const int32_t blk = j < total_pos ? idx[j >> 3] : -1;
-      posv[k] = (int64_t)blk * BLOCK + (j & 7);
-      okv[k] = blk >= 0 && blk < nblk && posv[k] < n;
-      if (blk >= nblk && i16 == 0 && (j & 7) == 0) raise_flag(FLAG_BAD_INDEX);
+      const int j = st * ATT_SP + (tid >> 4) + 16 * k;
+      blkv[k] = j < total_pos ? idx[j >> 3] : -1;
     }
+  };
+  auto fetch_rows = [&](int st) {
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
+      okv[k] = blkv[k] >= 0 && blkv[k] < cap_blocks;   // in bounds; masked by n later
       if (okv[k]) {
-        wr[k] = *reinterpret_cast<const u32x4 *>(codes + posv[k] * CODE_BYTES + 16 * i16);
-        scr[k] = *reinterpret_cast<const uint16_t *>(scales + posv[k] * SCALE_BYTES + 2 * i16);
+        const int64_t pos = (int64_t)blkv[k] * BLOCK + (((tid >> 4) + 16 * k) & 7);
+        wr[k] = *reinterpret_cast<const u32x4 *>(codes + pos * CODE_BYTES + 16 * i16);
+        scr[k] = *reinterpret_cast<const uint16_t *>(scales + pos * SCALE_BYTES + 2 * i16);
       } else {
         wr[k] = u32x4{0u, 0u, 0u, 0u};
         scr[k] = 0u;
       }
     }
   };
-  // the first stage's rows are requested before the query is staged
-  if (st0 < st1) fetch_stage(st0);
+  CSA2_TS(0);
+  // request order: the first stage's block ids, the query tile, then (once
+  // the ids are in) the rows, so the query and id latencies overlap
+  if (st0 < st1) fetch_ids(st0);
 
-  // Q^T operand: head ht*16 + n16, channels 32*kc + 8*g + 0..7.  q is staged
-  // through LDS (coalesced float4 loads issued 16 per thread at a time,
-  // stored as fp16 rows in the space the stages use later), then each lane
-  // reads its 16 operand chunks.
+  // ---- Q^T operand: head 16*ht + n16, channels 32*kc + 8*g + 0..7.  The
+  // tile's 16 query rows (32 KB) are staged through LDS as fp16 with one
+  // batch of coalesced float4 loads per thread, then read into registers.
   f16x8 qop[16];
   {
-    constexpr int NV = 16 * HT * D / 4 / ATT_THREADS;       // float4 per thread: 8*HT
-    constexpr int BATCH = NV < 16 ? NV : 16;
-    const float4 *src = reinterpret_cast<const float4 *>(a.q + (int64_t)b * (16 * HT) * D);
+    constexpr int NV = 16 * D / 4 / ATT_THREADS;            // 8 float4 per thread
+    const float4 *src = reinterpret_cast<const float4 *>(a.q + ((int64_t)b * a.heads + 16 * ht) * D);
+    float4 v[NV];
 #pragma unroll
-    for (int u0 = 0; u0 < NV; u0 += BATCH) {
-      float4 v[BATCH];
+    for (int u = 0; u < NV; ++u) v[u] = src[tid + u * ATT_THREADS];
+    if (st0 < st1) fetch_rows(st0);
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) v[u] = src[tid + (u0 + u) * ATT_THREADS];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int e = tid + (u0 + u) * ATT_THREADS;        // float4 index: head e/128, channels 4*(e%128)
-        f16x2 lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
-        *reinterpret_cast<u32x2 *>(s_v + (e >> 7) * ROW_HALVES + 4 * (e & 127)) =
-            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-      }
+    for (int u = 0; u < NV; ++u) {
+      const int e = tid + u * ATT_THREADS;                    // head e/128, channels 4*(e%128)
+      f16x2 lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
+      *reinterpret_cast<u32x2 *>(s_v + (e >> 7) * ROW_HALVES + 4 * (e & 127)) =
+          u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
     }
     __syncthreads();
-    const _Float16 *qrow = s_v + (ht * 16 + n16) * ROW_HALVES + 8 * g;
+    const _Float16 *qrow = s_v + n16 * ROW_HALVES + 8 * g;
 #pragma unroll
     for (int kc = 0; kc < 16; ++kc) qop[kc] = *reinterpret_cast<const f16x8 *>(qrow + 32 * kc);
   }
 
-  f32x4 acc[32];
+  const int64_t n = clamp_len(a.seq_len[b], a.limit);
+  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  CSA2_TS(1);
+  f32x4 acc[8];                           // O^T tiles 8*wv .. 8*wv+7
 #pragma unroll
-  for (int ct = 0; ct < 32; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_huge_valf();   // running max of this lane's head (log2 domain)
-  float l_run = 0.f;                      // this lane's share of the softmax sum
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_huge_valf();   // running max of head n16 (log2 domain)
+  float l_run = 0.f;                      // running sum of head n16
+
+  // V^T operand: rows (k) of chunk kk are positions 32*kk + 4g + 0..3 then
+  // 32*kk + 16 + 4g + 0..3; source lane s = 4r + q points at row k0 + r,
+  // channel n0 + 32q, so row m of O^T tile ct holds channel
+  // 128*(ct/8) + 4*(ct%8) + 32*(m/4) + m%4 (4 lanes of a group read 8 bytes
+  // 64 bytes apart: no LDS bank conflict).
+  const int r_src = n16 >> 2, q_src = n16 & 3;
 
 #pragma unroll 1
   for (int st = st0; st < st1; ++st) {
-    __syncthreads();                      // query / previous stage fully consumed
-    if (st != st0) fetch_stage(st);
+    __syncthreads();                      // q / previous stage fully consumed
+    if (st != st0) { fetch_ids(st); fetch_rows(st); }
     // ---- dequantise the stage's rows into LDS as fp16 (16 threads per row) ----
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
       const int pp = (tid >> 4) + 16 * k;
+      const int j = st * ATT_SP + pp;
+      const int32_t blk = blkv[k];
+      if ((j & 7) == 0 && i16 == 0 && blk >= nblk) raise_flag(FLAG_BAD_INDEX);
+      okv[k] = blk >= 0 && blk < nblk && (int64_t)blk * BLOCK + (j & 7) < n;
+      if (!okv[k]) { wr[k] = u32x4{0u, 0u, 0u, 0u}; scr[k] = 0u; }
       const _Float16 s0 = (_Float16)e4m3_to_f32(scr[k] & 0xffu);
       const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
       const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
@@ -165,89 +184,94 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     }
     __syncthreads();
 
-    // ---- this wave's 32-position sub-tiles of the stage (kept as a loop:
-    // every dispatch starts with a cold instruction cache) ----
-#pragma unroll 1
-    for (int sub = 0; sub < NSUB; ++sub) {
-      const int base = 32 * (wsub * NSUB + sub);          // first row of the sub-tile
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    CSA2_TS(2);
+    // ---- S^T for positions 16*wv .. 16*wv+15 ----
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    {
+      const _Float16 *krow = s_v + (16 * wv + n16) * ROW_HALVES + 8 * g;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const _Float16 *krow = s_v + (base + 16 * t + n16) * ROW_HALVES + 8 * g;
-#pragma unroll
-        for (int kc = 0; kc < 16; ++kc) {
-          f16x8 kop = *reinterpret_cast<const f16x8 *>(krow + 32 * kc);
-          sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kc], sacc[t], 0, 0, 0);
-        }
+      for (int kc = 0; kc < 16; ++kc) {
+        f16x8 kop = *reinterpret_cast<const f16x8 *>(krow + 32 * kc);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kc], sacc, 0, 0, 0);
       }
-      // lane (head n16, group g) holds logits of rows 4g..4g+3 of tiles 0 and 1:
-      // positions base + 4g + r and base + 16 + 4g + r
-      float z[8];
+    }
+    // lane (head n16, group g) holds positions 16*wv + 4g + r
+    float z[4];
+    float mx = -__builtin_huge_valf();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      z[r] = s_ok[16 * wv + 4 * g + r] ? sacc[r] * a.scale_log2 : -__builtin_huge_valf();
+      mx = fmaxf(mx, z[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) s_max[wv][n16] = mx;
+    __syncthreads();
+    const float m_new = fmaxf(m_run, fmaxf(fmaxf(s_max[0][n16], s_max[1][n16]),
+                                           fmaxf(s_max[2][n16], s_max[3][n16])));
+    _Float16 ph[4];
+    float psum = 0.f, corr = 1.f;
+    if (m_new == -__builtin_huge_valf()) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ph[r] = (_Float16)0.f;
+    } else {
+      corr = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        z[r] = s_ok[base + 4 * g + r] ? sacc[0][r] * a.scale_log2 : -__builtin_huge_valf();
-        z[4 + r] = s_ok[base + 16 + 4 * g + r] ? sacc[1][r] * a.scale_log2 : -__builtin_huge_valf();
+        ph[r] = (_Float16)__builtin_amdgcn_exp2f(z[r] - m_new);
+        psum += (float)ph[r];
       }
-      float mx = z[0];
+    }
+    *reinterpret_cast<u32x2 *>(s_p + n16 * P_STRIDE + 16 * wv + 4 * g) =
+        u32x2{__builtin_bit_cast(uint32_t, f16x2{ph[0], ph[1]}),
+              __builtin_bit_cast(uint32_t, f16x2{ph[2], ph[3]})};
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    if (g == 0) s_sum[wv][n16] = psum;
+    __syncthreads();
+    CSA2_TS(3);
+    l_run = l_run * corr + ((s_sum[0][n16] + s_sum[1][n16]) + (s_sum[2][n16] + s_sum[3][n16]));
+    m_run = m_new;
+    if (corr != 1.f) {
 #pragma unroll
-      for (int r = 1; r < 8; ++r) mx = fmaxf(mx, z[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      float corr = 1.f;
-      _Float16 ph[8];
-      if (m_new == -__builtin_huge_valf()) {
+      for (int t = 0; t < 8; ++t) acc[t] *= corr;
+    }
+
+    // ---- O^T tiles 8*wv .. 8*wv+7 over the stage's 64 positions ----
 #pragma unroll
-        for (int r = 0; r < 8; ++r) ph[r] = (_Float16)0.f;
-      } else {
-        corr = __builtin_amdgcn_exp2f(m_run - m_new);
-        float psum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          ph[r] = (_Float16)__builtin_amdgcn_exp2f(z[r] - m_new);
-          psum += (float)ph[r];
-        }
-        l_run = l_run * corr + psum;
-        m_run = m_new;
-      }
-      if (corr != 1.f) {
-#pragma unroll
-        for (int ct = 0; ct < 32; ++ct) acc[ct] *= corr;
-      }
-      const f16x8 pop = {ph[0], ph[1], ph[2], ph[3], ph[4], ph[5], ph[6], ph[7]};
-      // V^T operand rows (k) = positions base + 4g + 0..3 then base + 16 + 4g + 0..3;
-      // source lane s = 4r + q points at row k0 + r, channel n0 + 32q, so row
-      // m of O^T tile ct holds channel 128*(ct/8) + 4*(ct%8) + 32*(m/4) + m%4
-      // (groups of 4 lanes read 8 bytes 64 bytes apart: no LDS bank conflict)
-      const int r_src = n16 >> 2, q_src = n16 & 3;
+    for (int kk = 0; kk < 2; ++kk) {
+      const int base = 32 * kk;
+      const u32x2 p_lo = *reinterpret_cast<const u32x2 *>(s_p + n16 * P_STRIDE + base + 4 * g);
+      const u32x2 p_hi = *reinterpret_cast<const u32x2 *>(s_p + n16 * P_STRIDE + base + 16 + 4 * g);
+      const f16x8 pop = __builtin_bit_cast(f16x8, u32x4{p_lo[0], p_lo[1], p_hi[0], p_hi[1]});
       const _Float16 *v0 = s_v + (base + 4 * g + r_src) * ROW_HALVES + 32 * q_src;
       const _Float16 *v1 = v0 + 16 * ROW_HALVES;
 #pragma unroll
-      for (int ct = 0; ct < 32; ++ct) {
+      for (int t = 0; t < 8; ++t) {
+        const int ct = 8 * wv + t;
         const int n0 = 128 * (ct >> 3) + 4 * (ct & 7);
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4 *)(v0 + n0));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4 *)(v1 + n0));
         f16x8 vop = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, acc[ct], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, acc[t], 0, 0, 0);
       }
     }
   }
 
-  // ---- write this wave's partial: O^T rows 4g..4g+3 of every tile ----
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const int64_t slot = ((int64_t)b * a.splits + split) * 4 + wv;
+  CSA2_TS(4);
+  // ---- partial of this (sequence, split, head tile) ----
+  const int64_t slot = ((int64_t)b * a.splits + split) * HT + ht;
   f32x4 *po = reinterpret_cast<f32x4 *>(a.part_o + slot * (16 * D)) + lane;
 #pragma unroll
-  for (int ct = 0; ct < 32; ++ct) po[ct * 64] = acc[ct];
-  if (g == 0) {
+  for (int t = 0; t < 8; ++t) po[(8 * wv + t) * 64] = acc[t];
+  if (wv == 0 && g == 0) {
     float *pm = a.part_ml + (slot * 16 + n16) * 2;
     pm[0] = m_run;
-    pm[1] = l_tot;
+    pm[1] = l_run;
   }
+  CSA2_TS(5);
 }
 
 struct CombineArgs {
@@ -258,60 +282,61 @@ struct CombineArgs {
   float *out;               // [batch][heads][512]
 };
 
-// grid (heads, batch), 128 threads x 4 channels: merge every partial of a
-// head.  The (max, sum) of every slot go through LDS first (vector loads;
-// uniform-address loads would become serialised scalar loads), then each
-// thread reads its 4 channels of every slot, 8 slots per batch.
-constexpr int MAX_SLOTS = 1024;
-__global__ void __launch_bounds__(128) attend_combine_kernel(CombineArgs a) {
-  __shared__ float s_m[MAX_SLOTS], s_l[MAX_SLOTS];
-  constexpr int U = 8;
-  const int hh = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int HT = a.heads / 16, ht = hh / 16, n16 = hh % 16;
-  const int WPT = 4 / HT;
-  const int nslots = a.splits * WPT;
-  auto slot_of = [&](int s) -> int64_t {
-    return ((int64_t)b * a.splits + s / WPT) * 4 + ht + HT * (s % WPT);
-  };
-  float M = -__builtin_huge_valf();
-  for (int s = t; s < nslots; s += 128) {
-    const float2 ml = reinterpret_cast<const float2 *>(a.part_ml)[slot_of(s) * 16 + n16];
-    s_m[s] = ml.x;
-    s_l[s] = ml.y;
+// grid (heads/16 * 8, batch), 256 threads: one workgroup merges one eighth
+// (4 O^T tiles = 4 KB) of every split's partial of one head tile, so each
+// slot is read with one coalesced 4 KB load per workgroup; the per-head
+// (max, sum) of every slot go through LDS.
+constexpr int MAX_SPLITS = 256;
+__global__ void __launch_bounds__(256) attend_combine_kernel(CombineArgs a) {
+  __shared__ float s_m[MAX_SPLITS * 16], s_l[MAX_SPLITS * 16];
+  constexpr int U = 32;
+  const int b = blockIdx.y, t = threadIdx.x;
+  const int HT = a.heads / 16, ht = blockIdx.x >> 3, chunk = blockIdx.x & 7;
+  const int nslots = a.splits;
+  const int ct = 4 * chunk + (t >> 6), lane = t & 63, n16 = lane & 15, g = lane >> 4;
+  CSA2_TS(8);
+  for (int j = t; j < nslots * 16; j += 256) {
+    const int64_t sl = ((int64_t)b * a.splits + (j >> 4)) * HT + ht;
+    const float2 ml = reinterpret_cast<const float2 *>(a.part_ml)[sl * 16 + (j & 15)];
+    s_m[j] = ml.x;
+    s_l[j] = ml.y;
   }
   __syncthreads();
-  for (int s = 0; s < nslots; ++s) M = fmaxf(M, s_m[s]);
-  // channels 4t..4t+3 live in tile ct, lane 16g + n16 of the wave's partial
-  const int ct = 8 * (t >> 5) + (t & 7), g = (t >> 3) & 3;
-  const int64_t within = (int64_t)(ct * 64 + 16 * g + n16) * 4;
+  CSA2_TS(9);
+  float M = -__builtin_huge_valf();
+  for (int s = 0; s < nslots; ++s) M = fmaxf(M, s_m[s * 16 + n16]);
   float L = 0.f;
   float4 o = {0.f, 0.f, 0.f, 0.f};
   if (M != -__builtin_huge_valf()) {
+    const float4 *base = reinterpret_cast<const float4 *>(a.part_o) + (int64_t)chunk * 256 + t;
 #pragma unroll 1
     for (int s0 = 0; s0 < nslots; s0 += U) {
+      // every partial is written (an empty one as m = -inf, O = 0), so a
+      // batch past the last slot re-reads that slot with weight 0: the loads
+      // are unconditional and issue back to back
       float4 ov[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        ov[u] = (s0 + u < nslots) ? *reinterpret_cast<const float4 *>(a.part_o + slot_of(s0 + u) * (16 * D) + within)
-                                  : float4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < U; ++u) {
+        const int su = min(s0 + u, nslots - 1);
+        ov[u] = base[(((int64_t)b * a.splits + su) * HT + ht) * (16 * D / 4)];
+      }
+      __builtin_amdgcn_sched_barrier(0);      // keep the batch's loads ahead of their uses
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (s0 + u >= nslots) break;
-        const float m = s_m[s0 + u];
-        if (m == -__builtin_huge_valf()) continue;
-        const float e = __builtin_amdgcn_exp2f(m - M);
-        L += e * s_l[s0 + u];
+        const int su = min(s0 + u, nslots - 1);
+        const float m = s_m[su * 16 + n16];
+        const float e = (s0 + u < nslots && m != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(m - M) : 0.f;
+        L += e * s_l[su * 16 + n16];
         o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
       }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
-  reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.heads + hh) * D)[t] = o;
+  // lane (n16, g) of tile ct holds channels 128*(ct/8) + 4*(ct%8) + 32*g + 0..3
+  const int c0 = 128 * (ct >> 3) + 4 * (ct & 7) + 32 * g;
+  *reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.heads + 16 * ht + n16) * D + c0) = o;
+  CSA2_TS(10);
 }
-
-template __global__ void attend_partial_kernel<1>(AttendArgs);
-template __global__ void attend_partial_kernel<2>(AttendArgs);
-template __global__ void attend_partial_kernel<4>(AttendArgs);
 
 }  // namespace csa2

@@ -80,6 +80,25 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Phase timestamps for profiling builds only (compiled with
+// -DCSA2_PHASE_TIMING; the normal build compiles the hook away).  Thread 0
+// of each workgroup records s_memrealtime (100 MHz) after its wave's memory
+// operations complete.
+#ifdef CSA2_PHASE_TIMING
+constexpr int TS_SLOTS = 16;
+__device__ unsigned long long g_phase_ts[4096][TS_SLOTS];
+#define CSA2_TS(k)                                                                     \
+  do {                                                                                 \
+    __builtin_amdgcn_s_waitcnt(0);                                                     \
+    const unsigned wg_ = blockIdx.x + blockIdx.y * gridDim.x;                          \
+    if (threadIdx.x == 0 && wg_ < 4096) g_phase_ts[wg_][k] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define CSA2_TS(k) \
+  do {             \
+  } while (0)
+#endif
+
 // Device-wide flag word; read and cleared by csa2_device_error.
 extern __device__ uint32_t g_flags;
 __device__ __forceinline__ void raise_flag(uint32_t bit) {
@@ -140,6 +159,56 @@ __device__ __forceinline__ void st_agent(T *p, T v) {
 __device__ __forceinline__ float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
+}
+
+// ---- wave64 primitives on DPP lane moves (no LDS round trip) --------------
+// update_dpp(old, src, ctrl, row_mask, bank_mask, bound_ctrl): lanes whose
+// source is outside the 16-lane row, or whose row is masked off, keep `old`.
+#define CSA2_DPP(x, ctrl, rmask) \
+  ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(x), (ctrl), (rmask), 0xf, false))
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each row
+// (shift right 1, 2, 4, 8), then row 0's total into row 1 and row 2's into
+// row 3 (broadcast of lane 15), then lane 31's into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += CSA2_DPP(x, 0x111, 0xf);
+  x += CSA2_DPP(x, 0x112, 0xf);
+  x += CSA2_DPP(x, 0x114, 0xf);
+  x += CSA2_DPP(x, 0x118, 0xf);
+  x += CSA2_DPP(x, 0x142, 0xa);
+  x += CSA2_DPP(x, 0x143, 0xc);
+  return x;
+}
+
+// Sum over the wave, uniform (in a scalar register).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
+// Minimum / maximum over the wave, uniform: butterflies inside each row
+// (quad swaps, then rotations by 4 and 8), then the four row results.
+__device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x124, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xf, 0xf, false));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x124, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xf, 0xf, false));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Lanes below this one whose bit is set in `mask`.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 }  // namespace csa2

@@ -40,6 +40,7 @@ namespace csa2 {
 constexpr int SCAN_THREADS = 256;
 constexpr int BLOCKS_PER_ITER = 16;      // 4 waves x 4 blocks
 constexpr int LDS_KEYS = 8192;           // finisher key capacity (64 KB)
+constexpr int CSA2_TOPK_MAX = 2048;      // largest top-k (staged output in LDS)
 
 struct ScanArgs {
   const uint8_t *codes;
@@ -56,6 +57,7 @@ struct ScanArgs {
   uint32_t *hist;           // [batch][HIST_BINS]
   int32_t R;                // keys to select (pool or topk)
   int32_t fill_invalid;     // write -inf for blocks >= nblk (export only)
+  const float *qbar;        // [batch][512] precomputed Qbar, or NULL (computed in-kernel)
 };
 
 // Qbar of sequence b into LDS; all 256 threads call.  Each thread owns two
@@ -159,11 +161,7 @@ __device__ __forceinline__ float block_score(const BlockRows &r, int cnt, const 
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *total,
                                                          uint32_t *s_wave) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  uint32_t x = v;
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) s_wave[wv] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -177,56 +175,83 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *t
   return before + x - v;
 }
 
+constexpr int RADIX_BINS = 2048;   // 11-bit digits
+
 // Among keys[0..m) with valid[j] (LDS), find the key T such that exactly r
-// valid keys are >= T (keys distinct, 1 <= r <= #valid).  8-bit digits from
-// the top; stops as soon as a digit bucket is taken whole.
-__device__ uint64_t radix_threshold(const uint64_t *keys, const uint8_t *valid, int m, int r,
-                                    uint32_t *s_hist /*256*/, uint64_t *s_state /*2*/) {
+// valid keys are >= T (keys distinct, 1 <= r <= #valid).  Digits of 11 bits
+// from bit `hi` down; every valid key must share the bits above `hi` (63:
+// no assumption).  Stops as soon as a digit bucket is taken whole.  All
+// threads call; s_hist holds RADIX_BINS counters.
+__device__ uint64_t radix_threshold(const uint64_t *keys, const uint8_t *valid, int m, int r, int hi,
+                                    uint32_t *s_hist, uint64_t *s_state, uint32_t *s_wave) {
   const int t = threadIdx.x, nt = blockDim.x;
-  uint64_t prefix = 0, pmask = 0;
+  uint64_t pmask = hi >= 63 ? 0ull : ~((2ull << hi) - 1);   // bits above hi
+  if (t == 0) {
+    uint64_t common = 0;
+    for (int j = 0; j < m; ++j)
+      if (valid[j]) { common = keys[j] & pmask; break; }
+    s_state[0] = common;
+  }
+  __syncthreads();
+  uint64_t prefix = s_state[0];
   int remaining = r;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int j = t; j < 256; j += nt) s_hist[j] = 0;
+  __syncthreads();
+  for (; hi >= 0; hi -= 11) {
+    const int lo = hi >= 10 ? hi - 10 : 0;
+    const int nb = 1 << (hi - lo + 1);
+    for (int j = t; j < nb; j += nt) s_hist[j] = 0;
     __syncthreads();
     for (int j = t; j < m; j += nt) {
-      uint64_t k = keys[j];
-      if (valid[j] && (k & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(k >> shift) & 255u], 1u);
+      const uint64_t k = keys[j];
+      if (valid[j] && (k & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(k >> lo) & (nb - 1)], 1u);
     }
     __syncthreads();
-    if (t < 64) {
-      // bins 255..0 in descending order: lane owns 4 bins, top lane first
-      uint32_t c[4], sum = 0;
-      for (int j = 0; j < 4; ++j) { c[j] = s_hist[255 - (4 * t + j)]; sum += c[j]; }
-      uint32_t x = sum;
-      for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(x, d);
-        if (t >= d) x += y;
-      }
-      uint32_t above = x - sum;   // keys in higher bins than this lane's
-      if (above < (uint32_t)remaining && (uint32_t)remaining <= x) {
-        uint32_t acc = above;
-        for (int j = 0; j < 4; ++j) {
-          if (acc + c[j] >= (uint32_t)remaining) {
-            uint32_t d = 255 - (4 * t + j);
-            s_state[0] = prefix | ((uint64_t)d << shift);
-            // state[1]: remaining after this digit, with bit 63 = bucket taken whole
-            uint32_t rem = (uint32_t)remaining - acc;
-            s_state[1] = (uint64_t)rem | ((rem == c[j]) ? (1ull << 63) : 0ull);
-            break;
-          }
-          acc += c[j];
+    // thread t owns bins nb-1-(per*t+j), top thread first
+    const int per = (nb + nt - 1) / nt;
+    uint32_t sum = 0;
+    for (int j = 0; j < per; ++j) {
+      const int bin = nb - 1 - (per * t + j);
+      sum += bin >= 0 ? s_hist[bin] : 0u;
+    }
+    uint32_t total;
+    const uint32_t above = block_exclusive_scan(sum, &total, s_wave);
+    if (above < (uint32_t)remaining && (uint32_t)remaining <= above + sum) {
+      uint32_t acc = above;
+      for (int j = 0; j < per; ++j) {
+        const int bin = nb - 1 - (per * t + j);
+        const uint32_t c = bin >= 0 ? s_hist[bin] : 0u;
+        if (acc + c >= (uint32_t)remaining) {
+          s_state[0] = prefix | ((uint64_t)bin << lo);
+          const uint32_t rem = (uint32_t)remaining - acc;
+          s_state[1] = (uint64_t)rem | ((rem == c) ? (1ull << 63) : 0ull);
+          break;
         }
+        acc += c;
       }
     }
     __syncthreads();
+#ifdef CSA2_PROBE_TOPK
+    CSA2_TS(7 + (63 - hi) / 11);
+#endif
     prefix = s_state[0];
-    pmask |= 0xFFull << shift;
-    uint64_t st = s_state[1];
+    const uint64_t st = s_state[1];
+    pmask |= ((2ull << hi) - 1) & ~((1ull << lo) - 1);
     __syncthreads();
     remaining = (int)(uint32_t)st;
-    if (st >> 63) return prefix;   // every key with this prefix is taken
+    if ((st >> 63) || lo == 0) return prefix;   // bucket taken whole, or every bit fixed
   }
   return prefix;
+}
+
+// Qbar of every sequence, once per call: the full scan's workgroups then
+// read 2 KB each instead of every one of them summing the query heads (1,024
+// workgroups reading the same 128 KB of queries contended for ~13 us).
+__global__ void __launch_bounds__(SCAN_THREADS) qbar_kernel(const float *__restrict__ q, int heads,
+                                                            float *__restrict__ qbar) {
+  __shared__ float s_qbar[D];
+  compute_qbar<64>(q, heads, blockIdx.x, s_qbar);
+  reinterpret_cast<float2 *>(qbar + (int64_t)blockIdx.x * D)[threadIdx.x] =
+      reinterpret_cast<const float2 *>(s_qbar)[threadIdx.x];
 }
 
 // ---- full scan ----------------------------------------------------------
@@ -239,8 +264,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane >> 4, i = lane & 15;
-  const int64_t n = clamp_len(a.seq_len[b], a.limit);
-  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  CSA2_TS(0);
   if (HIST) {
     for (int j = threadIdx.x; j < HIST_BINS; j += SCAN_THREADS) s_hist[j] = 0;
   }
@@ -254,8 +278,20 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
   int it = blockIdx.x;
   int64_t blk = (int64_t)it * BLOCKS_PER_ITER + wv * 4 + slot;
   BlockRows cur;
-  if (it < iters && blk < nblk) load_block(cur, codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES, i);
-  compute_qbar<16>(a.q, a.heads, b, s_qbar);
+  // the first rows are requested before the length is known: the grid's
+  // block count is bounded by the cache capacity
+  if (it < iters && blk < a.nblk_grid)
+    load_block(cur, codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES, i);
+  const int64_t n = clamp_len(a.seq_len[b], a.limit);
+  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  if (a.qbar) {
+    reinterpret_cast<float2 *>(s_qbar)[threadIdx.x] =
+        reinterpret_cast<const float2 *>(a.qbar + (int64_t)b * D)[threadIdx.x];
+    __syncthreads();
+  } else {
+    compute_qbar<16>(a.q, a.heads, b, s_qbar);
+  }
+  CSA2_TS(1);
   const float *qb = s_qbar + 32 * i;
   for (; it < iters; it += gridDim.x) {
     if (blk < nblk) {
@@ -276,6 +312,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
   }
   if (!HIST) return;
   __syncthreads();
+  CSA2_TS(2);
   Ctrl *ctrl = a.ctrl + b;
   uint32_t *gh = a.hist + (int64_t)b * HIST_COPIES * HIST_BINS;
   {
@@ -286,6 +323,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
     }
   }
   if (!arrive_last(ctrl->scan_grp, &ctrl->scan_top, gridDim.x)) return;
+  CSA2_TS(3);
   // last workgroup: locate the digit of the R-th largest key
   const int t = threadIdx.x;
   if ((int64_t)a.R >= nblk) {
@@ -351,10 +389,11 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
   return ((uint64_t)ord_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - id);
 }
 
-// Writes the ids of the set bits of bitmap[0..nwords) in ascending order to
-// out[0..len) (and to s_out in LDS when given), padding with -1.  All
-// threads.  Each thread owns a contiguous run of words; the words of a run
-// are loaded 16 at a time so a pass costs a few memory round trips.
+// Ids of the set bits of bitmap[0..nwords), ascending, into s_out[0..len)
+// (LDS) and then out[0..len) with coalesced stores, -1 padded.  All
+// threads.  Each thread owns a contiguous run of words, loaded 16 at a time
+// (one memory round trip per 16 words); no global load sits between the
+// stores.
 __device__ void compact_bitmap(const uint32_t *bm, int nwords, int32_t *out, int32_t *s_out,
                                int len, uint32_t *s_wave) {
   constexpr int U = 16;
@@ -379,50 +418,194 @@ __device__ void compact_bitmap(const uint32_t *bm, int nwords, int32_t *out, int
     for (int u = 0; u < U; ++u) {
       uint32_t bits = v[u];
       while (bits && off < (uint32_t)len) {
-        int bpos = __ffs(bits) - 1;
+        const int bpos = __ffs(bits) - 1;
         bits &= bits - 1;
-        const int32_t id = (wb + u) * 32 + bpos;
-        out[off] = id;
-        if (s_out) s_out[off] = id;
-        ++off;
+        s_out[off++] = (wb + u) * 32 + bpos;
       }
     }
   }
-  for (int j = (int)total + t; j < len; j += nt) {
-    out[j] = -1;
-    if (s_out) s_out[j] = -1;
-  }
+  for (int j = (int)total + t; j < len; j += nt) s_out[j] = -1;
+  __syncthreads();
+  for (int j = t; j < len; j += nt) out[j] = s_out[j];
 }
 
-// Top r of the m keys in s_keys (LDS) by flag, compacting the corresponding
-// ids (in stored order) into out[0..len) with -1 padding.  All threads.
-__device__ void select_in_lds(uint64_t *s_keys, uint8_t *s_valid, const int32_t *ids, int m,
-                              int r, int32_t *out, int len, uint32_t *s_hist,
-                              uint64_t *s_state, uint32_t *s_wave) {
-  const int t = threadIdx.x, nt = blockDim.x;
-  uint32_t nvalid_local = 0;
-  for (int j = t; j < m; j += nt) nvalid_local += s_valid[j];
-  uint32_t nvalid;
-  (void)block_exclusive_scan(nvalid_local, &nvalid, s_wave);
+__device__ __forceinline__ float unord_key(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+constexpr int TIE_MAX = 256;     // threshold-bin members ranked pairwise
+
+// Threshold of a top-r choice among the valid keys of keys[0..m) (LDS):
+// returns T such that exactly min(r, #valid) valid keys are >= T (0 when
+// r >= #valid, ~0 when r <= 0 or nothing is valid); *r_eff = min(r, #valid).
+// All threads call; s_hist holds RADIX_BINS counters.
+//
+// One pass of linear bins over the valid scores' range [lo, hi]:
+// bin(s) = min(2047, floor((s - lo) * 2048 / (hi - lo))) is monotone in s,
+// so every key of a higher bin beats every key of a lower one, and equal
+// scores share a bin (their order is the id part of the key).  The bin
+// holding the r-th largest key usually has a handful of members, ranked
+// pairwise; a degenerate range or a crowded bin falls back to the radix
+// select above.
+__device__ uint64_t topk_threshold(const uint64_t *keys, const uint8_t *valid, int m, int r,
+                                   int *r_eff, uint32_t *s_hist, uint64_t *s_state,
+                                   uint32_t *s_wave) {
+  __shared__ uint32_t s_red[12];
+  __shared__ uint32_t s_tot[16];
+  __shared__ uint32_t s_find[4];
+  __shared__ uint64_t s_tie[TIE_MAX];
+  const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wv = t >> 6, nw = nt >> 6;
+  // count, smallest and largest score bits of the valid keys; clear the bins
+  uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0u;
+  for (int j = t; j < m; j += nt) {
+    if (valid[j]) {
+      const uint32_t u = (uint32_t)(keys[j] >> 32);
+      ++cnt;
+      umin = min(umin, u);
+      umax = max(umax, u);
+    }
+  }
+  for (int j = t; j < RADIX_BINS; j += nt) s_hist[j] = 0;
+  if (t == 0) s_find[3] = 0;                    // gather counter
+  cnt = wave_sum(cnt);
+  umin = wave_umin(umin);
+  umax = wave_umax(umax);
+  if (lane == 0) { s_red[wv] = cnt; s_red[4 + wv] = umin; s_red[8 + wv] = umax; }
+  __syncthreads();
+  uint32_t nvalid = 0;
+  umin = 0xFFFFFFFFu; umax = 0u;
+  for (int w = 0; w < nw; ++w) {
+    nvalid += s_red[w];
+    umin = min(umin, s_red[4 + w]);
+    umax = max(umax, s_red[8 + w]);
+  }
   r = min(r, (int)nvalid);
-  uint64_t T = r > 0 ? radix_threshold(s_keys, s_valid, m, r, s_hist, s_state) : ~0ull;
-  // ordered compaction of the kept entries; each thread owns a contiguous run
-  const int per = (m + nt - 1) / nt;
-  const int j0 = min(m, t * per), j1 = min(m, j0 + per);
-  uint32_t cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += (r > 0 && s_valid[j] && s_keys[j] >= T) ? 1u : 0u;
-  uint32_t total;
-  uint32_t off = block_exclusive_scan(cnt, &total, s_wave);
-  for (int j = j0; j < j1; ++j)
-    if (r > 0 && s_valid[j] && s_keys[j] >= T && off < (uint32_t)len) out[off++] = ids[j];
-  for (int j = (int)total + t; j < len; j += nt) out[j] = -1;
+  *r_eff = r;
+  if (r <= 0) return ~0ull;
+  if (r == (int)nvalid) return 0ull;
+  const float lo = unord_key(umin), hi = unord_key(umax);
+  const float range = hi - lo;
+  const float inv = (float)RADIX_BINS / range;
+  if (umin == umax || !(range < __builtin_huge_valf()) || !(inv < __builtin_huge_valf()) || !(inv > 0.f))
+    return radix_threshold(keys, valid, m, r, 63, s_hist, s_state, s_wave);
+  auto bin_of = [&](uint64_t k) {
+    const float sc = unord_key((uint32_t)(k >> 32));
+    return min(RADIX_BINS - 1, (int)((sc - lo) * inv));
+  };
+  for (int j = t; j < m; j += nt)
+    if (valid[j]) atomicAdd(&s_hist[bin_of(keys[j])], 1u);
+  __syncthreads();
+  // counts above each thread's 8 bins (thread 0 owns the top 8)
+  constexpr int PER = RADIX_BINS / SCAN_THREADS;
+  uint32_t c8[PER], sum = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) { c8[k] = s_hist[RADIX_BINS - 1 - (PER * t + k)]; sum += c8[k]; }
+  const uint32_t incl = wave_incl_scan(sum);
+  if (lane == 63) s_tot[wv] = incl;
+  __syncthreads();
+  uint32_t above = incl - sum;
+  for (int w = 0; w < wv; ++w) above += s_tot[w];
+  if (above < (uint32_t)r && (uint32_t)r <= above + sum) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (acc < (uint32_t)r && (uint32_t)r <= acc + c8[k]) {
+        s_find[0] = (uint32_t)(RADIX_BINS - 1 - (PER * t + k));
+        s_find[1] = (uint32_t)r - acc;          // keys still needed from the bin
+        s_find[2] = c8[k];                      // keys in the bin
+      }
+      acc += c8[k];
+    }
+  }
+  __syncthreads();
+  const int bstar = (int)s_find[0];
+  const uint32_t rem = s_find[1], c = s_find[2];
+  if (c > (uint32_t)TIE_MAX) return radix_threshold(keys, valid, m, r, 63, s_hist, s_state, s_wave);
+  for (int j = t; j < m; j += nt) {
+    if (valid[j]) {
+      const uint64_t k = keys[j];
+      if (bin_of(k) == bstar) {
+        const uint32_t slot = atomicAdd(&s_find[3], 1u);
+        if (slot < (uint32_t)TIE_MAX) s_tie[slot] = k;
+      }
+    }
+  }
+  __syncthreads();
+  if (t < (int)c) {
+    const uint64_t k = s_tie[t];
+    uint32_t gt = 0, ge = 0;                    // bin members above / not below k
+    for (uint32_t i2 = 0; i2 < c; ++i2) {
+      gt += s_tie[i2] > k ? 1u : 0u;
+      ge += s_tie[i2] >= k ? 1u : 0u;
+    }
+    if (gt < rem && rem <= ge) s_state[0] = k;  // k is the rem-th largest
+  }
+  __syncthreads();
+  return s_state[0];
+}
+
+// Top r of the m keys in s_keys (LDS, s_valid flags): the chosen entries'
+// s_ids, in stored order, go to s_sel (LDS) and out[0..len), -1 padded.
+// Ordered compaction by ballots: entry (round R, wave w) covers stored
+// positions R*nt + 64w + 0..63; one table of per-entry counts gives every
+// entry's output offset.  All 256 threads; m <= 8192.
+__device__ void select_in_lds(uint64_t *s_keys, uint8_t *s_valid, const int32_t *s_ids, int m,
+                              int r, int32_t *out, int32_t *s_sel, int len, uint32_t *s_hist,
+                              uint64_t *s_state, uint32_t *s_wave) {
+  __shared__ uint32_t s_cnt[2 * 64];
+  const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wv = t >> 6, nw = nt >> 6;
+#ifdef CSA2_PROBE_TOPK
+  CSA2_TS(6);
+#endif
+  int reff = 0;
+  const uint64_t T = topk_threshold(s_keys, s_valid, m, r, &reff, s_hist, s_state, s_wave);
+#ifdef CSA2_PROBE_TOPK
+  CSA2_TS(12);
+#endif
+  const int rounds = (m + nt - 1) / nt;          // <= 32
+  uint32_t mine = 0;                             // bit R: this thread's entry of round R is kept
+  for (int R = 0; R < rounds; ++R) {
+    const int j = R * nt + t;
+    const bool f = reff > 0 && j < m && s_valid[j] && s_keys[j] >= T;
+    const uint64_t mask = __ballot(f);
+    if (f) mine |= 1u << R;
+    if (lane == 0) s_cnt[R * nw + wv] = (uint32_t)__popcll(mask);
+  }
+  for (int e = rounds * nw + t; e < 2 * 64; e += nt) s_cnt[e] = 0;
+  __syncthreads();
+  // every wave: exclusive offsets of entry pairs (2 per lane)
+  const uint32_t c0 = s_cnt[2 * lane], c1 = s_cnt[2 * lane + 1];
+  const uint32_t incl = wave_incl_scan(c0 + c1);
+  const uint32_t pair_excl = incl - c0 - c1;
+  const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+  for (int R = 0; R < rounds; ++R) {
+    const int e = R * nw + wv;
+    const uint32_t base = __builtin_amdgcn_readlane(pair_excl, e >> 1) +
+                          ((e & 1) ? __builtin_amdgcn_readlane(c0, e >> 1) : 0u);
+    const bool f = (mine >> R) & 1u;
+    const uint64_t mask = __ballot(f);
+    if (f) {
+      const uint32_t pos = base + lanes_below(mask);
+      if (pos < (uint32_t)len) {
+        const int32_t id = s_ids[R * nt + t];
+        s_sel[pos] = id;
+        out[pos] = id;
+      }
+    }
+  }
+  for (int j = (int)total + t; j < len; j += nt) { s_sel[j] = -1; out[j] = -1; }
+  __syncthreads();
+#ifdef CSA2_PROBE_TOPK
+  CSA2_TS(13);
+#endif
 }
 
 __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   extern __shared__ uint64_t s_keys[];                 // lds_keys
   __shared__ uint8_t s_valid[LDS_KEYS];
   __shared__ int32_t s_ids[LDS_KEYS];
-  __shared__ uint32_t s_hist[256];
+  __shared__ int32_t s_sel[CSA2_TOPK_MAX];
+  __shared__ uint32_t s_hist[RADIX_BINS];
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;
@@ -435,6 +618,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   uint64_t *cands = a.cands + (int64_t)b * CAND_COPIES * a.cand_stride;
   const bool all = ctrl->all != 0;
   const uint32_t thr = ctrl->thr_digit;
+  CSA2_TS(8);
   // 64 ids per wave step: the ballot of ids above the tie digit is OR-ed
   // into the (zeroed) bitmap; ids in the tie digit go to one of 8 lists
   uint64_t *mylist = cands + (blockIdx.x % CAND_COPIES) * a.cand_stride;
@@ -469,10 +653,12 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
       }
     }
   }
+  CSA2_TS(9);
   if (!arrive_last(ctrl->sel_grp, &ctrl->sel_top, gridDim.x)) return;
 
   // ---- finisher: one workgroup per sequence ----
   const int t = threadIdx.x, nt = blockDim.x;
+  CSA2_TS(10);
   if (!all && nblk > 0) {
     uint32_t cnt[CAND_COPIES], off[CAND_COPIES + 1];
     off[0] = 0;
@@ -503,7 +689,11 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
         }
       }
       __syncthreads();
-      uint64_t T = radix_threshold(s_keys, s_valid, c, need, s_hist, s_state);
+      CSA2_TS(11);
+      // the candidates share the top 10 key bits (the tie digit)
+      int reff = 0;
+      const uint64_t T = topk_threshold(s_keys, s_valid, c, need, &reff, s_hist, s_state, s_wave);
+      CSA2_TS(12);
       for (int j = t; j < c; j += nt) {
         uint64_t k = s_keys[j];
         if (k >= T) {
@@ -558,8 +748,10 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
     __syncthreads();
   }
   int32_t *first = a.first_out + (int64_t)b * a.R;
-  compact_bitmap(bm, a.nwords, first, a.topk > 0 ? s_ids : nullptr, a.R, s_wave);
+  CSA2_TS(13);
+  compact_bitmap(bm, a.nwords, first, s_ids, a.R, s_wave);
   __syncthreads();
+  CSA2_TS(14);
   if (a.topk > 0) {
     // top-k inside the pool: keys of the pool members, in pool order
     constexpr int U = 8;
@@ -583,9 +775,10 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
       }
     }
     __syncthreads();
-    select_in_lds(s_keys, s_valid, s_ids, m, a.topk, a.idx_out + (int64_t)b * a.topk, a.topk,
+    select_in_lds(s_keys, s_valid, s_ids, m, a.topk, a.idx_out + (int64_t)b * a.topk, s_sel, a.topk,
                   s_hist, s_state, s_wave);
   }
+  CSA2_TS(15);
   __syncthreads();
   // leave the row clean for the next call (read only by later kernels)
   for (int j = t; j < a.nwords; j += nt) bm[j] = 0;
@@ -621,14 +814,15 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   extern __shared__ uint64_t s_keys[];
   __shared__ float s_qbar[D];
   __shared__ uint8_t s_valid[SELECT ? LDS_KEYS : 1];
-  __shared__ uint32_t s_hist[256];
+  __shared__ int32_t s_ids[SELECT ? LDS_KEYS : 1];
+  __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX : 1];
+  __shared__ uint32_t s_hist[SELECT ? RADIX_BINS : 1];
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane >> 4, i = lane & 15;
-  const int64_t n = clamp_len(a.seq_len[b], a.limit);
-  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  const int64_t cap_blocks = a.capacity / BLOCK;   // loads stay inside the cache
   const uint8_t *codes = a.codes + (int64_t)b * a.capacity * CODE_BYTES;
   const uint8_t *scales = a.scales + (int64_t)b * a.capacity * SCALE_BYTES;
   const int32_t *cand = a.cand + (int64_t)b * a.n_cand;
@@ -639,9 +833,14 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   int j = it * BLOCKS_PER_ITER + wv * 4 + slot;
   int32_t blk = (it < iters && j < a.n_cand) ? cand[j] : -1;
   BlockRows cur;
-  if (blk >= 0 && blk < nblk)
+  if (blk >= 0 && blk < cap_blocks)
     load_block(cur, codes + (int64_t)blk * BLOCK * CODE_BYTES, scales + (int64_t)blk * BLOCK * SCALE_BYTES, i);
+  CSA2_TS(0);
   compute_qbar<64>(a.q, a.heads, b, s_qbar);
+  // the length only masks: read after the first rows and the query sum
+  const int64_t n = clamp_len(a.seq_len[b], a.limit);
+  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  CSA2_TS(1);
   const float *qb = s_qbar + 32 * i;
   for (; it < iters; it += gridDim.x) {
     if (j < a.n_cand) {
@@ -657,12 +856,14 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
     const int it_next = it + gridDim.x;
     j = it_next * BLOCKS_PER_ITER + wv * 4 + slot;
     blk = (it_next < iters && j < a.n_cand) ? cand[j] : -1;
-    if (blk >= 0 && blk < nblk)
+    if (blk >= 0 && blk < cap_blocks)
       load_block(cur, codes + (int64_t)blk * BLOCK * CODE_BYTES, scales + (int64_t)blk * BLOCK * SCALE_BYTES, i);
   }
+  CSA2_TS(2);
   if (!SELECT) return;
   Ctrl *ctrl = a.ctrl + b;
   if (!arrive_last(ctrl->sel_grp, &ctrl->sel_top, gridDim.x)) return;
+  CSA2_TS(3);
   const int t = threadIdx.x, nt = blockDim.x;
   const int m = a.n_cand;
   constexpr int U = 8;
@@ -681,13 +882,16 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
       if (jj < m) {
         const bool ok = idv[u] >= 0 && idv[u] < nblk;
         s_valid[jj] = ok;
+        s_ids[jj] = idv[u];
         s_keys[jj] = ok ? make_key(sv[u], (uint32_t)idv[u]) : 0ull;
       }
     }
   }
   __syncthreads();
-  select_in_lds(s_keys, s_valid, cand, m, a.topk, a.idx_out + (int64_t)b * a.topk, a.topk,
+  CSA2_TS(4);
+  select_in_lds(s_keys, s_valid, s_ids, m, a.topk, a.idx_out + (int64_t)b * a.topk, s_sel, a.topk,
                 s_hist, s_state, s_wave);
+  CSA2_TS(5);
 }
 
 // Reuse: idx_out = prior (grid-stride copy).
