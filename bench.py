@@ -291,6 +291,7 @@ def main():
         ev[i][0].record(stream)
         plans[WU + i].run(stream)
         ev[i][1].record(stream)
+    enqueued = time.perf_counter() - t_start      # host time to submit the K steps
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     csa2.set_scan_events(None, None)
@@ -311,7 +312,8 @@ def main():
     scan_avg_s = float(np.mean(scan_ms)) * 1e-3
     achieved = scan_bytes / scan_avg_s / 1e9
     eff_gbs = uniq / (ms_per_step * 1e-3) / 1e9
-    log(f"step: wall {ms_per_step * 1e3:.1f} us, events median {np.median(step_ms) * 1e3:.1f} us; "
+    log(f"step: wall {ms_per_step * 1e3:.1f} us (host submit {enqueued * 1e6 / K:.1f} us), "
+        f"events median {np.median(step_ms) * 1e3:.1f} us; "
         f"scan kernel avg {scan_avg_s * 1e6:.1f} us = {achieved:.0f} GB/s; "
         f"unique {uniq / 1e6:.1f} MB -> {eff_gbs:.0f} GB/s ({eff_gbs / PEAK_HBM_GBS * 100:.1f}% of peak); "
         f"touched {touched / 1e6:.1f} MB")

@@ -61,7 +61,9 @@ csa2_status device_ready() {
       state[dev] = 2;
     } else {
       const int big = 160 * 1024 - 16 * 1024;
-      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel),
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel<false>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel<true>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, big);
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, big);
@@ -85,7 +87,7 @@ int att_splits(int workgroup_rows, int n_stages) {
 }
 
 struct Layout {
-  size_t ctrl, hist, scores, bitmap, cands, qbar, part_o, part_ml, total;
+  size_t ctrl, hist, scores, bitmap, cands, qbar, part_o, part_ml, cscores, total;
   int64_t score_stride, cand_stride;
   int32_t nwords;
   int32_t att_stages, att_splits;
@@ -106,6 +108,7 @@ bool make_layout(int32_t batch, int32_t heads, int64_t max_len, int32_t pool, in
   L->bitmap = off; off = align256(off + sizeof(uint32_t) * (size_t)L->nwords * batch);
   L->cands = off;  off = align256(off + sizeof(uint64_t) * CAND_COPIES * (size_t)L->cand_stride * batch);
   L->qbar = off;   off = align256(off + sizeof(float) * D * (size_t)batch);
+  L->cscores = off; off = align256(off + sizeof(float) * (size_t)(pool > 0 ? pool : 1) * batch);
   L->att_stages = L->att_splits = 0;
   L->part_o = L->part_ml = off;
   if (heads == 16 || heads == 32 || heads == 64) {
@@ -159,7 +162,7 @@ int grid_for(int64_t items, int batch, int target) {
 
 csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, int32_t R,
                             int32_t *first_out, int32_t topk2, int32_t *idx_out, void *ws,
-                            const Layout &L, hipStream_t s) {
+                            const Layout &L, hipStream_t s, float *pool_scores = nullptr) {
   const int B = kv->batch;
   const int64_t nblk_grid = ceil_div(kv->max_len, BLOCK);
   ScanArgs sa;
@@ -185,6 +188,7 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
   se.R = R; se.first_out = first_out; se.topk = topk2; se.idx_out = idx_out;
   int lk = R > 4096 ? R : 4096;
   se.lds_keys = lk;
+  se.pool_scores = pool_scores;
   dim3 g2(grid_for(ceil_div(L.nwords / 2, 4), B, 256), B);
   select_kernel<<<g2, SCAN_THREADS, (size_t)lk * sizeof(uint64_t), s>>>(se);
   return launched("select");
@@ -209,9 +213,12 @@ csa2_status run_rescore(const csa2_kv *kv, const float *q, int32_t heads, const 
   return launched("rescore");
 }
 
+// idx given: attend over it.  idx NULL: take the top-k of (cand,
+// cand_scores) inside the attention kernel and write it to idx_out.
 csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *idx,
                        int32_t topk, float scale, float *out, void *ws, const Layout &L,
-                       hipStream_t s) {
+                       hipStream_t s, const int32_t *cand = nullptr, const float *cand_scores = nullptr,
+                       int32_t n_cand = 0, int32_t *idx_out = nullptr) {
   const int B = kv->batch;
   AttendArgs aa;
   aa.codes = kv->codes; aa.scales = kv->scales; aa.seq_len = kv->seq_len; aa.capacity = kv->capacity;
@@ -221,13 +228,17 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   aa.n_stages = L.att_stages; aa.splits = L.att_splits;
   aa.part_o = at<float>(ws, L.part_o); aa.part_ml = at<float>(ws, L.part_ml);
   aa.heads = heads;
+  aa.cand = cand; aa.cand_scores = cand_scores; aa.n_cand = n_cand; aa.idx_out = idx_out;
   dim3 g(L.att_splits * (heads / 16), B);
   const size_t lds = (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16);
-  attend_partial_kernel<<<g, ATT_THREADS, lds, s>>>(aa);
+  if (idx)
+    attend_partial_kernel<false><<<g, ATT_THREADS, lds, s>>>(aa);
+  else
+    attend_partial_kernel<true><<<g, ATT_THREADS, lds, s>>>(aa);
   if (csa2_status st = launched("attend")) return st;
   CombineArgs ca;
   ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = L.att_splits; ca.heads = heads; ca.out = out;
-  attend_combine_kernel<<<dim3((heads / 16) * 8, B), 256, 0, s>>>(ca);
+  attend_combine_kernel<<<dim3((heads / 16) * 32, B), 64, 0, s>>>(ca);
   return launched("combine");
 }
 
@@ -459,6 +470,23 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
         copy_idx_kernel<<<(int)ceil_div(nidx, 256), 256, 0, s>>>(prev_idx, ly.idx, nidx);
         e = launched("reuse copy");
       }
+    } else if (st->pool > 0 && st->pool <= SEL_CAND_MAX) {
+      // the pool's top-k is taken inside the attention kernel: the index
+      // kernels stop at the scored candidate list (no hand-off to a single
+      // finishing workgroup, no re-read of the selection)
+      float *cs = at<float>(st->ws, L.cscores);
+      if (!pool_built) {
+        e = run_scan_select(kv, ly.q, st->heads, st->pool, st->pool_out, 0, nullptr, st->ws, L, s, cs);
+        pool_built = true;
+      } else {
+        e = run_rescore(kv, ly.q, st->heads, st->pool_out, st->pool, 0, nullptr, cs, st->pool, nullptr, s);
+      }
+      if (e) return e;
+      e = run_attend(kv, ly.q, st->heads, nullptr, st->topk, st->scale, ly.out, st->ws, L, s,
+                     st->pool_out, cs, st->pool, ly.idx);
+      if (e) return e;
+      prev_idx = ly.idx;
+      continue;
     } else if (st->pool > 0 && !pool_built) {
       e = run_scan_select(kv, ly.q, st->heads, st->pool, st->pool_out, st->topk, ly.idx, st->ws, L, s);
       pool_built = true;

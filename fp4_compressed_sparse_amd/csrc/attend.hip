@@ -51,7 +51,16 @@ struct AttendArgs {
   float *part_o;            // [batch][splits][heads/16][32 tiles][64 lanes][4]: O^T accumulators
                             // in lane order (contiguous stores)
   float *part_ml;           // [batch][splits][heads/16][16 heads][2]: running max (log2) and sum
+  // selecting variant only: the top-k is taken inside the kernel from a
+  // scored candidate list (every workgroup takes the same, deterministic
+  // choice; the first workgroup of each sequence also writes it to idx_out)
+  const int32_t *cand;      // [batch][n_cand] block ids (-1 = empty)
+  const float *cand_scores; // [batch][n_cand] their indexer scores
+  int32_t n_cand;           // 1..SEL_CAND_MAX
+  int32_t *idx_out;         // [batch][topk]
 };
+
+constexpr int SEL_CAND_MAX = 2048;  // candidates of the in-kernel top-k (8 per thread)
 
 // One workgroup = one 16-head tile x a range of stages of 64 gathered
 // positions.  Per stage: the 256 threads dequantise the 64 rows into LDS as
@@ -59,11 +68,15 @@ struct AttendArgs {
 // the per-head max and sum of the stage are exchanged through LDS; P is
 // written to LDS as fp16; wave w then accumulates O^T for channel tiles
 // 8w..8w+7 over all 64 positions.
+template <bool SELECT>
 __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs a) {
   extern __shared__ _Float16 s_v[];               // [ATT_SP][ROW_HALVES]; first holds q
   __shared__ _Float16 s_p[16 * P_STRIDE];         // P: [16 heads][64 positions]
   __shared__ float s_max[4][16], s_sum[4][16];
   __shared__ uint8_t s_ok[ATT_SP];
+  __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX : 1];   // in-kernel selection
+  __shared__ uint64_t s_state[2];
+  __shared__ uint32_t s_wave[16];
 
   const int b = blockIdx.y;
   const int HT = a.heads >> 4;
@@ -91,27 +104,67 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
       const int j = st * ATT_SP + (tid >> 4) + 16 * k;
-      blkv[k] = j < total_pos ? idx[j >> 3] : -1;
+      if (SELECT)
+        blkv[k] = s_sel[min(j, total_pos - 1) >> 3];
+      else
+        blkv[k] = idx[min(j, total_pos - 1) >> 3];   // unconditional: one batch
     }
   };
   auto fetch_rows = [&](int st) {
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      okv[k] = blkv[k] >= 0 && blkv[k] < cap_blocks;   // in bounds; masked by n later
-      if (okv[k]) {
-        const int64_t pos = (int64_t)blkv[k] * BLOCK + (((tid >> 4) + 16 * k) & 7);
-        wr[k] = *reinterpret_cast<const u32x4 *>(codes + pos * CODE_BYTES + 16 * i16);
-        scr[k] = *reinterpret_cast<const uint16_t *>(scales + pos * SCALE_BYTES + 2 * i16);
-      } else {
-        wr[k] = u32x4{0u, 0u, 0u, 0u};
-        scr[k] = 0u;
-      }
+      // in bounds (masked by the sequence length later); an id outside the
+      // cache reads row 0 and is dropped, so every load is unconditional and
+      // the stage's loads go out as one batch
+      if (st * ATT_SP + (tid >> 4) + 16 * k >= total_pos) blkv[k] = -1;   // past the selection
+      okv[k] = blkv[k] >= 0 && blkv[k] < cap_blocks;
+      const int64_t pos = okv[k] ? (int64_t)blkv[k] * BLOCK + (((tid >> 4) + 16 * k) & 7) : 0;
+      wr[k] = *reinterpret_cast<const u32x4 *>(codes + pos * CODE_BYTES + 16 * i16);
+      scr[k] = *reinterpret_cast<const uint16_t *>(scales + pos * SCALE_BYTES + 2 * i16);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   CSA2_TS(0);
+  // Selecting variant: candidates, their scores and the sequence length in
+  // one batch, then the block top-k in LDS (the key/id/bin arrays borrow the
+  // row buffer, which is free until the query is staged).
+  if constexpr (SELECT) {
+    constexpr int KPT = SEL_CAND_MAX / ATT_THREADS;
+    const int m = a.n_cand;
+    const int32_t *cb = a.cand + (int64_t)b * m;
+    const float *sb = a.cand_scores + (int64_t)b * m;
+    int32_t cid[KPT];
+    float csc[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int j = min(tid + ATT_THREADS * k, m - 1);
+      cid[k] = cb[j];
+      csc[k] = sb[j];
+    }
+    const int64_t nsel = clamp_len(a.seq_len[b], a.limit);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t nbs = (nsel + BLOCK - 1) / BLOCK;
+    uint64_t *s_keys = reinterpret_cast<uint64_t *>(s_v);
+    int32_t *s_ids = reinterpret_cast<int32_t *>(s_keys + SEL_CAND_MAX);
+    uint32_t *s_hist = reinterpret_cast<uint32_t *>(s_ids + SEL_CAND_MAX);
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int j = tid + ATT_THREADS * k;
+      if (j < m) {
+        const bool ok = cid[k] >= 0 && cid[k] < nbs;
+        s_keys[j] = ok ? make_key(csc[k], (uint32_t)cid[k]) : 0ull;
+        s_ids[j] = cid[k];
+      }
+    }
+    __syncthreads();
+    int32_t *io = blockIdx.x == 0 ? a.idx_out + (int64_t)b * a.topk : nullptr;
+    select_top<KPT>(s_keys, s_ids, m, a.topk, io, s_sel, a.topk, s_hist, s_state, s_wave);
+  }
   // request order: the first stage's block ids, the query tile, then (once
   // the ids are in) the rows, so the query and id latencies overlap
-  if (st0 < st1) fetch_ids(st0);
+  // every split owns at least one stage (splits <= stages)
+  fetch_ids(st0);
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- Q^T operand: head 16*ht + n16, channels 32*kc + 8*g + 0..7.  The
   // tile's 16 query rows (32 KB) are staged through LDS as fp16 with one
@@ -123,7 +176,8 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     float4 v[NV];
 #pragma unroll
     for (int u = 0; u < NV; ++u) v[u] = src[tid + u * ATT_THREADS];
-    if (st0 < st1) fetch_rows(st0);
+    __builtin_amdgcn_sched_barrier(0);    // query loads go out before the ids are awaited
+    fetch_rows(st0);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int e = tid + u * ATT_THREADS;                    // head e/128, channels 4*(e%128)
@@ -274,6 +328,9 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   CSA2_TS(5);
 }
 
+template __global__ void attend_partial_kernel<false>(AttendArgs);
+template __global__ void attend_partial_kernel<true>(AttendArgs);
+
 struct CombineArgs {
   const float *part_o;
   const float *part_ml;
@@ -282,51 +339,75 @@ struct CombineArgs {
   float *out;               // [batch][heads][512]
 };
 
-// grid (heads/16 * 8, batch), 256 threads: one workgroup merges one eighth
-// (4 O^T tiles = 4 KB) of every split's partial of one head tile, so each
-// slot is read with one coalesced 4 KB load per workgroup; the per-head
-// (max, sum) of every slot go through LDS.
+// grid (heads/16 * 32, batch), one wave per workgroup: workgroup (ht, ct)
+// merges O^T tile ct (1 KB) of head tile ht over every split, so the 4 MB of
+// partials of a 64-head step spread over 128 compute units.  The (max, sum)
+// pairs of the first 32 splits and the first 32 tiles are requested in one
+// batch, before any of them is used (one memory round trip for <= 32
+// splits); further splits follow in batches of 32.
 constexpr int MAX_SPLITS = 256;
-__global__ void __launch_bounds__(256) attend_combine_kernel(CombineArgs a) {
-  __shared__ float s_m[MAX_SPLITS * 16], s_l[MAX_SPLITS * 16];
-  constexpr int U = 32;
-  const int b = blockIdx.y, t = threadIdx.x;
-  const int HT = a.heads / 16, ht = blockIdx.x >> 3, chunk = blockIdx.x & 7;
-  const int nslots = a.splits;
-  const int ct = 4 * chunk + (t >> 6), lane = t & 63, n16 = lane & 15, g = lane >> 4;
+constexpr int CMB_U = 32;
+__global__ void __launch_bounds__(64) attend_combine_kernel(CombineArgs a) {
+  __shared__ float2 s_ml[MAX_SPLITS * 16];
+  const int b = blockIdx.y, lane = threadIdx.x;
+  const int HT = a.heads / 16, ht = blockIdx.x >> 5, ct = blockIdx.x & 31;
+  const int nslots = a.splits, nml = nslots * 16;
+  const int n16 = lane & 15, g = lane >> 4;
   CSA2_TS(8);
-  for (int j = t; j < nslots * 16; j += 256) {
-    const int64_t sl = ((int64_t)b * a.splits + (j >> 4)) * HT + ht;
-    const float2 ml = reinterpret_cast<const float2 *>(a.part_ml)[sl * 16 + (j & 15)];
-    s_m[j] = ml.x;
-    s_l[j] = ml.y;
+  const float2 *pml = reinterpret_cast<const float2 *>(a.part_ml);
+  const float4 *po = reinterpret_cast<const float4 *>(a.part_o) + ct * 64 + lane;
+  auto slot_of = [&](int s) { return ((int64_t)b * a.splits + s) * HT + ht; };
+  // (max, sum) of the first 32 splits: entry lane + 64u is split (lane + 64u) / 16,
+  // head (lane + 64u) % 16 (slots are contiguous in the partial layout only
+  // per head tile, so the index goes through slot_of)
+  float2 mlv[CMB_U * 16 / 64];
+#pragma unroll
+  for (int u = 0; u < CMB_U * 16 / 64; ++u) {
+    const int e = min(lane + 64 * u, nml - 1);
+    mlv[u] = pml[slot_of(e >> 4) * 16 + (e & 15)];
   }
-  __syncthreads();
+  float4 ov[CMB_U];
+#pragma unroll
+  for (int u = 0; u < CMB_U; ++u) ov[u] = po[slot_of(min(u, nslots - 1)) * (16 * D / 4)];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < CMB_U * 16 / 64; ++u) {
+    const int e = lane + 64 * u;
+    if (e < nml) s_ml[e] = mlv[u];
+  }
+  // splits beyond the first 32 (long selections): their (max, sum) pairs
+  for (int e0 = CMB_U * 16; e0 < nml; e0 += 64) {
+    const int e = e0 + lane;
+    if (e < nml) s_ml[e] = pml[slot_of(e >> 4) * 16 + (e & 15)];
+  }
+  __syncthreads();                        // one wave: orders the LDS writes before the reads
   CSA2_TS(9);
   float M = -__builtin_huge_valf();
-  for (int s = 0; s < nslots; ++s) M = fmaxf(M, s_m[s * 16 + n16]);
+  for (int s0 = 0; s0 < nslots; s0 += 16) {
+    float mv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) mv[u] = s_ml[min(s0 + u, nslots - 1) * 16 + n16].x;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) M = fmaxf(M, mv[u]);     // a repeated split changes nothing
+  }
   float L = 0.f;
   float4 o = {0.f, 0.f, 0.f, 0.f};
   if (M != -__builtin_huge_valf()) {
-    const float4 *base = reinterpret_cast<const float4 *>(a.part_o) + (int64_t)chunk * 256 + t;
+    // every partial is written (an empty one as m = -inf, O = 0), so a
+    // batch past the last split re-reads that split with weight 0
 #pragma unroll 1
-    for (int s0 = 0; s0 < nslots; s0 += U) {
-      // every partial is written (an empty one as m = -inf, O = 0), so a
-      // batch past the last slot re-reads that slot with weight 0: the loads
-      // are unconditional and issue back to back
-      float4 ov[U];
+    for (int s0 = 0; s0 < nslots; s0 += CMB_U) {
+      if (s0 > 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int su = min(s0 + u, nslots - 1);
-        ov[u] = base[(((int64_t)b * a.splits + su) * HT + ht) * (16 * D / 4)];
+        for (int u = 0; u < CMB_U; ++u) ov[u] = po[slot_of(min(s0 + u, nslots - 1)) * (16 * D / 4)];
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);      // keep the batch's loads ahead of their uses
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < CMB_U; ++u) {
         const int su = min(s0 + u, nslots - 1);
-        const float m = s_m[su * 16 + n16];
-        const float e = (s0 + u < nslots && m != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(m - M) : 0.f;
-        L += e * s_l[su * 16 + n16];
+        const float2 ml = s_ml[su * 16 + n16];
+        const float e = (s0 + u < nslots && ml.x != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
+        L += e * ml.y;
         o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
       }
     }

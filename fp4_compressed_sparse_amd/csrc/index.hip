@@ -62,22 +62,30 @@ struct ScanArgs {
 
 // Qbar of sequence b into LDS; all 256 threads call.  Each thread owns two
 // channels and adds the heads in order; the loads of HB heads are issued
-// together so the sum costs 64/HB memory round trips, not one per head
+// together so the sum costs heads/HB memory round trips, not one per head
 // (HB = 16 keeps the scan's register budget; the pool rescoring uses 64).
 template <int HB>
 __device__ __forceinline__ void compute_qbar(const float *__restrict__ q, int heads, int b,
                                              float *s_qbar) {
   const int t = threadIdx.x;
   const float2 *qp = reinterpret_cast<const float2 *>(q + (int64_t)b * heads * D) + t;
-  float2 acc = qp[0];
-  for (int h0 = 1; h0 < heads; h0 += HB) {
+  float2 acc = make_float2(0.f, 0.f);
+  for (int h0 = 0; h0 < heads; h0 += HB) {
+    // unconditional loads (a head past the end re-reads the last one and is
+    // dropped below), so the batch is issued back to back
     float2 v[HB];
 #pragma unroll
-    for (int j = 0; j < HB; ++j)
-      v[j] = (h0 + j < heads) ? qp[(int64_t)(h0 + j) * (D / 2)] : make_float2(0.f, 0.f);
+    for (int j = 0; j < HB; ++j) v[j] = qp[(int64_t)min(h0 + j, heads - 1) * (D / 2)];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < HB; ++j) {
-      if (h0 + j < heads) { acc.x = acc.x + v[j].x; acc.y = acc.y + v[j].y; }
+      const int h = h0 + j;
+      if (h == 0) {
+        acc = v[j];
+      } else if (h < heads) {
+        acc.x = acc.x + v[j].x;
+        acc.y = acc.y + v[j].y;
+      }
     }
   }
   if (!(__builtin_isfinite(acc.x) && __builtin_isfinite(acc.y))) raise_flag(FLAG_NONFINITE_Q);
@@ -177,19 +185,20 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *t
 
 constexpr int RADIX_BINS = 2048;   // 11-bit digits
 
-// Among keys[0..m) with valid[j] (LDS), find the key T such that exactly r
-// valid keys are >= T (keys distinct, 1 <= r <= #valid).  Digits of 11 bits
+// Among the nonzero keys of keys[0..m) (LDS; 0 marks an empty entry), find
+// the key T such that exactly r of them are >= T (keys distinct,
+// 1 <= r <= #nonzero).  Digits of 11 bits
 // from bit `hi` down; every valid key must share the bits above `hi` (63:
 // no assumption).  Stops as soon as a digit bucket is taken whole.  All
 // threads call; s_hist holds RADIX_BINS counters.
-__device__ uint64_t radix_threshold(const uint64_t *keys, const uint8_t *valid, int m, int r, int hi,
+__device__ __forceinline__ uint64_t radix_threshold(const uint64_t *keys, int m, int r, int hi,
                                     uint32_t *s_hist, uint64_t *s_state, uint32_t *s_wave) {
   const int t = threadIdx.x, nt = blockDim.x;
   uint64_t pmask = hi >= 63 ? 0ull : ~((2ull << hi) - 1);   // bits above hi
   if (t == 0) {
     uint64_t common = 0;
     for (int j = 0; j < m; ++j)
-      if (valid[j]) { common = keys[j] & pmask; break; }
+      if (keys[j]) { common = keys[j] & pmask; break; }
     s_state[0] = common;
   }
   __syncthreads();
@@ -203,7 +212,7 @@ __device__ uint64_t radix_threshold(const uint64_t *keys, const uint8_t *valid, 
     __syncthreads();
     for (int j = t; j < m; j += nt) {
       const uint64_t k = keys[j];
-      if (valid[j] && (k & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(k >> lo) & (nb - 1)], 1u);
+      if (k && (k & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(k >> lo) & (nb - 1)], 1u);
     }
     __syncthreads();
     // thread t owns bins nb-1-(per*t+j), top thread first
@@ -383,6 +392,7 @@ struct SelectArgs {
   int32_t topk;             // second level (pool > 0) or 0
   int32_t *idx_out;         // [batch][topk] when topk > 0
   int32_t lds_keys;         // dynamic LDS keys (>= R, <= LDS_KEYS)
+  float *pool_scores;       // [batch][R]: scores of first_out in its order (or NULL)
 };
 
 __device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
@@ -394,7 +404,7 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
 // threads.  Each thread owns a contiguous run of words, loaded 16 at a time
 // (one memory round trip per 16 words); no global load sits between the
 // stores.
-__device__ void compact_bitmap(const uint32_t *bm, int nwords, int32_t *out, int32_t *s_out,
+__device__ __forceinline__ void compact_bitmap(const uint32_t *bm, int nwords, int32_t *out, int32_t *s_out,
                                int len, uint32_t *s_wave) {
   constexpr int U = 16;
   const int t = threadIdx.x, nt = blockDim.x;
@@ -404,19 +414,19 @@ __device__ void compact_bitmap(const uint32_t *bm, int nwords, int32_t *out, int
   for (int wb = w0; wb < w1; wb += U) {
     uint32_t v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = (wb + u < w1) ? ld_agent(bm + wb + u) : 0u;
+    for (int u = 0; u < U; ++u) v[u] = ld_agent(bm + min(wb + u, w1 - 1));   // clamped: no branch
 #pragma unroll
-    for (int u = 0; u < U; ++u) cnt += __popc(v[u]);
+    for (int u = 0; u < U; ++u) cnt += (wb + u < w1) ? __popc(v[u]) : 0u;
   }
   uint32_t total;
   uint32_t off = block_exclusive_scan(cnt, &total, s_wave);
   for (int wb = w0; wb < w1 && off < (uint32_t)len; wb += U) {
     uint32_t v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = (wb + u < w1) ? ld_agent(bm + wb + u) : 0u;
+    for (int u = 0; u < U; ++u) v[u] = ld_agent(bm + min(wb + u, w1 - 1));
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      uint32_t bits = v[u];
+      uint32_t bits = (wb + u < w1) ? v[u] : 0u;
       while (bits && off < (uint32_t)len) {
         const int bpos = __ffs(bits) - 1;
         bits &= bits - 1;
@@ -435,50 +445,52 @@ __device__ __forceinline__ float unord_key(uint32_t u) {
 
 constexpr int TIE_MAX = 256;     // threshold-bin members ranked pairwise
 
-// Threshold of a top-r choice among the valid keys of keys[0..m) (LDS):
-// returns T such that exactly min(r, #valid) valid keys are >= T (0 when
-// r >= #valid, ~0 when r <= 0 or nothing is valid); *r_eff = min(r, #valid).
-// All threads call; s_hist holds RADIX_BINS counters.
+#ifndef CSA2_TOPK_TS
+#define CSA2_TOPK_TS(k) do { } while (0)
+#endif
+
+// Threshold of a top-r choice among the nonzero keys held in registers:
+// thread t holds entries t, t + 256, ..., t + 256 (KPT - 1) of a list of
+// 256 * KPT keys (0 = empty; make_key never yields 0).  Returns T such that
+// exactly min(r, #nonzero) nonzero keys are >= T (0 when r >= #nonzero, ~0
+// when r <= 0 or the list is empty); *r_eff = min(r, #nonzero).  All 256
+// threads call; s_keys is the same list in LDS (read only by the fallback),
+// s_hist holds RADIX_BINS counters.
 //
-// One pass of linear bins over the valid scores' range [lo, hi]:
+// One pass of linear bins over the scores' range [lo, hi]:
 // bin(s) = min(2047, floor((s - lo) * 2048 / (hi - lo))) is monotone in s,
-// so every key of a higher bin beats every key of a lower one, and equal
+// so every key of a higher bin beats every key of a lower one and equal
 // scores share a bin (their order is the id part of the key).  The bin
 // holding the r-th largest key usually has a handful of members, ranked
 // pairwise; a degenerate range or a crowded bin falls back to the radix
 // select above.
-__device__ uint64_t topk_threshold(const uint64_t *keys, const uint8_t *valid, int m, int r,
+template <int KPT>
+__device__ __forceinline__ uint64_t topk_threshold(const uint64_t (&kr)[KPT], const uint64_t *s_keys, int m, int r,
                                    int *r_eff, uint32_t *s_hist, uint64_t *s_state,
                                    uint32_t *s_wave) {
   __shared__ uint32_t s_red[12];
-  __shared__ uint32_t s_tot[16];
+  __shared__ uint32_t s_tot[4];
   __shared__ uint32_t s_find[4];
   __shared__ uint64_t s_tie[TIE_MAX];
-  const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wv = t >> 6, nw = nt >> 6;
-  // count, smallest and largest score bits of the valid keys; clear the bins
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0u;
-  for (int j = t; j < m; j += nt) {
-    if (valid[j]) {
-      const uint32_t u = (uint32_t)(keys[j] >> 32);
-      ++cnt;
-      umin = min(umin, u);
-      umax = max(umax, u);
-    }
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const uint32_t u = (uint32_t)(kr[k] >> 32);
+    if (kr[k]) { ++cnt; umin = min(umin, u); umax = max(umax, u); }
   }
-  for (int j = t; j < RADIX_BINS; j += nt) s_hist[j] = 0;
+#pragma unroll
+  for (int k = 0; k < RADIX_BINS / 256; ++k) s_hist[t + 256 * k] = 0;
   if (t == 0) s_find[3] = 0;                    // gather counter
   cnt = wave_sum(cnt);
   umin = wave_umin(umin);
   umax = wave_umax(umax);
   if (lane == 0) { s_red[wv] = cnt; s_red[4 + wv] = umin; s_red[8 + wv] = umax; }
   __syncthreads();
-  uint32_t nvalid = 0;
-  umin = 0xFFFFFFFFu; umax = 0u;
-  for (int w = 0; w < nw; ++w) {
-    nvalid += s_red[w];
-    umin = min(umin, s_red[4 + w]);
-    umax = max(umax, s_red[8 + w]);
-  }
+  CSA2_TOPK_TS(1);
+  const uint32_t nvalid = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  umin = min(min(s_red[4], s_red[5]), min(s_red[6], s_red[7]));
+  umax = max(max(s_red[8], s_red[9]), max(s_red[10], s_red[11]));
   r = min(r, (int)nvalid);
   *r_eff = r;
   if (r <= 0) return ~0ull;
@@ -487,16 +499,18 @@ __device__ uint64_t topk_threshold(const uint64_t *keys, const uint8_t *valid, i
   const float range = hi - lo;
   const float inv = (float)RADIX_BINS / range;
   if (umin == umax || !(range < __builtin_huge_valf()) || !(inv < __builtin_huge_valf()) || !(inv > 0.f))
-    return radix_threshold(keys, valid, m, r, 63, s_hist, s_state, s_wave);
-  auto bin_of = [&](uint64_t k) {
-    const float sc = unord_key((uint32_t)(k >> 32));
-    return min(RADIX_BINS - 1, (int)((sc - lo) * inv));
-  };
-  for (int j = t; j < m; j += nt)
-    if (valid[j]) atomicAdd(&s_hist[bin_of(keys[j])], 1u);
+    return radix_threshold(s_keys, m, r, 63, s_hist, s_state, s_wave);
+  int bin[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const float sc = unord_key((uint32_t)(kr[k] >> 32));
+    bin[k] = kr[k] ? min(RADIX_BINS - 1, (int)((sc - lo) * inv)) : -1;
+    if (kr[k]) atomicAdd(&s_hist[bin[k]], 1u);
+  }
   __syncthreads();
+  CSA2_TOPK_TS(2);
   // counts above each thread's 8 bins (thread 0 owns the top 8)
-  constexpr int PER = RADIX_BINS / SCAN_THREADS;
+  constexpr int PER = RADIX_BINS / 256;
   uint32_t c8[PER], sum = 0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) { c8[k] = s_hist[RADIX_BINS - 1 - (PER * t + k)]; sum += c8[k]; }
@@ -504,7 +518,7 @@ __device__ uint64_t topk_threshold(const uint64_t *keys, const uint8_t *valid, i
   if (lane == 63) s_tot[wv] = incl;
   __syncthreads();
   uint32_t above = incl - sum;
-  for (int w = 0; w < wv; ++w) above += s_tot[w];
+  above += (wv > 0 ? s_tot[0] : 0u) + (wv > 1 ? s_tot[1] : 0u) + (wv > 2 ? s_tot[2] : 0u);
   if (above < (uint32_t)r && (uint32_t)r <= above + sum) {
     uint32_t acc = above;
 #pragma unroll
@@ -518,91 +532,120 @@ __device__ uint64_t topk_threshold(const uint64_t *keys, const uint8_t *valid, i
     }
   }
   __syncthreads();
+  CSA2_TOPK_TS(3);
   const int bstar = (int)s_find[0];
   const uint32_t rem = s_find[1], c = s_find[2];
-  if (c > (uint32_t)TIE_MAX) return radix_threshold(keys, valid, m, r, 63, s_hist, s_state, s_wave);
-  for (int j = t; j < m; j += nt) {
-    if (valid[j]) {
-      const uint64_t k = keys[j];
-      if (bin_of(k) == bstar) {
-        const uint32_t slot = atomicAdd(&s_find[3], 1u);
-        if (slot < (uint32_t)TIE_MAX) s_tie[slot] = k;
-      }
+  if (c > (uint32_t)TIE_MAX) return radix_threshold(s_keys, m, r, 63, s_hist, s_state, s_wave);
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    if (bin[k] == bstar) {
+      const uint32_t slot = atomicAdd(&s_find[3], 1u);
+      if (slot < (uint32_t)TIE_MAX) s_tie[slot] = kr[k];
     }
   }
   __syncthreads();
+  CSA2_TOPK_TS(4);
   if (t < (int)c) {
     const uint64_t k = s_tie[t];
     uint32_t gt = 0, ge = 0;                    // bin members above / not below k
     for (uint32_t i2 = 0; i2 < c; ++i2) {
-      gt += s_tie[i2] > k ? 1u : 0u;
-      ge += s_tie[i2] >= k ? 1u : 0u;
+      const uint64_t o = s_tie[i2];
+      gt += o > k ? 1u : 0u;
+      ge += o >= k ? 1u : 0u;
     }
     if (gt < rem && rem <= ge) s_state[0] = k;  // k is the rem-th largest
   }
   __syncthreads();
+  CSA2_TOPK_TS(5);
   return s_state[0];
 }
 
-// Top r of the m keys in s_keys (LDS, s_valid flags): the chosen entries'
-// s_ids, in stored order, go to s_sel (LDS) and out[0..len), -1 padded.
-// Ordered compaction by ballots: entry (round R, wave w) covers stored
-// positions R*nt + 64w + 0..63; one table of per-entry counts gives every
-// entry's output offset.  All 256 threads; m <= 8192.
-__device__ void select_in_lds(uint64_t *s_keys, uint8_t *s_valid, const int32_t *s_ids, int m,
-                              int r, int32_t *out, int32_t *s_sel, int len, uint32_t *s_hist,
-                              uint64_t *s_state, uint32_t *s_wave) {
-  __shared__ uint32_t s_cnt[2 * 64];
-  const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wv = t >> 6, nw = nt >> 6;
-#ifdef CSA2_PROBE_TOPK
-  CSA2_TS(6);
-#endif
+// Top r of the list s_keys[0..m) (LDS, 0 = empty entry, m <= 256 * KPT):
+// the chosen entries' s_ids, in list order, go to s_sel (LDS) and, unless
+// out is NULL, to out[0..len), -1 padded.  Ordered compaction by ballots: entry (round k,
+// wave w) covers list positions 256k + 64w + 0..63; a table of per-entry
+// counts gives each entry's output offset.  All 256 threads.
+template <int KPT>
+__device__ __forceinline__ void select_top(const uint64_t *s_keys, const int32_t *s_ids, int m, int r, int32_t *out,
+                           int32_t *s_sel, int len, uint32_t *s_hist, uint64_t *s_state,
+                           uint32_t *s_wave) {
+  static_assert(KPT * 4 <= 128, "entry table holds 128 counts");
+  __shared__ uint32_t s_cnt[128];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  uint64_t kr[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) kr[k] = (t + 256 * k < m) ? s_keys[t + 256 * k] : 0ull;
   int reff = 0;
-  const uint64_t T = topk_threshold(s_keys, s_valid, m, r, &reff, s_hist, s_state, s_wave);
-#ifdef CSA2_PROBE_TOPK
-  CSA2_TS(12);
-#endif
-  const int rounds = (m + nt - 1) / nt;          // <= 32
-  uint32_t mine = 0;                             // bit R: this thread's entry of round R is kept
-  for (int R = 0; R < rounds; ++R) {
-    const int j = R * nt + t;
-    const bool f = reff > 0 && j < m && s_valid[j] && s_keys[j] >= T;
+  const uint64_t T = topk_threshold<KPT>(kr, s_keys, m, r, &reff, s_hist, s_state, s_wave);
+  uint32_t mine = 0;                             // bit k: entry t + 256k is kept
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const bool f = reff > 0 && kr[k] != 0 && kr[k] >= T;
     const uint64_t mask = __ballot(f);
-    if (f) mine |= 1u << R;
-    if (lane == 0) s_cnt[R * nw + wv] = (uint32_t)__popcll(mask);
+    if (f) mine |= 1u << k;
+    if (lane == 0) s_cnt[4 * k + wv] = (uint32_t)__popcll(mask);
   }
-  for (int e = rounds * nw + t; e < 2 * 64; e += nt) s_cnt[e] = 0;
+  if (t >= 4 * KPT && t < 128) s_cnt[t] = 0;
   __syncthreads();
+  CSA2_TOPK_TS(6);
   // every wave: exclusive offsets of entry pairs (2 per lane)
   const uint32_t c0 = s_cnt[2 * lane], c1 = s_cnt[2 * lane + 1];
   const uint32_t incl = wave_incl_scan(c0 + c1);
   const uint32_t pair_excl = incl - c0 - c1;
   const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
-  for (int R = 0; R < rounds; ++R) {
-    const int e = R * nw + wv;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int e = 4 * k + wv;
     const uint32_t base = __builtin_amdgcn_readlane(pair_excl, e >> 1) +
                           ((e & 1) ? __builtin_amdgcn_readlane(c0, e >> 1) : 0u);
-    const bool f = (mine >> R) & 1u;
+    const bool f = (mine >> k) & 1u;
     const uint64_t mask = __ballot(f);
     if (f) {
       const uint32_t pos = base + lanes_below(mask);
       if (pos < (uint32_t)len) {
-        const int32_t id = s_ids[R * nt + t];
+        const int32_t id = s_ids[t + 256 * k];
         s_sel[pos] = id;
-        out[pos] = id;
+        if (out) out[pos] = id;
       }
     }
   }
-  for (int j = (int)total + t; j < len; j += nt) { s_sel[j] = -1; out[j] = -1; }
+  for (int j = (int)total + t; j < len; j += 256) {
+    s_sel[j] = -1;
+    if (out) out[j] = -1;
+  }
   __syncthreads();
-#ifdef CSA2_PROBE_TOPK
-  CSA2_TS(13);
-#endif
+  CSA2_TOPK_TS(7);
+}
+
+// Runtime dispatch on the list length (up to 8,192 entries).
+__device__ __forceinline__ void select_in_lds(const uint64_t *s_keys, const int32_t *s_ids, int m, int r, int32_t *out,
+                              int32_t *s_sel, int len, uint32_t *s_hist, uint64_t *s_state,
+                              uint32_t *s_wave) {
+  if (m <= 2048)
+    select_top<8>(s_keys, s_ids, m, r, out, s_sel, len, s_hist, s_state, s_wave);
+  else
+    select_top<32>(s_keys, s_ids, m, r, out, s_sel, len, s_hist, s_state, s_wave);
+}
+
+// Threshold only, over an LDS list of up to 8,192 entries.
+__device__ __forceinline__ uint64_t threshold_in_lds(const uint64_t *s_keys, int m, int r, uint32_t *s_hist,
+                                     uint64_t *s_state, uint32_t *s_wave) {
+  const int t = threadIdx.x;
+  int reff = 0;
+  if (m <= 2048) {
+    uint64_t kr[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) kr[k] = (t + 256 * k < m) ? s_keys[t + 256 * k] : 0ull;
+    return topk_threshold<8>(kr, s_keys, m, r, &reff, s_hist, s_state, s_wave);
+  }
+  uint64_t kr[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) kr[k] = (t + 256 * k < m) ? s_keys[t + 256 * k] : 0ull;
+  return topk_threshold<32>(kr, s_keys, m, r, &reff, s_hist, s_state, s_wave);
 }
 
 __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   extern __shared__ uint64_t s_keys[];                 // lds_keys
-  __shared__ uint8_t s_valid[LDS_KEYS];
   __shared__ int32_t s_ids[LDS_KEYS];
   __shared__ int32_t s_sel[CSA2_TOPK_MAX];
   __shared__ uint32_t s_hist[RADIX_BINS];
@@ -676,23 +719,22 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
         uint64_t kv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int j = j0 + u * nt;
+          const int j = min(j0 + u * nt, c - 1);        // clamped: no branch
           int k = 0;
 #pragma unroll
           for (int kk = 1; kk < CAND_COPIES; ++kk) k += (j >= (int)off[kk]) ? 1 : 0;
-          kv[u] = j < c ? ld_agent(cands + k * a.cand_stride + (j - (int)off[k])) : 0ull;
+          kv[u] = ld_agent(cands + k * a.cand_stride + (j - (int)off[k]));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int j = j0 + u * nt;
-          if (j < c) { s_keys[j] = kv[u]; s_valid[j] = 1; }
+          if (j < c) s_keys[j] = kv[u];
         }
       }
       __syncthreads();
       CSA2_TS(11);
       // the candidates share the top 10 key bits (the tie digit)
-      int reff = 0;
-      const uint64_t T = topk_threshold(s_keys, s_valid, c, need, &reff, s_hist, s_state, s_wave);
+      const uint64_t T = threshold_in_lds(s_keys, c, need, s_hist, s_state, s_wave);
       CSA2_TS(12);
       for (int j = t; j < c; j += nt) {
         uint64_t k = s_keys[j];
@@ -752,6 +794,24 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   compact_bitmap(bm, a.nwords, first, s_ids, a.R, s_wave);
   __syncthreads();
   CSA2_TS(14);
+  if (a.pool_scores) {
+    // the chosen list's scores in list order (-1 entries get any value):
+    // the attention kernel takes the layer's top-k from them
+    constexpr int U = 8;
+    const int m = a.R;
+    float *ps = a.pool_scores + (int64_t)b * m;
+    for (int j0 = t; j0 < m; j0 += nt * U) {
+      float sv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t id = s_ids[min(j0 + u * nt, m - 1)];
+        sv[u] = scores[id >= 0 ? id : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (j0 + u * nt < m) ps[j0 + u * nt] = sv[u];
+    }
+  }
   if (a.topk > 0) {
     // top-k inside the pool: keys of the pool members, in pool order
     constexpr int U = 8;
@@ -760,22 +820,20 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
       float sv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * nt;
-        const int32_t id = j < m ? s_ids[j] : -1;
-        sv[u] = id >= 0 ? scores[id] : 0.f;
+        const int32_t id = s_ids[min(j0 + u * nt, m - 1)];
+        sv[u] = scores[id >= 0 ? id : 0];               // unconditional: no branch
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = j0 + u * nt;
         if (j < m) {
           const int32_t id = s_ids[j];
-          s_valid[j] = id >= 0;
           s_keys[j] = id >= 0 ? make_key(sv[u], (uint32_t)id) : 0ull;
         }
       }
     }
     __syncthreads();
-    select_in_lds(s_keys, s_valid, s_ids, m, a.topk, a.idx_out + (int64_t)b * a.topk, s_sel, a.topk,
+    select_in_lds(s_keys, s_ids, m, a.topk, a.idx_out + (int64_t)b * a.topk, s_sel, a.topk,
                   s_hist, s_state, s_wave);
   }
   CSA2_TS(15);
@@ -813,7 +871,6 @@ template <bool SELECT>
 __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   extern __shared__ uint64_t s_keys[];
   __shared__ float s_qbar[D];
-  __shared__ uint8_t s_valid[SELECT ? LDS_KEYS : 1];
   __shared__ int32_t s_ids[SELECT ? LDS_KEYS : 1];
   __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX : 1];
   __shared__ uint32_t s_hist[SELECT ? RADIX_BINS : 1];
@@ -831,10 +888,15 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   // first group's candidate ids and rows are requested before the query sum
   int it = blockIdx.x;
   int j = it * BLOCKS_PER_ITER + wv * 4 + slot;
-  int32_t blk = (it < iters && j < a.n_cand) ? cand[j] : -1;
+  int32_t blk = cand[min(j, a.n_cand - 1)];          // unconditional: no branch
+  if (!(it < iters && j < a.n_cand)) blk = -1;
   BlockRows cur;
-  if (blk >= 0 && blk < cap_blocks)
-    load_block(cur, codes + (int64_t)blk * BLOCK * CODE_BYTES, scales + (int64_t)blk * BLOCK * SCALE_BYTES, i);
+  {
+    // unconditional (an id outside the cache reads block 0, dropped later),
+    // so the rows and the query loads below form one batch
+    const int64_t lb = (blk >= 0 && blk < cap_blocks) ? blk : 0;
+    load_block(cur, codes + lb * BLOCK * CODE_BYTES, scales + lb * BLOCK * SCALE_BYTES, i);
+  }
   CSA2_TS(0);
   compute_qbar<64>(a.q, a.heads, b, s_qbar);
   // the length only masks: read after the first rows and the query sum
@@ -855,9 +917,12 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
     }
     const int it_next = it + gridDim.x;
     j = it_next * BLOCKS_PER_ITER + wv * 4 + slot;
-    blk = (it_next < iters && j < a.n_cand) ? cand[j] : -1;
-    if (blk >= 0 && blk < cap_blocks)
-      load_block(cur, codes + (int64_t)blk * BLOCK * CODE_BYTES, scales + (int64_t)blk * BLOCK * SCALE_BYTES, i);
+    blk = cand[min(j, a.n_cand - 1)];
+    if (!(it_next < iters && j < a.n_cand)) blk = -1;
+    if (it_next < iters) {
+      const int64_t lb = (blk >= 0 && blk < cap_blocks) ? blk : 0;
+      load_block(cur, codes + lb * BLOCK * CODE_BYTES, scales + lb * BLOCK * SCALE_BYTES, i);
+    }
   }
   CSA2_TS(2);
   if (!SELECT) return;
@@ -873,15 +938,14 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int jj = j0 + u * nt;
-      idv[u] = jj < m ? cand[jj] : -1;
-      sv[u] = jj < m ? ld_agent(scores + jj) : 0.f;
+      idv[u] = cand[min(jj, m - 1)];                  // clamped: no branch
+      sv[u] = ld_agent(scores + min(jj, m - 1));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int jj = j0 + u * nt;
       if (jj < m) {
         const bool ok = idv[u] >= 0 && idv[u] < nblk;
-        s_valid[jj] = ok;
         s_ids[jj] = idv[u];
         s_keys[jj] = ok ? make_key(sv[u], (uint32_t)idv[u]) : 0ull;
       }
@@ -889,7 +953,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   }
   __syncthreads();
   CSA2_TS(4);
-  select_in_lds(s_keys, s_valid, s_ids, m, a.topk, a.idx_out + (int64_t)b * a.topk, s_sel, a.topk,
+  select_in_lds(s_keys, s_ids, m, a.topk, a.idx_out + (int64_t)b * a.topk, s_sel, a.topk,
                 s_hist, s_state, s_wave);
   CSA2_TS(5);
 }

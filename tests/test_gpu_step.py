@@ -79,3 +79,15 @@ def test_workload4_ragged_batch_appending():
     w = W.scaled(W.WORKLOADS[4], context=0, batch=6)
     lengths = np.random.default_rng(4).integers(4000, 20000, 6)
     run_and_compare(w, lengths, 2)
+
+
+def test_pool_not_a_multiple_of_256():
+    # in-attention top-k over a ragged candidate list (600 entries, 40 kept)
+    w = W.scaled(W.WORKLOADS[3], context=12000, pool=600, topk=40)
+    run_and_compare(w, [12000 - 2], 2)
+
+
+def test_pool_above_in_kernel_limit():
+    # a pool beyond 2,048 candidates takes the separate top-k kernels
+    w = W.scaled(W.WORKLOADS[2], context=40000, pool=2600, topk=256)
+    run_and_compare(w, [40000], 1)
