@@ -5,7 +5,8 @@ compiled into one translation unit (csrc/api.hip includes the others), so
 the device flag word has a single definition without relocatable device
 code.  Flags: -ffp-contract=off keeps every float32 multiply and add of the
 pinned score order separate (fused forms are written explicitly where they
-are exact); packed-fp32 instructions are disabled.
+are exact); packed-fp32 instructions are disabled; the atomic optimizer is
+off (every atomic in the kernels is already issued by one lane).
 """
 import os
 import subprocess
@@ -20,6 +21,10 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep single-lane atomics as written: the wave-level atomic rewrite
+    # reads the result back at once, which would stall the full scan's
+    # work-counter prefetch
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc"),
 ]
 

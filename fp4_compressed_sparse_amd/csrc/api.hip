@@ -175,8 +175,10 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
   sa.qbar = at<float>(ws, L.qbar);
   qbar_kernel<<<B, SCAN_THREADS, 0, s>>>(q, heads, at<float>(ws, L.qbar));
   if (csa2_status st = launched("qbar")) return st;
-  const int iters = (int)ceil_div(nblk_grid > 0 ? nblk_grid : 1, BLOCKS_PER_ITER);
-  dim3 g1(grid_for(iters, B, 1024), B);
+  // a workgroup scores 8 blocks per round (4 waves x 2); 1,536 workgroups
+  // fill the 256 compute units at 6 waves per SIMD
+  const int64_t rounds = ceil_div(nblk_grid > 0 ? nblk_grid : 1, 8);
+  dim3 g1(grid_for(rounds, B, 1536), B);
   if (t_scan_before) (void)hipEventRecord(t_scan_before, s);
   scan_kernel<true><<<g1, SCAN_THREADS, 0, s>>>(sa);
   if (csa2_status st = launched("scan")) return st;

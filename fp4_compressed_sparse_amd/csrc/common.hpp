@@ -38,6 +38,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Per-row control words of a workspace (1 KB per sequence).
+constexpr int SCAN_GROUPS = 64;         // full-scan workgroup groups sharing a work counter
+
 struct Ctrl {
   uint32_t scan_grp[MAX_GRID_X / 32];   // scan arrivals per group of 32 workgroups
   uint32_t scan_top;                    // groups of the scan complete
@@ -48,6 +50,7 @@ struct Ctrl {
   uint32_t need;                        // keys still to take from that digit
   uint32_t all;                         // 1: every block is selected (nblk <= R)
   uint32_t pad[256 - 2 * (MAX_GRID_X / 32) - 2 - CAND_COPIES - 3];
+  uint32_t work[SCAN_GROUPS * 32];      // full-scan work counters, one per 128-byte line
 };
 
 // E4M3FN byte -> float (exact).  gfx950 decodes the OCP FN variant.

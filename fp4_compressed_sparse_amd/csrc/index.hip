@@ -57,7 +57,8 @@ struct ScanArgs {
   uint32_t *hist;           // [batch][HIST_BINS]
   int32_t R;                // keys to select (pool or topk)
   int32_t fill_invalid;     // write -inf for blocks >= nblk (export only)
-  const float *qbar;        // [batch][512] precomputed Qbar, or NULL (computed in-kernel)
+  const float *qbar;        // [batch][512] precomputed Qbar (required with the histogram),
+                            // or NULL (computed in-kernel)
 };
 
 // Qbar of sequence b into LDS; all 256 threads call.  Each thread owns two
@@ -110,10 +111,15 @@ __device__ __forceinline__ void load_block(BlockRows &r, const uint8_t *__restri
 
 // Score of one block from its loaded rows; the 16 lanes of a slot call it
 // together (lane16 = i).  cnt: rows present (1..8).  qb: this lane's 32
-// Qbar values (LDS).
-__device__ __forceinline__ float block_score(const BlockRows &r, int cnt, const float *qb) {
-  const u32x4 *w = r.w;
-  const uint32_t *sc = r.sc;
+// Qbar values (LDS).  RELOAD: as soon as row t is consumed its registers
+// receive row t of the block at (nrow, nsrow), so the next block's loads
+// are in flight while this one is scored (unconditional loads).
+template <bool RELOAD = false>
+__device__ __forceinline__ float block_score(BlockRows &r, int cnt, const float *qb,
+                                             const uint8_t *__restrict__ nrow = nullptr,
+                                             const uint8_t *__restrict__ nsrow = nullptr, int i = 0) {
+  u32x4 *w = r.w;
+  uint32_t *sc = r.sc;
   float S[32];
 #pragma unroll
   for (int t = 0; t < BLOCK; ++t) {
@@ -138,6 +144,10 @@ __device__ __forceinline__ float block_score(const BlockRows &r, int cnt, const 
         }
       }
     }
+    if (RELOAD) {
+      w[t] = *reinterpret_cast<const u32x4 *>(nrow + (int64_t)t * CODE_BYTES + 16 * i);
+      sc[t] = *reinterpret_cast<const uint16_t *>(nsrow + (int64_t)t * SCALE_BYTES + 2 * i);
+    }
   }
   float g0, g1;
   if (cnt == BLOCK) {
@@ -160,6 +170,79 @@ __device__ __forceinline__ float block_score(const BlockRows &r, int cnt, const 
   v = v + __shfl_xor(v, 4);             // level 4
   v = v + __shfl_xor(v, 8);             // level 5
   return v + 0.0f;
+}
+
+// Full-scan variant: 32 lanes per block, lane j owns scale group j
+// (channels 16j..16j+15: 8 code bytes and 1 scale byte of each row), so a
+// wave scores two blocks per step with about half the registers of the
+// 16-lane layout (twice the resident waves to cover memory latency).  Same
+// arithmetic in the same order: row sums by FMA in position order, x 0.125
+// (or / count), products with Qbar added left to right inside the group,
+// then the adjacent-pair tree over the 32 groups as lane butterflies
+// (xor 1, 2, 4, 8, 16).
+struct BlockRows32 {
+  u32x2 w[BLOCK];       // code bytes 8j..8j+7 of each row
+  uint32_t sc[BLOCK];   // scale byte j of each row
+};
+
+__device__ __forceinline__ void load_block32(BlockRows32 &r, const uint8_t *__restrict__ rowbase,
+                                             const uint8_t *__restrict__ srow, int j) {
+#pragma unroll
+  for (int t = 0; t < BLOCK; ++t) {
+    r.w[t] = *reinterpret_cast<const u32x2 *>(rowbase + (int64_t)t * CODE_BYTES + 8 * j);
+    r.sc[t] = srow[(int64_t)t * SCALE_BYTES + j];
+  }
+}
+
+// cnt: rows present (1..8); qb: Qbar[16j..16j+15] (LDS).  As each row is
+// consumed its registers receive the same row of the block at (nrow, nsrow),
+// so the next block's loads are in flight while this one is scored.
+__device__ __forceinline__ float block_score32(BlockRows32 &r, int cnt, const float *qb,
+                                               const uint8_t *__restrict__ nrow,
+                                               const uint8_t *__restrict__ nsrow, int j) {
+  float S[16];
+#pragma unroll
+  for (int t = 0; t < BLOCK; ++t) {
+    if (t < cnt) {
+      const float s = e4m3_to_f32(r.sc[t]);
+#pragma unroll
+      for (int dw = 0; dw < 2; ++dw) {
+        const uint32_t word = r.w[t][dw];
+        f32x2 v0 = e2m1x2_to_f32<0>(word);
+        f32x2 v1 = e2m1x2_to_f32<1>(word);
+        f32x2 v2 = e2m1x2_to_f32<2>(word);
+        f32x2 v3 = e2m1x2_to_f32<3>(word);
+        float *o = S + 8 * dw;
+        if (t == 0) {
+          o[0] = v0.x * s; o[1] = v0.y * s; o[2] = v1.x * s; o[3] = v1.y * s;
+          o[4] = v2.x * s; o[5] = v2.y * s; o[6] = v3.x * s; o[7] = v3.y * s;
+        } else {
+          o[0] = __builtin_fmaf(v0.x, s, o[0]); o[1] = __builtin_fmaf(v0.y, s, o[1]);
+          o[2] = __builtin_fmaf(v1.x, s, o[2]); o[3] = __builtin_fmaf(v1.y, s, o[3]);
+          o[4] = __builtin_fmaf(v2.x, s, o[4]); o[5] = __builtin_fmaf(v2.y, s, o[5]);
+          o[6] = __builtin_fmaf(v3.x, s, o[6]); o[7] = __builtin_fmaf(v3.y, s, o[7]);
+        }
+      }
+    }
+    r.w[t] = *reinterpret_cast<const u32x2 *>(nrow + (int64_t)t * CODE_BYTES + 8 * j);
+    r.sc[t] = nsrow[(int64_t)t * SCALE_BYTES + j];
+  }
+  float g;
+  if (cnt == BLOCK) {
+    g = qb[0] * (S[0] * 0.125f);
+#pragma unroll
+    for (int c = 1; c < 16; ++c) g = g + qb[c] * (S[c] * 0.125f);
+  } else {
+    const float fc = (float)cnt;
+    g = qb[0] * __fdiv_rn(S[0], fc);
+    for (int c = 1; c < 16; ++c) g = g + qb[c] * __fdiv_rn(S[c], fc);
+  }
+  g = g + __shfl_xor(g, 1);             // tree level 1: groups 2k, 2k+1
+  g = g + __shfl_xor(g, 2);
+  g = g + __shfl_xor(g, 4);
+  g = g + __shfl_xor(g, 8);
+  g = g + __shfl_xor(g, 16);            // level 5
+  return g + 0.0f;
 }
 
 // ---- block-level helpers (256 threads) ---------------------------------
@@ -265,14 +348,15 @@ __global__ void __launch_bounds__(SCAN_THREADS) qbar_kernel(const float *__restr
 
 // ---- full scan ----------------------------------------------------------
 
+// 80 registers: six waves per SIMD (24 per compute unit) keep the stream
+// of row requests going while other waves score.
 template <bool HIST>
-__global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
+__global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(6))) scan_kernel(ScanArgs a) {
   __shared__ float s_qbar[D];
   __shared__ uint32_t s_hist[HIST ? HIST_BINS : 1];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int slot = lane >> 4, i = lane & 15;
   CSA2_TS(0);
   if (HIST) {
     for (int j = threadIdx.x; j < HIST_BINS; j += SCAN_THREADS) s_hist[j] = 0;
@@ -280,49 +364,110 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
   const uint8_t *codes = a.codes + (int64_t)b * a.capacity * CODE_BYTES;
   const uint8_t *scales = a.scales + (int64_t)b * a.capacity * SCALE_BYTES;
   float *scores = a.scores + (int64_t)b * a.score_stride;
-  const int iters = (a.nblk_grid + BLOCKS_PER_ITER - 1) / BLOCKS_PER_ITER;
-  // Rows of the first block group are requested before the query sum so the
-  // two latencies overlap; afterwards the next group's rows are requested
-  // before the current group is scored.
-  int it = blockIdx.x;
-  int64_t blk = (int64_t)it * BLOCKS_PER_ITER + wv * 4 + slot;
-  BlockRows cur;
-  // the first rows are requested before the length is known: the grid's
-  // block count is bounded by the cache capacity
-  if (it < iters && blk < a.nblk_grid)
-    load_block(cur, codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES, i);
-  const int64_t n = clamp_len(a.seq_len[b], a.limit);
-  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
-  if (a.qbar) {
-    reinterpret_cast<float2 *>(s_qbar)[threadIdx.x] =
-        reinterpret_cast<const float2 *>(a.qbar + (int64_t)b * D)[threadIdx.x];
-    __syncthreads();
-  } else {
-    compute_qbar<16>(a.q, a.heads, b, s_qbar);
-  }
-  CSA2_TS(1);
-  const float *qb = s_qbar + 32 * i;
-  for (; it < iters; it += gridDim.x) {
-    if (blk < nblk) {
-      const int cnt = (int)min((int64_t)BLOCK, n - blk * BLOCK);
-      float s = block_score(cur, cnt, qb);
-      if (i == 0) {
-        scores[blk] = s;
-        if (HIST) atomicAdd(&s_hist[ord_key(s) >> HIST_SHIFT], 1u);
-      }
-    } else if (a.fill_invalid && i == 0 && blk < a.score_stride) {
-      scores[blk] = -__builtin_huge_valf();
+  // Rows of the first chunk are requested before the query sum so the two
+  // latencies overlap; afterwards each row of the next chunk is requested
+  // as soon as the same row of the current chunk is consumed.
+  Ctrl *ctrl = a.ctrl + b;
+  int64_t n, nblk;
+  if constexpr (HIST) {
+    // Dynamic schedule.  Each wave scores chunks of 2 blocks (one per half
+    // wave): its first chunk is fixed (blockIdx.x * 4 + wave); later ones
+    // come from its group's counter, group g of the workgroups (blockIdx.x =
+    // g mod G, G = min(64, grid), spanning every dispatch slot of the compute
+    // units) sharing chunks first + g, first + g + G, ...  Older workgroups
+    // win the issue arbiter, so a static split leaves the youngest finishing
+    // last; here the waves finish within about one chunk of each other.
+    // The grab of the next chunk is in flight while the current one is
+    // scored, and so are the next chunk's rows.
+    const int half = lane >> 5, j = lane & 31;
+    const int ngrp = min(SCAN_GROUPS, (int)gridDim.x);   // every group has a workgroup
+    const int grp = blockIdx.x % ngrp;
+    uint32_t *ctr = &ctrl->work[grp * 32];
+    const int64_t nchunks = (a.nblk_grid + 1) / 2;
+    const int64_t first = (int64_t)gridDim.x * 4;
+    auto grab = [&]() {
+      uint32_t k = 0;
+      if (lane == 0) k = atomic_add_agent(ctr, 1u);
+      return k;
+    };
+    // request order: length, query sum, first grab, first rows (the rows
+    // unconditionally, clamped into the cache), so no use waits on a later
+    // request
+    const int64_t seq = a.seq_len[b];
+    const float2 qv = reinterpret_cast<const float2 *>(a.qbar + (int64_t)b * D)[threadIdx.x];
+    int64_t c = (int64_t)blockIdx.x * 4 + wv;
+    uint32_t pending = grab();
+    BlockRows32 cur;
+    {
+      const int64_t blk = max((int64_t)0, min(2 * c + half, (int64_t)a.nblk_grid - 1));  // block 0 always exists
+      load_block32(cur, codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES, j);
     }
-    // next group: one buffer of rows per wave; the other resident waves
-    // cover this wave's memory latency
-    blk = (int64_t)(it + gridDim.x) * BLOCKS_PER_ITER + wv * 4 + slot;
-    if (it + (int)gridDim.x < iters && blk < nblk)
-      load_block(cur, codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES, i);
+    __builtin_amdgcn_sched_barrier(0);
+    n = clamp_len(seq, a.limit);
+    nblk = (n + BLOCK - 1) / BLOCK;
+    reinterpret_cast<float2 *>(s_qbar)[threadIdx.x] = qv;
+    __syncthreads();
+    CSA2_TS(1);
+    const float *qb = s_qbar + 16 * j;
+    while (c < nchunks) {
+      const int64_t blk = 2 * c + half;
+      const int64_t cn = first + grp + (int64_t)ngrp * __builtin_amdgcn_readlane(pending, 0);
+      pending = grab();
+      // past the end (or the sequence) block 0 is re-read, an L2 hit
+      int64_t nb = 2 * cn + half;
+      if (cn >= nchunks || nb >= nblk) nb = 0;
+      const int cnt = (int)max((int64_t)1, min((int64_t)BLOCK, n - blk * BLOCK));
+      const float sc = block_score32(cur, cnt, qb, codes + nb * BLOCK * CODE_BYTES,
+                                     scales + nb * BLOCK * SCALE_BYTES, j);
+      if (j == 0 && blk < nblk) {
+        scores[blk] = sc;
+        atomicAdd(&s_hist[ord_key(sc) >> HIST_SHIFT], 1u);
+      }
+      c = cn;
+    }
+  } else {
+    // static schedule (score export): wave chunks blockIdx.x * 4 + wave,
+    // then every gridDim.x * 4 chunks
+    const int half = lane >> 5, j = lane & 31;
+    const int64_t nchunks = (a.nblk_grid + 1) / 2;
+    const int64_t step = (int64_t)gridDim.x * 4;
+    int64_t c = (int64_t)blockIdx.x * 4 + wv;
+    BlockRows32 cur;
+    {
+      const int64_t blk = max((int64_t)0, min(2 * c + half, (int64_t)a.nblk_grid - 1));
+      load_block32(cur, codes + blk * BLOCK * CODE_BYTES, scales + blk * BLOCK * SCALE_BYTES, j);
+    }
+    n = clamp_len(a.seq_len[b], a.limit);
+    nblk = (n + BLOCK - 1) / BLOCK;
+    if (a.qbar) {
+      reinterpret_cast<float2 *>(s_qbar)[threadIdx.x] =
+          reinterpret_cast<const float2 *>(a.qbar + (int64_t)b * D)[threadIdx.x];
+      __syncthreads();
+    } else {
+      compute_qbar<16>(a.q, a.heads, b, s_qbar);
+    }
+    CSA2_TS(1);
+    const float *qb = s_qbar + 16 * j;
+    for (; c < nchunks; c += step) {
+      const int64_t blk = 2 * c + half;
+      int64_t nb = 2 * (c + step) + half;
+      if (c + step >= nchunks || nb >= nblk) nb = 0;
+      const int cnt = (int)max((int64_t)1, min((int64_t)BLOCK, n - blk * BLOCK));
+      const float sc = block_score32(cur, cnt, qb, codes + nb * BLOCK * CODE_BYTES,
+                                     scales + nb * BLOCK * SCALE_BYTES, j);
+      if (j == 0) {
+        if (blk < nblk) {
+          scores[blk] = sc;
+          if (HIST) atomicAdd(&s_hist[ord_key(sc) >> HIST_SHIFT], 1u);
+        } else if (a.fill_invalid && blk < a.score_stride) {
+          scores[blk] = -__builtin_huge_valf();
+        }
+      }
+    }
   }
   if (!HIST) return;
   __syncthreads();
   CSA2_TS(2);
-  Ctrl *ctrl = a.ctrl + b;
   uint32_t *gh = a.hist + (int64_t)b * HIST_COPIES * HIST_BINS;
   {
     uint32_t *mine = gh + (blockIdx.x % HIST_COPIES) * HIST_BINS;
@@ -373,6 +518,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) scan_kernel(ScanArgs a) {
   }
   __syncthreads();
   for (int j = t; j < HIST_COPIES * HIST_BINS; j += SCAN_THREADS) gh[j] = 0;
+  if (t < SCAN_GROUPS) st_agent(&ctrl->work[t * 32], 0u);   // counters ready for the next call
 }
 
 // ---- select (after a full scan) ------------------------------------------
