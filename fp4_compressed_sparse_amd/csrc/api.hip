@@ -191,6 +191,7 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
   int lk = R > 4096 ? R : 4096;
   se.lds_keys = lk;
   se.pool_scores = pool_scores;
+  se.hist = sa.hist;
   dim3 g2(grid_for(ceil_div(L.nwords / 2, 4), B, 256), B);
   select_kernel<<<g2, SCAN_THREADS, (size_t)lk * sizeof(uint64_t), s>>>(se);
   return launched("select");
@@ -308,7 +309,8 @@ csa2_status fp4_quantize_kv(const float *x, int64_t rows, const int64_t *dst_row
     return fail(CSA2_E_CAPACITY, "dst_rows %lld too small for %lld rows", (long long)dst_rows, (long long)rows);
   if (csa2_status st = device_ready()) return st;
   const int64_t quads = rows * 128;
-  const int grid = (int)(ceil_div(quads, 256) < 4096 ? ceil_div(quads, 256) : 4096);
+  const int64_t want = ceil_div(quads, 256 * QU);     // one round of QU quads per thread
+  const int grid = (int)(want < 4096 ? want : 4096);
   quantize_rows_kernel<<<grid, 256, 0, as_stream(stream)>>>(x, rows, dst_row, dst_rows, codes, scales);
   return launched("quantize");
 }

@@ -144,21 +144,18 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     const int64_t nsel = clamp_len(a.seq_len[b], a.limit);
     __builtin_amdgcn_sched_barrier(0);
     const int64_t nbs = (nsel + BLOCK - 1) / BLOCK;
-    uint64_t *s_keys = reinterpret_cast<uint64_t *>(s_v);
-    int32_t *s_ids = reinterpret_cast<int32_t *>(s_keys + SEL_CAND_MAX);
-    uint32_t *s_hist = reinterpret_cast<uint32_t *>(s_ids + SEL_CAND_MAX);
+    uint64_t *s_keys = reinterpret_cast<uint64_t *>(s_v);     // for the radix fallback only
+    uint32_t *s_hist = reinterpret_cast<uint32_t *>(s_keys + SEL_CAND_MAX);
+    uint64_t kr[KPT];
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
       const int j = tid + ATT_THREADS * k;
-      if (j < m) {
-        const bool ok = cid[k] >= 0 && cid[k] < nbs;
-        s_keys[j] = ok ? make_key(csc[k], (uint32_t)cid[k]) : 0ull;
-        s_ids[j] = cid[k];
-      }
+      const bool ok = j < m && cid[k] >= 0 && cid[k] < nbs;
+      kr[k] = ok ? make_key(csc[k], (uint32_t)cid[k]) : 0ull;
+      if (j < m) s_keys[j] = kr[k];
     }
-    __syncthreads();
     int32_t *io = blockIdx.x == 0 ? a.idx_out + (int64_t)b * a.topk : nullptr;
-    select_top<KPT>(s_keys, s_ids, m, a.topk, io, s_sel, a.topk, s_hist, s_state, s_wave);
+    select_top_regs<KPT>(kr, cid, s_keys, m, a.topk, io, s_sel, a.topk, s_hist, s_state, s_wave);
   }
   // request order: the first stage's block ids, the query tile, then (once
   // the ids are in) the rows, so the query and id latencies overlap

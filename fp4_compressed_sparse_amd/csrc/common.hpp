@@ -154,9 +154,12 @@ __device__ __forceinline__ bool arrive_last(uint32_t *grp, uint32_t *top, uint32
   return s_last != 0;
 }
 
+// Agent-scope store: written through to the device coherence point (a plain
+// store with the device-scope cache bit), so a later ld_agent on another XCD
+// sees it once the writer's vmcnt has drained.
 template <typename T>
 __device__ __forceinline__ void st_agent(T *p, T v) {
-  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

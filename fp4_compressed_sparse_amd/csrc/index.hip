@@ -476,49 +476,9 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
       if (c) atomic_add_agent(mine + j, c);
     }
   }
-  if (!arrive_last(ctrl->scan_grp, &ctrl->scan_top, gridDim.x)) return;
-  CSA2_TS(3);
-  // last workgroup: locate the digit of the R-th largest key
-  const int t = threadIdx.x;
-  if ((int64_t)a.R >= nblk) {
-    if (t == 0) { ctrl->all = 1; ctrl->thr_digit = 0; ctrl->need = 0; }
-  } else {
-    // thread t owns bins HIST_BINS-1-(4t+j), j = 0..3 (top thread first),
-    // summed over the copies
-    constexpr int PER = HIST_BINS / SCAN_THREADS;
-    uint32_t v[PER][HIST_COPIES];
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-#pragma unroll
-      for (int k = 0; k < HIST_COPIES; ++k)
-        v[j][k] = ld_agent(gh + k * HIST_BINS + (HIST_BINS - 1 - (PER * t + j)));
-    uint32_t c[PER], sum = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      c[j] = 0;
-#pragma unroll
-      for (int k = 0; k < HIST_COPIES; ++k) c[j] += v[j][k];
-      sum += c[j];
-    }
-    uint32_t total;
-    uint32_t above = block_exclusive_scan(sum, &total, s_wave);
-    const uint32_t R = (uint32_t)a.R;
-    if (above < R && R <= above + sum) {
-      uint32_t acc = above;
-      for (int j = 0; j < PER; ++j) {
-        if (acc + c[j] >= R) {
-          ctrl->thr_digit = HIST_BINS - 1 - (PER * t + j);
-          ctrl->need = R - acc;
-          ctrl->all = 0;
-          break;
-        }
-        acc += c[j];
-      }
-    }
-  }
-  __syncthreads();
-  for (int j = t; j < HIST_COPIES * HIST_BINS; j += SCAN_THREADS) gh[j] = 0;
-  if (t < SCAN_GROUPS) st_agent(&ctrl->work[t * 32], 0u);   // counters ready for the next call
+  // The threshold digit is found by every workgroup of the select kernel
+  // from these copies (no last-workgroup hand-off here); the select
+  // kernel's last workgroup clears the copies and the work counters.
 }
 
 // ---- select (after a full scan) ------------------------------------------
@@ -539,6 +499,7 @@ struct SelectArgs {
   int32_t *idx_out;         // [batch][topk] when topk > 0
   int32_t lds_keys;         // dynamic LDS keys (>= R, <= LDS_KEYS)
   float *pool_scores;       // [batch][R]: scores of first_out in its order (or NULL)
+  uint32_t *hist;           // [batch][HIST_COPIES][HIST_BINS] from the full scan (cleared here)
 };
 
 __device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
@@ -547,29 +508,38 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
 
 // Ids of the set bits of bitmap[0..nwords), ascending, into s_out[0..len)
 // (LDS) and then out[0..len) with coalesced stores, -1 padded.  All
-// threads.  Each thread owns a contiguous run of words, loaded 16 at a time
-// (one memory round trip per 16 words); no global load sits between the
-// stores.
-__device__ __forceinline__ void compact_bitmap(const uint32_t *bm, int nwords, int32_t *out, int32_t *s_out,
-                               int len, uint32_t *s_wave) {
-  constexpr int U = 16;
+// threads.  Each thread owns a contiguous run of words; with MAXW > 0 the run
+// (at most MAXW words) is loaded once into registers, one memory round trip;
+// MAXW = 0 streams it twice in batches of 16 (any length).
+template <int MAXW>
+__device__ __forceinline__ void compact_bitmap_t(const uint32_t *bm, int nwords, int32_t *out,
+                                                 int32_t *s_out, int len, uint32_t *s_wave) {
+  constexpr int U = MAXW > 0 ? MAXW : 16;
   const int t = threadIdx.x, nt = blockDim.x;
   const int per = (nwords + nt - 1) / nt;
   const int w0 = min(nwords, t * per), w1 = min(nwords, w0 + per);
+  uint32_t v[U];
   uint32_t cnt = 0;
-  for (int wb = w0; wb < w1; wb += U) {
-    uint32_t v[U];
+  if (MAXW > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld_agent(bm + min(wb + u, w1 - 1));   // clamped: no branch
+    for (int u = 0; u < U; ++u) v[u] = ld_agent(bm + max(0, min(w0 + u, w1 - 1)));   // clamped: no branch
 #pragma unroll
-    for (int u = 0; u < U; ++u) cnt += (wb + u < w1) ? __popc(v[u]) : 0u;
+    for (int u = 0; u < U; ++u) cnt += (w0 + u < w1) ? __popc(v[u]) : 0u;
+  } else {
+    for (int wb = w0; wb < w1; wb += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld_agent(bm + min(wb + u, w1 - 1));
+#pragma unroll
+      for (int u = 0; u < U; ++u) cnt += (wb + u < w1) ? __popc(v[u]) : 0u;
+    }
   }
   uint32_t total;
   uint32_t off = block_exclusive_scan(cnt, &total, s_wave);
   for (int wb = w0; wb < w1 && off < (uint32_t)len; wb += U) {
-    uint32_t v[U];
+    if (MAXW == 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld_agent(bm + min(wb + u, w1 - 1));
+      for (int u = 0; u < U; ++u) v[u] = ld_agent(bm + min(wb + u, w1 - 1));
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       uint32_t bits = (wb + u < w1) ? v[u] : 0u;
@@ -583,6 +553,17 @@ __device__ __forceinline__ void compact_bitmap(const uint32_t *bm, int nwords, i
   for (int j = (int)total + t; j < len; j += nt) s_out[j] = -1;
   __syncthreads();
   for (int j = t; j < len; j += nt) out[j] = s_out[j];
+}
+
+__device__ __forceinline__ void compact_bitmap(const uint32_t *bm, int nwords, int32_t *out,
+                                               int32_t *s_out, int len, uint32_t *s_wave) {
+  const int per = (nwords + (int)blockDim.x - 1) / (int)blockDim.x;
+  if (per <= 16)
+    compact_bitmap_t<16>(bm, nwords, out, s_out, len, s_wave);
+  else if (per <= 32)
+    compact_bitmap_t<32>(bm, nwords, out, s_out, len, s_wave);
+  else
+    compact_bitmap_t<0>(bm, nwords, out, s_out, len, s_wave);
 }
 
 __device__ __forceinline__ float unord_key(uint32_t u) {
@@ -706,21 +687,17 @@ __device__ __forceinline__ uint64_t topk_threshold(const uint64_t (&kr)[KPT], co
   return s_state[0];
 }
 
-// Top r of the list s_keys[0..m) (LDS, 0 = empty entry, m <= 256 * KPT):
-// the chosen entries' s_ids, in list order, go to s_sel (LDS) and, unless
-// out is NULL, to out[0..len), -1 padded.  Ordered compaction by ballots: entry (round k,
-// wave w) covers list positions 256k + 64w + 0..63; a table of per-entry
-// counts gives each entry's output offset.  All 256 threads.
+// Register form of the block top-k: thread t holds list entries t + 256k
+// (keys kr, 0 = empty, and their ids); s_keys is the same list in LDS, read
+// only by the radix fallback.
 template <int KPT>
-__device__ __forceinline__ void select_top(const uint64_t *s_keys, const int32_t *s_ids, int m, int r, int32_t *out,
-                           int32_t *s_sel, int len, uint32_t *s_hist, uint64_t *s_state,
-                           uint32_t *s_wave) {
+__device__ __forceinline__ void select_top_regs(const uint64_t (&kr)[KPT], const int32_t (&ids)[KPT],
+                                                const uint64_t *s_keys, int m, int r, int32_t *out,
+                                                int32_t *s_sel, int len, uint32_t *s_hist,
+                                                uint64_t *s_state, uint32_t *s_wave) {
   static_assert(KPT * 4 <= 128, "entry table holds 128 counts");
   __shared__ uint32_t s_cnt[128];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  uint64_t kr[KPT];
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) kr[k] = (t + 256 * k < m) ? s_keys[t + 256 * k] : 0ull;
   int reff = 0;
   const uint64_t T = topk_threshold<KPT>(kr, s_keys, m, r, &reff, s_hist, s_state, s_wave);
   uint32_t mine = 0;                             // bit k: entry t + 256k is kept
@@ -749,9 +726,8 @@ __device__ __forceinline__ void select_top(const uint64_t *s_keys, const int32_t
     if (f) {
       const uint32_t pos = base + lanes_below(mask);
       if (pos < (uint32_t)len) {
-        const int32_t id = s_ids[t + 256 * k];
-        s_sel[pos] = id;
-        if (out) out[pos] = id;
+        s_sel[pos] = ids[k];
+        if (out) out[pos] = ids[k];
       }
     }
   }
@@ -761,6 +737,27 @@ __device__ __forceinline__ void select_top(const uint64_t *s_keys, const int32_t
   }
   __syncthreads();
   CSA2_TOPK_TS(7);
+}
+
+// Top r of the list s_keys[0..m) (LDS, 0 = empty entry, m <= 256 * KPT):
+// the chosen entries' s_ids, in list order, go to s_sel (LDS) and, unless
+// out is NULL, to out[0..len), -1 padded.  Ordered compaction by ballots:
+// entry (round k, wave w) covers list positions 256k + 64w + 0..63; a table
+// of per-entry counts gives each entry's output offset.  All 256 threads.
+template <int KPT>
+__device__ __forceinline__ void select_top(const uint64_t *s_keys, const int32_t *s_ids, int m, int r, int32_t *out,
+                           int32_t *s_sel, int len, uint32_t *s_hist, uint64_t *s_state,
+                           uint32_t *s_wave) {
+  const int t = threadIdx.x;
+  uint64_t kr[KPT];
+  int32_t ids[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int j = min(t + 256 * k, m - 1);
+    kr[k] = (t + 256 * k < m) ? s_keys[j] : 0ull;
+    ids[k] = s_ids[j];
+  }
+  select_top_regs<KPT>(kr, ids, s_keys, m, r, out, s_sel, len, s_hist, s_state, s_wave);
 }
 
 // Runtime dispatch on the list length (up to 8,192 entries).
@@ -800,45 +797,106 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   Ctrl *ctrl = a.ctrl + b;
+  const int t = threadIdx.x, nt = blockDim.x;
   const int64_t n = clamp_len(a.seq_len[b], a.limit);
   const int64_t nblk = (n + BLOCK - 1) / BLOCK;
   const float *scores = a.scores + (int64_t)b * a.score_stride;
   uint32_t *bm = a.bitmap + (int64_t)b * a.nwords;
   uint64_t *cands = a.cands + (int64_t)b * CAND_COPIES * a.cand_stride;
-  const bool all = ctrl->all != 0;
-  const uint32_t thr = ctrl->thr_digit;
+  uint32_t *gh = a.hist + (int64_t)b * HIST_COPIES * HIST_BINS;
   CSA2_TS(8);
-  // 64 ids per wave step: the ballot of ids above the tie digit is OR-ed
-  // into the (zeroed) bitmap; ids in the tie digit go to one of 8 lists
-  uint64_t *mylist = cands + (blockIdx.x % CAND_COPIES) * a.cand_stride;
-  uint32_t *mycount = &ctrl->ncand[blockIdx.x % CAND_COPIES];
+  // This wave's scores (up to PRE chunks of 64 blocks), requested together
+  // with the histogram copies: one memory round trip for both.
+  constexpr int PRE = 4;
   const int chunks = a.nwords / 2;
-  for (int ch = blockIdx.x * 4 + wv; ch < chunks; ch += gridDim.x * 4) {
-    const int64_t id = (int64_t)ch * 64 + lane;
-    bool in = false, tie = false;
-    uint32_t key_hi = 0;
-    if (id < nblk) {
-      if (all) {
-        in = true;
-      } else {
-        float s = scores[id];
-        key_hi = ord_key(s);
-        uint32_t dg = key_hi >> HIST_SHIFT;
-        in = dg > thr;
-        tie = dg == thr;
+  const int ch0 = blockIdx.x * 4 + wv, chs = gridDim.x * 4;
+  float sv[PRE];
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const int64_t id = (int64_t)(ch0 + k * chs) * 64 + lane;
+    sv[k] = scores[id < nblk ? id : 0];
+  }
+  // Threshold digit, found by every workgroup from the scan's copies:
+  // thread t owns bins HIST_BINS-1-(4t+j), j = 0..3 (top thread first).
+  constexpr int PER = HIST_BINS / SCAN_THREADS;
+  uint32_t hv[PER][HIST_COPIES];
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+#pragma unroll
+    for (int k = 0; k < HIST_COPIES; ++k) hv[j][k] = gh[k * HIST_BINS + (HIST_BINS - 1 - (PER * t + j))];
+  __builtin_amdgcn_sched_barrier(0);
+  const bool all = (int64_t)a.R >= nblk;
+  uint32_t thr = 0, need = 0;
+  {
+    uint32_t c[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      c[j] = 0;
+#pragma unroll
+      for (int k = 0; k < HIST_COPIES; ++k) c[j] += hv[j][k];
+      sum += c[j];
+    }
+    uint32_t total;
+    const uint32_t above = block_exclusive_scan(sum, &total, s_wave);
+    const uint32_t R = (uint32_t)a.R;
+    if (t == 0) s_state[0] = 0;
+    __syncthreads();
+    if (!all && above < R && R <= above + sum) {
+      uint32_t acc = above;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (acc < R && R <= acc + c[j])
+          s_state[0] = ((uint64_t)(HIST_BINS - 1 - (PER * t + j)) << 32) | (uint64_t)(R - acc);
+        acc += c[j];
       }
     }
-    uint64_t m_in = __ballot(in);
-    if (lane == 0 && (uint32_t)m_in) atomicOr(bm + 2 * ch, (uint32_t)m_in);
-    if (lane == 1 && (uint32_t)(m_in >> 32)) atomicOr(bm + 2 * ch + 1, (uint32_t)(m_in >> 32));
-    uint64_t m_tie = __ballot(tie);
-    if (m_tie) {
+    __syncthreads();
+    thr = (uint32_t)(s_state[0] >> 32);
+    need = (uint32_t)s_state[0];
+  }
+  // 64 ids per chunk: the ballot of ids above the tie digit is OR-ed into
+  // the (zeroed) bitmap; ids in the tie digit go to one of 8 lists, with one
+  // counter reservation per wave for all its chunks
+  uint64_t *mylist = cands + (blockIdx.x % CAND_COPIES) * a.cand_stride;
+  uint32_t *mycount = &ctrl->ncand[blockIdx.x % CAND_COPIES];
+  for (int base_ch = ch0; base_ch < chunks; base_ch += PRE * chs) {
+    if (base_ch != ch0) {
+#pragma unroll
+      for (int k = 0; k < PRE; ++k) {
+        const int64_t id = (int64_t)(base_ch + k * chs) * 64 + lane;
+        sv[k] = scores[id < nblk ? id : 0];
+      }
+    }
+    uint64_t m_tie[PRE];
+    uint32_t key_hi[PRE];
+    uint32_t ntie = 0;
+#pragma unroll
+    for (int k = 0; k < PRE; ++k) {
+      const int ch = base_ch + k * chs;
+      const int64_t id = (int64_t)ch * 64 + lane;
+      key_hi[k] = ord_key(sv[k]);
+      const uint32_t dg = key_hi[k] >> HIST_SHIFT;
+      const bool valid = ch < chunks && id < nblk;
+      const bool in = valid && (all || dg > thr);
+      const bool tie = valid && !all && dg == thr;
+      const uint64_t m_in = __ballot(in);
+      if (lane == 0 && (uint32_t)m_in) atomicOr(bm + 2 * ch, (uint32_t)m_in);
+      if (lane == 1 && (uint32_t)(m_in >> 32)) atomicOr(bm + 2 * ch + 1, (uint32_t)(m_in >> 32));
+      m_tie[k] = __ballot(tie);
+      ntie += (uint32_t)__popcll(m_tie[k]);
+    }
+    if (ntie) {
       uint32_t base = 0;
-      if (lane == 0) base = atomic_add_agent(mycount, (uint32_t)__popcll(m_tie));
-      base = __shfl(base, 0);
-      if (tie) {
-        uint32_t rank = (uint32_t)__popcll(m_tie & ((1ull << lane) - 1));
-        st_agent(mylist + base + rank, ((uint64_t)key_hi << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id));
+      if (lane == 0) base = atomic_add_agent(mycount, ntie);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int k = 0; k < PRE; ++k) {
+        if ((m_tie[k] >> lane) & 1ull) {
+          const uint32_t rank = base + (uint32_t)__popcll(m_tie[k] & ((1ull << lane) - 1));
+          const int64_t id = (int64_t)(base_ch + k * chs) * 64 + lane;
+          st_agent(mylist + rank, ((uint64_t)key_hi[k] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id));
+        }
+        base += (uint32_t)__popcll(m_tie[k]);
       }
     }
   }
@@ -846,7 +904,6 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   if (!arrive_last(ctrl->sel_grp, &ctrl->sel_top, gridDim.x)) return;
 
   // ---- finisher: one workgroup per sequence ----
-  const int t = threadIdx.x, nt = blockDim.x;
   CSA2_TS(10);
   if (!all && nblk > 0) {
     uint32_t cnt[CAND_COPIES], off[CAND_COPIES + 1];
@@ -857,10 +914,10 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
       off[k + 1] = off[k] + cnt[k];
     }
     const int c = (int)off[CAND_COPIES];
-    const int need = (int)ctrl->need;
     if (c <= a.lds_keys) {
-      // flat index over the 8 lists, 8 loads in flight per thread
-      constexpr int U = 8;
+      // flat index over the 8 lists, 16 loads in flight per thread (one
+      // round trip up to 4,096 candidates)
+      constexpr int U = 16;
       for (int j0 = t; j0 < c; j0 += nt * U) {
         uint64_t kv[U];
 #pragma unroll
@@ -880,7 +937,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
       __syncthreads();
       CSA2_TS(11);
       // the candidates share the top 10 key bits (the tie digit)
-      const uint64_t T = threshold_in_lds(s_keys, c, need, s_hist, s_state, s_wave);
+      const uint64_t T = threshold_in_lds(s_keys, c, (int)need, s_hist, s_state, s_wave);
       CSA2_TS(12);
       for (int j = t; j < c; j += nt) {
         uint64_t k = s_keys[j];
@@ -893,7 +950,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
       // rare: the tie digit holds more keys than LDS; select through global
       // memory one 8-bit digit at a time (same rule, slower)
       uint64_t prefix = 0, pmask = 0;
-      int remaining = need;
+      int remaining = (int)need;
       for (int shift = 56; shift >= 0; shift -= 8) {
         for (int j = t; j < 256; j += nt) s_hist[j] = 0;
         __syncthreads();
@@ -984,14 +1041,12 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   }
   CSA2_TS(15);
   __syncthreads();
-  // leave the row clean for the next call (read only by later kernels)
+  // leave the row clean for the next call (read only by later kernels):
+  // bitmap, tie counters, the scan's histogram copies and work counters
   for (int j = t; j < a.nwords; j += nt) bm[j] = 0;
+  for (int j = t; j < HIST_COPIES * HIST_BINS; j += nt) gh[j] = 0;
   if (t < CAND_COPIES) ctrl->ncand[t] = 0;
-  if (t == 0) {
-    ctrl->all = 0;
-    ctrl->need = 0;
-    ctrl->thr_digit = 0;
-  }
+  if (t < SCAN_GROUPS) ctrl->work[t * 32] = 0;
 }
 
 // ---- rescoring of a candidate list (pool) + top-k --------------------------

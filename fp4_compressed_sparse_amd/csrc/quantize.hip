@@ -93,27 +93,44 @@ __device__ __forceinline__ uint32_t quantize_quad(float4 v, uint32_t *sbyte, boo
   return n0 | (n1 << 4) | (n2 << 8) | (n3 << 12);
 }
 
-// rows x 512 floats -> codes/scales rows dst_row[r] (or r).
+// rows x 512 floats -> codes/scales rows dst_row[r] (or r).  Each thread
+// takes QU quads per round, QU grid strides apart, and requests all of them
+// (and their destination rows) before quantising any: QU loads in flight
+// per lane instead of one.  The stride is a multiple of 128 quads (one row),
+// so a wave's 64 lanes always cover half of one row.
+constexpr int QU = 4;
 __global__ void __launch_bounds__(256) quantize_rows_kernel(
     const float *__restrict__ x, int64_t rows, const int64_t *__restrict__ dst_row,
     int64_t dst_rows, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
   const int64_t total = rows * 128;  // a multiple of 64: whole waves stay together
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    int64_t r = i >> 7;
-    int q = (int)(i & 127);
-    float4 v = reinterpret_cast<const float4 *>(x)[i];
-    uint32_t sb;
-    bool bad;
-    uint32_t packed = quantize_quad(v, &sb, &bad);
-    int64_t d = dst_row ? dst_row[r] : r;
-    if (d < 0 || d >= dst_rows) {
-      if ((q & 127) == 0) raise_flag(FLAG_CAPACITY);
-      continue;
+  const float4 *x4 = reinterpret_cast<const float4 *>(x);
+  for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < total; i0 += stride * QU) {
+    float4 v[QU];
+    int64_t d[QU];
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int64_t i = min(i0 + u * stride, total - 1);      // clamped: no branch
+      v[u] = x4[i];
+      d[u] = dst_row ? dst_row[i >> 7] : (i >> 7);
     }
-    if (bad && (q & 3) == 0) raise_flag(FLAG_NONFINITE_KV);
-    reinterpret_cast<uint16_t *>(codes + d * CODE_BYTES)[q] = (uint16_t)packed;
-    if ((q & 3) == 0) scales[d * SCALE_BYTES + (q >> 2)] = (uint8_t)sb;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i >= total) break;                                  // uniform per wave
+      const int q = (int)(i & 127);
+      uint32_t sb;
+      bool bad;
+      const uint32_t packed = quantize_quad(v[u], &sb, &bad);
+      if (d[u] < 0 || d[u] >= dst_rows) {
+        if (q == 0) raise_flag(FLAG_CAPACITY);
+        continue;
+      }
+      if (bad && (q & 3) == 0) raise_flag(FLAG_NONFINITE_KV);
+      reinterpret_cast<uint16_t *>(codes + d[u] * CODE_BYTES)[q] = (uint16_t)packed;
+      if ((q & 3) == 0) scales[d[u] * SCALE_BYTES + (q >> 2)] = (uint8_t)sb;
+    }
   }
 }
 
