@@ -1,0 +1,179 @@
+"""Full-size parity of the 20-layer decoder at 1,048,576 positions, in the
+launch configuration bench.py times (GPU-quantised caches, one decode step
+through csa2_decode_step with the Reuse layers sharing their predecessor's
+index buffer).
+
+The oracle cannot run the whole step at this size in seconds, so the test
+checks sampled outputs one by one against the oracle and everything else by
+properties that hold at any size:
+  * bytes: the appended rows and sampled prefill rows equal the oracle's
+    quantisation of the same synthetic rows;
+  * scores: sampled blocks of the full scan and of every layer's pool
+    rescoring equal the oracle's pinned-order score of those blocks
+    (rows regenerated and quantised by the oracle);
+  * selection: the pool is the top 2,048 blocks of the exported scores
+    (every pool key beats every other key, ties to the lowest id), each
+    layer's top-256 is the top of its pool scores, Reuse layers repeat;
+  * attention: two layers' outputs against the oracle's float64 attention
+    over the selected positions (rows regenerated and quantised by the
+    oracle), within the 2e-3 normwise bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import fp4_compressed_sparse_amd as csa2
+import workloads as W
+from oracle.attend import gather_positions, sparse_attend
+from oracle.indexer import block_keys, block_scores_from_keys, collapse_query
+from oracle.quantize import quantize_rows
+from tests._gpu import ATT_TOL, log, normwise_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+BLOCK = 8
+
+
+_CHUNKS = {}
+
+
+def _chunks(wid, cache, chunk_ids):
+    """Synthetic prefill chunks of one cache (kept for reuse), drawn on a
+    thread pool: each chunk has its own seed."""
+    from concurrent.futures import ThreadPoolExecutor
+    need = [c for c in sorted(set(chunk_ids)) if (cache, c) not in _CHUNKS]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        for c, rows in zip(need, ex.map(lambda c: W._kv_chunk(wid, cache, 0, c), need)):
+            _CHUNKS[(cache, c)] = rows
+    return {c: _CHUNKS[(cache, c)] for c in chunk_ids}
+
+
+def _rows(wid, cache, positions, n_prefill, step_rows):
+    """Synthetic float32 rows at the given positions of one cache: prefill
+    rows from their chunks, position n_prefill is the step's appended row."""
+    positions = np.asarray(positions, dtype=np.int64)
+    out = np.empty((positions.size, 512), dtype=np.float32)
+    pre = positions[positions != n_prefill]
+    chunks = _chunks(wid, cache, (pre // W.CHUNK).tolist())
+    for i, p in enumerate(positions.tolist()):
+        out[i] = step_rows[cache] if p == n_prefill else chunks[p // W.CHUNK][p % W.CHUNK]
+    return out
+
+
+def _oracle_scores(wid, cache, blocks, n, n_prefill, step_rows, qbar):
+    """Oracle scores of the given blocks (each block's rows quantised by the
+    oracle, its key and pinned-order score computed on its own)."""
+    out = []
+    for beta in np.asarray(blocks).tolist():
+        cnt = min(BLOCK, n - BLOCK * beta)
+        pos = np.arange(BLOCK * beta, BLOCK * beta + cnt)
+        codes, scales = quantize_rows(_rows(wid, cache, pos, n_prefill, step_rows))
+        key = block_keys(codes, scales, cnt)
+        out.append(block_scores_from_keys(qbar, key)[0])
+    return np.asarray(out, dtype=np.float32)
+
+
+def _top_keys_ok(ids, scores, chosen):
+    """chosen (ascending ids) are exactly the top len(chosen) of (ids, scores)
+    by (score descending, id ascending)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    order = np.lexsort((ids, -scores.astype(np.float64)))
+    want = np.sort(ids[order[:len(chosen)]])
+    return np.array_equal(want, np.asarray(chosen, dtype=np.int64))
+
+
+def test_decoder20_1m_full_size_sampled():
+    require_gpu()
+    _CHUNKS.clear()
+    w = W.WORKLOADS[3]
+    n0 = int(w.context)
+    n = n0 + 1                                       # after this step's append
+    cap = (n + 7) // 8 * 8
+    rng = np.random.default_rng(20)
+    log(f"building 4 caches of {n0} positions")
+    caches = bench.build_caches(w, np.array([n0]), cap, log_every=1000)
+    for c in caches:
+        c.max_len = n
+    L, H, K, P = len(w.pattern), w.heads, w.topk, w.pool
+    lc = w.layer_caches()
+    qs = [W.queries(w.wid, l, 0, 1, H) for l in range(L)]
+    step_rows = np.stack([W.append_rows(w.wid, c, 0, 1) for c in range(w.n_caches)])   # [4, 1, 512]
+    qt = [torch.from_numpy(q).cuda() for q in qs]
+    outs = [torch.zeros((1, H, 512), dtype=torch.float32, device="cuda") for _ in range(L)]
+    idxs = []
+    for m in w.pattern:
+        idxs.append(idxs[-1] if m == 2 else torch.full((1, K), -9, dtype=torch.int32, device="cuda"))
+    pool = torch.full((1, P), -9, dtype=torch.int32, device="cuda")
+    ws = csa2.workspace(1, H, n, P, K)
+    layers = [(m, lc[l], qt[l], outs[l], idxs[l]) for l, m in enumerate(w.pattern)]
+    csa2.decode_step(caches, layers, H, K, P, w.scale, ws, pool_out=pool,
+                     new_rows=torch.from_numpy(step_rows).cuda())
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    log("decode step done")
+
+    # appended rows and sampled prefill rows: bytes equal the oracle's
+    for c, g in enumerate(caches):
+        assert int(g.seq_len[0]) == n
+        oc, osc = quantize_rows(step_rows[c])
+        assert np.array_equal(g.codes[0, n0].cpu().numpy(), oc[0])
+        assert np.array_equal(g.scales[0, n0].cpu().numpy(), osc[0])
+    samp = np.sort(rng.choice(np.arange(0, 2 * W.CHUNK), 48, replace=False))
+    oc, osc = quantize_rows(_rows(w.wid, 0, samp, n0, step_rows[:, 0]))
+    assert np.array_equal(caches[0].codes[0, samp].cpu().numpy(), oc)
+    assert np.array_equal(caches[0].scales[0, samp].cpu().numpy(), osc)
+    log("appended and sampled rows byte-equal")
+
+    nblk = (n + BLOCK - 1) // BLOCK
+    # full scan: exported scores, sampled against the oracle; pool by property
+    s0 = torch.zeros((1, nblk), dtype=torch.float32, device="cuda")
+    csa2.block_scores(caches[lc[0]], qt[0], s0)
+    s0 = s0.cpu().numpy()[0]
+    qbar0 = collapse_query(qs[0][0])
+    blocks = np.unique(np.concatenate([rng.choice(2 * W.CHUNK // BLOCK, 24, replace=False),
+                                       [0, nblk - 1]]))
+    want = _oracle_scores(w.wid, lc[0], blocks, n, n0, step_rows[:, 0], qbar0)
+    assert np.array_equal(s0[blocks].view(np.uint32), want.view(np.uint32))
+    p = pool.cpu().numpy()[0]
+    assert np.all(np.diff(p) > 0) and p[0] >= 0 and p[-1] < nblk
+    assert _top_keys_ok(np.arange(nblk), s0, p)
+    log(f"full scan: {blocks.size} sampled scores bit-exact, pool = top {P} of {nblk} blocks")
+
+    # every layer's selection: top-K of its pool scores (pool rescoring sampled)
+    pool_t = pool.clone()
+    prev = None
+    for l, m in enumerate(w.pattern):
+        got = idxs[l].cpu().numpy()[0]
+        if m == 2:
+            assert np.array_equal(got, prev), l
+            continue
+        sl = torch.zeros((1, P), dtype=torch.float32, device="cuda")
+        csa2.block_scores(caches[lc[l]], qt[l], sl, cand=pool_t)
+        sl = sl.cpu().numpy()[0]
+        assert _top_keys_ok(p, sl, got), l
+        if l > 0 and l % 5 == 0 or l == 1:
+            near = np.flatnonzero(p < 2 * W.CHUNK // BLOCK)      # pool blocks in the first two chunks
+            pick = rng.choice(near, min(6, near.size), replace=False)
+            want = _oracle_scores(w.wid, lc[l], p[pick], n, n0, step_rows[:, 0], collapse_query(qs[l][0]))
+            assert np.array_equal(sl[pick].view(np.uint32), want.view(np.uint32)), l
+        prev = got
+    log("every layer's selection is the top of its pool scores")
+
+    # attention of two layers against the oracle (float64)
+    for l in (0, L - 1):
+        idx = idxs[l].cpu().numpy()[0]
+        pos = gather_positions(idx, n)
+        codes, scales = quantize_rows(_rows(w.wid, lc[l], pos, n0, step_rows[:, 0]))
+        # compact cache: selected blocks in ascending order, the partial last
+        # block (if chosen) last, so the compact length masks it the same way
+        kept = idx[idx >= 0]
+        ccodes = np.zeros((BLOCK * kept.size, 256), dtype=np.uint8)
+        cscales = np.zeros((BLOCK * kept.size, 32), dtype=np.uint8)
+        ccodes[:pos.size] = codes
+        cscales[:pos.size] = scales
+        ref = sparse_attend(ccodes, cscales, pos.size, qs[l][0], np.arange(kept.size), w.scale)
+        err = normwise_err(outs[l].cpu().numpy()[0][None], ref[None])
+        log(f"layer {l}: attention error {err:.2e} over {pos.size} positions")
+        assert err <= ATT_TOL, (l, err)
+    _CHUNKS.clear()
