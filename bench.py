@@ -226,6 +226,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="workload id (default 3: 20 layers at 1M)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--mall-flush", action="store_true",
+                    help="read a 512 MB scratch buffer between steps (cold last-level cache, no "
+                         "dirty lines left to write back); step time from the events around each step")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -284,9 +287,13 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     hev = HipEvents()
     sev = [(hev.create(), hev.create()) for _ in range(K)]
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda") if args.mall_flush else None
+    flush_sink = torch.zeros((), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=flush_sink)   # evicts the caches from the 256 MB MALL
         csa2.set_scan_events(*sev[i])
         ev[i][0].record(stream)
         plans[WU + i].run(stream)
@@ -306,6 +313,9 @@ def main():
         hev.destroy(b)
 
     ms_per_step = elapsed * 1e3 / K
+    if flush is not None:                          # the flush writes are not part of a step
+        ms_per_step = float(np.median(step_ms))
+        elapsed = ms_per_step * 1e-3 * K
     n_mid = [int(n) + (WU + K // 2 + 1 if w.append else 0) for n in lengths]
     uniq, touched = step_bytes(w, n_mid)
     scan_bytes = sum(n * TOKEN_BYTES for n in n_mid)
@@ -340,6 +350,7 @@ def main():
             "effective_kv_frac_of_peak": round(eff_gbs / PEAK_HBM_GBS, 4),
             "unique_kv_bytes_per_step": uniq, "touched_kv_bytes_per_step": touched,
             "median_event_step_us": round(float(np.median(step_ms)) * 1e3, 2),
+            "mall_flush_between_steps": bool(args.mall_flush),
         },
         "roofline": {
             "bound": "hbm",
