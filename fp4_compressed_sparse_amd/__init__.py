@@ -6,8 +6,8 @@ and the stream.  There is no fallback: if the library is missing, importing
 the binding's entry points raises.
 
 Names follow the C ABI: fp4_quantize_kv, append_kv, index_topk,
-sparse_attend, decode_step, block_scores, device_error, workspace_bytes,
-workspace_init.
+sparse_attend, prefill_attend, decode_step, block_scores, device_error,
+workspace_bytes, workspace_init.
 """
 import ctypes
 import os
@@ -21,7 +21,8 @@ MAX_POOL, MAX_TOPK, MAX_CACHES = 8192, 2048, 16
 FLAG_NONFINITE_KV, FLAG_CAPACITY, FLAG_NONFINITE_Q, FLAG_BAD_INDEX = 1, 2, 4, 8
 
 EXPORTED = ("fp4_quantize_kv", "csa2_append_kv", "csa2_workspace_bytes", "csa2_workspace_init",
-            "csa2_index_topk", "csa2_sparse_attend", "csa2_decode_step", "csa2_block_scores",
+            "csa2_index_topk", "csa2_sparse_attend", "csa2_prefill_workspace_bytes",
+            "csa2_prefill_attend", "csa2_decode_step", "csa2_block_scores",
             "csa2_device_error", "csa2_set_scan_events", "csa2_status_string", "csa2_last_error")
 
 
@@ -69,6 +70,9 @@ def load():
         "csa2_workspace_init": (i32, [vp, sz, vp]),
         "csa2_index_topk": (i32, [i32, ctypes.POINTER(_Kv), vp, i32, vp, i32, i32, vp, i32, vp, vp, vp, sz, vp]),
         "csa2_sparse_attend": (i32, [ctypes.POINTER(_Kv), vp, i32, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
+        "csa2_prefill_workspace_bytes": (sz, [i32, i32, i32]),
+        "csa2_prefill_attend": (i32, [ctypes.POINTER(_Kv), i32, vp, i32, i32, vp, vp, i32, ctypes.c_float,
+                                      vp, vp, sz, vp]),
         "csa2_decode_step": (i32, [ctypes.POINTER(_Step), vp]),
         "csa2_block_scores": (i32, [ctypes.POINTER(_Kv), vp, i32, vp, i32, vp, vp]),
         "csa2_device_error": (i32, [ctypes.POINTER(ctypes.c_int32), vp]),
@@ -172,6 +176,25 @@ def sparse_attend(cache, q, idx, scale, out, ws, max_len=None, stream=None):
     kv = cache.view(max_len)
     _check(lib.csa2_sparse_attend(ctypes.byref(kv), _ptr(q), q.shape[1], _ptr(idx), idx.shape[1],
                                   float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def prefill_attend(cache, seq, q, qpos, idx, scale, out, ws=None, max_len=None, stream=None):
+    """n_q queries of sequence `seq`: q float32 [n_q, H, 512], qpos int64
+    [n_q], idx int32 [n_q, topk] -> out float32 [n_q, H, 512] (causal:
+    positions <= qpos).  ws: None or a tensor of prefill_workspace_bytes."""
+    lib = load()
+    kv = cache.view(max_len)
+    nbytes = ws.numel() if ws is not None else 0
+    _check(lib.csa2_prefill_attend(ctypes.byref(kv), int(seq), _ptr(q), q.shape[0], q.shape[1], _ptr(qpos),
+                                   _ptr(idx), idx.shape[1], float(scale), _ptr(out), _ptr(ws), nbytes,
+                                   _stream(stream)))
+
+
+def prefill_workspace(n_q, heads, topk, device="cuda"):
+    """Workspace tensor for prefill_attend (None when none is needed)."""
+    import torch
+    n = load().csa2_prefill_workspace_bytes(n_q, heads, topk)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
 def block_scores(cache, q, scores, cand=None, max_len=None, stream=None):

@@ -114,7 +114,8 @@ bool make_layout(int32_t batch, int32_t heads, int64_t max_len, int32_t pool, in
   if (heads == 16 || heads == 32 || heads == 64) {
     L->att_stages = (int32_t)ceil_div((int64_t)topk * BLOCK, ATT_SP);
     L->att_splits = att_splits(batch * (heads / 16), L->att_stages);
-    const size_t slots = (size_t)batch * L->att_splits * (heads / 16) * 16;
+    // one split: the attention kernel normalises its output itself
+    const size_t slots = L->att_splits > 1 ? (size_t)batch * L->att_splits * (heads / 16) * 16 : 0;
     L->part_o = off;  off = align256(off + sizeof(float) * slots * D);
     L->part_ml = off; off = align256(off + sizeof(float) * slots * 2);
   }
@@ -232,6 +233,7 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   aa.part_o = at<float>(ws, L.part_o); aa.part_ml = at<float>(ws, L.part_ml);
   aa.heads = heads;
   aa.cand = cand; aa.cand_scores = cand_scores; aa.n_cand = n_cand; aa.idx_out = idx_out;
+  aa.seq_stride = kv->capacity; aa.len_add = 0; aa.out = out;
   dim3 g(L.att_splits * (heads / 16), B);
   const size_t lds = (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16);
   if (idx)
@@ -239,6 +241,7 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   else
     attend_partial_kernel<true><<<g, ATT_THREADS, lds, s>>>(aa);
   if (csa2_status st = launched("attend")) return st;
+  if (L.att_splits == 1) return CSA2_OK;
   CombineArgs ca;
   ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = L.att_splits; ca.heads = heads; ca.out = out;
   attend_combine_kernel<<<dim3((heads / 16) * 32, B), 64, 0, s>>>(ca);
@@ -250,6 +253,22 @@ csa2_status check_select_args(int32_t topk, int32_t pool) {
   if (pool < 0 || pool > CSA2_MAX_POOL) return fail(CSA2_E_SHAPE, "pool %d outside [0, %d]", pool, CSA2_MAX_POOL);
   if (pool > 0 && pool < topk) return fail(CSA2_E_ARG, "pool %d < topk %d", pool, topk);
   return CSA2_OK;
+}
+
+// Attention-only layout of the prefill entry: partials only with more
+// than one split.
+bool prefill_layout(int32_t n_q, int32_t heads, int32_t topk, Layout *L) {
+  if (n_q < 1 || n_q > 65535 || topk < 1 || topk > CSA2_MAX_TOPK) return false;
+  if (heads != 16 && heads != 32 && heads != 64) return false;
+  memset(L, 0, sizeof *L);
+  L->att_stages = (int32_t)ceil_div((int64_t)topk * BLOCK, ATT_SP);
+  L->att_splits = att_splits(n_q * (heads / 16), L->att_stages);
+  const size_t slots = L->att_splits > 1 ? (size_t)n_q * L->att_splits * (heads / 16) * 16 : 0;
+  size_t off = 0;
+  L->part_o = off;  off = align256(off + sizeof(float) * slots * D);
+  L->part_ml = off; off = align256(off + sizeof(float) * slots * 2);
+  L->total = slots ? off : 0;
+  return true;
 }
 
 }  // namespace
@@ -386,6 +405,58 @@ csa2_status csa2_sparse_attend(const csa2_kv *kv, const float *q, int32_t heads,
   if (csa2_status st = check_ws(ws, ws_bytes, L)) return st;
   if (csa2_status st = device_ready()) return st;
   return run_attend(kv, q, heads, idx, topk, scale, out, ws, L, as_stream(stream));
+}
+
+size_t csa2_prefill_workspace_bytes(int32_t n_q, int32_t heads, int32_t topk) {
+  Layout L;
+  if (!prefill_layout(n_q, heads, topk, &L)) return 0;
+  return L.total;
+}
+
+csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, int32_t n_q,
+                                int32_t heads, const int64_t *qpos, const int32_t *idx,
+                                int32_t topk, float scale, float *out, void *ws,
+                                size_t ws_bytes, void *stream) {
+  t_last_error.clear();
+  if (csa2_status st = check_kv(kv)) return st;
+  if (seq < 0 || seq >= kv->batch) return fail(CSA2_E_ARG, "seq %d outside [0, %d)", seq, kv->batch);
+  if (!q || !aligned(q, 16) || !out || !aligned(out, 16))
+    return fail(CSA2_E_ARG, "q/out must be non-NULL and 16-byte aligned");
+  if (!qpos || !aligned(qpos, 8) || !idx || !aligned(idx, 4)) return fail(CSA2_E_ARG, "qpos/idx must be non-NULL");
+  if (heads != 16 && heads != 32 && heads != 64)
+    return fail(CSA2_E_SHAPE, "attention heads must be 16, 32 or 64 (got %d)", heads);
+  if (topk < 1 || topk > CSA2_MAX_TOPK) return fail(CSA2_E_SHAPE, "topk %d outside [1, %d]", topk, CSA2_MAX_TOPK);
+  if (n_q < 1 || n_q > 65535) return fail(CSA2_E_SHAPE, "n_q %d outside [1, 65535]", n_q);
+  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
+    return fail(CSA2_E_ARG, "scale must be finite");
+  Layout L;
+  if (!prefill_layout(n_q, heads, topk, &L)) return fail(CSA2_E_SHAPE, "bad sizes");
+  if (L.total) {
+    if (csa2_status st = check_ws(ws, ws_bytes, L)) return st;
+  }
+  if (csa2_status st = device_ready()) return st;
+  hipStream_t s = as_stream(stream);
+  AttendArgs aa;
+  memset(&aa, 0, sizeof aa);
+  aa.codes = kv->codes + (int64_t)seq * kv->capacity * CODE_BYTES;
+  aa.scales = kv->scales + (int64_t)seq * kv->capacity * SCALE_BYTES;
+  aa.seq_len = qpos; aa.len_add = 1; aa.seq_stride = 0;      // every row b is a query of one sequence
+  aa.capacity = kv->capacity; aa.limit = kv->max_len;
+  aa.q = q; aa.idx = idx; aa.topk = topk; aa.heads = heads;
+  aa.scale_log2 = scale * 1.4426950408889634f;
+  aa.n_stages = L.att_stages; aa.splits = L.att_splits;
+  aa.part_o = L.total ? at<float>(ws, L.part_o) : nullptr;
+  aa.part_ml = L.total ? at<float>(ws, L.part_ml) : nullptr;
+  aa.out = out;
+  dim3 g(L.att_splits * (heads / 16), n_q);
+  const size_t lds = (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16);
+  attend_partial_kernel<false><<<g, ATT_THREADS, lds, s>>>(aa);
+  if (csa2_status st = launched("prefill attend")) return st;
+  if (L.att_splits == 1) return CSA2_OK;
+  CombineArgs ca;
+  ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = L.att_splits; ca.heads = heads; ca.out = out;
+  attend_combine_kernel<<<dim3((heads / 16) * 32, n_q), 64, 0, s>>>(ca);
+  return launched("prefill combine");
 }
 
 csa2_status csa2_block_scores(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *cand,

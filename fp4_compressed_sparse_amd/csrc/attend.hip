@@ -58,6 +58,11 @@ struct AttendArgs {
   const float *cand_scores; // [batch][n_cand] their indexer scores
   int32_t n_cand;           // 1..SEL_CAND_MAX
   int32_t *idx_out;         // [batch][topk]
+  // batch row b of the cache is at codes + b * seq_stride rows (capacity for
+  // decode; 0 when every row b is a query of one sequence, prefill side)
+  int64_t seq_stride;
+  int32_t len_add;          // valid positions of row b: seq_len[b] + len_add
+  float *out;               // splits == 1: final output [batch][heads][512] written here
 };
 
 constexpr int SEL_CAND_MAX = 2048;  // candidates of the in-kernel top-k (8 per thread)
@@ -87,8 +92,8 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   // by the cache capacity, so they are issued without waiting for it.
   const int64_t cap_blocks = a.capacity / BLOCK;  // blocks a load may touch
   const int32_t *idx = a.idx + (int64_t)b * a.topk;
-  const uint8_t *codes = a.codes + (int64_t)b * a.capacity * CODE_BYTES;
-  const uint8_t *scales = a.scales + (int64_t)b * a.capacity * SCALE_BYTES;
+  const uint8_t *codes = a.codes + (int64_t)b * a.seq_stride * CODE_BYTES;
+  const uint8_t *scales = a.scales + (int64_t)b * a.seq_stride * SCALE_BYTES;
   const int total_pos = a.topk * BLOCK;
   const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
   const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
@@ -141,7 +146,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
       cid[k] = cb[j];
       csc[k] = sb[j];
     }
-    const int64_t nsel = clamp_len(a.seq_len[b], a.limit);
+    const int64_t nsel = clamp_len(a.seq_len[b] + a.len_add, a.limit);
     __builtin_amdgcn_sched_barrier(0);
     const int64_t nbs = (nsel + BLOCK - 1) / BLOCK;
     uint64_t *s_keys = reinterpret_cast<uint64_t *>(s_v);     // for the radix fallback only
@@ -188,7 +193,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     for (int kc = 0; kc < 16; ++kc) qop[kc] = *reinterpret_cast<const f16x8 *>(qrow + 32 * kc);
   }
 
-  const int64_t n = clamp_len(a.seq_len[b], a.limit);
+  const int64_t n = clamp_len(a.seq_len[b] + a.len_add, a.limit);
   const int64_t nblk = (n + BLOCK - 1) / BLOCK;
   CSA2_TS(1);
   f32x4 acc[8];                           // O^T tiles 8*wv .. 8*wv+7
@@ -312,6 +317,20 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   }
 
   CSA2_TS(4);
+  if (a.splits == 1) {
+    // one workgroup holds the whole softmax of its heads: normalise here.
+    // lane (n16, g) of tile ct holds channels 128*(ct/8) + 4*(ct%8) + 32*g + 0..3
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float *orow = a.out + ((int64_t)b * a.heads + 16 * ht + n16) * D + 32 * g;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int ct = 8 * wv + t;
+      *reinterpret_cast<float4 *>(orow + 128 * (ct >> 3) + 4 * (ct & 7)) =
+          float4{acc[t][0] * inv, acc[t][1] * inv, acc[t][2] * inv, acc[t][3] * inv};
+    }
+    CSA2_TS(5);
+    return;
+  }
   // ---- partial of this (sequence, split, head tile) ----
   const int64_t slot = ((int64_t)b * a.splits + split) * HT + ht;
   f32x4 *po = reinterpret_cast<f32x4 *>(a.part_o + slot * (16 * D)) + lane;

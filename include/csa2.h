@@ -191,11 +191,41 @@ csa2_status csa2_index_topk(int32_t mode, const csa2_kv *kv, const float *q, int
  * idx   device int32 [batch][topk], topk 1..CSA2_MAX_TOPK.
  * out   device float32 [batch][heads][512].
  * Accumulates in float32 with fp16 matrix-core operands (the dequantised
- * values are exact in fp16; q enters as an fp16 high+low pair).
+ * values are exact in fp16; q is rounded to fp16).
  */
 csa2_status csa2_sparse_attend(const csa2_kv *kv, const float *q, int32_t heads,
                                const int32_t *idx, int32_t topk, float scale,
                                float *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * csa2_prefill_workspace_bytes — workspace needed by csa2_prefill_attend
+ * (0 when every query's heads fit one workgroup per head tile: no partials).
+ * Returns 0 as well for unsupported sizes; csa2_prefill_attend reports why.
+ */
+size_t csa2_prefill_workspace_bytes(int32_t n_q, int32_t heads, int32_t topk);
+
+/*
+ * csa2_prefill_attend — batched prefill-side sparse attention: n_q queries
+ * of sequence `seq`, query t at cache position qpos[t] with its own block
+ * selection idx[t], each attending causally to the selected positions
+ * p <= qpos[t] (its own position included).  The pages put the cost of long
+ * inputs in the prefill [P2 introduction]; the per-query arithmetic is the
+ * decode attention's (csa2_sparse_attend).
+ * kv    cache view; seq in [0, batch): the sequence whose rows are read.
+ *       Positions are also clamped below kv->max_len.
+ * q     device float32 [n_q][heads][512], 16-byte aligned; heads 16/32/64.
+ * qpos  device int64 [n_q]: cache position of each query.
+ * idx   device int32 [n_q][topk], topk 1..CSA2_MAX_TOPK; -1 = none.  A block
+ *       wholly after its query's position flags CSA2_FLAG_BAD_INDEX.
+ * out   device float32 [n_q][heads][512].
+ * ws    csa2_prefill_workspace_bytes(n_q, heads, topk) bytes, 256-byte
+ *       aligned (may be NULL when that is 0).
+ * n_q   1..65535.
+ */
+csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, int32_t n_q,
+                                int32_t heads, const int64_t *qpos, const int32_t *idx,
+                                int32_t topk, float scale, float *out, void *ws,
+                                size_t ws_bytes, void *stream);
 
 /* One layer of a decode step. */
 typedef struct {

@@ -115,3 +115,25 @@ def test_decode_step_pattern_errors(lib):
     assert step([(0, 0), (0, 1), (1, 0)]) == 1  # Reindex must use the latest Full cache
     assert step([(0, 0)], heads=48) == 2
     assert step([(0, 0)], pool=64) == 1         # pool > 0 without pool_out
+
+
+def test_prefill_attend_argument_errors(lib):
+    q, qpos, idx, out = (ctypes.c_void_p(a) for a in (0x50000, 0x58000, 0x40000, 0x70000))
+    # the workspace holds partials only when one split per head tile is not enough
+    assert lib.csa2_prefill_workspace_bytes(1024, 64, 256) == 0
+    assert lib.csa2_prefill_workspace_bytes(4, 16, 256) > 0
+    assert lib.csa2_prefill_workspace_bytes(0, 16, 64) == 0
+    assert lib.csa2_prefill_workspace_bytes(4, 24, 64) == 0
+    call = lambda seq=0, n_q=8, heads=16, topk=64, scale=0.04, qp=qpos, kv=None: lib.csa2_prefill_attend(
+        ctypes.byref(kv or _kv()), seq, q, n_q, heads, qp, idx, topk, ctypes.c_float(scale), out, None, 0, None)
+    assert call(seq=1) == 1                                      # sequence outside the batch
+    assert call(seq=-1) == 1
+    assert call(heads=24) == 2
+    assert call(topk=0) == 2
+    assert call(n_q=0) == 2
+    assert call(n_q=70000) == 2
+    assert call(scale=float("inf")) == 1
+    assert call(qp=None) == 1
+    assert call(n_q=4) == 1                                      # partials needed, workspace NULL
+    assert "workspace" in _err(lib)
+    assert call(kv=_kv(capacity=4092)) == 2

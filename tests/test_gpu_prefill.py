@@ -1,0 +1,67 @@
+"""GPU batched prefill-side sparse attention (csa2_prefill_attend) against
+the oracle (oracle.prefill): every output within 2e-3 (normwise per head).
+Cache bytes come from the oracle's quantiser; each query's selection is a
+seeded random choice of blocks at or before its own block (its own,
+possibly partial, block always included), -1 padded."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_compressed_sparse_amd as csa2
+import workloads as W
+from oracle.prefill import prefill_attend
+from tests._gpu import ATT_TOL, cap_for, log, normwise_err, oracle_cache, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _selection(rng, qpos, topk):
+    idx = np.full((len(qpos), topk), -1, dtype=np.int32)
+    for t, p in enumerate(qpos):
+        own = int(p) // 8
+        avail = np.arange(own)
+        k = min(topk - 1, avail.size)
+        pick = rng.choice(avail, k, replace=False) if k else np.zeros(0, dtype=np.int64)
+        sel = np.sort(np.concatenate([pick, [own]]))
+        idx[t, :sel.size] = sel
+    return idx
+
+
+def _run(n, qpos, heads, topk, seed):
+    require_gpu()
+    rng = np.random.default_rng(seed)
+    oc = oracle_cache(2, 0, [n], cap_for(n))
+    g = to_device(oc)
+    qpos = np.asarray(qpos, dtype=np.int64)
+    T = qpos.size
+    q = W.queries(2, 7, seed, T, heads)
+    idx = _selection(rng, qpos, topk)
+    scale = 1 / np.sqrt(512)
+    out = torch.full((T, heads, 512), float("nan"), dtype=torch.float32, device="cuda")
+    ws = csa2.prefill_workspace(T, heads, topk)
+    csa2.prefill_attend(g, 0, torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
+                        torch.from_numpy(idx).cuda(), scale, out, ws)
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    ref = prefill_attend(oc.codes[0], oc.scales[0], qpos, q, idx, scale)
+    err = normwise_err(out.cpu().numpy(), ref)
+    log(f"prefill T={T} H={heads} K={topk} (workspace {0 if ws is None else ws.numel()} B): error {err:.2e}")
+    assert err <= ATT_TOL
+
+
+def test_prefill_chunk_few_queries_split_k():
+    # 5 queries x 4 head tiles: the selection is split over workgroups and merged
+    n = 9000
+    _run(n, [n - 5, n - 4, n - 3, n - 2, n - 1], 64, 256, 1)
+
+
+def test_prefill_chunk_many_queries_one_split():
+    # 300 queries x 4 head tiles: one workgroup per (query, head tile), no merge
+    n = 12000
+    _run(n, np.arange(n - 300, n), 64, 256, 2)
+
+
+def test_prefill_ragged_positions_16_heads():
+    # early queries with fewer blocks than topk (-1 padding), partial own blocks
+    qpos = [0, 1, 7, 8, 63, 64, 200, 511, 1000, 4093, 4094, 4095]
+    _run(4096, qpos, 16, 64, 3)
