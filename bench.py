@@ -218,6 +218,102 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
 
 
+def prefill_bench(args):
+    """Batched prefill-side sparse attention (csa2_prefill_attend): T queries
+    at the last T positions of one 1,048,576-position cache, each with its
+    own seeded selection of 256 blocks at or before its own block."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import fp4_compressed_sparse_amd as csa2
+    import workloads as W
+
+    csa2.load()
+    torch.cuda.set_device(0)
+    w = dataclasses.replace(W.WORKLOADS[3], pattern=(0,))          # one cache
+    n = int(w.context)
+    T, H, K = args.prefill, w.heads, w.topk
+    t0 = time.perf_counter()
+    cache = build_caches(w, np.array([n]), (n + 7) // 8 * 8)[0]
+    cache.max_len = n
+    log(f"cache built in {time.perf_counter() - t0:.1f} s")
+    rng = np.random.default_rng(4096)
+    qpos = np.arange(n - T, n, dtype=np.int64)
+    idx = np.full((T, K), -1, dtype=np.int32)
+    for t, p in enumerate(qpos.tolist()):
+        own = p // 8
+        sel = np.sort(np.concatenate([rng.choice(own, K - 1, replace=False), [own]]))
+        idx[t] = sel
+    positions = int(sum(min(8, int(p) + 1 - 8 * int(b)) for t, p in enumerate(qpos.tolist())
+                        for b in idx[t].tolist()))
+    q = torch.from_numpy(W.queries(w.wid, 100, 0, T, H)).cuda()
+    qp, it = torch.from_numpy(qpos).cuda(), torch.from_numpy(idx).cuda()
+    out = torch.empty((T, H, 512), dtype=torch.float32, device="cuda")
+    ws = csa2.prefill_workspace(T, H, K)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        csa2.prefill_attend(cache, 0, q, qp, it, w.scale, out, ws)
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    reps = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    t_start = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        csa2.prefill_attend(cache, 0, q, qp, it, w.scale, out, ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    launch_s = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    flops = 4.0 * H * 512 * positions
+    tflops = flops / launch_s / 1e12
+    gather = positions * TOKEN_BYTES
+    log(f"prefill: {T} queries, {positions} attended positions: {launch_s * 1e6:.1f} us per launch, "
+        f"{tflops:.1f} TFLOP/s, gathered rows {gather / launch_s / 1e9:.0f} GB/s")
+    result = {
+        "metric": "prefill-side sparse attention queries/s (1M ctx, 64 heads, top-256 blocks per query, 1 GPU)",
+        "value": round(T * reps / elapsed, 1),
+        "unit": "queries/s",
+        "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / reps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 MFMA operands, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": "prefill-attend-1m", "queries": T, "context": n, "heads": H,
+                   "topk_blocks": K, "attended_positions": positions,
+                   "median_event_launch_us": round(launch_s * 1e6, 2)},
+        "roofline": {"bound": "mfma", "kernel": "attend_partial_kernel (one split per query and head tile)",
+                     "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "gathered_bytes_per_launch": gather},
+    }
+    if not args.no_cpu_baseline:
+        from oracle.prefill import prefill_attend
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:                           # pragma: no cover
+            threadpool_limits = None
+        import contextlib
+        S = 16
+        rows = W.kv_rows_threaded(w.wid, 0, 0, n)      # the oracle's own copy of the cache
+        from oracle.quantize import quantize_rows
+        need = np.unique(np.concatenate([8 * idx[t][:, None] + np.arange(8)[None, :] for t in range(S)]).ravel())
+        need = need[need < n]
+        codes = np.zeros((n, 256), dtype=np.uint8)
+        scales = np.zeros((n, 32), dtype=np.uint8)
+        codes[need], scales[need] = quantize_rows(rows[need])
+        ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+        with ctx:
+            t1 = time.perf_counter()
+            prefill_attend(codes, scales, qpos[:S], W.queries(w.wid, 100, 0, T, H)[:S], idx[:S], w.scale)
+            cpu_s = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": round(S / cpu_s, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"{S} of the {T} queries (same cache, selections and heads) on 1 host "
+                                            f"thread: {cpu_s:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +322,10 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="workload id (default 3: 20 layers at 1M)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--prefill", type=int, default=0, metavar="T",
+                    help="instead of the decode step: batched prefill-side sparse attention of T "
+                         "queries (the last T positions of a 1M-position cache, 64 heads, top-256 "
+                         "blocks each); prints its own JSON line")
     ap.add_argument("--mall-flush", action="store_true",
                     help="read a 512 MB scratch buffer between steps (cold last-level cache, no "
                          "dirty lines left to write back); step time from the events around each step")
@@ -237,6 +337,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.prefill:
+        prefill_bench(args)
         return
 
     import numpy as np
