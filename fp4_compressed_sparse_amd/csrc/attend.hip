@@ -105,16 +105,18 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   bool okv[PASSES];
   u32x4 wr[PASSES];
   uint32_t scr[PASSES];
-  auto fetch_ids = [&](int st) {
+  auto fetch_ids_into = [&](int st, int32_t (&dst)[PASSES]) {
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
       const int j = st * ATT_SP + (tid >> 4) + 16 * k;
       if (SELECT)
-        blkv[k] = s_sel[min(j, total_pos - 1) >> 3];
+        dst[k] = s_sel[min(j, total_pos - 1) >> 3];
       else
-        blkv[k] = idx[min(j, total_pos - 1) >> 3];   // unconditional: one batch
+        dst[k] = idx[min(j, total_pos - 1) >> 3];    // unconditional: one batch
     }
   };
+  auto fetch_ids = [&](int st) { fetch_ids_into(st, blkv); };
+  int32_t nxt[PASSES];                    // block ids of the stage after the one in flight
   auto fetch_rows = [&](int st) {
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
@@ -180,6 +182,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     for (int u = 0; u < NV; ++u) v[u] = src[tid + u * ATT_THREADS];
     __builtin_amdgcn_sched_barrier(0);    // query loads go out before the ids are awaited
     fetch_rows(st0);
+    if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int e = tid + u * ATT_THREADS;                    // head e/128, channels 4*(e%128)
@@ -212,7 +215,6 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
 #pragma unroll 1
   for (int st = st0; st < st1; ++st) {
     __syncthreads();                      // q / previous stage fully consumed
-    if (st != st0) { fetch_ids(st); fetch_rows(st); }
     // ---- dequantise the stage's rows into LDS as fp16 (16 threads per row) ----
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
@@ -237,6 +239,14 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
                         __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
       }
       if (i16 == 0) s_ok[pp] = okv[k] ? 1 : 0;
+    }
+    // the next stage's rows (and the ids of the one after) are requested now,
+    // so they arrive while this stage is computed
+    if (st + 1 < st1) {
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) blkv[k] = nxt[k];
+      fetch_rows(st + 1);
+      if (st + 2 < st1) fetch_ids_into(st + 2, nxt);
     }
     __syncthreads();
 
