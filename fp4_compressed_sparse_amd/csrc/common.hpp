@@ -37,19 +37,15 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Per-row control words of a workspace (1 KB per sequence).
+// Per-sequence control words of a workspace (1 KB of arrival/tie counters,
+// then 8 KB of full-scan work counters).
 constexpr int SCAN_GROUPS = 64;         // full-scan workgroup groups sharing a work counter
 
 struct Ctrl {
-  uint32_t scan_grp[MAX_GRID_X / 32];   // scan arrivals per group of 32 workgroups
-  uint32_t scan_top;                    // groups of the scan complete
-  uint32_t sel_grp[MAX_GRID_X / 32];    // select / rescore arrivals
-  uint32_t sel_top;
+  uint32_t sel_grp[MAX_GRID_X / 32];    // select / rescore arrivals per group of 32 workgroups
+  uint32_t sel_top;                     // groups complete
   uint32_t ncand[CAND_COPIES];          // tie candidates collected per list
-  uint32_t thr_digit;                   // top-10-bit digit holding the R-th largest key
-  uint32_t need;                        // keys still to take from that digit
-  uint32_t all;                         // 1: every block is selected (nblk <= R)
-  uint32_t pad[256 - 2 * (MAX_GRID_X / 32) - 2 - CAND_COPIES - 3];
+  uint32_t pad[256 - (MAX_GRID_X / 32) - 1 - CAND_COPIES];
   uint32_t work[SCAN_GROUPS * 32];      // full-scan work counters, one per 128-byte line
 };
 
@@ -125,8 +121,9 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v) {
 // arrival on one counter costs about 75 ns per workgroup, serialised (77 us
 // for 1024 workgroups, measured), and same-address atomics serialise at
 // about 12 ns each.  So: every value the last workgroup reads is written
-// with a device-scope atomic (performed at the device coherence point, not
-// in an XCD's L2); each wave waits for all of its memory operations to
+// with a device-scope store or atomic (st_agent, atomic_add_agent: written
+// through to the device coherence point, not left in an XCD's L2); each
+// wave waits for all of its memory operations to
 // complete (s_waitcnt 0) before the workgroup barrier; the arrival counts on
 // two levels (groups of 32 workgroups, then groups), so no address sees more
 // than 64 contending atomics; the last workgroup reads with device-scope

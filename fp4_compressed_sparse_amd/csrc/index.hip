@@ -20,19 +20,22 @@
 // The row sum uses FMA: each dequantised value code*scale is exact in
 // float32, so fma(code, scale, acc) == fl(acc + code*scale).
 //
-// Work layout of the scan: 16 lanes per block, lane i owns channels
-// 32i..32i+31 (16 code bytes and 2 scale bytes of each of the 8 rows), so
-// every load instruction of a wave covers 4 blocks x 8 rows of 256-byte
-// contiguous runs; the two 16-channel groups of a lane are summed in-lane
-// and the tree's levels 2..5 are lane butterflies (xor 1, 2, 4, 8).
+// Work layout: the full scan gives each block 32 lanes (lane j owns scale
+// group j: 8 code bytes and 1 scale byte of each of the 8 rows; the five
+// tree levels are lane butterflies xor 1..16); the pool rescoring gives
+// each block 16 lanes (lane i owns channels 32i..32i+31, the two groups of a
+// lane summed in-lane, levels 2..5 as butterflies xor 1..8).  Same
+// arithmetic, same order.
 //
 // Selection: keys are (order-preserving score bits << 32) | ~block_id, so
-// all keys differ and ties go to the lowest id.  The scan adds the top 12
-// key bits of every block to a histogram; the last scan workgroup finds the
-// digit that holds the R-th largest key.  The select kernel marks every
-// block above that digit in a bitmap and collects the digit's blocks; its
-// last workgroup finishes the choice among them with an LDS radix select,
-// then writes the chosen ids in ascending order by compacting the bitmap.
+// all keys differ and ties go to the lowest id.  The scan adds the top 10
+// key bits of every block to a histogram (8 copies); every select
+// workgroup finds the digit that holds the R-th largest key from it, marks
+// every block above that digit in a bitmap and collects the digit's blocks;
+// the last select workgroup finishes the choice among them in LDS, then
+// writes the chosen ids in ascending order by compacting the bitmap.
+// A block top-k inside LDS (a candidate list) uses linear bins over the
+// score range with an exact pairwise finish (topk_threshold).
 #include "common.hpp"
 
 namespace csa2 {
