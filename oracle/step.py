@@ -21,11 +21,15 @@ Readings (the pages leave these open):
     its pool.  With pool size 0 every selecting layer scans all blocks.
   * Step order: each Full cache first appends this step's new row for every
     sequence (quantised like every other row), then the layers run in order.
+  * Optional local branch (oracle/swa.py): a layer with an SWA cache writes
+    its own FP8 row for the new token and attends to its window together
+    with its CSA2 positions in one softmax.
 """
 import numpy as np
 
 from . import attend as _attend
 from . import indexer as _indexer
+from . import swa as _swa
 from .quantize import BYTES_PER_TOKEN, CODE_BYTES, D, SCALE_BYTES, quantize_rows
 from .select import select
 
@@ -67,12 +71,15 @@ class Cache:
             self.seq_len[b] += 1
 
 
-def decode_step(caches, layers, new_rows, topk, pool, scale):
+def decode_step(caches, layers, new_rows, topk, pool, scale, swa=None, swa_rows=None, window=0):
     """Run one decode step.
 
     caches:   list of Cache (one per Full layer); mutated by the append.
     layers:   list of (mode, cache_index, q float32 [B, H, 512]).
     new_rows: float32 [n_caches, B, 512] appended first, or None.
+    swa:      None, or one swa.SwaCache (or None) per layer: the layer's local
+              branch, window positions wide; swa_rows float32 [n_layers, B, 512]
+              (rows of layers without a cache are ignored) are appended first.
     Returns dict with 'idx' (list of int32 [B, topk]), 'out' (list of float64
     [B, H, 512]) and 'pool' (int32 [B, pool] or None).
     """
@@ -115,10 +122,19 @@ def decode_step(caches, layers, new_rows, topk, pool, scale):
                     keep = np.isin(ids, pool_ids[b])
                     ids, sc = ids[keep], sc[keep]
                 idx[b] = select(ids, sc, topk)
-        out = np.stack([
-            _attend.sparse_attend(cache.codes[b], cache.scales[b], int(cache.seq_len[b]),
-                                  q[b], idx[b], scale)
-            for b in range(B)])
+        sw = swa[li] if swa is not None else None
+        if sw is not None:
+            sw.append(swa_rows[li])
+            out = np.stack([
+                _swa.attend_with_window(cache.codes[b], cache.scales[b], int(cache.seq_len[b]),
+                                        q[b], idx[b], scale, sw.codes[b], sw.scales[b],
+                                        int(sw.seq_len[b]), window)
+                for b in range(B)])
+        else:
+            out = np.stack([
+                _attend.sparse_attend(cache.codes[b], cache.scales[b], int(cache.seq_len[b]),
+                                      q[b], idx[b], scale)
+                for b in range(B)])
         idx_all.append(idx)
         out_all.append(out)
         prev_idx = idx
