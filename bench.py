@@ -326,6 +326,10 @@ def main():
                     help="instead of the decode step: batched prefill-side sparse attention of T "
                          "queries (the last T positions of a 1M-position cache, 64 heads, top-256 "
                          "blocks each); prints its own JSON line")
+    ap.add_argument("--swa", type=int, default=0, metavar="W",
+                    help="give every layer a local branch: an FP8 sliding-window ring of W positions "
+                         "(prefilled, one row appended per layer per step) attended in the same "
+                         "softmax; reported as its own configuration")
     ap.add_argument("--mall-flush", action="store_true",
                     help="read a 512 MB scratch buffer between steps (cold last-level cache, no "
                          "dirty lines left to write back); step time from the events around each step")
@@ -377,7 +381,22 @@ def main():
         idxs.append(idxs[-1] if m == 2 else torch.zeros((B, w.topk), dtype=torch.int32, device="cuda"))
     pool_out = torch.zeros((B, w.pool), dtype=torch.int32, device="cuda") if w.pool else None
     ws = csa2.workspace(B, H, max_len, w.pool, w.topk)
-    plans = [csa2.StepPlan(caches, [(m, lc[l], q_all[s][l], outs[l], idxs[l]) for l, m in enumerate(w.pattern)],
+    rings, srows_all = [None] * L, [[None] * L for _ in range(total_steps)]
+    if args.swa:
+        # every layer's ring holds the last W positions of each sequence
+        for l in range(L):
+            rings[l] = csa2.SwaCache(B, args.swa)
+            for b in range(B):
+                n = int(lengths[b])
+                lo = max(0, n - args.swa)
+                x = torch.from_numpy(W.swa_rows(w.wid, l, b, lo, n - lo)).cuda()
+                dst = torch.arange(lo, n, dtype=torch.int64, device="cuda") % args.swa + b * args.swa
+                csa2.fp8_quantize_kv(x, rings[l].codes, rings[l].scales, dst_row=dst)
+            rings[l].seq_len.copy_(torch.from_numpy(lengths.astype(np.int64)))
+        srows_all = [[torch.from_numpy(W.swa_append_rows(w.wid, l, s, B)).cuda() for l in range(L)]
+                     for s in range(total_steps)]
+    plans = [csa2.StepPlan(caches, [(m, lc[l], q_all[s][l], outs[l], idxs[l], rings[l], srows_all[s][l])
+                                    for l, m in enumerate(w.pattern)],
                            H, w.topk, w.pool, w.scale, ws, pool_out=pool_out, new_rows=rows_all[s])
              for s in range(total_steps)]
     stream = torch.cuda.current_stream()
@@ -421,6 +440,9 @@ def main():
         elapsed = ms_per_step * 1e-3 * K
     n_mid = [int(n) + (WU + K // 2 + 1 if w.append else 0) for n in lengths]
     uniq, touched = step_bytes(w, n_mid)
+    if args.swa:                                   # every layer reads its own window (512 + 4 B per position)
+        win_bytes = L * sum(min(args.swa, n) * 516 for n in n_mid)
+        uniq, touched = uniq + win_bytes, touched + win_bytes
     scan_bytes = sum(n * TOKEN_BYTES for n in n_mid)
     scan_avg_s = float(np.mean(scan_ms)) * 1e-3
     achieved = scan_bytes / scan_avg_s / 1e9
@@ -454,6 +476,7 @@ def main():
             "unique_kv_bytes_per_step": uniq, "touched_kv_bytes_per_step": touched,
             "median_event_step_us": round(float(np.median(step_ms)) * 1e3, 2),
             "mall_flush_between_steps": bool(args.mall_flush),
+            "swa_window": args.swa,
         },
         "roofline": {
             "bound": "hbm",

@@ -5,9 +5,9 @@ behind the C ABI declared in include/csa2.h.  PyTorch supplies device memory
 and the stream.  There is no fallback: if the library is missing, importing
 the binding's entry points raises.
 
-Names follow the C ABI: fp4_quantize_kv, append_kv, index_topk,
-sparse_attend, prefill_attend, decode_step, block_scores, device_error,
-workspace_bytes, workspace_init.
+Names follow the C ABI: fp4_quantize_kv, append_kv, fp8_quantize_kv,
+swa_append, index_topk, sparse_attend, prefill_attend, decode_step,
+block_scores, device_error, workspace_bytes, workspace_init.
 """
 import ctypes
 import os
@@ -18,9 +18,11 @@ LIB_PATH = os.path.join(HERE, "libcsa2.so")
 FULL, REINDEX, REUSE = 0, 1, 2
 D, BLOCK, CODE_BYTES, SCALE_BYTES = 512, 8, 256, 32
 MAX_POOL, MAX_TOPK, MAX_CACHES = 8192, 2048, 16
-FLAG_NONFINITE_KV, FLAG_CAPACITY, FLAG_NONFINITE_Q, FLAG_BAD_INDEX = 1, 2, 4, 8
+FLAG_NONFINITE_KV, FLAG_CAPACITY, FLAG_NONFINITE_Q, FLAG_BAD_INDEX, FLAG_SWA_RANGE = 1, 2, 4, 8, 16
+MAX_WINDOW, MAX_SWA_LAYERS = 1024, 64
 
-EXPORTED = ("fp4_quantize_kv", "csa2_append_kv", "csa2_workspace_bytes", "csa2_workspace_init",
+EXPORTED = ("fp4_quantize_kv", "csa2_append_kv", "fp8_quantize_kv", "csa2_swa_append",
+            "csa2_workspace_bytes", "csa2_workspace_init",
             "csa2_index_topk", "csa2_sparse_attend", "csa2_prefill_workspace_bytes",
             "csa2_prefill_attend", "csa2_decode_step", "csa2_block_scores",
             "csa2_device_error", "csa2_set_scan_events", "csa2_status_string", "csa2_last_error")
@@ -37,9 +39,15 @@ class _Kv(ctypes.Structure):
                 ("capacity", ctypes.c_int64), ("max_len", ctypes.c_int64), ("batch", ctypes.c_int32)]
 
 
+class _Swa(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
+                ("window", ctypes.c_int32), ("batch", ctypes.c_int32)]
+
+
 class _Layer(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("cache", ctypes.c_int32), ("q", ctypes.c_void_p),
-                ("out", ctypes.c_void_p), ("idx", ctypes.c_void_p)]
+                ("out", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("swa", ctypes.POINTER(_Swa)),
+                ("swa_row", ctypes.c_void_p)]
 
 
 class _Step(ctypes.Structure):
@@ -66,10 +74,13 @@ def load():
     sig = {
         "fp4_quantize_kv": (i32, [vp, i64, vp, i64, vp, vp, vp]),
         "csa2_append_kv": (i32, [ctypes.POINTER(_Kv), vp, vp]),
+        "fp8_quantize_kv": (i32, [vp, i64, vp, i64, vp, vp, vp]),
+        "csa2_swa_append": (i32, [ctypes.POINTER(_Swa), vp, vp]),
         "csa2_workspace_bytes": (sz, [i32, i32, i64, i32, i32]),
         "csa2_workspace_init": (i32, [vp, sz, vp]),
         "csa2_index_topk": (i32, [i32, ctypes.POINTER(_Kv), vp, i32, vp, i32, i32, vp, i32, vp, vp, vp, sz, vp]),
-        "csa2_sparse_attend": (i32, [ctypes.POINTER(_Kv), vp, i32, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
+        "csa2_sparse_attend": (i32, [ctypes.POINTER(_Kv), vp, i32, vp, i32, ctypes.c_float,
+                                     ctypes.POINTER(_Swa), vp, vp, sz, vp]),
         "csa2_prefill_workspace_bytes": (sz, [i32, i32, i32]),
         "csa2_prefill_attend": (i32, [ctypes.POINTER(_Kv), i32, vp, i32, i32, vp, vp, i32, ctypes.c_float,
                                       vp, vp, sz, vp]),
@@ -142,6 +153,43 @@ def append_kv(cache: KVCache, x, stream=None):
     _check(lib.csa2_append_kv(ctypes.byref(kv), _ptr(x), _stream(stream)))
 
 
+class SwaCache:
+    """One layer's FP8 sliding-window ring: torch uint8 codes [B][window][512],
+    float32 scales [B][window] and int64 seq_len [B] (positions written) on
+    the GPU; position p lives in slot p % window."""
+
+    def __init__(self, batch, window, device="cuda"):
+        import torch
+        if not 1 <= window <= MAX_WINDOW:
+            raise ValueError(f"window must be in [1, {MAX_WINDOW}]")
+        self.codes = torch.zeros((batch, window, D), dtype=torch.uint8, device=device)
+        self.scales = torch.zeros((batch, window), dtype=torch.float32, device=device)
+        self.seq_len = torch.zeros(batch, dtype=torch.int64, device=device)
+        self.batch, self.window = batch, window
+
+    def view(self):
+        return _Swa(self.codes.data_ptr(), self.scales.data_ptr(), self.seq_len.data_ptr(),
+                    self.window, self.batch)
+
+
+def fp8_quantize_kv(x, codes, scales, dst_row=None, stream=None):
+    """x float32 [rows, 512] -> codes [*, 512] uint8 / scales [*] float32 rows
+    dst_row (or 0..rows-1)."""
+    lib = load()
+    rows = x.shape[0]
+    dst_rows = codes.numel() // D
+    if scales.numel() != dst_rows:
+        raise ValueError("codes and scales hold different row counts")
+    _check(lib.fp8_quantize_kv(_ptr(x), rows, _ptr(dst_row), dst_rows, _ptr(codes), _ptr(scales),
+                               _stream(stream)))
+
+
+def swa_append(swa: SwaCache, x, stream=None):
+    """Append x float32 [B, 512] at each sequence's seq_len (slot seq_len % window)."""
+    v = swa.view()
+    _check(load().csa2_swa_append(ctypes.byref(v), _ptr(x), _stream(stream)))
+
+
 def workspace_bytes(batch, heads, max_len, pool, topk):
     n = load().csa2_workspace_bytes(batch, heads, max_len, pool, topk)
     if n == 0:
@@ -171,11 +219,13 @@ def index_topk(mode, cache, q, topk, idx_out, ws, cand=None, pool=0, pool_out=No
                                ws.numel() if ws is not None else 0, _stream(stream)))
 
 
-def sparse_attend(cache, q, idx, scale, out, ws, max_len=None, stream=None):
+def sparse_attend(cache, q, idx, scale, out, ws, max_len=None, stream=None, swa=None):
+    """swa: None or the layer's SwaCache (its window joins the softmax)."""
     lib = load()
     kv = cache.view(max_len)
+    sv = ctypes.byref(swa.view()) if swa is not None else None
     _check(lib.csa2_sparse_attend(ctypes.byref(kv), _ptr(q), q.shape[1], _ptr(idx), idx.shape[1],
-                                  float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+                                  float(scale), sv, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def prefill_attend(cache, seq, q, qpos, idx, scale, out, ws=None, max_len=None, stream=None):
@@ -208,13 +258,21 @@ def block_scores(cache, q, scores, cand=None, max_len=None, stream=None):
 class StepPlan:
     """A decode step's C structures, built once and reusable (e.g. for
     repeated launches or graph capture).  layers: list of (mode, cache, q,
-    out, idx) with torch tensors."""
+    out, idx) or (mode, cache, q, out, idx, swa, swa_row) with torch tensors
+    (swa: the layer's SwaCache or None; swa_row float32 [B, 512] or None)."""
 
     def __init__(self, caches, layers, heads, topk, pool, scale, ws, pool_out=None, new_rows=None):
         self.caches = caches
         self._kv = (_Kv * len(caches))(*[c.view() for c in caches])
-        self._layers = (_Layer * len(layers))(*[
-            _Layer(m, ci, q.data_ptr(), out.data_ptr(), idx.data_ptr()) for (m, ci, q, out, idx) in layers])
+        self._swa = [ly[5].view() if len(ly) > 5 and ly[5] is not None else None for ly in layers]
+        built = []
+        for ly, sv in zip(layers, self._swa):
+            m, ci, q, out, idx = ly[:5]
+            row = ly[6] if len(ly) > 6 else None
+            built.append(_Layer(m, ci, q.data_ptr(), out.data_ptr(), idx.data_ptr(),
+                                ctypes.pointer(sv) if sv is not None else None,
+                                row.data_ptr() if row is not None else None))
+        self._layers = (_Layer * len(layers))(*built)
         self._keep = (layers, ws, pool_out, new_rows)
         self._step = _Step(self._kv, len(caches), self._layers, len(layers),
                            new_rows.data_ptr() if new_rows is not None else None, heads, topk, pool,

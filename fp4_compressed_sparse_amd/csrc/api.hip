@@ -61,10 +61,11 @@ csa2_status device_ready() {
       state[dev] = 2;
     } else {
       const int big = 160 * 1024 - 16 * 1024;
-      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel<false>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
-      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_partial_kernel<true>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
+      for (const void *k : {reinterpret_cast<const void *>(&attend_partial_kernel<false, false>),
+                            reinterpret_cast<const void *>(&attend_partial_kernel<true, false>),
+                            reinterpret_cast<const void *>(&attend_partial_kernel<false, true>),
+                            reinterpret_cast<const void *>(&attend_partial_kernel<true, true>)})
+        (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, big);
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, big);
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&rescore_kernel<true>),
@@ -114,8 +115,10 @@ bool make_layout(int32_t batch, int32_t heads, int64_t max_len, int32_t pool, in
   if (heads == 16 || heads == 32 || heads == 64) {
     L->att_stages = (int32_t)ceil_div((int64_t)topk * BLOCK, ATT_SP);
     L->att_splits = att_splits(batch * (heads / 16), L->att_stages);
-    // one split: the attention kernel normalises its output itself
-    const size_t slots = L->att_splits > 1 ? (size_t)batch * L->att_splits * (heads / 16) * 16 : 0;
+    // partials for the most splits any call may use: a local branch adds up
+    // to CSA2_MAX_WINDOW / ATT_SP stages; one split normalises in-kernel
+    const int cap = att_splits(batch * (heads / 16), L->att_stages + CSA2_MAX_WINDOW / ATT_SP);
+    const size_t slots = cap > 1 ? (size_t)batch * cap * (heads / 16) * 16 : 0;
     L->part_o = off;  off = align256(off + sizeof(float) * slots * D);
     L->part_ml = off; off = align256(off + sizeof(float) * slots * 2);
   }
@@ -135,6 +138,18 @@ csa2_status check_kv(const csa2_kv *kv) {
   if (kv->max_len < 0 || kv->max_len > kv->capacity)
     return fail(CSA2_E_CAPACITY, "kv max_len %lld outside [0, capacity %lld]", (long long)kv->max_len,
                 (long long)kv->capacity);
+  return CSA2_OK;
+}
+
+static_assert(MAX_SWA_RINGS == CSA2_MAX_SWA_LAYERS, "ring table size");
+
+csa2_status check_swa(const csa2_swa *swa, int32_t batch) {
+  if (!swa->codes || !swa->scales || !swa->seq_len) return fail(CSA2_E_ARG, "swa has a NULL pointer");
+  if (!aligned(swa->codes, 16) || !aligned(swa->scales, 4) || !aligned(swa->seq_len, 8))
+    return fail(CSA2_E_ARG, "swa codes/scales/seq_len misaligned");
+  if (swa->window < 1 || swa->window > CSA2_MAX_WINDOW)
+    return fail(CSA2_E_SHAPE, "swa window %d outside [1, %d]", swa->window, CSA2_MAX_WINDOW);
+  if (swa->batch != batch) return fail(CSA2_E_ARG, "swa batch %d != %d", swa->batch, batch);
   return CSA2_OK;
 }
 
@@ -222,28 +237,45 @@ csa2_status run_rescore(const csa2_kv *kv, const float *q, int32_t heads, const 
 csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *idx,
                        int32_t topk, float scale, float *out, void *ws, const Layout &L,
                        hipStream_t s, const int32_t *cand = nullptr, const float *cand_scores = nullptr,
-                       int32_t n_cand = 0, int32_t *idx_out = nullptr) {
+                       int32_t n_cand = 0, int32_t *idx_out = nullptr, const csa2_swa *swa = nullptr) {
   const int B = kv->batch;
   AttendArgs aa;
   aa.codes = kv->codes; aa.scales = kv->scales; aa.seq_len = kv->seq_len; aa.capacity = kv->capacity;
   aa.limit = kv->max_len;
   aa.q = q; aa.idx = idx; aa.topk = topk;
   aa.scale_log2 = scale * 1.4426950408889634f;
-  aa.n_stages = L.att_stages; aa.splits = L.att_splits;
+  aa.n_sparse = L.att_stages;
+  aa.window = swa ? swa->window : 0;
+  aa.swa_codes = swa ? swa->codes : kv->codes;
+  aa.swa_scales = swa ? swa->scales : reinterpret_cast<const float *>(kv->scales);
+  aa.swa_len = swa ? swa->seq_len : kv->seq_len;
+  aa.n_stages = L.att_stages + (int32_t)ceil_div(aa.window, ATT_SP);
+  // window stages add workgroups only while the combine still merges every
+  // split in the same number of load batches; beyond that they are spread
+  // over the existing splits (<= the layout's capacity either way)
+  const int base = att_splits(B * (heads / 16), aa.n_sparse);
+  const int room = (int)ceil_div(base, CMB_U) * CMB_U;
+  int splits = att_splits(B * (heads / 16), aa.n_stages);
+  if (splits > room) splits = room;
+  aa.splits = splits;
   aa.part_o = at<float>(ws, L.part_o); aa.part_ml = at<float>(ws, L.part_ml);
   aa.heads = heads;
   aa.cand = cand; aa.cand_scores = cand_scores; aa.n_cand = n_cand; aa.idx_out = idx_out;
   aa.seq_stride = kv->capacity; aa.len_add = 0; aa.out = out;
-  dim3 g(L.att_splits * (heads / 16), B);
+  dim3 g(splits * (heads / 16), B);
   const size_t lds = (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16);
-  if (idx)
-    attend_partial_kernel<false><<<g, ATT_THREADS, lds, s>>>(aa);
+  if (idx && swa)
+    attend_partial_kernel<false, true><<<g, ATT_THREADS, lds, s>>>(aa);
+  else if (idx)
+    attend_partial_kernel<false, false><<<g, ATT_THREADS, lds, s>>>(aa);
+  else if (swa)
+    attend_partial_kernel<true, true><<<g, ATT_THREADS, lds, s>>>(aa);
   else
-    attend_partial_kernel<true><<<g, ATT_THREADS, lds, s>>>(aa);
+    attend_partial_kernel<true, false><<<g, ATT_THREADS, lds, s>>>(aa);
   if (csa2_status st = launched("attend")) return st;
-  if (L.att_splits == 1) return CSA2_OK;
+  if (splits == 1) return CSA2_OK;
   CombineArgs ca;
-  ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = L.att_splits; ca.heads = heads; ca.out = out;
+  ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = splits; ca.heads = heads; ca.out = out;
   attend_combine_kernel<<<dim3((heads / 16) * 32, B), 64, 0, s>>>(ca);
   return launched("combine");
 }
@@ -342,8 +374,45 @@ csa2_status csa2_append_kv(const csa2_kv *kv, const float *x, void *stream) {
   AppendArgs aa;
   memset(&aa, 0, sizeof aa);
   aa.codes[0] = kv->codes; aa.scales[0] = kv->scales; aa.seq_len[0] = kv->seq_len; aa.capacity[0] = kv->capacity;
-  append_kernel<<<dim3(kv->batch, 1), 128, 0, as_stream(stream)>>>(aa, x, kv->batch);
+  SwaRings rr;
+  memset(&rr, 0, sizeof rr);
+  append_kernel<<<dim3(kv->batch, 1), 128, 0, as_stream(stream)>>>(aa, rr, x, kv->batch, 1);
   return launched("append");
+}
+
+csa2_status fp8_quantize_kv(const float *x, int64_t rows, const int64_t *dst_row, int64_t dst_rows,
+                            uint8_t *codes, float *scales, void *stream) {
+  t_last_error.clear();
+  if (rows < 0) return fail(CSA2_E_ARG, "rows %lld < 0", (long long)rows);
+  if (rows == 0) return CSA2_OK;
+  if (!x || !codes || !scales) return fail(CSA2_E_ARG, "NULL pointer");
+  if (!aligned(x, 16)) return fail(CSA2_E_ARG, "x must be 16-byte aligned");
+  if (!aligned(codes, 8) || !aligned(scales, 4)) return fail(CSA2_E_ARG, "codes/scales misaligned");
+  if (dst_row && !aligned(dst_row, 8)) return fail(CSA2_E_ARG, "dst_row must be 8-byte aligned");
+  if (dst_rows < 0 || (!dst_row && dst_rows < rows))
+    return fail(CSA2_E_CAPACITY, "dst_rows %lld too small for %lld rows", (long long)dst_rows, (long long)rows);
+  if (csa2_status st = device_ready()) return st;
+  const int64_t want = ceil_div(rows, 4);            // one row per wave
+  const int grid = (int)(want < 4096 ? want : 4096);
+  fp8_quantize_kernel<<<grid, 256, 0, as_stream(stream)>>>(x, rows, dst_row, dst_rows, codes, scales);
+  return launched("fp8 quantize");
+}
+
+csa2_status csa2_swa_append(const csa2_swa *swa, const float *x, void *stream) {
+  t_last_error.clear();
+  if (!swa) return fail(CSA2_E_ARG, "swa is NULL");
+  if (swa->batch < 1 || swa->batch > 65535) return fail(CSA2_E_ARG, "swa batch %d out of range", swa->batch);
+  if (csa2_status st = check_swa(swa, swa->batch)) return st;
+  if (!x || !aligned(x, 16)) return fail(CSA2_E_ARG, "x must be non-NULL and 16-byte aligned");
+  if (csa2_status st = device_ready()) return st;
+  AppendArgs aa;
+  memset(&aa, 0, sizeof aa);
+  SwaRings rr;
+  memset(&rr, 0, sizeof rr);
+  rr.codes[0] = swa->codes; rr.scales[0] = swa->scales; rr.seq_len[0] = swa->seq_len;
+  rr.rows[0] = x; rr.window[0] = swa->window;
+  append_kernel<<<dim3(swa->batch, 1), 128, 0, as_stream(stream)>>>(aa, rr, nullptr, swa->batch, 0);
+  return launched("swa append");
 }
 
 csa2_status csa2_index_topk(int32_t mode, const csa2_kv *kv, const float *q, int32_t heads,
@@ -388,10 +457,13 @@ csa2_status csa2_index_topk(int32_t mode, const csa2_kv *kv, const float *q, int
 }
 
 csa2_status csa2_sparse_attend(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *idx,
-                               int32_t topk, float scale, float *out, void *ws, size_t ws_bytes,
-                               void *stream) {
+                               int32_t topk, float scale, const csa2_swa *swa, float *out, void *ws,
+                               size_t ws_bytes, void *stream) {
   t_last_error.clear();
   if (csa2_status st = check_kv(kv)) return st;
+  if (swa) {
+    if (csa2_status st = check_swa(swa, kv->batch)) return st;
+  }
   if (!q || !aligned(q, 16) || !out || !aligned(out, 16))
     return fail(CSA2_E_ARG, "q/out must be non-NULL and 16-byte aligned");
   if (!idx || !aligned(idx, 4)) return fail(CSA2_E_ARG, "idx must be non-NULL");
@@ -404,7 +476,8 @@ csa2_status csa2_sparse_attend(const csa2_kv *kv, const float *q, int32_t heads,
   if (!make_layout(kv->batch, heads, kv->max_len, 0, topk, &L)) return fail(CSA2_E_SHAPE, "bad sizes");
   if (csa2_status st = check_ws(ws, ws_bytes, L)) return st;
   if (csa2_status st = device_ready()) return st;
-  return run_attend(kv, q, heads, idx, topk, scale, out, ws, L, as_stream(stream));
+  return run_attend(kv, q, heads, idx, topk, scale, out, ws, L, as_stream(stream), nullptr, nullptr, 0,
+                    nullptr, swa);
 }
 
 size_t csa2_prefill_workspace_bytes(int32_t n_q, int32_t heads, int32_t topk) {
@@ -445,12 +518,14 @@ csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, 
   aa.q = q; aa.idx = idx; aa.topk = topk; aa.heads = heads;
   aa.scale_log2 = scale * 1.4426950408889634f;
   aa.n_stages = L.att_stages; aa.splits = L.att_splits;
+  aa.n_sparse = L.att_stages; aa.window = 0;                 // no local branch
+  aa.swa_codes = aa.codes; aa.swa_scales = nullptr; aa.swa_len = qpos;
   aa.part_o = L.total ? at<float>(ws, L.part_o) : nullptr;
   aa.part_ml = L.total ? at<float>(ws, L.part_ml) : nullptr;
   aa.out = out;
   dim3 g(L.att_splits * (heads / 16), n_q);
   const size_t lds = (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16);
-  attend_partial_kernel<false><<<g, ATT_THREADS, lds, s>>>(aa);
+  attend_partial_kernel<false, false><<<g, ATT_THREADS, lds, s>>>(aa);
   if (csa2_status st = launched("prefill attend")) return st;
   if (L.att_splits == 1) return CSA2_OK;
   CombineArgs ca;
@@ -504,7 +579,7 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
   if (st->pool > 0 && (!st->pool_out || !aligned(st->pool_out, 4))) return fail(CSA2_E_ARG, "pool > 0 needs pool_out");
   if (st->new_rows && !aligned(st->new_rows, 16)) return fail(CSA2_E_ARG, "new_rows misaligned");
   // mode pattern: layer 0 Full; Reindex/Reuse use the latest Full cache
-  int latest = -1;
+  int latest = -1, n_rings = 0;
   for (int l = 0; l < st->n_layers; ++l) {
     const csa2_layer &ly = st->layers[l];
     if (ly.mode != CSA2_FULL && ly.mode != CSA2_REINDEX && ly.mode != CSA2_REUSE)
@@ -515,6 +590,12 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
     else if (ly.cache != latest) return fail(CSA2_E_ARG, "layer %d: must use the latest Full cache %d", l, latest);
     if (!ly.q || !aligned(ly.q, 16) || !ly.out || !aligned(ly.out, 16) || !ly.idx || !aligned(ly.idx, 4))
       return fail(CSA2_E_ARG, "layer %d: q/out/idx missing or misaligned", l);
+    if (ly.swa) {
+      if (csa2_status e = check_swa(ly.swa, B)) return e;
+      if (ly.swa_row && !aligned(ly.swa_row, 16)) return fail(CSA2_E_ARG, "layer %d: swa_row misaligned", l);
+      if (ly.swa_row && ++n_rings > CSA2_MAX_SWA_LAYERS)
+        return fail(CSA2_E_SHAPE, "more than %d layers append SWA rows", CSA2_MAX_SWA_LAYERS);
+    }
   }
   Layout L;
   if (!make_layout(B, st->heads, max_len, st->pool, st->topk, &L)) return fail(CSA2_E_SHAPE, "bad sizes");
@@ -522,14 +603,26 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
   if (csa2_status e = device_ready()) return e;
   hipStream_t s = as_stream(stream);
 
-  if (st->new_rows) {
+  if (st->new_rows || n_rings) {
+    // one launch: the Full caches' rows, then every layer's SWA row
     AppendArgs aa;
     memset(&aa, 0, sizeof aa);
-    for (int c = 0; c < st->n_caches; ++c) {
+    const int nc = st->new_rows ? st->n_caches : 0;
+    for (int c = 0; c < nc; ++c) {
       aa.codes[c] = st->caches[c].codes; aa.scales[c] = st->caches[c].scales;
       aa.seq_len[c] = st->caches[c].seq_len; aa.capacity[c] = st->caches[c].capacity;
     }
-    append_kernel<<<dim3(B, st->n_caches), 128, 0, s>>>(aa, st->new_rows, B);
+    SwaRings rr;
+    memset(&rr, 0, sizeof rr);
+    int nr = 0;
+    for (int l = 0; l < st->n_layers; ++l) {
+      const csa2_layer &ly = st->layers[l];
+      if (!ly.swa || !ly.swa_row) continue;
+      rr.codes[nr] = ly.swa->codes; rr.scales[nr] = ly.swa->scales; rr.seq_len[nr] = ly.swa->seq_len;
+      rr.rows[nr] = ly.swa_row; rr.window[nr] = ly.swa->window;
+      ++nr;
+    }
+    append_kernel<<<dim3(B, nc + nr), 128, 0, s>>>(aa, rr, st->new_rows, B, nc);
     if (csa2_status e = launched("append")) return e;
   }
   bool pool_built = false;
@@ -558,7 +651,7 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
       }
       if (e) return e;
       e = run_attend(kv, ly.q, st->heads, nullptr, st->topk, st->scale, ly.out, st->ws, L, s,
-                     st->pool_out, cs, st->pool, ly.idx);
+                     st->pool_out, cs, st->pool, ly.idx, ly.swa);
       if (e) return e;
       prev_idx = ly.idx;
       continue;
@@ -572,7 +665,8 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
       e = run_scan_select(kv, ly.q, st->heads, st->topk, ly.idx, 0, nullptr, st->ws, L, s);
     }
     if (e) return e;
-    e = run_attend(kv, ly.q, st->heads, ly.idx, st->topk, st->scale, ly.out, st->ws, L, s);
+    e = run_attend(kv, ly.q, st->heads, ly.idx, st->topk, st->scale, ly.out, st->ws, L, s, nullptr,
+                   nullptr, 0, nullptr, ly.swa);
     if (e) return e;
     prev_idx = ly.idx;
   }

@@ -20,6 +20,11 @@
 //    the row-major LDS tile with ds_read_b64_tr_b16.
 //  * Each workgroup writes its (max, sum, O) partial; a combine kernel
 //    merges the partials of every head (split-K over positions).
+//  * Optional local branch: the sliding window of the newest positions in
+//    an FP8 (E4M3, float32 row scale) ring [rebasdaily.com, sections "halve
+//    the long input" and "same notes, many layers"] is appended as further
+//    stages of the same softmax; its rows are dequantised as e4m3 * scale
+//    rounded to fp16 (rows need |x| <= 65504).
 //
 // MFMA 16x16x32 f16 lane layout (checked on gfx950): A row = lane%16 with
 // k = 8*(lane/16)..+7; B column = lane%16, same k; C column = lane%16,
@@ -63,6 +68,14 @@ struct AttendArgs {
   int64_t seq_stride;
   int32_t len_add;          // valid positions of row b: seq_len[b] + len_add
   float *out;               // splits == 1: final output [batch][heads][512] written here
+  // local branch: stages n_sparse .. n_stages-1 hold the last
+  // min(window, swa_len[b]) positions of sequence b's FP8 ring (position p
+  // in slot p % window), attended in the same softmax as the gathered ones
+  int32_t n_sparse;         // stages of gathered positions: ceil(topk*8 / ATT_SP)
+  int32_t window;           // 0 = no local branch
+  const uint8_t *swa_codes; // [batch][window][512] E4M3
+  const float *swa_scales;  // [batch][window]
+  const int64_t *swa_len;   // [batch]; any valid int64 array when window == 0
 };
 
 constexpr int SEL_CAND_MAX = 2048;  // candidates of the in-kernel top-k (8 per thread)
@@ -73,7 +86,7 @@ constexpr int SEL_CAND_MAX = 2048;  // candidates of the in-kernel top-k (8 per 
 // the per-head max and sum of the stage are exchanged through LDS; P is
 // written to LDS as fp16; wave w then accumulates O^T for channel tiles
 // 8w..8w+7 over all 64 positions.
-template <bool SELECT>
+template <bool SELECT, bool WIN>
 __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs a) {
   extern __shared__ _Float16 s_v[];               // [ATT_SP][ROW_HALVES]; first holds q
   __shared__ _Float16 s_p[16 * P_STRIDE];         // P: [16 heads][64 positions]
@@ -97,6 +110,9 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   const int total_pos = a.topk * BLOCK;
   const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
   const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
+  // local branch: read now, with the first ids, so that the window rows'
+  // addresses are known when the first window stage is fetched
+  const int64_t wlen_raw = WIN ? a.swa_len[b] : 0;
 
   // ---- gathered rows of a stage: block ids, then rows (two round trips) --
   constexpr int PASSES = ATT_SP / 16;     // rows per thread per stage
@@ -106,6 +122,11 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   u32x4 wr[PASSES];
   uint32_t scr[PASSES];
   auto fetch_ids_into = [&](int st, int32_t (&dst)[PASSES]) {
+    if (WIN && st >= a.n_sparse) {               // window stage: the position's index in the window
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) dst[k] = (st - a.n_sparse) * ATT_SP + (tid >> 4) + 16 * k;
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
       const int j = st * ATT_SP + (tid >> 4) + 16 * k;
@@ -117,7 +138,26 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   };
   auto fetch_ids = [&](int st) { fetch_ids_into(st, blkv); };
   int32_t nxt[PASSES];                    // block ids of the stage after the one in flight
+  u32x4 wr2[PASSES];                      // window rows: second 16 bytes of the thread's 32
+  int64_t nw = 0, wbase = 0;              // window positions held; slot of the oldest
+  const uint8_t *wcodes = a.swa_codes + (int64_t)b * a.window * D;
+  const float *wscales = a.swa_scales + (int64_t)b * a.window;
   auto fetch_rows = [&](int st) {
+    if (WIN && st >= a.n_sparse) {
+      // window rows: 512 code bytes (32 per thread) and the row scale
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) {
+        okv[k] = blkv[k] < nw;
+        int64_t slot = wbase + blkv[k];
+        slot = okv[k] ? (slot >= a.window ? slot - a.window : slot) : 0;
+        const uint8_t *row = wcodes + slot * D + 32 * i16;
+        wr[k] = *reinterpret_cast<const u32x4 *>(row);
+        wr2[k] = *reinterpret_cast<const u32x4 *>(row + 16);
+        scr[k] = __float_as_uint(wscales[slot]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
       // in bounds (masked by the sequence length later); an id outside the
@@ -181,6 +221,11 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
 #pragma unroll
     for (int u = 0; u < NV; ++u) v[u] = src[tid + u * ATT_THREADS];
     __builtin_amdgcn_sched_barrier(0);    // query loads go out before the ids are awaited
+    if (WIN) {
+      const int64_t wl = wlen_raw < 0 ? 0 : wlen_raw;
+      nw = wl < a.window ? wl : a.window;
+      wbase = (wl - nw) % a.window;
+    }
     fetch_rows(st0);
     if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);
 #pragma unroll
@@ -216,6 +261,34 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   for (int st = st0; st < st1; ++st) {
     __syncthreads();                      // q / previous stage fully consumed
     // ---- dequantise the stage's rows into LDS as fp16 (16 threads per row) ----
+    if (WIN && st >= a.n_sparse) {
+      // window rows: e4m3 * row scale, rounded to fp16 (16 threads per row,
+      // 32 channels each)
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) {
+        const int pp = (tid >> 4) + 16 * k;
+        if (!okv[k]) { wr[k] = u32x4{0u, 0u, 0u, 0u}; wr2[k] = wr[k]; }   // masked: finite zeros
+        const float sc = okv[k] ? __uint_as_float(scr[k]) : 0.f;
+        u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i16);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 w = h ? wr2[k] : wr[k];
+          uint32_t o[8];
+#pragma unroll
+          for (int dw = 0; dw < 4; ++dw) {
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[dw], false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[dw], true);
+            const f16x2 a0 = {(_Float16)(lo.x * sc), (_Float16)(lo.y * sc)};
+            const f16x2 a1 = {(_Float16)(hi.x * sc), (_Float16)(hi.y * sc)};
+            o[2 * dw] = __builtin_bit_cast(uint32_t, a0);
+            o[2 * dw + 1] = __builtin_bit_cast(uint32_t, a1);
+          }
+          dst[2 * h] = u32x4{o[0], o[1], o[2], o[3]};
+          dst[2 * h + 1] = u32x4{o[4], o[5], o[6], o[7]};
+        }
+        if (i16 == 0) s_ok[pp] = okv[k] ? 1 : 0;
+      }
+    } else {
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
       const int pp = (tid >> 4) + 16 * k;
@@ -239,6 +312,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
                         __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
       }
       if (i16 == 0) s_ok[pp] = okv[k] ? 1 : 0;
+    }
     }
     // the next stage's rows (and the ids of the one after) are requested now,
     // so they arrive while this stage is computed
@@ -354,8 +428,10 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   CSA2_TS(5);
 }
 
-template __global__ void attend_partial_kernel<false>(AttendArgs);
-template __global__ void attend_partial_kernel<true>(AttendArgs);
+template __global__ void attend_partial_kernel<false, false>(AttendArgs);
+template __global__ void attend_partial_kernel<true, false>(AttendArgs);
+template __global__ void attend_partial_kernel<false, true>(AttendArgs);
+template __global__ void attend_partial_kernel<true, true>(AttendArgs);
 
 struct CombineArgs {
   const float *part_o;

@@ -134,19 +134,125 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(
   }
 }
 
-// Caches appended in one launch (decode step: one row per sequence each).
+// ---- FP8 rows of the sliding-window (SWA) cache -------------------------
+//
+// The local branch's KV stays FP8 because it is more sensitive to
+// quantisation (rebasdaily.com "DeepSeek-V4.1-Flash KV compression",
+// section "same notes, many layers").  Reading (the pages give no layout):
+// E4M3FN codes with one float32 scale per row, s = fl(amax / 448), code =
+// E4M3 nearest to fl(x / s) (ties to even; |x / s| <= 448 by construction),
+// sign kept; s == 0 leaves only the signs.  Both divisions are IEEE
+// (correctly rounded), the E4M3 rounding is the hardware's RNE converter.
+
+// Codes of 4 values (bytes in channel order) for scale s.
+__device__ __forceinline__ uint32_t fp8_encode4(float4 v, float s) {
+  if (s > 0.0f) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(v.x, s), __fdiv_rn(v.y, s), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(v.z, s), __fdiv_rn(v.w, s), w, true);
+    return (uint32_t)w;
+  }
+  return ((__float_as_uint(v.x) >> 31) << 7) | ((__float_as_uint(v.y) >> 31) << 15) |
+         ((__float_as_uint(v.z) >> 31) << 23) | ((__float_as_uint(v.w) >> 31) << 31);
+}
+
+__device__ __forceinline__ bool finite4(float4 v) {
+  return __builtin_isfinite(v.x) && __builtin_isfinite(v.y) && __builtin_isfinite(v.z) &&
+         __builtin_isfinite(v.w);
+}
+
+__device__ __forceinline__ uint32_t amax_bits4(float4 v) {
+  // non-negative floats order like their bit patterns
+  return max(max(__float_as_uint(fabsf(v.x)), __float_as_uint(fabsf(v.y))),
+             max(__float_as_uint(fabsf(v.z)), __float_as_uint(fabsf(v.w))));
+}
+
+// The largest magnitude the attention can stage as fp16, and the flag bit a
+// larger SWA row raises.
+constexpr float SWA_FP16_MAX = 65504.0f;
+constexpr uint32_t FLAG_SWA_RANGE = 16;
+
+// rows x 512 floats -> codes [dst][512], scales [dst]: one wave per row,
+// 8 channels (two float4) per lane; rows grid-strided.
+__global__ void __launch_bounds__(256) fp8_quantize_kernel(
+    const float *__restrict__ x, int64_t rows, const int64_t *__restrict__ dst_row,
+    int64_t dst_rows, uint8_t *__restrict__ codes, float *__restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows; r += waves) {
+    const float4 *src = reinterpret_cast<const float4 *>(x + r * D) + 2 * lane;
+    const float4 v0 = src[0], v1 = src[1];
+    const int64_t d = dst_row ? dst_row[r] : r;
+    const bool bad = __builtin_amdgcn_ballot_w64(!(finite4(v0) && finite4(v1))) != 0;
+    const float amax = __uint_as_float(wave_umax(max(amax_bits4(v0), amax_bits4(v1))));
+    if (d < 0 || d >= dst_rows) {
+      if (lane == 0) raise_flag(FLAG_CAPACITY);
+      continue;
+    }
+    float s = bad ? 0.0f : __fdiv_rn(amax, 448.0f);
+    uint32_t c0 = 0, c1 = 0;
+    if (!bad) { c0 = fp8_encode4(v0, s); c1 = fp8_encode4(v1, s); }
+    reinterpret_cast<uint2 *>(codes + d * D)[lane] = uint2{c0, c1};
+    if (lane == 0) {
+      scales[d] = s;
+      if (bad) raise_flag(FLAG_NONFINITE_KV);
+      else if (amax > SWA_FP16_MAX) raise_flag(FLAG_SWA_RANGE);
+    }
+  }
+}
+
+// Caches appended in one launch (decode step: one row per sequence each):
+// the FP4 global caches of the Full layers, then the FP8 SWA rings.
 struct AppendArgs {
   uint8_t *codes[16];
   uint8_t *scales[16];
   int64_t *seq_len[16];
   int64_t capacity[16];
 };
+constexpr int MAX_SWA_RINGS = 64;
+struct SwaRings {
+  uint8_t *codes[MAX_SWA_RINGS];     // [batch][window][512]
+  float *scales[MAX_SWA_RINGS];      // [batch][window]
+  int64_t *seq_len[MAX_SWA_RINGS];   // [batch]
+  const float *rows[MAX_SWA_RINGS];  // [batch][512]
+  int32_t window[MAX_SWA_RINGS];
+};
 
-// grid (batch, n_caches), 128 threads: x[c][b][512] -> position seq_len[b].
-__global__ void __launch_bounds__(128) append_kernel(AppendArgs a, const float *__restrict__ x,
-                                                     int32_t batch) {
+// grid (batch, n_caches + n_rings), 128 threads.  y < n_caches:
+// x[y][b][512] -> position seq_len[b] of cache y.  Otherwise ring
+// y - n_caches: rows[b] -> position seq_len[b], slot seq_len[b] % window.
+__global__ void __launch_bounds__(128) append_kernel(AppendArgs a, SwaRings r, const float *__restrict__ x,
+                                                     int32_t batch, int32_t n_caches) {
   const int b = blockIdx.x, c = blockIdx.y;
   const int q = threadIdx.x;
+  if (c >= n_caches) {
+    __shared__ uint32_t s_red[2];
+    const int i = c - n_caches;
+    int64_t *len = r.seq_len[i] + b;
+    const int64_t pos = *len;
+    const float4 v = reinterpret_cast<const float4 *>(r.rows[i] + (int64_t)b * D)[q];
+    const bool bad_w = __builtin_amdgcn_ballot_w64(!finite4(v)) != 0;
+    const uint32_t am = wave_umax(amax_bits4(v));
+    if ((q & 63) == 0) s_red[q >> 6] = am | (bad_w ? 0x80000000u : 0u);   // |x| bits have no sign
+    __syncthreads();
+    const uint32_t both = max(s_red[0] & 0x7fffffffu, s_red[1] & 0x7fffffffu);
+    const bool bad = ((s_red[0] | s_red[1]) & 0x80000000u) != 0;
+    if (pos < 0) {
+      if (q == 0) raise_flag(FLAG_CAPACITY);
+      return;
+    }
+    const float amax = __uint_as_float(both);
+    const float s = bad ? 0.0f : __fdiv_rn(amax, 448.0f);
+    const int64_t row = (int64_t)b * r.window[i] + pos % r.window[i];
+    reinterpret_cast<uint32_t *>(r.codes[i] + row * D)[q] = bad ? 0u : fp8_encode4(v, s);
+    if (q == 0) {
+      r.scales[i][row] = s;
+      if (bad) raise_flag(FLAG_NONFINITE_KV);
+      else if (amax > SWA_FP16_MAX) raise_flag(FLAG_SWA_RANGE);
+    }
+    __syncthreads();
+    if (q == 0) *len = pos + 1;
+    return;
+  }
   int64_t *len = a.seq_len[c] + b;
   const int64_t pos = *len;
   float4 v = reinterpret_cast<const float4 *>(x + ((int64_t)c * batch + b) * D)[q];

@@ -72,7 +72,9 @@ enum {
   CSA2_FLAG_NONFINITE_KV = 1,   /* a quantised group held NaN/Inf: written as zeros     */
   CSA2_FLAG_CAPACITY = 2,       /* append into a full sequence, or dst_row out of range */
   CSA2_FLAG_NONFINITE_Q = 4,    /* an indexer query sum held NaN/Inf (scores unspecified) */
-  CSA2_FLAG_BAD_INDEX = 8       /* a candidate/selected block id was >= the block count */
+  CSA2_FLAG_BAD_INDEX = 8,      /* a candidate/selected block id was >= the block count */
+  CSA2_FLAG_SWA_RANGE = 16      /* an SWA row's largest magnitude exceeded 65504, the
+                                   attention's fp16 operand range (stored as given)      */
 };
 
 #define CSA2_D 512              /* latent channels                 */
@@ -83,6 +85,8 @@ enum {
 #define CSA2_MAX_TOPK 2048      /* largest top-k (blocks)          */
 #define CSA2_MAX_HEADS 64       /* indexer heads 1..64; attention 16, 32 or 64 */
 #define CSA2_MAX_CACHES 16      /* Full caches in one decode step  */
+#define CSA2_MAX_WINDOW 1024    /* largest sliding window (positions) */
+#define CSA2_MAX_SWA_LAYERS 64  /* layers with a local branch in one decode step */
 
 /* Non-owning view of one Full layer's cache for a batch of sequences. */
 typedef struct {
@@ -127,9 +131,52 @@ csa2_status fp4_quantize_kv(const float *x, int64_t rows, const int64_t *dst_row
 csa2_status csa2_append_kv(const csa2_kv *kv, const float *x, void *stream);
 
 /*
+ * Non-owning view of one layer's sliding-window (SWA) cache for a batch of
+ * sequences.  Local context goes through sliding-window attention [P2
+ * "halve the long input"]; entries older than the window are never read by
+ * the current decode step [P1 section 三]; the SWA KV stays FP8 while the
+ * global KV moves to FP4 [P2 "same notes, many layers"].  Reading: E4M3FN
+ * codes with one float32 scale per position, kept in a ring of `window`
+ * slots: position p of sequence b lives in slot p % window.
+ */
+typedef struct {
+  uint8_t *codes;       /* device [batch][window][512] E4M3FN, 16-byte aligned   */
+  float *scales;        /* device [batch][window]                                  */
+  int64_t *seq_len;     /* device [batch]: positions written; appends increment it */
+  int32_t window;       /* 1..CSA2_MAX_WINDOW                                      */
+  int32_t batch;        /* sequences, >= 1                                         */
+} csa2_swa;
+
+/*
+ * fp8_quantize_kv — quantise float32 rows into the SWA row format.
+ *   s = fl32(amax / 448) of the row's largest magnitude; each value becomes
+ *   the E4M3FN code nearest to fl32(x / s) (both divisions IEEE; ties to
+ *   the even code), sign bit kept; s == 0 keeps only the signs.
+ * x        device float32 [rows][512], 16-byte aligned; rows >= 0.
+ * dst_row  device int64 [rows]: destination row of each input row, or NULL
+ *          for row i -> row i.  Rows outside [0, dst_rows) are skipped and
+ *          flag CSA2_FLAG_CAPACITY.  (A ring slot is row b*window + p%window.)
+ * codes    device uint8 [dst_rows][512], 8-byte aligned; scales device
+ *          float32 [dst_rows].
+ * A row with NaN/Inf is written as zeros with scale 0 and flags
+ * CSA2_FLAG_NONFINITE_KV; a row with amax > 65504 flags CSA2_FLAG_SWA_RANGE.
+ */
+csa2_status fp8_quantize_kv(const float *x, int64_t rows, const int64_t *dst_row,
+                            int64_t dst_rows, uint8_t *codes, float *scales, void *stream);
+
+/*
+ * csa2_swa_append — for each b: quantise x[b] (device float32 [batch][512],
+ * 16-byte aligned) as position seq_len[b] into slot seq_len[b] % window,
+ * then seq_len[b] += 1.  A negative seq_len[b] is left alone and flags
+ * CSA2_FLAG_CAPACITY.
+ */
+csa2_status csa2_swa_append(const csa2_swa *swa, const float *x, void *stream);
+
+/*
  * csa2_workspace_bytes — workspace needed by csa2_index_topk,
  * csa2_sparse_attend, and csa2_decode_step for these
- * bounds (max_len = longest sequence in positions).  Returns 0 for
+ * bounds (max_len = longest sequence in positions), with or without a
+ * local branch of any window up to CSA2_MAX_WINDOW.  Returns 0 for
  * unsupported bounds.
  */
 size_t csa2_workspace_bytes(int32_t batch, int32_t heads, int64_t max_len,
@@ -187,15 +234,19 @@ csa2_status csa2_index_topk(int32_t mode, const csa2_kv *kv, const float *q, int
  * shared by all heads.  Positions 8*idx+t at or beyond seq_len[b] are
  * skipped; -1 entries are ignored; no position gives a zero output.
  *   out[b][h] = sum_p softmax_p(scale * q[b][h] . k_p) k_p
+ * swa   NULL, or the layer's SWA cache (same batch): the local branch.  Its
+ *       last min(window, swa->seq_len[b]) positions join the same softmax
+ *       as further keys = values (reading: one softmax over both branches).
  * q     device float32 [batch][heads][512]; heads in {16, 32, 64}.
  * idx   device int32 [batch][topk], topk 1..CSA2_MAX_TOPK.
  * out   device float32 [batch][heads][512].
- * Accumulates in float32 with fp16 matrix-core operands (the dequantised
- * values are exact in fp16; q is rounded to fp16).
+ * Accumulates in float32 with fp16 matrix-core operands (the FP4 values
+ * are exact in fp16; q and the SWA values e4m3 * scale are rounded to fp16).
  */
 csa2_status csa2_sparse_attend(const csa2_kv *kv, const float *q, int32_t heads,
                                const int32_t *idx, int32_t topk, float scale,
-                               float *out, void *ws, size_t ws_bytes, void *stream);
+                               const csa2_swa *swa, float *out, void *ws, size_t ws_bytes,
+                               void *stream);
 
 /*
  * csa2_prefill_workspace_bytes — workspace needed by csa2_prefill_attend
@@ -234,6 +285,9 @@ typedef struct {
   const float *q;      /* device float32 [batch][heads][512]                        */
   float *out;          /* device float32 [batch][heads][512]                        */
   int32_t *idx;        /* device int32 [batch][topk]: this layer's selection        */
+  const csa2_swa *swa; /* host pointer: this layer's SWA cache, or NULL (no local branch) */
+  const float *swa_row;/* device float32 [batch][512]: the SWA row of the new token,
+                          appended before the layers run; NULL = append nothing        */
 } csa2_layer;
 
 typedef struct {
@@ -256,7 +310,10 @@ typedef struct {
  * runs the layers in order: the first Full layer scans all blocks (into
  * the pool when pool > 0); later Full/Reindex layers search the pool (or
  * all blocks when pool == 0) of their cache; Reuse layers take the previous
- * layer's selection; every layer then attends over its selection.
+ * layer's selection; every layer then attends over its selection, joined
+ * by its sliding window when it has an SWA cache (at most
+ * CSA2_MAX_SWA_LAYERS such layers; their swa_rows are appended in the same
+ * launch as new_rows).
  * Capacity: each cache's max_len must already count the appended position.
  */
 csa2_status csa2_decode_step(const csa2_step *step, void *stream);

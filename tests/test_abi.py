@@ -74,6 +74,12 @@ def _kv(**kw):
                     base["max_len"], base["batch"])
 
 
+def _swa(**kw):
+    base = dict(codes=0x20000, scales=0x60000, seq_len=0x30000, window=128, batch=1)
+    base.update(kw)
+    return csa2._Swa(base["codes"], base["scales"], base["seq_len"] or None, base["window"], base["batch"])
+
+
 def test_index_and_attend_argument_errors(lib):
     idx = ctypes.c_void_p(0x40000)
     q = ctypes.c_void_p(0x50000)
@@ -92,10 +98,15 @@ def test_index_and_attend_argument_errors(lib):
     assert "workspace" in _err(lib)
     assert call(2, _kv()) == 1                                   # Reuse without prior_idx
     out = ctypes.c_void_p(0x70000)
-    assert lib.csa2_sparse_attend(ctypes.byref(_kv()), q, 24, idx, 64, ctypes.c_float(0.04), out, ws,
-                                  need, None) == 2               # 24 heads unsupported
+    assert lib.csa2_sparse_attend(ctypes.byref(_kv()), q, 24, idx, 64, ctypes.c_float(0.04), None, out,
+                                  ws, need, None) == 2           # 24 heads unsupported
     assert lib.csa2_sparse_attend(ctypes.byref(_kv()), q, 16, idx, 64, ctypes.c_float(float("nan")),
-                                  out, ws, need, None) == 1
+                                  None, out, ws, need, None) == 1
+    # local branch: window outside [1, 1024], batch mismatch, misaligned ring
+    for bad, code in ((_swa(window=0), 2), (_swa(window=1025), 2), (_swa(batch=2), 1),
+                      (_swa(codes=0x20008), 1), (_swa(seq_len=0), 1)):
+        assert lib.csa2_sparse_attend(ctypes.byref(_kv()), q, 16, idx, 64, ctypes.c_float(0.04),
+                                      ctypes.byref(bad), out, ws, need, None) == code
 
 
 def test_decode_step_pattern_errors(lib):
@@ -105,7 +116,7 @@ def test_decode_step_pattern_errors(lib):
     need = lib.csa2_workspace_bytes(1, 16, 4096, 0, 64)
 
     def step(layers, heads=16, pool=0):
-        arr = (csa2._Layer * len(layers))(*[csa2._Layer(m, c, q, out, idx) for m, c in layers])
+        arr = (csa2._Layer * len(layers))(*[csa2._Layer(m, c, q, out, idx, None, None) for m, c in layers])
         st = csa2._Step(kv, 2, arr, len(layers), None, heads, 64, pool, 0.04, None, ws, need)
         return lib.csa2_decode_step(ctypes.byref(st), None)
 
@@ -115,6 +126,29 @@ def test_decode_step_pattern_errors(lib):
     assert step([(0, 0), (0, 1), (1, 0)]) == 1  # Reindex must use the latest Full cache
     assert step([(0, 0)], heads=48) == 2
     assert step([(0, 0)], pool=64) == 1         # pool > 0 without pool_out
+
+
+def test_swa_argument_errors(lib):
+    x = ctypes.c_void_p(0x50000)
+    assert lib.fp8_quantize_kv(None, 0, None, 0, None, None, None) == 0     # no-op
+    assert lib.fp8_quantize_kv(x, -1, None, 0, None, None, None) == 1
+    assert lib.fp8_quantize_kv(x, 4, None, 4, None, ctypes.c_void_p(0x60000), None) == 1
+    assert lib.fp8_quantize_kv(ctypes.c_void_p(0x50004), 4, None, 4, ctypes.c_void_p(0x70000),
+                               ctypes.c_void_p(0x60000), None) == 1       # x misaligned
+    assert lib.fp8_quantize_kv(x, 4, None, 3, ctypes.c_void_p(0x70000), ctypes.c_void_p(0x60000),
+                               None) == 4                                 # too few rows
+    assert lib.csa2_swa_append(None, x, None) == 1
+    assert lib.csa2_swa_append(ctypes.byref(_swa(window=2000)), x, None) == 2
+    assert lib.csa2_swa_append(ctypes.byref(_swa(batch=0)), x, None) == 1
+    assert lib.csa2_swa_append(ctypes.byref(_swa()), ctypes.c_void_p(0x50008), None) == 1
+    # a decode-step layer with a bad ring
+    kv = (csa2._Kv * 1)(_kv())
+    bad = _swa(window=0)
+    arr = (csa2._Layer * 1)(csa2._Layer(0, 0, 0x50000, 0x70000, 0x40000, ctypes.pointer(bad), 0x58000))
+    need = lib.csa2_workspace_bytes(1, 16, 4096, 0, 64)
+    st = csa2._Step(kv, 1, arr, 1, None, 16, 64, 0, 0.04, None, 0x100000, need)
+    assert lib.csa2_decode_step(ctypes.byref(st), None) == 2
+    assert "window" in _err(lib)
 
 
 def test_prefill_attend_argument_errors(lib):

@@ -10,11 +10,14 @@ import fp4_compressed_sparse_amd as csa2
 import workloads as W
 from oracle.step import decode_step as oracle_step
 from tests._gpu import ATT_TOL, cap_for, log, normwise_err, oracle_cache, require_gpu, to_device
+from tests.test_gpu_swa import oracle_swa, ring_to_device
 
 pytestmark = pytest.mark.gpu
 
 
-def run_and_compare(w, lengths, steps):
+def run_and_compare(w, lengths, steps, window=0):
+    """window > 0: every layer has a local branch (FP8 ring of that many
+    positions, prefilled like the caches, one row appended per step)."""
     require_gpu()
     lengths = np.asarray(lengths, dtype=np.int64)
     B = len(lengths)
@@ -23,20 +26,26 @@ def run_and_compare(w, lengths, steps):
     gcs = [to_device(oc) for oc in ocs]
     caches_of = w.layer_caches()
     L = len(w.pattern)
+    oswa = [oracle_swa(w.wid, l, lengths, window, int(lengths.max()) + steps) for l in range(L)] if window else None
+    rings = [ring_to_device(o, window) for o in oswa] if window else None
     max_len = int(lengths.max()) + (steps if w.append else 0)
     ws = csa2.workspace(B, w.heads, max_len, w.pool, w.topk)
     pool_out = torch.zeros((B, w.pool), dtype=torch.int32, device="cuda") if w.pool else None
     for step in range(steps):
         qs = [W.queries(w.wid, l, step, B, w.heads) for l in range(L)]
         new_rows = np.stack([W.append_rows(w.wid, c, step, B) for c in range(w.n_caches)]) if w.append else None
+        srows = np.stack([W.swa_append_rows(w.wid, l, step, B) for l in range(L)]) if window else None
         ref = oracle_step(ocs, [(m, caches_of[l], qs[l]) for l, m in enumerate(w.pattern)],
-                          new_rows, w.topk, w.pool, w.scale)
+                          new_rows, w.topk, w.pool, w.scale, swa=oswa, swa_rows=srows, window=window)
         for g in gcs:
             g.max_len = int(lengths.max()) + ((step + 1) if w.append else 0)
         qt = [torch.from_numpy(q).cuda() for q in qs]
         outs = [torch.zeros((B, w.heads, 512), dtype=torch.float32, device="cuda") for _ in range(L)]
         idxs = [torch.full((B, w.topk), -9, dtype=torch.int32, device="cuda") for _ in range(L)]
         layers = [(m, caches_of[l], qt[l], outs[l], idxs[l]) for l, m in enumerate(w.pattern)]
+        if window:
+            st = [torch.from_numpy(srows[l]).cuda() for l in range(L)]
+            layers = [ly + (rings[l], st[l]) for l, ly in enumerate(layers)]
         nr = torch.from_numpy(new_rows).cuda() if new_rows is not None else None
         csa2.decode_step(gcs, layers, w.heads, w.topk, w.pool, w.scale, ws, pool_out=pool_out, new_rows=nr)
         torch.cuda.synchronize()
@@ -52,7 +61,11 @@ def run_and_compare(w, lengths, steps):
             err = normwise_err(outs[l].cpu().numpy(), ref["out"][l])
             worst = max(worst, err)
             assert err <= ATT_TOL, (step, l, err)
-        log(f"{w.name} step {step}: idx equal on {L} layers, worst attention error {worst:.2e}")
+        if window:
+            for l in range(L):
+                assert np.array_equal(rings[l].seq_len.cpu().numpy(), oswa[l].seq_len)
+        log(f"{w.name} step {step}: idx equal on {L} layers, worst attention error {worst:.2e}"
+            + (f" (window {window})" if window else ""))
 
 
 def test_workload0_single_full_4k():
@@ -91,3 +104,15 @@ def test_pool_above_in_kernel_limit():
     # a pool beyond 2,048 candidates takes the separate top-k kernels
     w = W.scaled(W.WORKLOADS[2], context=40000, pool=2600, topk=256)
     run_and_compare(w, [40000], 1)
+
+
+def test_local_branch_twenty_layers_fused_selection():
+    # every layer joins a 128-position FP8 window; pool <= 2,048 (top-k in the attention kernel)
+    w = W.scaled(W.WORKLOADS[3], context=9000)
+    run_and_compare(w, [9000 - 5], 2, window=128)
+
+
+def test_local_branch_ragged_batch_separate_selection():
+    # pool 0 (every selecting layer scans all blocks), ragged batch, window not a multiple of 64
+    w = W.scaled(W.WORKLOADS[1], context=3000, batch=3)
+    run_and_compare(w, [3000, 150, 1200], 2, window=200)

@@ -27,6 +27,7 @@ D = 512
 CHUNK = 65536
 
 STREAM_KV, STREAM_ROT, STREAM_Q, STREAM_APPEND, STREAM_LEN = 1, 2, 3, 4, 5
+STREAM_SWA, STREAM_SWA_APPEND = 6, 7
 
 FULL, REINDEX, REUSE = 0, 1, 2
 
@@ -157,6 +158,20 @@ def queries(wid, layer, step, batch, heads):
 def append_rows(wid, cache, step, batch):
     """Rows appended by one Full cache at one step -> float32 [B, 512]."""
     z = _rng(wid, STREAM_APPEND, cache, step).standard_normal((batch, D), dtype=np.float32)
+    return shape_rows(z, wid)
+
+
+def swa_rows(wid, layer, seq, start, count):
+    """Sliding-window (local branch) rows of one layer, positions
+    [start, start+count) of one sequence -> float32 [count, 512]; shaped like
+    the global rows (RMSNorm, rotation)."""
+    z = _rng(wid, STREAM_SWA, layer, seq, start).standard_normal((count, D), dtype=np.float32)
+    return shape_rows(z, wid)
+
+
+def swa_append_rows(wid, layer, step, batch):
+    """Local-branch rows one layer writes at one decode step -> float32 [B, 512]."""
+    z = _rng(wid, STREAM_SWA_APPEND, layer, step).standard_normal((batch, D), dtype=np.float32)
     return shape_rows(z, wid)
 
 
