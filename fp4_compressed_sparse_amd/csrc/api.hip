@@ -250,11 +250,11 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   aa.swa_scales = swa ? swa->scales : reinterpret_cast<const float *>(kv->scales);
   aa.swa_len = swa ? swa->seq_len : kv->seq_len;
   aa.n_stages = L.att_stages + (int32_t)ceil_div(aa.window, ATT_SP);
-  // window stages add workgroups only while the combine still merges every
-  // split in the same number of load batches; beyond that they are spread
-  // over the existing splits (<= the layout's capacity either way)
+  // window stages add workgroups only up to the next multiple of 64 splits
+  // (the combine merges up to 64 in one load batch); beyond that they are
+  // spread over the existing splits (<= the layout's capacity either way)
   const int base = att_splits(B * (heads / 16), aa.n_sparse);
-  const int room = (int)ceil_div(base, CMB_U) * CMB_U;
+  const int room = (int)ceil_div(base, 64) * 64;
   int splits = att_splits(B * (heads / 16), aa.n_stages);
   if (splits > room) splits = room;
   aa.splits = splits;
@@ -276,7 +276,10 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   if (splits == 1) return CSA2_OK;
   CombineArgs ca;
   ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = splits; ca.heads = heads; ca.out = out;
-  attend_combine_kernel<<<dim3((heads / 16) * 32, B), 64, 0, s>>>(ca);
+  if (splits <= CMB_U)
+    attend_combine_kernel<1><<<dim3((heads / 16) * 32, B), 64, 0, s>>>(ca);
+  else
+    attend_combine_kernel<2><<<dim3((heads / 16) * 32, B), 128, 0, s>>>(ca);
   return launched("combine");
 }
 
@@ -530,7 +533,10 @@ csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, 
   if (L.att_splits == 1) return CSA2_OK;
   CombineArgs ca;
   ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = L.att_splits; ca.heads = heads; ca.out = out;
-  attend_combine_kernel<<<dim3((heads / 16) * 32, n_q), 64, 0, s>>>(ca);
+  if (L.att_splits <= CMB_U)
+    attend_combine_kernel<1><<<dim3((heads / 16) * 32, n_q), 64, 0, s>>>(ca);
+  else
+    attend_combine_kernel<2><<<dim3((heads / 16) * 32, n_q), 128, 0, s>>>(ca);
   return launched("prefill combine");
 }
 

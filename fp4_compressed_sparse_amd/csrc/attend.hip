@@ -441,48 +441,55 @@ struct CombineArgs {
   float *out;               // [batch][heads][512]
 };
 
-// grid (heads/16 * 32, batch), one wave per workgroup: workgroup (ht, ct)
+// grid (heads/16 * 32, batch), NW waves per workgroup: workgroup (ht, ct)
 // merges O^T tile ct (1 KB) of head tile ht over every split, so the 4 MB of
-// partials of a 64-head step spread over 128 compute units.  The (max, sum)
-// pairs of the first 32 splits and the first 32 tiles are requested in one
-// batch, before any of them is used (one memory round trip for <= 32
-// splits); further splits follow in batches of 32.
+// partials of a 64-head step spread over 128 compute units.  Wave w takes
+// splits 32w.. of each batch of 32*NW; the (max, sum) pairs of the first
+// 32*NW splits and each wave's first 32 tiles are requested in one batch,
+// before any of them is used (one memory round trip for <= 32*NW splits);
+// further splits follow in batches.  With two waves, wave 1 hands its
+// partial sum to wave 0 through LDS.
 constexpr int MAX_SPLITS = 256;
-constexpr int CMB_U = 32;
-__global__ void __launch_bounds__(64) attend_combine_kernel(CombineArgs a) {
+constexpr int CMB_U = 32;                 // splits per wave per batch
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) attend_combine_kernel(CombineArgs a) {
   __shared__ float2 s_ml[MAX_SPLITS * 16];
-  const int b = blockIdx.y, lane = threadIdx.x;
+  __shared__ float4 s_o[NW > 1 ? 64 : 1];
+  __shared__ float s_l[NW > 1 ? 64 : 1];
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int HT = a.heads / 16, ht = blockIdx.x >> 5, ct = blockIdx.x & 31;
   const int nslots = a.splits, nml = nslots * 16;
   const int n16 = lane & 15, g = lane >> 4;
+  constexpr int BATCH = CMB_U * NW;       // splits per batch
+  constexpr int MLV = BATCH * 16 / (64 * NW);
   CSA2_TS(8);
   const float2 *pml = reinterpret_cast<const float2 *>(a.part_ml);
   const float4 *po = reinterpret_cast<const float4 *>(a.part_o) + ct * 64 + lane;
   auto slot_of = [&](int s) { return ((int64_t)b * a.splits + s) * HT + ht; };
-  // (max, sum) of the first 32 splits: entry lane + 64u is split (lane + 64u) / 16,
-  // head (lane + 64u) % 16 (slots are contiguous in the partial layout only
-  // per head tile, so the index goes through slot_of)
-  float2 mlv[CMB_U * 16 / 64];
+  // (max, sum) of the first BATCH splits: entry tid + 64*NW*u is split
+  // (tid + 64*NW*u) / 16, head (tid + 64*NW*u) % 16 (slots are contiguous in
+  // the partial layout only per head tile, so the index goes through slot_of)
+  float2 mlv[MLV];
 #pragma unroll
-  for (int u = 0; u < CMB_U * 16 / 64; ++u) {
-    const int e = min(lane + 64 * u, nml - 1);
+  for (int u = 0; u < MLV; ++u) {
+    const int e = min(tid + 64 * NW * u, nml - 1);
     mlv[u] = pml[slot_of(e >> 4) * 16 + (e & 15)];
   }
   float4 ov[CMB_U];
 #pragma unroll
-  for (int u = 0; u < CMB_U; ++u) ov[u] = po[slot_of(min(u, nslots - 1)) * (16 * D / 4)];
+  for (int u = 0; u < CMB_U; ++u) ov[u] = po[slot_of(min(CMB_U * wv + u, nslots - 1)) * (16 * D / 4)];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int u = 0; u < CMB_U * 16 / 64; ++u) {
-    const int e = lane + 64 * u;
+  for (int u = 0; u < MLV; ++u) {
+    const int e = tid + 64 * NW * u;
     if (e < nml) s_ml[e] = mlv[u];
   }
-  // splits beyond the first 32 (long selections): their (max, sum) pairs
-  for (int e0 = CMB_U * 16; e0 < nml; e0 += 64) {
-    const int e = e0 + lane;
+  // splits beyond the first batch (long selections): their (max, sum) pairs
+  for (int e0 = BATCH * 16; e0 < nml; e0 += 64 * NW) {
+    const int e = e0 + tid;
     if (e < nml) s_ml[e] = pml[slot_of(e >> 4) * 16 + (e & 15)];
   }
-  __syncthreads();                        // one wave: orders the LDS writes before the reads
+  __syncthreads();
   CSA2_TS(9);
   float M = -__builtin_huge_valf();
   for (int s0 = 0; s0 < nslots; s0 += 16) {
@@ -498,21 +505,30 @@ __global__ void __launch_bounds__(64) attend_combine_kernel(CombineArgs a) {
     // every partial is written (an empty one as m = -inf, O = 0), so a
     // batch past the last split re-reads that split with weight 0
 #pragma unroll 1
-    for (int s0 = 0; s0 < nslots; s0 += CMB_U) {
+    for (int s0 = 0; s0 < nslots; s0 += BATCH) {
+      const int sw = s0 + CMB_U * wv;    // this wave's first split of the batch
       if (s0 > 0) {
 #pragma unroll
-        for (int u = 0; u < CMB_U; ++u) ov[u] = po[slot_of(min(s0 + u, nslots - 1)) * (16 * D / 4)];
+        for (int u = 0; u < CMB_U; ++u) ov[u] = po[slot_of(min(sw + u, nslots - 1)) * (16 * D / 4)];
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int u = 0; u < CMB_U; ++u) {
-        const int su = min(s0 + u, nslots - 1);
+        const int su = min(sw + u, nslots - 1);
         const float2 ml = s_ml[su * 16 + n16];
-        const float e = (s0 + u < nslots && ml.x != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
+        const float e = (sw + u < nslots && ml.x != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
         L += e * ml.y;
         o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
       }
     }
+  }
+  if constexpr (NW > 1) {
+    if (wv == 1) { s_o[lane] = o; s_l[lane] = L; }
+    __syncthreads();
+    if (wv != 0) return;
+    const float4 o1 = s_o[lane];
+    o.x += o1.x; o.y += o1.y; o.z += o1.z; o.w += o1.w;
+    L += s_l[lane];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
@@ -521,5 +537,8 @@ __global__ void __launch_bounds__(64) attend_combine_kernel(CombineArgs a) {
   *reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.heads + 16 * ht + n16) * D + c0) = o;
   CSA2_TS(10);
 }
+
+template __global__ void attend_combine_kernel<1>(CombineArgs);
+template __global__ void attend_combine_kernel<2>(CombineArgs);
 
 }  // namespace csa2

@@ -22,7 +22,9 @@ def _attend(g, q, idx, scale, ws=None):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("heads,topk", [(16, 64), (32, 100), (64, 256), (16, 128)])
+# (16, 400): 50 splits per head tile (two-wave combine, one batch);
+# (16, 1024): 128 splits (two-wave combine, two batches)
+@pytest.mark.parametrize("heads,topk", [(16, 64), (32, 100), (64, 256), (16, 128), (16, 400), (16, 1024)])
 def test_attend_matches_oracle(heads, topk):
     require_gpu()
     lengths = [4096 + 5, 2000, 3]
