@@ -61,7 +61,8 @@ csa2_status device_ready() {
       state[dev] = 2;
     } else {
       const int big = 160 * 1024 - 16 * 1024;
-      for (const void *k : {reinterpret_cast<const void *>(&attend_partial_kernel<false, false>),
+      for (const void *k : {reinterpret_cast<const void *>(&attend64_kernel),
+                            reinterpret_cast<const void *>(&attend_partial_kernel<false, false>),
                             reinterpret_cast<const void *>(&attend_partial_kernel<true, false>),
                             reinterpret_cast<const void *>(&attend_partial_kernel<false, true>),
                             reinterpret_cast<const void *>(&attend_partial_kernel<true, true>)})
@@ -297,7 +298,8 @@ bool prefill_layout(int32_t n_q, int32_t heads, int32_t topk, Layout *L) {
   if (heads != 16 && heads != 32 && heads != 64) return false;
   memset(L, 0, sizeof *L);
   L->att_stages = (int32_t)ceil_div((int64_t)topk * BLOCK, ATT_SP);
-  L->att_splits = att_splits(n_q * (heads / 16), L->att_stages);
+  // 64 heads: one workgroup per (query, split) covers all four head tiles
+  L->att_splits = att_splits(heads == 64 ? n_q : n_q * (heads / 16), L->att_stages);
   const size_t slots = L->att_splits > 1 ? (size_t)n_q * L->att_splits * (heads / 16) * 16 : 0;
   size_t off = 0;
   L->part_o = off;  off = align256(off + sizeof(float) * slots * D);
@@ -526,9 +528,11 @@ csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, 
   aa.part_o = L.total ? at<float>(ws, L.part_o) : nullptr;
   aa.part_ml = L.total ? at<float>(ws, L.part_ml) : nullptr;
   aa.out = out;
-  dim3 g(L.att_splits * (heads / 16), n_q);
   const size_t lds = (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16);
-  attend_partial_kernel<false, false><<<g, ATT_THREADS, lds, s>>>(aa);
+  if (heads == 64)
+    attend64_kernel<<<dim3(L.att_splits, n_q), ATT_THREADS, lds, s>>>(aa);
+  else
+    attend_partial_kernel<false, false><<<dim3(L.att_splits * (heads / 16), n_q), ATT_THREADS, lds, s>>>(aa);
   if (csa2_status st = launched("prefill attend")) return st;
   if (L.att_splits == 1) return CSA2_OK;
   CombineArgs ca;

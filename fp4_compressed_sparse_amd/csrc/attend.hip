@@ -433,6 +433,268 @@ template __global__ void attend_partial_kernel<true, false>(AttendArgs);
 template __global__ void attend_partial_kernel<false, true>(AttendArgs);
 template __global__ void attend_partial_kernel<true, true>(AttendArgs);
 
+// ---- 64 heads per workgroup (prefill side) ------------------------------
+//
+// Many queries, each with its own selection: one workgroup takes one query
+// and a range of stages for all four 16-head tiles, so a gathered row is
+// dequantised once for 64 heads (the kernel above dequantises it once per
+// tile, and the FP4 convert then outweighs the matrix work).  Wave w owns
+// head tile w for S^T = K Q^T over the stage's 64 positions (its 16 query
+// rows stay in registers as fp16; K fragments come from LDS), so the
+// softmax of a head never leaves its wave; the stage's P of all 64 heads
+// and each head's rescale factor go through LDS, and wave w then
+// accumulates O^T channel tiles 8w..8w+7 of all four head tiles (each V^T
+// fragment read once, used for the four tiles).
+__global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
+  extern __shared__ _Float16 s_v[];               // [ATT_SP][ROW_HALVES]; first holds q (64 heads)
+  __shared__ _Float16 s_p[64 * P_STRIDE];         // P: [64 heads][64 positions]
+  __shared__ float s_corr[64], s_fin[2][64];
+  __shared__ uint8_t s_ok[ATT_SP];
+
+  const int b = blockIdx.y, split = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int64_t cap_blocks = a.capacity / BLOCK;
+  const int32_t *idx = a.idx + (int64_t)b * a.topk;
+  const uint8_t *codes = a.codes + (int64_t)b * a.seq_stride * CODE_BYTES;
+  const uint8_t *scales = a.scales + (int64_t)b * a.seq_stride * SCALE_BYTES;
+  const int total_pos = a.topk * BLOCK;
+  const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
+  const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
+
+  constexpr int PASSES = ATT_SP / 16;
+  const int i16 = tid & 15;
+  int32_t blkv[PASSES], nxt[PASSES];
+  bool okv[PASSES];
+  u32x4 wr[PASSES];
+  uint32_t scr[PASSES];
+  auto fetch_ids_into = [&](int st, int32_t (&dst)[PASSES]) {
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      const int j = st * ATT_SP + (tid >> 4) + 16 * k;
+      dst[k] = idx[min(j, total_pos - 1) >> 3];
+    }
+  };
+  auto fetch_rows = [&](int st) {
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      if (st * ATT_SP + (tid >> 4) + 16 * k >= total_pos) blkv[k] = -1;
+      const bool ok = blkv[k] >= 0 && blkv[k] < cap_blocks;
+      const int64_t pos = ok ? (int64_t)blkv[k] * BLOCK + (((tid >> 4) + 16 * k) & 7) : 0;
+      wr[k] = *reinterpret_cast<const u32x4 *>(codes + pos * CODE_BYTES + 16 * i16);
+      scr[k] = *reinterpret_cast<const uint16_t *>(scales + pos * SCALE_BYTES + 2 * i16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  CSA2_TS(0);
+  fetch_ids_into(st0, blkv);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- the query's 64 x 512 tile -> fp16 in LDS (two batches of 16 float4
+  // per thread), then wave w's 16 rows into registers
+  f16x8 qop[16];
+  {
+    constexpr int NV = 16;
+    const float4 *src = reinterpret_cast<const float4 *>(a.q + (int64_t)b * 64 * D);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float4 v[NV];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) v[u] = src[tid + (h * NV + u) * ATT_THREADS];
+      __builtin_amdgcn_sched_barrier(0);
+      if (h == 0) {
+        fetch_rows(st0);
+        if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int e = tid + (h * NV + u) * ATT_THREADS;        // head e/128, channels 4*(e%128)
+        f16x2 lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
+        *reinterpret_cast<u32x2 *>(s_v + (e >> 7) * ROW_HALVES + 4 * (e & 127)) =
+            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      }
+    }
+    __syncthreads();
+    const _Float16 *qrow = s_v + (16 * wv + n16) * ROW_HALVES + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < 16; ++kc) qop[kc] = *reinterpret_cast<const f16x8 *>(qrow + 32 * kc);
+  }
+
+  const int64_t n = clamp_len(a.seq_len[b] + a.len_add, a.limit);
+  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  CSA2_TS(1);
+  f32x4 acc[4][8];                        // [head tile][O^T tile 8*wv + t]
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_huge_valf();   // head 16*wv + n16 (log2 domain)
+  float l_run = 0.f;
+  const int r_src = n16 >> 2, q_src = n16 & 3;
+
+#pragma unroll 1
+  for (int st = st0; st < st1; ++st) {
+    __syncthreads();                      // q / previous stage fully consumed
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      const int pp = (tid >> 4) + 16 * k;
+      const int j = st * ATT_SP + pp;
+      const int32_t blk = blkv[k];
+      if ((j & 7) == 0 && i16 == 0 && blk >= nblk) raise_flag(FLAG_BAD_INDEX);
+      okv[k] = blk >= 0 && blk < nblk && (int64_t)blk * BLOCK + (j & 7) < n;
+      if (!okv[k]) { wr[k] = u32x4{0u, 0u, 0u, 0u}; scr[k] = 0u; }
+      const _Float16 s0 = (_Float16)e4m3_to_f32(scr[k] & 0xffu);
+      const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
+      const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
+      u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i16);
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) {
+        const f16x2 sv = dw < 2 ? sv0 : sv1;
+        f16x2 h0 = e2m1x2_to_f16<0>(wr[k][dw]) * sv;
+        f16x2 h1 = e2m1x2_to_f16<1>(wr[k][dw]) * sv;
+        f16x2 h2 = e2m1x2_to_f16<2>(wr[k][dw]) * sv;
+        f16x2 h3 = e2m1x2_to_f16<3>(wr[k][dw]) * sv;
+        dst[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                        __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
+      }
+      if (i16 == 0) s_ok[pp] = okv[k] ? 1 : 0;
+    }
+    if (st + 1 < st1) {
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) blkv[k] = nxt[k];
+      fetch_rows(st + 1);
+      if (st + 2 < st1) fetch_ids_into(st + 2, nxt);
+    }
+    __syncthreads();
+
+    CSA2_TS(2);
+    // ---- S^T of head tile wv over the 4 position tiles ----
+    f32x4 sacc[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) sacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 16; ++kc) {
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const f16x8 kop = *reinterpret_cast<const f16x8 *>(s_v + (16 * pt + n16) * ROW_HALVES + 8 * g + 32 * kc);
+        sacc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kc], sacc[pt], 0, 0, 0);
+      }
+    }
+    // lane (head n16 of tile wv, group g) holds positions 16*pt + 4g + r
+    float mx = -__builtin_huge_valf();
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sacc[pt][r] = s_ok[16 * pt + 4 * g + r] ? sacc[pt][r] * a.scale_log2 : -__builtin_huge_valf();
+        mx = fmaxf(mx, sacc[pt][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    float psum = 0.f, corr = 1.f;
+    _Float16 *prow = s_p + (16 * wv + n16) * P_STRIDE + 4 * g;
+    if (m_new == -__builtin_huge_valf()) {
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) *reinterpret_cast<u32x2 *>(prow + 16 * pt) = u32x2{0u, 0u};
+    } else {
+      corr = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        _Float16 ph[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ph[r] = (_Float16)__builtin_amdgcn_exp2f(sacc[pt][r] - m_new);
+          psum += (float)ph[r];
+        }
+        *reinterpret_cast<u32x2 *>(prow + 16 * pt) =
+            u32x2{__builtin_bit_cast(uint32_t, f16x2{ph[0], ph[1]}),
+                  __builtin_bit_cast(uint32_t, f16x2{ph[2], ph[3]})};
+      }
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+    if (g == 0) s_corr[16 * wv + n16] = corr;
+    __syncthreads();
+    CSA2_TS(3);
+
+    // ---- O^T tiles 8*wv .. 8*wv+7 of the four head tiles ----
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float c = s_corr[16 * h + n16];
+      if (c != 1.f) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[h][t] *= c;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int base = 32 * kk;
+      f16x8 pop[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const _Float16 *pr = s_p + (16 * h + n16) * P_STRIDE + base + 4 * g;
+        const u32x2 p_lo = *reinterpret_cast<const u32x2 *>(pr);
+        const u32x2 p_hi = *reinterpret_cast<const u32x2 *>(pr + 16);
+        pop[h] = __builtin_bit_cast(f16x8, u32x4{p_lo[0], p_lo[1], p_hi[0], p_hi[1]});
+      }
+      const _Float16 *v0 = s_v + (base + 4 * g + r_src) * ROW_HALVES + 32 * q_src;
+      const _Float16 *v1 = v0 + 16 * ROW_HALVES;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int ct = 8 * wv + t;
+        const int n0 = 128 * (ct >> 3) + 4 * (ct & 7);
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(v0 + n0));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(v1 + n0));
+        f16x8 vop = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[h], acc[h][t], 0, 0, 0);
+      }
+    }
+  }
+
+  CSA2_TS(4);
+  // each head's (max, sum) lives in the wave of its tile: share them
+  if (g == 0) { s_fin[0][16 * wv + n16] = m_run; s_fin[1][16 * wv + n16] = l_run; }
+  __syncthreads();
+  if (a.splits == 1) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float l = s_fin[1][16 * h + n16];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float *orow = a.out + ((int64_t)b * 64 + 16 * h + n16) * D + 32 * g;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int ct = 8 * wv + t;
+        *reinterpret_cast<float4 *>(orow + 128 * (ct >> 3) + 4 * (ct & 7)) =
+            float4{acc[h][t][0] * inv, acc[h][t][1] * inv, acc[h][t][2] * inv, acc[h][t][3] * inv};
+      }
+    }
+    CSA2_TS(5);
+    return;
+  }
+  // partials in the 16-head kernel's layout: slot (b, split, tile h)
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int64_t slot = ((int64_t)b * a.splits + split) * 4 + h;
+    f32x4 *po = reinterpret_cast<f32x4 *>(a.part_o + slot * (16 * D)) + lane;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) po[(8 * wv + t) * 64] = acc[h][t];
+  }
+  if (g == 0) {
+    const int64_t slot = ((int64_t)b * a.splits + split) * 4 + wv;
+    float *pm = a.part_ml + (slot * 16 + n16) * 2;
+    pm[0] = m_run;
+    pm[1] = l_run;
+  }
+  CSA2_TS(5);
+}
+
 struct CombineArgs {
   const float *part_o;
   const float *part_ml;
