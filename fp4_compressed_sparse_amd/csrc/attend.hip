@@ -438,22 +438,25 @@ template __global__ void attend_partial_kernel<true, true>(AttendArgs);
 // Many queries, each with its own selection: one workgroup takes one query
 // and a range of stages for all four 16-head tiles, so a gathered row is
 // dequantised once for 64 heads (the kernel above dequantises it once per
-// tile, and the FP4 convert then outweighs the matrix work).  Wave w owns
-// head tile w for S^T = K Q^T over the stage's 64 positions (its 16 query
-// rows stay in registers as fp16; K fragments come from LDS), so the
-// softmax of a head never leaves its wave; the stage's P of all 64 heads
-// and each head's rescale factor go through LDS, and wave w then
-// accumulates O^T channel tiles 8w..8w+7 of all four head tiles (each V^T
+// tile, and the FP4 convert then outweighs the matrix work).  Eight waves,
+// two per SIMD: wave w computes S^T = K Q^T for head tile w%4 over
+// positions 32*(w/4)..+31 of the stage (its 16 query rows stay in registers
+// as fp16; K fragments come from LDS); the two halves of a head exchange
+// their stage maxima through LDS and keep their own partial sums; P of all
+// 64 heads and each head's rescale factor go through LDS, and wave w then
+// accumulates O^T channel tiles 4w..4w+3 of all four head tiles (each V^T
 // fragment read once, used for the four tiles).
-__global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
+constexpr int ATT64_THREADS = 512;
+__global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
   extern __shared__ _Float16 s_v[];               // [ATT_SP][ROW_HALVES]; first holds q (64 heads)
   __shared__ _Float16 s_p[64 * P_STRIDE];         // P: [64 heads][64 positions]
-  __shared__ float s_corr[64], s_fin[2][64];
+  __shared__ float s_max[2][64], s_corr[64], s_fin[2][64];
   __shared__ uint8_t s_ok[ATT_SP];
 
   const int b = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;
+  const int ht = wv & 3, ph = wv >> 2;            // S: head tile, position half
   const int64_t cap_blocks = a.capacity / BLOCK;
   const int32_t *idx = a.idx + (int64_t)b * a.topk;
   const uint8_t *codes = a.codes + (int64_t)b * a.seq_stride * CODE_BYTES;
@@ -462,7 +465,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
   const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
   const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
 
-  constexpr int PASSES = ATT_SP / 16;
+  constexpr int PASSES = ATT_SP / 32;     // rows per thread per stage
   const int i16 = tid & 15;
   int32_t blkv[PASSES], nxt[PASSES];
   bool okv[PASSES];
@@ -471,16 +474,16 @@ __global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
   auto fetch_ids_into = [&](int st, int32_t (&dst)[PASSES]) {
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      const int j = st * ATT_SP + (tid >> 4) + 16 * k;
+      const int j = st * ATT_SP + (tid >> 4) + 32 * k;
       dst[k] = idx[min(j, total_pos - 1) >> 3];
     }
   };
   auto fetch_rows = [&](int st) {
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      if (st * ATT_SP + (tid >> 4) + 16 * k >= total_pos) blkv[k] = -1;
+      if (st * ATT_SP + (tid >> 4) + 32 * k >= total_pos) blkv[k] = -1;
       const bool ok = blkv[k] >= 0 && blkv[k] < cap_blocks;
-      const int64_t pos = ok ? (int64_t)blkv[k] * BLOCK + (((tid >> 4) + 16 * k) & 7) : 0;
+      const int64_t pos = ok ? (int64_t)blkv[k] * BLOCK + (((tid >> 4) + 32 * k) & 7) : 0;
       wr[k] = *reinterpret_cast<const u32x4 *>(codes + pos * CODE_BYTES + 16 * i16);
       scr[k] = *reinterpret_cast<const uint16_t *>(scales + pos * SCALE_BYTES + 2 * i16);
     }
@@ -490,32 +493,27 @@ __global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
   fetch_ids_into(st0, blkv);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- the query's 64 x 512 tile -> fp16 in LDS (two batches of 16 float4
-  // per thread), then wave w's 16 rows into registers
+  // ---- the query's 64 x 512 tile -> fp16 in LDS (one batch of 16 float4
+  // per thread), then wave w's 16 rows of head tile w%4 into registers
   f16x8 qop[16];
   {
     constexpr int NV = 16;
     const float4 *src = reinterpret_cast<const float4 *>(a.q + (int64_t)b * 64 * D);
+    float4 v[NV];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float4 v[NV];
+    for (int u = 0; u < NV; ++u) v[u] = src[tid + u * ATT64_THREADS];
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_rows(st0);
+    if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);
 #pragma unroll
-      for (int u = 0; u < NV; ++u) v[u] = src[tid + (h * NV + u) * ATT_THREADS];
-      __builtin_amdgcn_sched_barrier(0);
-      if (h == 0) {
-        fetch_rows(st0);
-        if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);
-      }
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const int e = tid + (h * NV + u) * ATT_THREADS;        // head e/128, channels 4*(e%128)
-        f16x2 lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
-        *reinterpret_cast<u32x2 *>(s_v + (e >> 7) * ROW_HALVES + 4 * (e & 127)) =
-            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-      }
+    for (int u = 0; u < NV; ++u) {
+      const int e = tid + u * ATT64_THREADS;                  // head e/128, channels 4*(e%128)
+      f16x2 lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
+      *reinterpret_cast<u32x2 *>(s_v + (e >> 7) * ROW_HALVES + 4 * (e & 127)) =
+          u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
     }
     __syncthreads();
-    const _Float16 *qrow = s_v + (16 * wv + n16) * ROW_HALVES + 8 * g;
+    const _Float16 *qrow = s_v + (16 * ht + n16) * ROW_HALVES + 8 * g;
 #pragma unroll
     for (int kc = 0; kc < 16; ++kc) qop[kc] = *reinterpret_cast<const f16x8 *>(qrow + 32 * kc);
   }
@@ -523,13 +521,13 @@ __global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
   const int64_t n = clamp_len(a.seq_len[b] + a.len_add, a.limit);
   const int64_t nblk = (n + BLOCK - 1) / BLOCK;
   CSA2_TS(1);
-  f32x4 acc[4][8];                        // [head tile][O^T tile 8*wv + t]
+  f32x4 acc[4][4];                        // [head tile][O^T tile 4*wv + t]
 #pragma unroll
   for (int h = 0; h < 4; ++h)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_huge_valf();   // head 16*wv + n16 (log2 domain)
-  float l_run = 0.f;
+    for (int t = 0; t < 4; ++t) acc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_huge_valf();   // head 16*ht + n16 (log2 domain), same in both halves
+  float l_run = 0.f;                      // this half's share of the head's sum
   const int r_src = n16 >> 2, q_src = n16 & 3;
 
 #pragma unroll 1
@@ -537,7 +535,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
     __syncthreads();                      // q / previous stage fully consumed
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      const int pp = (tid >> 4) + 16 * k;
+      const int pp = (tid >> 4) + 32 * k;
       const int j = st * ATT_SP + pp;
       const int32_t blk = blkv[k];
       if ((j & 7) == 0 && i16 == 0 && blk >= nblk) raise_flag(FLAG_BAD_INDEX);
@@ -568,65 +566,66 @@ __global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
     __syncthreads();
 
     CSA2_TS(2);
-    // ---- S^T of head tile wv over the 4 position tiles ----
-    f32x4 sacc[4];
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) sacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- S^T of head tile ht over position tiles 2*ph, 2*ph+1 ----
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kc = 0; kc < 16; ++kc) {
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const f16x8 kop = *reinterpret_cast<const f16x8 *>(s_v + (16 * pt + n16) * ROW_HALVES + 8 * g + 32 * kc);
-        sacc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kc], sacc[pt], 0, 0, 0);
+      for (int u = 0; u < 2; ++u) {
+        const f16x8 kop = *reinterpret_cast<const f16x8 *>(
+            s_v + (32 * ph + 16 * u + n16) * ROW_HALVES + 8 * g + 32 * kc);
+        sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kc], sacc[u], 0, 0, 0);
       }
     }
-    // lane (head n16 of tile wv, group g) holds positions 16*pt + 4g + r
+    // lane (head n16 of tile ht, group g) holds positions 32*ph + 16*u + 4g + r
     float mx = -__builtin_huge_valf();
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sacc[pt][r] = s_ok[16 * pt + 4 * g + r] ? sacc[pt][r] * a.scale_log2 : -__builtin_huge_valf();
-        mx = fmaxf(mx, sacc[pt][r]);
+        sacc[u][r] = s_ok[32 * ph + 16 * u + 4 * g + r] ? sacc[u][r] * a.scale_log2 : -__builtin_huge_valf();
+        mx = fmaxf(mx, sacc[u][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+    if (g == 0) s_max[ph][16 * ht + n16] = mx;
+    __syncthreads();
+    const float m_new = fmaxf(m_run, fmaxf(s_max[0][16 * ht + n16], s_max[1][16 * ht + n16]));
     float psum = 0.f, corr = 1.f;
-    _Float16 *prow = s_p + (16 * wv + n16) * P_STRIDE + 4 * g;
+    _Float16 *prow = s_p + (16 * ht + n16) * P_STRIDE + 32 * ph + 4 * g;
     if (m_new == -__builtin_huge_valf()) {
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) *reinterpret_cast<u32x2 *>(prow + 16 * pt) = u32x2{0u, 0u};
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x2 *>(prow + 16 * u) = u32x2{0u, 0u};
     } else {
       corr = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        _Float16 ph[4];
+      for (int u = 0; u < 2; ++u) {
+        _Float16 pv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          ph[r] = (_Float16)__builtin_amdgcn_exp2f(sacc[pt][r] - m_new);
-          psum += (float)ph[r];
+          pv[r] = (_Float16)__builtin_amdgcn_exp2f(sacc[u][r] - m_new);
+          psum += (float)pv[r];
         }
-        *reinterpret_cast<u32x2 *>(prow + 16 * pt) =
-            u32x2{__builtin_bit_cast(uint32_t, f16x2{ph[0], ph[1]}),
-                  __builtin_bit_cast(uint32_t, f16x2{ph[2], ph[3]})};
+        *reinterpret_cast<u32x2 *>(prow + 16 * u) =
+            u32x2{__builtin_bit_cast(uint32_t, f16x2{pv[0], pv[1]}),
+                  __builtin_bit_cast(uint32_t, f16x2{pv[2], pv[3]})};
       }
     }
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
     l_run = l_run * corr + psum;
     m_run = m_new;
-    if (g == 0) s_corr[16 * wv + n16] = corr;
+    if (g == 0 && ph == 0) s_corr[16 * ht + n16] = corr;
     __syncthreads();
     CSA2_TS(3);
 
-    // ---- O^T tiles 8*wv .. 8*wv+7 of the four head tiles ----
+    // ---- O^T tiles 4*wv .. 4*wv+3 of the four head tiles ----
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const float c = s_corr[16 * h + n16];
       if (c != 1.f) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[h][t] *= c;
+        for (int t = 0; t < 4; ++t) acc[h][t] *= c;
       }
     }
 #pragma unroll
@@ -643,8 +642,8 @@ __global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
       const _Float16 *v0 = s_v + (base + 4 * g + r_src) * ROW_HALVES + 32 * q_src;
       const _Float16 *v1 = v0 + 16 * ROW_HALVES;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int ct = 8 * wv + t;
+      for (int t = 0; t < 4; ++t) {
+        const int ct = 4 * wv + t;
         const int n0 = 128 * (ct >> 3) + 4 * (ct & 7);
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4 *)(v0 + n0));
@@ -659,18 +658,19 @@ __global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
   }
 
   CSA2_TS(4);
-  // each head's (max, sum) lives in the wave of its tile: share them
-  if (g == 0) { s_fin[0][16 * wv + n16] = m_run; s_fin[1][16 * wv + n16] = l_run; }
+  // a head's max is the same in both halves; its sum is the two halves' sum
+  if (g == 0) s_fin[ph][16 * ht + n16] = l_run;
+  if (g == 0 && ph == 0) s_max[0][16 * ht + n16] = m_run;
   __syncthreads();
   if (a.splits == 1) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float l = s_fin[1][16 * h + n16];
+      const float l = s_fin[0][16 * h + n16] + s_fin[1][16 * h + n16];
       const float inv = l > 0.f ? 1.f / l : 0.f;
       float *orow = a.out + ((int64_t)b * 64 + 16 * h + n16) * D + 32 * g;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int ct = 8 * wv + t;
+      for (int t = 0; t < 4; ++t) {
+        const int ct = 4 * wv + t;
         *reinterpret_cast<float4 *>(orow + 128 * (ct >> 3) + 4 * (ct & 7)) =
             float4{acc[h][t][0] * inv, acc[h][t][1] * inv, acc[h][t][2] * inv, acc[h][t][3] * inv};
       }
@@ -684,13 +684,13 @@ __global__ void __launch_bounds__(ATT_THREADS) attend64_kernel(AttendArgs a) {
     const int64_t slot = ((int64_t)b * a.splits + split) * 4 + h;
     f32x4 *po = reinterpret_cast<f32x4 *>(a.part_o + slot * (16 * D)) + lane;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) po[(8 * wv + t) * 64] = acc[h][t];
+    for (int t = 0; t < 4; ++t) po[(4 * wv + t) * 64] = acc[h][t];
   }
-  if (g == 0) {
-    const int64_t slot = ((int64_t)b * a.splits + split) * 4 + wv;
+  if (g == 0 && ph == 0) {
+    const int64_t slot = ((int64_t)b * a.splits + split) * 4 + ht;
     float *pm = a.part_ml + (slot * 16 + n16) * 2;
-    pm[0] = m_run;
-    pm[1] = l_run;
+    pm[0] = s_max[0][16 * ht + n16];
+    pm[1] = s_fin[0][16 * ht + n16] + s_fin[1][16 * ht + n16];
   }
   CSA2_TS(5);
 }

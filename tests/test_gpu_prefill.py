@@ -50,15 +50,28 @@ def _run(n, qpos, heads, topk, seed):
 
 
 def test_prefill_chunk_few_queries_split_k():
-    # 5 queries x 4 head tiles: the selection is split over workgroups and merged
+    # 5 queries of 64 heads: each query's selection is split over 32
+    # workgroups (all four head tiles each) and merged
     n = 9000
     _run(n, [n - 5, n - 4, n - 3, n - 2, n - 1], 64, 256, 1)
 
 
-def test_prefill_chunk_many_queries_one_split():
-    # 300 queries x 4 head tiles: one workgroup per (query, head tile), no merge
+def test_prefill_chunk_many_queries_two_splits():
+    # 300 queries of 64 heads: two workgroups per query, merged
     n = 12000
     _run(n, np.arange(n - 300, n), 64, 256, 2)
+
+
+def test_prefill_chunk_many_queries_one_split():
+    # 520 queries of 64 heads: one workgroup per query normalises in-kernel
+    n = 6000
+    _run(n, np.sort(np.random.default_rng(9).choice(n, 520, replace=False)), 64, 40, 4)
+
+
+def test_prefill_16_heads_many_queries_one_split():
+    # 16 heads, 600 queries: the per-head-tile kernel with one split
+    n = 5000
+    _run(n, np.arange(n - 600, n), 16, 24, 5)
 
 
 def test_prefill_ragged_positions_16_heads():
