@@ -283,7 +283,7 @@ def prefill_bench(args):
         "config": {"workload": "prefill-attend-1m", "queries": T, "context": n, "heads": H,
                    "topk_blocks": K, "attended_positions": positions,
                    "median_event_launch_us": round(launch_s * 1e6, 2)},
-        "roofline": {"bound": "mfma", "kernel": "attend_partial_kernel (one split per query and head tile)",
+        "roofline": {"bound": "mfma", "kernel": "attend64_kernel (all 64 heads of a query per workgroup, one split)",
                      "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4), "traffic": None,
                      "algorithmic_flops_per_launch": flops, "gathered_bytes_per_launch": gather},
