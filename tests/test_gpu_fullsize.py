@@ -177,3 +177,91 @@ def test_decoder20_1m_full_size_sampled():
         log(f"layer {l}: attention error {err:.2e} over {pos.size} positions")
         assert err <= ATT_TOL, (l, err)
     _CHUNKS.clear()
+
+
+def test_decoder20_1m_full_size_with_local_branch():
+    """The same 20-layer step at 1,048,576 positions with a 128-position FP8
+    window on every layer (ring bytes from the oracle's quantiser): the
+    appended SWA rows are bit-equal to the oracle's, the selections are the
+    top of their pool scores as before, and two layers' outputs match the
+    oracle's joint softmax over the selected and the window positions."""
+    from oracle import swa as S
+    require_gpu()
+    _CHUNKS.clear()
+    w = W.WORKLOADS[3]
+    n0 = int(w.context)
+    n = n0 + 1
+    cap = (n + 7) // 8 * 8
+    win = 128
+    log(f"building 4 caches of {n0} positions and 20 rings of {win}")
+    caches = bench.build_caches(w, np.array([n0]), cap, log_every=1000)
+    for c in caches:
+        c.max_len = n
+    L, H, K, P = len(w.pattern), w.heads, w.topk, w.pool
+    lc = w.layer_caches()
+    rings, wrows = [], []
+    for l in range(L):
+        rows = W.swa_rows(w.wid, l, 0, n0 - win, win)                 # positions n0-win .. n0-1
+        c8, s8 = S.quantize_fp8_rows(rows)
+        ring = csa2.SwaCache(1, win)
+        slots = np.arange(n0 - win, n0) % win
+        codes = np.zeros((win, 512), dtype=np.uint8)
+        scales = np.zeros(win, dtype=np.float32)
+        codes[slots], scales[slots] = c8, s8
+        ring.codes[0].copy_(torch.from_numpy(codes))
+        ring.scales[0].copy_(torch.from_numpy(scales))
+        ring.seq_len.fill_(n0)
+        rings.append(ring)
+        wrows.append(rows)
+    qs = [W.queries(w.wid, l, 0, 1, H) for l in range(L)]
+    step_rows = np.stack([W.append_rows(w.wid, c, 0, 1) for c in range(w.n_caches)])
+    srows = np.stack([W.swa_append_rows(w.wid, l, 0, 1) for l in range(L)])   # [L, 1, 512]
+    qt = [torch.from_numpy(q).cuda() for q in qs]
+    outs = [torch.zeros((1, H, 512), dtype=torch.float32, device="cuda") for _ in range(L)]
+    idxs = []
+    for m in w.pattern:
+        idxs.append(idxs[-1] if m == 2 else torch.full((1, K), -9, dtype=torch.int32, device="cuda"))
+    pool = torch.full((1, P), -9, dtype=torch.int32, device="cuda")
+    ws = csa2.workspace(1, H, n, P, K)
+    st = [torch.from_numpy(srows[l]).cuda() for l in range(L)]
+    layers = [(m, lc[l], qt[l], outs[l], idxs[l], rings[l], st[l]) for l, m in enumerate(w.pattern)]
+    csa2.decode_step(caches, layers, H, K, P, w.scale, ws, pool_out=pool,
+                     new_rows=torch.from_numpy(step_rows).cuda())
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    log("decode step with local branch done")
+
+    for l in range(L):
+        assert int(rings[l].seq_len[0]) == n
+        c8, s8 = S.quantize_fp8_rows(srows[l])
+        assert np.array_equal(rings[l].codes[0, n0 % win].cpu().numpy(), c8[0])
+        assert rings[l].scales[0, n0 % win].item() == s8[0]
+    log("appended SWA rows bit-equal")
+
+    p = pool.cpu().numpy()[0]
+    pool_t = pool.clone()
+    for l, m in enumerate(w.pattern):
+        if m == 2:
+            assert np.array_equal(idxs[l].cpu().numpy(), idxs[l - 1].cpu().numpy())
+            continue
+        sl = torch.zeros((1, P), dtype=torch.float32, device="cuda")
+        csa2.block_scores(caches[lc[l]], qt[l], sl, cand=pool_t)
+        assert _top_keys_ok(p, sl.cpu().numpy()[0], idxs[l].cpu().numpy()[0]), l
+
+    for l in (0, L - 1):
+        idx = idxs[l].cpu().numpy()[0]
+        pos = gather_positions(idx, n)
+        codes, scales = quantize_rows(_rows(w.wid, lc[l], pos, n0, step_rows[:, 0]))
+        kept = idx[idx >= 0]
+        ccodes = np.zeros((BLOCK * kept.size, 256), dtype=np.uint8)
+        cscales = np.zeros((BLOCK * kept.size, 32), dtype=np.uint8)
+        ccodes[:pos.size] = codes
+        cscales[:pos.size] = scales
+        # the window by position: n0-win+1 .. n0 (the appended row last)
+        wc, wsc = S.quantize_fp8_rows(np.concatenate([wrows[l][1:], srows[l]], axis=0))
+        ref = S.attend_with_window(ccodes, cscales, pos.size, qs[l][0], np.arange(kept.size), w.scale,
+                                   wc, wsc, win, win)
+        err = normwise_err(outs[l].cpu().numpy()[0][None], ref[None])
+        log(f"layer {l}: attention with window error {err:.2e} over {pos.size} + {win} positions")
+        assert err <= ATT_TOL, (l, err)
+    _CHUNKS.clear()
