@@ -530,7 +530,7 @@ csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, 
   aa.out = out;
   const size_t lds = (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16);
   if (heads == 64)
-    attend64_kernel<<<dim3(L.att_splits, n_q), ATT64_THREADS, lds, s>>>(aa);
+    attend64_kernel<<<dim3(L.att_splits, n_q), ATT64_THREADS, ATT64_LDS, s>>>(aa);
   else
     attend_partial_kernel<false, false><<<dim3(L.att_splits * (heads / 16), n_q), ATT_THREADS, lds, s>>>(aa);
   if (csa2_status st = launched("prefill attend")) return st;

@@ -445,13 +445,16 @@ template __global__ void attend_partial_kernel<true, true>(AttendArgs);
 // their stage maxima through LDS and keep their own partial sums; P of all
 // 64 heads and each head's rescale factor go through LDS, and wave w then
 // accumulates O^T channel tiles 4w..4w+3 of all four head tiles (each V^T
-// fragment read once, used for the four tiles).
+// fragment read once, used for the four tiles).  The stage rows are double
+// buffered: the next stage is dequantised right after this stage's S
+// matrix instructions are issued, so the convert overlaps them.
 constexpr int ATT64_THREADS = 512;
+constexpr size_t ATT64_LDS = (size_t)2 * ATT_SP * ROW_HALVES * sizeof(_Float16);
 __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
-  extern __shared__ _Float16 s_v[];               // [ATT_SP][ROW_HALVES]; first holds q (64 heads)
+  extern __shared__ _Float16 s_v[];               // [2][ATT_SP][ROW_HALVES]; first holds q (64 heads)
   __shared__ _Float16 s_p[64 * P_STRIDE];         // P: [64 heads][64 positions]
   __shared__ float s_max[2][64], s_corr[64], s_fin[2][64];
-  __shared__ uint8_t s_ok[ATT_SP];
+  __shared__ uint8_t s_ok[2][ATT_SP];
 
   const int b = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -468,7 +471,6 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
   constexpr int PASSES = ATT_SP / 32;     // rows per thread per stage
   const int i16 = tid & 15;
   int32_t blkv[PASSES], nxt[PASSES];
-  bool okv[PASSES];
   u32x4 wr[PASSES];
   uint32_t scr[PASSES];
   auto fetch_ids_into = [&](int st, int32_t (&dst)[PASSES]) {
@@ -520,6 +522,45 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
 
   const int64_t n = clamp_len(a.seq_len[b] + a.len_add, a.limit);
   const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+
+  // dequantise stage st (its rows are in wr/scr) into buffer `buf`, then
+  // request the rows of stage st + 1 (ids in nxt) and the ids of st + 2
+  auto dequant_and_fetch = [&](int st, int buf) {
+    _Float16 *sv = s_v + buf * (ATT_SP * ROW_HALVES);
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      const int pp = (tid >> 4) + 32 * k;
+      const int j = st * ATT_SP + pp;
+      const int32_t blk = blkv[k];
+      if ((j & 7) == 0 && i16 == 0 && blk >= nblk) raise_flag(FLAG_BAD_INDEX);
+      const bool ok = blk >= 0 && blk < nblk && (int64_t)blk * BLOCK + (j & 7) < n;
+      if (!ok) { wr[k] = u32x4{0u, 0u, 0u, 0u}; scr[k] = 0u; }
+      const _Float16 s0 = (_Float16)e4m3_to_f32(scr[k] & 0xffu);
+      const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
+      const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
+      u32x4 *dst = reinterpret_cast<u32x4 *>(sv + pp * ROW_HALVES + 32 * i16);
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) {
+        const f16x2 svs = dw < 2 ? sv0 : sv1;
+        f16x2 h0 = e2m1x2_to_f16<0>(wr[k][dw]) * svs;
+        f16x2 h1 = e2m1x2_to_f16<1>(wr[k][dw]) * svs;
+        f16x2 h2 = e2m1x2_to_f16<2>(wr[k][dw]) * svs;
+        f16x2 h3 = e2m1x2_to_f16<3>(wr[k][dw]) * svs;
+        dst[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                        __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
+      }
+      if (i16 == 0) s_ok[buf][pp] = ok ? 1 : 0;
+    }
+    if (st + 1 < st1) {
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) blkv[k] = nxt[k];
+      fetch_rows(st + 1);
+      if (st + 2 < st1) fetch_ids_into(st + 2, nxt);
+    }
+  };
+  __syncthreads();                        // every wave has its query rows: buffer 0 is free
+  dequant_and_fetch(st0, 0);
+
   CSA2_TS(1);
   f32x4 acc[4][4];                        // [head tile][O^T tile 4*wv + t]
 #pragma unroll
@@ -532,39 +573,9 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
 
 #pragma unroll 1
   for (int st = st0; st < st1; ++st) {
-    __syncthreads();                      // q / previous stage fully consumed
-#pragma unroll
-    for (int k = 0; k < PASSES; ++k) {
-      const int pp = (tid >> 4) + 32 * k;
-      const int j = st * ATT_SP + pp;
-      const int32_t blk = blkv[k];
-      if ((j & 7) == 0 && i16 == 0 && blk >= nblk) raise_flag(FLAG_BAD_INDEX);
-      okv[k] = blk >= 0 && blk < nblk && (int64_t)blk * BLOCK + (j & 7) < n;
-      if (!okv[k]) { wr[k] = u32x4{0u, 0u, 0u, 0u}; scr[k] = 0u; }
-      const _Float16 s0 = (_Float16)e4m3_to_f32(scr[k] & 0xffu);
-      const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
-      const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
-      u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i16);
-#pragma unroll
-      for (int dw = 0; dw < 4; ++dw) {
-        const f16x2 sv = dw < 2 ? sv0 : sv1;
-        f16x2 h0 = e2m1x2_to_f16<0>(wr[k][dw]) * sv;
-        f16x2 h1 = e2m1x2_to_f16<1>(wr[k][dw]) * sv;
-        f16x2 h2 = e2m1x2_to_f16<2>(wr[k][dw]) * sv;
-        f16x2 h3 = e2m1x2_to_f16<3>(wr[k][dw]) * sv;
-        dst[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
-                        __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
-      }
-      if (i16 == 0) s_ok[pp] = okv[k] ? 1 : 0;
-    }
-    if (st + 1 < st1) {
-#pragma unroll
-      for (int k = 0; k < PASSES; ++k) blkv[k] = nxt[k];
-      fetch_rows(st + 1);
-      if (st + 2 < st1) fetch_ids_into(st + 2, nxt);
-    }
-    __syncthreads();
-
+    const int cur = (st - st0) & 1;
+    const _Float16 *sv = s_v + cur * (ATT_SP * ROW_HALVES);
+    __syncthreads();                      // stage st is in buffer cur; buffer cur^1 is free
     CSA2_TS(2);
     // ---- S^T of head tile ht over position tiles 2*ph, 2*ph+1 ----
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -573,17 +584,19 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const f16x8 kop = *reinterpret_cast<const f16x8 *>(
-            s_v + (32 * ph + 16 * u + n16) * ROW_HALVES + 8 * g + 32 * kc);
+            sv + (32 * ph + 16 * u + n16) * ROW_HALVES + 8 * g + 32 * kc);
         sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kc], sacc[u], 0, 0, 0);
       }
     }
+    // the next stage's rows, while the matrix instructions run
+    if (st + 1 < st1) dequant_and_fetch(st + 1, cur ^ 1);
     // lane (head n16 of tile ht, group g) holds positions 32*ph + 16*u + 4g + r
     float mx = -__builtin_huge_valf();
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sacc[u][r] = s_ok[32 * ph + 16 * u + 4 * g + r] ? sacc[u][r] * a.scale_log2 : -__builtin_huge_valf();
+        sacc[u][r] = s_ok[cur][32 * ph + 16 * u + 4 * g + r] ? sacc[u][r] * a.scale_log2 : -__builtin_huge_valf();
         mx = fmaxf(mx, sacc[u][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -639,7 +652,7 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
         const u32x2 p_hi = *reinterpret_cast<const u32x2 *>(pr + 16);
         pop[h] = __builtin_bit_cast(f16x8, u32x4{p_lo[0], p_lo[1], p_hi[0], p_hi[1]});
       }
-      const _Float16 *v0 = s_v + (base + 4 * g + r_src) * ROW_HALVES + 32 * q_src;
+      const _Float16 *v0 = sv + (base + 4 * g + r_src) * ROW_HALVES + 32 * q_src;
       const _Float16 *v1 = v0 + 16 * ROW_HALVES;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
