@@ -177,9 +177,12 @@ int grid_for(int64_t items, int batch, int target) {
 
 // ---- launches (arguments already validated) -----------------------------
 
+// qbar_ready: the query sum is already in the workspace (computed in the
+// decode step's append launch for this same query).
 csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, int32_t R,
                             int32_t *first_out, int32_t topk2, int32_t *idx_out, void *ws,
-                            const Layout &L, hipStream_t s, float *pool_scores = nullptr) {
+                            const Layout &L, hipStream_t s, float *pool_scores = nullptr,
+                            bool qbar_ready = false) {
   const int B = kv->batch;
   const int64_t nblk_grid = ceil_div(kv->max_len, BLOCK);
   ScanArgs sa;
@@ -190,8 +193,10 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
   sa.ctrl = at<Ctrl>(ws, L.ctrl); sa.hist = at<uint32_t>(ws, L.hist);
   sa.R = R; sa.fill_invalid = 0;
   sa.qbar = at<float>(ws, L.qbar);
-  qbar_kernel<<<B, SCAN_THREADS, 0, s>>>(q, heads, at<float>(ws, L.qbar));
-  if (csa2_status st = launched("qbar")) return st;
+  if (!qbar_ready) {
+    qbar_kernel<<<B, SCAN_THREADS, 0, s>>>(q, heads, at<float>(ws, L.qbar));
+    if (csa2_status st = launched("qbar")) return st;
+  }
   // a workgroup scores 8 blocks per round (4 waves x 2); 1,536 workgroups
   // fill the 256 compute units at 6 waves per SIMD
   const int64_t rounds = ceil_div(nblk_grid > 0 ? nblk_grid : 1, 8);
@@ -381,7 +386,7 @@ csa2_status csa2_append_kv(const csa2_kv *kv, const float *x, void *stream) {
   aa.codes[0] = kv->codes; aa.scales[0] = kv->scales; aa.seq_len[0] = kv->seq_len; aa.capacity[0] = kv->capacity;
   SwaRings rr;
   memset(&rr, 0, sizeof rr);
-  append_kernel<<<dim3(kv->batch, 1), 128, 0, as_stream(stream)>>>(aa, rr, x, kv->batch, 1);
+  append_kernel<<<dim3(kv->batch, 1), 128, 0, as_stream(stream)>>>(aa, rr, x, kv->batch, 1, 0, QbarJob{});
   return launched("append");
 }
 
@@ -416,7 +421,8 @@ csa2_status csa2_swa_append(const csa2_swa *swa, const float *x, void *stream) {
   memset(&rr, 0, sizeof rr);
   rr.codes[0] = swa->codes; rr.scales[0] = swa->scales; rr.seq_len[0] = swa->seq_len;
   rr.rows[0] = x; rr.window[0] = swa->window;
-  append_kernel<<<dim3(swa->batch, 1), 128, 0, as_stream(stream)>>>(aa, rr, nullptr, swa->batch, 0);
+  append_kernel<<<dim3(swa->batch, 1), 128, 0, as_stream(stream)>>>(aa, rr, nullptr, swa->batch, 0, 1,
+                                                                     QbarJob{});
   return launched("swa append");
 }
 
@@ -613,6 +619,7 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
   if (csa2_status e = device_ready()) return e;
   hipStream_t s = as_stream(stream);
 
+  bool qbar_ready = false;                // layer 0's query sum is in the workspace
   if (st->new_rows || n_rings) {
     // one launch: the Full caches' rows, then every layer's SWA row
     AppendArgs aa;
@@ -632,8 +639,11 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
       rr.rows[nr] = ly.swa_row; rr.window[nr] = ly.swa->window;
       ++nr;
     }
-    append_kernel<<<dim3(B, nc + nr), 128, 0, s>>>(aa, rr, st->new_rows, B, nc);
+    // the first layer (Full) scans all blocks: its query sum rides along
+    QbarJob qj{st->layers[0].q, st->heads, at<float>(st->ws, L.qbar)};
+    append_kernel<<<dim3(B, nc + nr + 1), 128, 0, s>>>(aa, rr, st->new_rows, B, nc, nr, qj);
     if (csa2_status e = launched("append")) return e;
+    qbar_ready = true;
   }
   bool pool_built = false;
   const int32_t *prev_idx = nullptr;
@@ -654,7 +664,8 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
       // finishing workgroup, no re-read of the selection)
       float *cs = at<float>(st->ws, L.cscores);
       if (!pool_built) {
-        e = run_scan_select(kv, ly.q, st->heads, st->pool, st->pool_out, 0, nullptr, st->ws, L, s, cs);
+        e = run_scan_select(kv, ly.q, st->heads, st->pool, st->pool_out, 0, nullptr, st->ws, L, s, cs,
+                            qbar_ready && l == 0);
         pool_built = true;
       } else {
         e = run_rescore(kv, ly.q, st->heads, st->pool_out, st->pool, 0, nullptr, cs, st->pool, nullptr, s);
@@ -666,13 +677,15 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
       prev_idx = ly.idx;
       continue;
     } else if (st->pool > 0 && !pool_built) {
-      e = run_scan_select(kv, ly.q, st->heads, st->pool, st->pool_out, st->topk, ly.idx, st->ws, L, s);
+      e = run_scan_select(kv, ly.q, st->heads, st->pool, st->pool_out, st->topk, ly.idx, st->ws, L, s,
+                          nullptr, qbar_ready && l == 0);
       pool_built = true;
     } else if (st->pool > 0) {
       e = run_rescore(kv, ly.q, st->heads, st->pool_out, st->pool, st->topk, ly.idx,
                       at<float>(st->ws, L.scores), L.score_stride, at<Ctrl>(st->ws, L.ctrl), s);
     } else {
-      e = run_scan_select(kv, ly.q, st->heads, st->topk, ly.idx, 0, nullptr, st->ws, L, s);
+      e = run_scan_select(kv, ly.q, st->heads, st->topk, ly.idx, 0, nullptr, st->ws, L, s, nullptr,
+                          qbar_ready && l == 0);
     }
     if (e) return e;
     e = run_attend(kv, ly.q, st->heads, ly.idx, st->topk, st->scale, ly.out, st->ws, L, s, nullptr,

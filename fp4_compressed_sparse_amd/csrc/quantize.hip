@@ -217,13 +217,48 @@ struct SwaRings {
   int32_t window[MAX_SWA_RINGS];
 };
 
-// grid (batch, n_caches + n_rings), 128 threads.  y < n_caches:
-// x[y][b][512] -> position seq_len[b] of cache y.  Otherwise ring
-// y - n_caches: rows[b] -> position seq_len[b], slot seq_len[b] % window.
+// The indexer's query sum of one layer, computed in the same launch as the
+// appends (it only reads the query): Qbar[b] = heads added in order.
+struct QbarJob {
+  const float *q;           // [batch][heads][512]; NULL = none
+  int32_t heads;
+  float *qbar;              // [batch][512]
+};
+
+// grid (batch, n_caches + n_rings [+ 1]), 128 threads.  y < n_caches:
+// x[y][b][512] -> position seq_len[b] of cache y.  Then ring y - n_caches:
+// rows[b] -> position seq_len[b], slot seq_len[b] % window.  A last row of
+// workgroups (when qj.q is set) sums the query heads of sequence b.
 __global__ void __launch_bounds__(128) append_kernel(AppendArgs a, SwaRings r, const float *__restrict__ x,
-                                                     int32_t batch, int32_t n_caches) {
+                                                     int32_t batch, int32_t n_caches, int32_t n_rings,
+                                                     QbarJob qj) {
   const int b = blockIdx.x, c = blockIdx.y;
   const int q = threadIdx.x;
+  if (c >= n_caches + n_rings) {
+    // channels 4q..4q+3, heads in order, 16 heads per batch of loads
+    constexpr int HB = 16;
+    const float4 *qp = reinterpret_cast<const float4 *>(qj.q + (int64_t)b * qj.heads * D) + q;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int h0 = 0; h0 < qj.heads; h0 += HB) {
+      float4 v[HB];
+#pragma unroll
+      for (int j = 0; j < HB; ++j) v[j] = qp[(int64_t)min(h0 + j, qj.heads - 1) * (D / 4)];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        const int h = h0 + j;
+        if (h == 0) {
+          acc = v[j];
+        } else if (h < qj.heads) {
+          acc.x = acc.x + v[j].x; acc.y = acc.y + v[j].y;
+          acc.z = acc.z + v[j].z; acc.w = acc.w + v[j].w;
+        }
+      }
+    }
+    if (!finite4(acc)) raise_flag(FLAG_NONFINITE_Q);
+    reinterpret_cast<float4 *>(qj.qbar + (int64_t)b * D)[q] = acc;
+    return;
+  }
   if (c >= n_caches) {
     __shared__ uint32_t s_red[2];
     const int i = c - n_caches;
