@@ -25,6 +25,9 @@
 //    the long input" and "same notes, many layers"] is appended as further
 //    stages of the same softmax; its rows are dequantised as e4m3 * scale
 //    rounded to fp16 (rows need |x| <= 65504).
+//  * Prefill side with 64 heads (many queries, each with its own
+//    selection): attend64_kernel below covers all four head tiles of a
+//    query in one workgroup, so each gathered row is dequantised once.
 //
 // MFMA 16x16x32 f16 lane layout (checked on gfx950): A row = lane%16 with
 // k = 8*(lane/16)..+7; B column = lane%16, same k; C column = lane%16,
@@ -51,7 +54,7 @@ struct AttendArgs {
   int32_t topk;
   int32_t heads;            // 16, 32 or 64
   float scale_log2;         // scale * log2(e)
-  int32_t n_stages;         // ceil(topk*8 / ATT_SP)
+  int32_t n_stages;         // n_sparse + ceil(window / ATT_SP)
   int32_t splits;           // workgroups per (sequence, head tile)
   float *part_o;            // [batch][splits][heads/16][32 tiles][64 lanes][4]: O^T accumulators
                             // in lane order (contiguous stores)
