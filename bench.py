@@ -110,13 +110,15 @@ def build_caches(w, lengths, capacity, log_every=8):
     return caches
 
 
-def cpu_baseline(w):
+def cpu_baseline(w, window=0):
     """The oracle's decode step timed on the host (1 thread), on two bounded
-    contexts, extrapolated linearly in context to the workload's context."""
+    contexts, extrapolated linearly in context to the workload's context
+    (window > 0: every layer with its local branch, as the GPU step)."""
     import numpy as np
 
     import workloads as W
     from oracle.step import Cache, decode_step
+    from oracle.swa import SwaCache
 
     try:
         from threadpoolctl import threadpool_limits
@@ -134,11 +136,20 @@ def cpu_baseline(w):
         lc = w.layer_caches()
         layers = [(m, lc[l], W.queries(w.wid, l, 0, 1, w.heads)) for l, m in enumerate(w.pattern)]
         rows = np.stack([W.append_rows(w.wid, c, 0, 1) for c in range(w.n_caches)])
+        swa = srows = None
+        if window:
+            swa = []
+            for l in range(len(w.pattern)):
+                sw = SwaCache(1, n + 1)
+                sw.write(0, n - window, W.swa_rows(w.wid, l, 0, n - window, window))
+                sw.seq_len[0] = n
+                swa.append(sw)
+            srows = np.stack([W.swa_append_rows(w.wid, l, 0, 1) for l in range(len(w.pattern))])
         import contextlib
         ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
         with ctx:
             t0 = time.perf_counter()
-            decode_step(caches, layers, rows, w.topk, w.pool, w.scale)
+            decode_step(caches, layers, rows, w.topk, w.pool, w.scale, swa=swa, swa_rows=srows, window=window)
             times.append(time.perf_counter() - t0)
         log(f"cpu oracle: context {n}: {times[-1]:.2f} s per step")
     (n1, n2), (t1, t2) = samples, times
@@ -149,7 +160,8 @@ def cpu_baseline(w):
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"one decode step of the same 20-layer pattern (64 heads, pool 2048, top-256, batch 1) "
+        "sample": (f"one decode step of the same 20-layer pattern (64 heads, pool 2048, top-256, batch 1"
+                   + (f", a {window}-position window on every layer" if window else "") + ") "
                    f"at contexts {n1} and {n2}: {t1:.2f} s and {t2:.2f} s on 1 host thread; "
                    f"extrapolated linearly in context to {w.context} positions: {t_full:.1f} s per step"),
     }
@@ -491,7 +503,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(w, args.swa)
     print(json.dumps(result), flush=True)
 
 
