@@ -419,14 +419,16 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     return;
   }
   // ---- partial of this (sequence, split, head tile) ----
+  // streaming stores: the partials are read once, by the combine kernel
+  // (measured: 4 us per 20-layer step less than ordinary stores)
   const int64_t slot = ((int64_t)b * a.splits + split) * HT + ht;
   f32x4 *po = reinterpret_cast<f32x4 *>(a.part_o + slot * (16 * D)) + lane;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) po[(8 * wv + t) * 64] = acc[t];
+  for (int t = 0; t < 8; ++t) __builtin_nontemporal_store(acc[t], &po[(8 * wv + t) * 64]);
   if (wv == 0 && g == 0) {
     float *pm = a.part_ml + (slot * 16 + n16) * 2;
-    pm[0] = m_run;
-    pm[1] = l_run;
+    __builtin_nontemporal_store(m_run, &pm[0]);
+    __builtin_nontemporal_store(l_run, &pm[1]);
   }
   CSA2_TS(5);
 }
