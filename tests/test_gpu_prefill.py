@@ -78,3 +78,9 @@ def test_prefill_ragged_positions_16_heads():
     # early queries with fewer blocks than topk (-1 padding), partial own blocks
     qpos = [0, 1, 7, 8, 63, 64, 200, 511, 1000, 4093, 4094, 4095]
     _run(4096, qpos, 16, 64, 3)
+
+
+def test_prefill_32_heads_split_k():
+    # 32 heads (two head tiles per query in the per-tile kernel), a few queries, split over workgroups
+    n = 7000
+    _run(n, [100, 3000, 6999, 6998, 5555, 17], 32, 128, 6)
