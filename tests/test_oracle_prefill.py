@@ -63,3 +63,21 @@ def test_causal_and_independent():
         assert np.array_equal(prefill_attend(c2, s2, qpos[t:t + 1], q[t:t + 1], idx[t:t + 1], 0.05)[0], got[t])
     perm = np.array([3, 0, 4, 1, 2])
     assert np.array_equal(prefill_attend(c, s, qpos[perm], q[perm], idx[perm], 0.05), got[perm])
+
+
+def test_local_branch_query_is_the_decode_step_with_window():
+    # each prefill query with a window equals the decode-step oracle with the
+    # same window over a sequence that ends at the query's position
+    from oracle import swa as S
+    n, win = 8 * 11 + 3, 20
+    c, s = _cache(n)
+    sc, ss = S.quantize_fp8_rows(W.swa_rows(0, 3, 0, 0, n))
+    qpos = np.int64([0, 5, 19, 20, 50, n - 1])
+    q = W.queries(0, 4, 0, qpos.size, 16)
+    idx = np.tile(np.int32([0, 3, 9, -1]), (qpos.size, 1))
+    got = prefill_attend(c, s, qpos, q, idx, 0.06, sc, ss, win)
+    for t, p in enumerate(qpos):
+        want = S.attend_with_window(c, s, int(p) + 1, q[t], idx[t], 0.06, sc, ss, int(p) + 1, win)
+        assert np.array_equal(got[t], want)
+    # a window of 0 is the plain prefill attention
+    assert np.array_equal(prefill_attend(c, s, qpos, q, idx, 0.06, sc, ss, 0), prefill_attend(c, s, qpos, q, idx, 0.06))
