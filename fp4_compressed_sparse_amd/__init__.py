@@ -19,7 +19,7 @@ FULL, REINDEX, REUSE = 0, 1, 2
 D, BLOCK, CODE_BYTES, SCALE_BYTES = 512, 8, 256, 32
 MAX_POOL, MAX_TOPK, MAX_CACHES = 8192, 2048, 16
 FLAG_NONFINITE_KV, FLAG_CAPACITY, FLAG_NONFINITE_Q, FLAG_BAD_INDEX, FLAG_SWA_RANGE = 1, 2, 4, 8, 16
-MAX_WINDOW, MAX_SWA_LAYERS = 1024, 64
+MAX_WINDOW, MAX_SWA_LAYERS, MAX_SWA_SLOTS = 1024, 64, 1 << 22
 
 EXPORTED = ("fp4_quantize_kv", "csa2_append_kv", "fp8_quantize_kv", "csa2_swa_append",
             "csa2_workspace_bytes", "csa2_workspace_init",
@@ -41,7 +41,7 @@ class _Kv(ctypes.Structure):
 
 class _Swa(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
-                ("window", ctypes.c_int32), ("batch", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("batch", ctypes.c_int32), ("slots", ctypes.c_int32)]
 
 
 class _Layer(ctypes.Structure):
@@ -83,7 +83,7 @@ def load():
                                      ctypes.POINTER(_Swa), vp, vp, sz, vp]),
         "csa2_prefill_workspace_bytes": (sz, [i32, i32, i32]),
         "csa2_prefill_attend": (i32, [ctypes.POINTER(_Kv), i32, vp, i32, i32, vp, vp, i32, ctypes.c_float,
-                                      vp, vp, sz, vp]),
+                                      ctypes.POINTER(_Swa), vp, vp, sz, vp]),
         "csa2_decode_step": (i32, [ctypes.POINTER(_Step), vp]),
         "csa2_block_scores": (i32, [ctypes.POINTER(_Kv), vp, i32, vp, i32, vp, vp]),
         "csa2_device_error": (i32, [ctypes.POINTER(ctypes.c_int32), vp]),
@@ -154,22 +154,27 @@ def append_kv(cache: KVCache, x, stream=None):
 
 
 class SwaCache:
-    """One layer's FP8 sliding-window ring: torch uint8 codes [B][window][512],
-    float32 scales [B][window] and int64 seq_len [B] (positions written) on
-    the GPU; position p lives in slot p % window."""
+    """One layer's FP8 sliding-window ring: torch uint8 codes [B][slots][512],
+    float32 scales [B][slots] and int64 seq_len [B] (positions written) on
+    the GPU; position p lives in slot p % slots.  A decode step attends to
+    the last `window` positions; slots (default: window) may be larger so a
+    prefill chunk's queries find their own windows."""
 
-    def __init__(self, batch, window, device="cuda"):
+    def __init__(self, batch, window, device="cuda", slots=None):
         import torch
         if not 1 <= window <= MAX_WINDOW:
             raise ValueError(f"window must be in [1, {MAX_WINDOW}]")
-        self.codes = torch.zeros((batch, window, D), dtype=torch.uint8, device=device)
-        self.scales = torch.zeros((batch, window), dtype=torch.float32, device=device)
+        slots = window if slots is None else int(slots)
+        if slots < window:
+            raise ValueError("slots must be >= window")
+        self.codes = torch.zeros((batch, slots, D), dtype=torch.uint8, device=device)
+        self.scales = torch.zeros((batch, slots), dtype=torch.float32, device=device)
         self.seq_len = torch.zeros(batch, dtype=torch.int64, device=device)
-        self.batch, self.window = batch, window
+        self.batch, self.window, self.slots = batch, window, slots
 
     def view(self):
         return _Swa(self.codes.data_ptr(), self.scales.data_ptr(), self.seq_len.data_ptr(),
-                    self.window, self.batch)
+                    self.window, self.batch, self.slots)
 
 
 def fp8_quantize_kv(x, codes, scales, dst_row=None, stream=None):
@@ -228,15 +233,17 @@ def sparse_attend(cache, q, idx, scale, out, ws, max_len=None, stream=None, swa=
                                   float(scale), sv, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def prefill_attend(cache, seq, q, qpos, idx, scale, out, ws=None, max_len=None, stream=None):
+def prefill_attend(cache, seq, q, qpos, idx, scale, out, ws=None, max_len=None, stream=None, swa=None):
     """n_q queries of sequence `seq`: q float32 [n_q, H, 512], qpos int64
     [n_q], idx int32 [n_q, topk] -> out float32 [n_q, H, 512] (causal:
-    positions <= qpos).  ws: None or a tensor of prefill_workspace_bytes."""
+    positions <= qpos).  ws: None or a tensor of prefill_workspace_bytes.
+    swa: None or the layer's SwaCache (each query's window joins its softmax)."""
     lib = load()
     kv = cache.view(max_len)
     nbytes = ws.numel() if ws is not None else 0
+    sv = ctypes.byref(swa.view()) if swa is not None else None
     _check(lib.csa2_prefill_attend(ctypes.byref(kv), int(seq), _ptr(q), q.shape[0], q.shape[1], _ptr(qpos),
-                                   _ptr(idx), idx.shape[1], float(scale), _ptr(out), _ptr(ws), nbytes,
+                                   _ptr(idx), idx.shape[1], float(scale), sv, _ptr(out), _ptr(ws), nbytes,
                                    _stream(stream)))
 
 

@@ -144,12 +144,17 @@ csa2_status check_kv(const csa2_kv *kv) {
 
 static_assert(MAX_SWA_RINGS == CSA2_MAX_SWA_LAYERS, "ring table size");
 
+// Ring positions of an SWA view (0 means as many as the window).
+inline int32_t swa_slots(const csa2_swa *swa) { return swa->slots ? swa->slots : swa->window; }
+
 csa2_status check_swa(const csa2_swa *swa, int32_t batch) {
   if (!swa->codes || !swa->scales || !swa->seq_len) return fail(CSA2_E_ARG, "swa has a NULL pointer");
   if (!aligned(swa->codes, 16) || !aligned(swa->scales, 4) || !aligned(swa->seq_len, 8))
     return fail(CSA2_E_ARG, "swa codes/scales/seq_len misaligned");
   if (swa->window < 1 || swa->window > CSA2_MAX_WINDOW)
     return fail(CSA2_E_SHAPE, "swa window %d outside [1, %d]", swa->window, CSA2_MAX_WINDOW);
+  if (swa->slots != 0 && (swa->slots < swa->window || swa->slots > CSA2_MAX_SWA_SLOTS))
+    return fail(CSA2_E_SHAPE, "swa slots %d outside [window %d, %d]", swa->slots, swa->window, CSA2_MAX_SWA_SLOTS);
   if (swa->batch != batch) return fail(CSA2_E_ARG, "swa batch %d != %d", swa->batch, batch);
   return CSA2_OK;
 }
@@ -252,6 +257,9 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   aa.scale_log2 = scale * 1.4426950408889634f;
   aa.n_sparse = L.att_stages;
   aa.window = swa ? swa->window : 0;
+  aa.swa_slots = swa ? swa_slots(swa) : 1;
+  aa.swa_stride = 1;
+  aa.win_at_query = 0;
   aa.swa_codes = swa ? swa->codes : kv->codes;
   aa.swa_scales = swa ? swa->scales : reinterpret_cast<const float *>(kv->scales);
   aa.swa_len = swa ? swa->seq_len : kv->seq_len;
@@ -298,13 +306,17 @@ csa2_status check_select_args(int32_t topk, int32_t pool) {
 
 // Attention-only layout of the prefill entry: partials only with more
 // than one split.
-bool prefill_layout(int32_t n_q, int32_t heads, int32_t topk, Layout *L) {
+// window > 0: the local branch adds ceil(window / 64) stages and runs on
+// the per-head-tile kernel; without it 64 heads take one workgroup per
+// (query, split) for all four head tiles.  att_stages counts the gathered
+// stages only.
+bool prefill_layout(int32_t n_q, int32_t heads, int32_t topk, int32_t window, Layout *L) {
   if (n_q < 1 || n_q > 65535 || topk < 1 || topk > CSA2_MAX_TOPK) return false;
   if (heads != 16 && heads != 32 && heads != 64) return false;
   memset(L, 0, sizeof *L);
   L->att_stages = (int32_t)ceil_div((int64_t)topk * BLOCK, ATT_SP);
-  // 64 heads: one workgroup per (query, split) covers all four head tiles
-  L->att_splits = att_splits(heads == 64 ? n_q : n_q * (heads / 16), L->att_stages);
+  const int wstages = (int)ceil_div(window, ATT_SP);
+  L->att_splits = att_splits(heads == 64 && window == 0 ? n_q : n_q * (heads / 16), L->att_stages + wstages);
   const size_t slots = L->att_splits > 1 ? (size_t)n_q * L->att_splits * (heads / 16) * 16 : 0;
   size_t off = 0;
   L->part_o = off;  off = align256(off + sizeof(float) * slots * D);
@@ -420,7 +432,7 @@ csa2_status csa2_swa_append(const csa2_swa *swa, const float *x, void *stream) {
   SwaRings rr;
   memset(&rr, 0, sizeof rr);
   rr.codes[0] = swa->codes; rr.scales[0] = swa->scales; rr.seq_len[0] = swa->seq_len;
-  rr.rows[0] = x; rr.window[0] = swa->window;
+  rr.rows[0] = x; rr.slots[0] = swa_slots(swa);
   append_kernel<<<dim3(swa->batch, 1), 128, 0, as_stream(stream)>>>(aa, rr, nullptr, swa->batch, 0, 1,
                                                                      QbarJob{});
   return launched("swa append");
@@ -492,18 +504,22 @@ csa2_status csa2_sparse_attend(const csa2_kv *kv, const float *q, int32_t heads,
 }
 
 size_t csa2_prefill_workspace_bytes(int32_t n_q, int32_t heads, int32_t topk) {
-  Layout L;
-  if (!prefill_layout(n_q, heads, topk, &L)) return 0;
-  return L.total;
+  Layout L0, L1;                          // without and with the largest local branch
+  if (!prefill_layout(n_q, heads, topk, 0, &L0) || !prefill_layout(n_q, heads, topk, CSA2_MAX_WINDOW, &L1))
+    return 0;
+  return L0.total > L1.total ? L0.total : L1.total;
 }
 
 csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, int32_t n_q,
                                 int32_t heads, const int64_t *qpos, const int32_t *idx,
-                                int32_t topk, float scale, float *out, void *ws,
-                                size_t ws_bytes, void *stream) {
+                                int32_t topk, float scale, const csa2_swa *swa, float *out,
+                                void *ws, size_t ws_bytes, void *stream) {
   t_last_error.clear();
   if (csa2_status st = check_kv(kv)) return st;
   if (seq < 0 || seq >= kv->batch) return fail(CSA2_E_ARG, "seq %d outside [0, %d)", seq, kv->batch);
+  if (swa) {
+    if (csa2_status st = check_swa(swa, kv->batch)) return st;
+  }
   if (!q || !aligned(q, 16) || !out || !aligned(out, 16))
     return fail(CSA2_E_ARG, "q/out must be non-NULL and 16-byte aligned");
   if (!qpos || !aligned(qpos, 8) || !idx || !aligned(idx, 4)) return fail(CSA2_E_ARG, "qpos/idx must be non-NULL");
@@ -514,7 +530,8 @@ csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, 
   if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
     return fail(CSA2_E_ARG, "scale must be finite");
   Layout L;
-  if (!prefill_layout(n_q, heads, topk, &L)) return fail(CSA2_E_SHAPE, "bad sizes");
+  const int32_t window = swa ? swa->window : 0;
+  if (!prefill_layout(n_q, heads, topk, window, &L)) return fail(CSA2_E_SHAPE, "bad sizes");
   if (L.total) {
     if (csa2_status st = check_ws(ws, ws_bytes, L)) return st;
   }
@@ -528,17 +545,32 @@ csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, 
   aa.capacity = kv->capacity; aa.limit = kv->max_len;
   aa.q = q; aa.idx = idx; aa.topk = topk; aa.heads = heads;
   aa.scale_log2 = scale * 1.4426950408889634f;
-  aa.n_stages = L.att_stages; aa.splits = L.att_splits;
-  aa.n_sparse = L.att_stages; aa.window = 0;                 // no local branch
-  aa.swa_codes = aa.codes; aa.swa_scales = nullptr; aa.swa_len = qpos;
+  aa.n_sparse = L.att_stages;
+  aa.n_stages = L.att_stages + (int32_t)ceil_div(window, ATT_SP);
+  aa.splits = L.att_splits;
+  aa.window = window;
+  if (swa) {
+    // every query reads the ring of sequence seq, its window ending at its own position
+    const int32_t slots = swa_slots(swa);
+    aa.swa_slots = slots; aa.swa_stride = 0; aa.win_at_query = 1;
+    aa.swa_codes = swa->codes + (int64_t)seq * slots * D;
+    aa.swa_scales = swa->scales + (int64_t)seq * slots;
+    aa.swa_len = swa->seq_len + seq;
+  } else {
+    aa.swa_slots = 1; aa.swa_stride = 0; aa.win_at_query = 0;
+    aa.swa_codes = aa.codes; aa.swa_scales = nullptr; aa.swa_len = qpos;
+  }
   aa.part_o = L.total ? at<float>(ws, L.part_o) : nullptr;
   aa.part_ml = L.total ? at<float>(ws, L.part_ml) : nullptr;
   aa.out = out;
   const size_t lds = (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16);
-  if (heads == 64)
+  const dim3 g16(L.att_splits * (heads / 16), n_q);
+  if (swa)
+    attend_partial_kernel<false, true><<<g16, ATT_THREADS, lds, s>>>(aa);
+  else if (heads == 64)
     attend64_kernel<<<dim3(L.att_splits, n_q), ATT64_THREADS, ATT64_LDS, s>>>(aa);
   else
-    attend_partial_kernel<false, false><<<dim3(L.att_splits * (heads / 16), n_q), ATT_THREADS, lds, s>>>(aa);
+    attend_partial_kernel<false, false><<<g16, ATT_THREADS, lds, s>>>(aa);
   if (csa2_status st = launched("prefill attend")) return st;
   if (L.att_splits == 1) return CSA2_OK;
   CombineArgs ca;
@@ -636,7 +668,7 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
       const csa2_layer &ly = st->layers[l];
       if (!ly.swa || !ly.swa_row) continue;
       rr.codes[nr] = ly.swa->codes; rr.scales[nr] = ly.swa->scales; rr.seq_len[nr] = ly.swa->seq_len;
-      rr.rows[nr] = ly.swa_row; rr.window[nr] = ly.swa->window;
+      rr.rows[nr] = ly.swa_row; rr.slots[nr] = swa_slots(ly.swa);
       ++nr;
     }
     // the first layer (Full) scans all blocks: its query sum rides along

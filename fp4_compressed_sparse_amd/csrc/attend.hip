@@ -71,14 +71,20 @@ struct AttendArgs {
   int64_t seq_stride;
   int32_t len_add;          // valid positions of row b: seq_len[b] + len_add
   float *out;               // splits == 1: final output [batch][heads][512] written here
-  // local branch: stages n_sparse .. n_stages-1 hold the last
-  // min(window, swa_len[b]) positions of sequence b's FP8 ring (position p
-  // in slot p % window), attended in the same softmax as the gathered ones
+  // local branch: stages n_sparse .. n_stages-1 hold up to `window`
+  // positions of an FP8 ring (position p in slot p % swa_slots), attended in
+  // the same softmax as the gathered ones.  The window ends at the ring's
+  // length (decode) or, with win_at_query, at row b's own length
+  // seq_len[b] + len_add (prefill); only positions still in the ring
+  // (below its length, at or above length - swa_slots) are read.
   int32_t n_sparse;         // stages of gathered positions: ceil(topk*8 / ATT_SP)
   int32_t window;           // 0 = no local branch
-  const uint8_t *swa_codes; // [batch][window][512] E4M3
-  const float *swa_scales;  // [batch][window]
-  const int64_t *swa_len;   // [batch]; any valid int64 array when window == 0
+  int32_t swa_slots;        // ring positions (>= window)
+  int32_t swa_stride;       // rings per row b: 1 (decode), 0 (prefill: one sequence's ring)
+  int32_t win_at_query;
+  const uint8_t *swa_codes; // [rows][swa_slots][512] E4M3
+  const float *swa_scales;  // [rows][swa_slots]
+  const int64_t *swa_len;   // [rows]; any valid int64 array when window == 0
 };
 
 constexpr int SEL_CAND_MAX = 2048;  // candidates of the in-kernel top-k (8 per thread)
@@ -115,7 +121,8 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
   // local branch: read now, with the first ids, so that the window rows'
   // addresses are known when the first window stage is fetched
-  const int64_t wlen_raw = WIN ? a.swa_len[b] : 0;
+  const int64_t wlen_raw = WIN ? a.swa_len[(int64_t)b * a.swa_stride] : 0;
+  const int64_t wq_raw = WIN && a.win_at_query ? a.seq_len[b] + a.len_add : 0;
 
   // ---- gathered rows of a stage: block ids, then rows (two round trips) --
   constexpr int PASSES = ATT_SP / 16;     // rows per thread per stage
@@ -142,17 +149,20 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   auto fetch_ids = [&](int st) { fetch_ids_into(st, blkv); };
   int32_t nxt[PASSES];                    // block ids of the stage after the one in flight
   u32x4 wr2[PASSES];                      // window rows: second 16 bytes of the thread's 32
-  int64_t nw = 0, wbase = 0;              // window positions held; slot of the oldest
-  const uint8_t *wcodes = a.swa_codes + (int64_t)b * a.window * D;
-  const float *wscales = a.swa_scales + (int64_t)b * a.window;
+  // window: nw positions from wfirst; those in [wlo, wrl) are in the ring;
+  // wbase = slot of wfirst
+  int64_t nw = 0, wbase = 0, wfirst = 0, wlo = 0, wrl = 0;
+  const uint8_t *wcodes = a.swa_codes + (int64_t)b * a.swa_stride * a.swa_slots * D;
+  const float *wscales = a.swa_scales + (int64_t)b * a.swa_stride * a.swa_slots;
   auto fetch_rows = [&](int st) {
     if (WIN && st >= a.n_sparse) {
       // window rows: 512 code bytes (32 per thread) and the row scale
 #pragma unroll
       for (int k = 0; k < PASSES; ++k) {
-        okv[k] = blkv[k] < nw;
+        const int64_t p = wfirst + blkv[k];
+        okv[k] = blkv[k] < nw && p >= wlo && p < wrl;
         int64_t slot = wbase + blkv[k];
-        slot = okv[k] ? (slot >= a.window ? slot - a.window : slot) : 0;
+        slot = okv[k] ? (slot >= a.swa_slots ? slot - a.swa_slots : slot) : 0;
         const uint8_t *row = wcodes + slot * D + 32 * i16;
         wr[k] = *reinterpret_cast<const u32x4 *>(row);
         wr2[k] = *reinterpret_cast<const u32x4 *>(row + 16);
@@ -225,9 +235,13 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     for (int u = 0; u < NV; ++u) v[u] = src[tid + u * ATT_THREADS];
     __builtin_amdgcn_sched_barrier(0);    // query loads go out before the ids are awaited
     if (WIN) {
-      const int64_t wl = wlen_raw < 0 ? 0 : wlen_raw;
-      nw = wl < a.window ? wl : a.window;
-      wbase = (wl - nw) % a.window;
+      wrl = wlen_raw < 0 ? 0 : wlen_raw;                      // positions in the ring
+      wlo = wrl - a.swa_slots;                                // older ones are overwritten
+      const int64_t wend = a.win_at_query ? (wq_raw < 0 ? 0 : wq_raw) : wrl;
+      nw = wend < a.window ? wend : a.window;
+      wfirst = wend - nw;
+      wbase = wfirst % a.swa_slots;
+      if (tid == 0 && nw > 0 && (wfirst < wlo || wend > wrl)) raise_flag(FLAG_BAD_INDEX);
     }
     fetch_rows(st0);
     if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);

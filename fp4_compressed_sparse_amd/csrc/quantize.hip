@@ -210,11 +210,11 @@ struct AppendArgs {
 };
 constexpr int MAX_SWA_RINGS = 64;
 struct SwaRings {
-  uint8_t *codes[MAX_SWA_RINGS];     // [batch][window][512]
-  float *scales[MAX_SWA_RINGS];      // [batch][window]
+  uint8_t *codes[MAX_SWA_RINGS];     // [batch][slots][512]
+  float *scales[MAX_SWA_RINGS];      // [batch][slots]
   int64_t *seq_len[MAX_SWA_RINGS];   // [batch]
   const float *rows[MAX_SWA_RINGS];  // [batch][512]
-  int32_t window[MAX_SWA_RINGS];
+  int32_t slots[MAX_SWA_RINGS];      // ring positions
 };
 
 // The indexer's query sum of one layer, computed in the same launch as the
@@ -227,7 +227,7 @@ struct QbarJob {
 
 // grid (batch, n_caches + n_rings [+ 1]), 128 threads.  y < n_caches:
 // x[y][b][512] -> position seq_len[b] of cache y.  Then ring y - n_caches:
-// rows[b] -> position seq_len[b], slot seq_len[b] % window.  A last row of
+// rows[b] -> position seq_len[b], slot seq_len[b] % slots.  A last row of
 // workgroups (when qj.q is set) sums the query heads of sequence b.
 __global__ void __launch_bounds__(128) append_kernel(AppendArgs a, SwaRings r, const float *__restrict__ x,
                                                      int32_t batch, int32_t n_caches, int32_t n_rings,
@@ -277,7 +277,7 @@ __global__ void __launch_bounds__(128) append_kernel(AppendArgs a, SwaRings r, c
     }
     const float amax = __uint_as_float(both);
     const float s = bad ? 0.0f : __fdiv_rn(amax, 448.0f);
-    const int64_t row = (int64_t)b * r.window[i] + pos % r.window[i];
+    const int64_t row = (int64_t)b * r.slots[i] + pos % r.slots[i];
     reinterpret_cast<uint32_t *>(r.codes[i] + row * D)[q] = bad ? 0u : fp8_encode4(v, s);
     if (q == 0) {
       r.scales[i][row] = s;

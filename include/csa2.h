@@ -86,6 +86,7 @@ enum {
 #define CSA2_MAX_HEADS 64       /* indexer heads 1..64; attention 16, 32 or 64 */
 #define CSA2_MAX_CACHES 16      /* Full caches in one decode step  */
 #define CSA2_MAX_WINDOW 1024    /* largest sliding window (positions) */
+#define CSA2_MAX_SWA_SLOTS (1 << 22)  /* largest SWA ring (positions)  */
 #define CSA2_MAX_SWA_LAYERS 64  /* layers with a local branch in one decode step */
 
 /* Non-owning view of one Full layer's cache for a batch of sequences. */
@@ -136,15 +137,19 @@ csa2_status csa2_append_kv(const csa2_kv *kv, const float *x, void *stream);
  * "halve the long input"]; entries older than the window are never read by
  * the current decode step [P1 section 三]; the SWA KV stays FP8 while the
  * global KV moves to FP4 [P2 "same notes, many layers"].  Reading: E4M3FN
- * codes with one float32 scale per position, kept in a ring of `window`
- * slots: position p of sequence b lives in slot p % window.
+ * codes with one float32 scale per position, kept in a ring of `slots`
+ * positions: position p of sequence b lives in slot p % slots.  A decode
+ * step attends to the last `window` positions; a ring with more slots than
+ * the window also holds what a prefill chunk's queries need (each query's
+ * own window, see csa2_prefill_attend).
  */
 typedef struct {
-  uint8_t *codes;       /* device [batch][window][512] E4M3FN, 16-byte aligned   */
-  float *scales;        /* device [batch][window]                                  */
+  uint8_t *codes;       /* device [batch][slots][512] E4M3FN, 16-byte aligned    */
+  float *scales;        /* device [batch][slots]                                   */
   int64_t *seq_len;     /* device [batch]: positions written; appends increment it */
-  int32_t window;       /* 1..CSA2_MAX_WINDOW                                      */
+  int32_t window;       /* attention window, 1..CSA2_MAX_WINDOW                    */
   int32_t batch;        /* sequences, >= 1                                         */
+  int32_t slots;        /* ring positions, window..CSA2_MAX_SWA_SLOTS; 0 = window  */
 } csa2_swa;
 
 /*
@@ -155,7 +160,7 @@ typedef struct {
  * x        device float32 [rows][512], 16-byte aligned; rows >= 0.
  * dst_row  device int64 [rows]: destination row of each input row, or NULL
  *          for row i -> row i.  Rows outside [0, dst_rows) are skipped and
- *          flag CSA2_FLAG_CAPACITY.  (A ring slot is row b*window + p%window.)
+ *          flag CSA2_FLAG_CAPACITY.  (A ring slot is row b*slots + p%slots.)
  * codes    device uint8 [dst_rows][512], 8-byte aligned; scales device
  *          float32 [dst_rows].
  * A row with NaN/Inf is written as zeros with scale 0 and flags
@@ -166,7 +171,7 @@ csa2_status fp8_quantize_kv(const float *x, int64_t rows, const int64_t *dst_row
 
 /*
  * csa2_swa_append — for each b: quantise x[b] (device float32 [batch][512],
- * 16-byte aligned) as position seq_len[b] into slot seq_len[b] % window,
+ * 16-byte aligned) as position seq_len[b] into slot seq_len[b] % slots,
  * then seq_len[b] += 1.  A negative seq_len[b] is left alone and flags
  * CSA2_FLAG_CAPACITY.
  */
@@ -249,9 +254,10 @@ csa2_status csa2_sparse_attend(const csa2_kv *kv, const float *q, int32_t heads,
                                void *stream);
 
 /*
- * csa2_prefill_workspace_bytes — workspace needed by csa2_prefill_attend
- * (0 when every query's heads fit one workgroup per head tile: no partials).
- * Returns 0 as well for unsupported sizes; csa2_prefill_attend reports why.
+ * csa2_prefill_workspace_bytes — workspace needed by csa2_prefill_attend,
+ * with or without a local branch of any window up to CSA2_MAX_WINDOW (0
+ * when every query is handled without partials).  Returns 0 as well for
+ * unsupported sizes; csa2_prefill_attend reports why.
  */
 size_t csa2_prefill_workspace_bytes(int32_t n_q, int32_t heads, int32_t topk);
 
@@ -268,6 +274,13 @@ size_t csa2_prefill_workspace_bytes(int32_t n_q, int32_t heads, int32_t topk);
  * qpos  device int64 [n_q]: cache position of each query.
  * idx   device int32 [n_q][topk], topk 1..CSA2_MAX_TOPK; -1 = none.  A block
  *       wholly after its query's position flags CSA2_FLAG_BAD_INDEX.
+ * swa   NULL, or the layer's SWA cache (same batch; its ring of sequence
+ *       `seq` is read): query t also attends, in the same softmax, to the
+ *       positions max(0, qpos[t] - window + 1) .. qpos[t] of that ring.  They
+ *       must have been written and not yet overwritten: below seq_len[seq]
+ *       and at or above seq_len[seq] - slots (so a chunk of queries spanning
+ *       S positions needs slots >= S + window - 1); positions outside are
+ *       skipped and flag CSA2_FLAG_BAD_INDEX.
  * out   device float32 [n_q][heads][512].
  * ws    csa2_prefill_workspace_bytes(n_q, heads, topk) bytes, 256-byte
  *       aligned (may be NULL when that is 0).
@@ -275,8 +288,8 @@ size_t csa2_prefill_workspace_bytes(int32_t n_q, int32_t heads, int32_t topk);
  */
 csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, int32_t n_q,
                                 int32_t heads, const int64_t *qpos, const int32_t *idx,
-                                int32_t topk, float scale, float *out, void *ws,
-                                size_t ws_bytes, void *stream);
+                                int32_t topk, float scale, const csa2_swa *swa, float *out,
+                                void *ws, size_t ws_bytes, void *stream);
 
 /* One layer of a decode step. */
 typedef struct {

@@ -75,9 +75,10 @@ def _kv(**kw):
 
 
 def _swa(**kw):
-    base = dict(codes=0x20000, scales=0x60000, seq_len=0x30000, window=128, batch=1)
+    base = dict(codes=0x20000, scales=0x60000, seq_len=0x30000, window=128, batch=1, slots=0)
     base.update(kw)
-    return csa2._Swa(base["codes"], base["scales"], base["seq_len"] or None, base["window"], base["batch"])
+    return csa2._Swa(base["codes"], base["scales"], base["seq_len"] or None, base["window"], base["batch"],
+                     base["slots"])
 
 
 def test_index_and_attend_argument_errors(lib):
@@ -104,7 +105,8 @@ def test_index_and_attend_argument_errors(lib):
                                   None, out, ws, need, None) == 1
     # local branch: window outside [1, 1024], batch mismatch, misaligned ring
     for bad, code in ((_swa(window=0), 2), (_swa(window=1025), 2), (_swa(batch=2), 1),
-                      (_swa(codes=0x20008), 1), (_swa(seq_len=0), 1)):
+                      (_swa(codes=0x20008), 1), (_swa(seq_len=0), 1), (_swa(slots=100), 2),
+                      (_swa(slots=(1 << 22) + 1), 2)):
         assert lib.csa2_sparse_attend(ctypes.byref(_kv()), q, 16, idx, 64, ctypes.c_float(0.04),
                                       ctypes.byref(bad), out, ws, need, None) == code
 
@@ -158,8 +160,9 @@ def test_prefill_attend_argument_errors(lib):
     assert lib.csa2_prefill_workspace_bytes(4, 16, 256) > 0
     assert lib.csa2_prefill_workspace_bytes(0, 16, 64) == 0
     assert lib.csa2_prefill_workspace_bytes(4, 24, 64) == 0
-    call = lambda seq=0, n_q=8, heads=16, topk=64, scale=0.04, qp=qpos, kv=None: lib.csa2_prefill_attend(
-        ctypes.byref(kv or _kv()), seq, q, n_q, heads, qp, idx, topk, ctypes.c_float(scale), out, None, 0, None)
+    call = lambda seq=0, n_q=8, heads=16, topk=64, scale=0.04, qp=qpos, kv=None, sw=None: lib.csa2_prefill_attend(
+        ctypes.byref(kv or _kv()), seq, q, n_q, heads, qp, idx, topk, ctypes.c_float(scale),
+        ctypes.byref(sw) if sw is not None else None, out, None, 0, None)
     assert call(seq=1) == 1                                      # sequence outside the batch
     assert call(seq=-1) == 1
     assert call(heads=24) == 2
@@ -171,3 +174,5 @@ def test_prefill_attend_argument_errors(lib):
     assert call(n_q=4) == 1                                      # partials needed, workspace NULL
     assert "workspace" in _err(lib)
     assert call(kv=_kv(capacity=4092)) == 2
+    assert call(sw=_swa(window=0)) == 2                          # bad local branch
+    assert call(sw=_swa(batch=3)) == 1

@@ -27,7 +27,7 @@ def _selection(rng, qpos, topk):
     return idx
 
 
-def _run(n, qpos, heads, topk, seed):
+def _run(n, qpos, heads, topk, seed, window=0, slots=0):
     require_gpu()
     rng = np.random.default_rng(seed)
     oc = oracle_cache(2, 0, [n], cap_for(n))
@@ -39,13 +39,28 @@ def _run(n, qpos, heads, topk, seed):
     scale = 1 / np.sqrt(512)
     out = torch.full((T, heads, 512), float("nan"), dtype=torch.float32, device="cuda")
     ws = csa2.prefill_workspace(T, heads, topk)
+    ring = sc = ss = None
+    if window:
+        # the sequence's SWA rows (oracle bytes) in a ring of `slots` positions
+        # ending at position n - 1 (the chunk's last query)
+        from oracle import swa as S
+        sc, ss = S.quantize_fp8_rows(W.swa_rows(2, 9, 0, 0, n))
+        ring = csa2.SwaCache(1, window, slots=slots)
+        keep = np.arange(max(0, n - slots), n)
+        codes = np.zeros((slots, 512), dtype=np.uint8)
+        scales = np.zeros(slots, dtype=np.float32)
+        codes[keep % slots], scales[keep % slots] = sc[keep], ss[keep]
+        ring.codes[0].copy_(torch.from_numpy(codes))
+        ring.scales[0].copy_(torch.from_numpy(scales))
+        ring.seq_len.fill_(n)
     csa2.prefill_attend(g, 0, torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
-                        torch.from_numpy(idx).cuda(), scale, out, ws)
+                        torch.from_numpy(idx).cuda(), scale, out, ws, swa=ring)
     torch.cuda.synchronize()
     assert csa2.device_error() == 0
-    ref = prefill_attend(oc.codes[0], oc.scales[0], qpos, q, idx, scale)
+    ref = prefill_attend(oc.codes[0], oc.scales[0], qpos, q, idx, scale, sc, ss, window)
     err = normwise_err(out.cpu().numpy(), ref)
-    log(f"prefill T={T} H={heads} K={topk} (workspace {0 if ws is None else ws.numel()} B): error {err:.2e}")
+    log(f"prefill T={T} H={heads} K={topk} window={window} (workspace {0 if ws is None else ws.numel()} B): "
+        f"error {err:.2e}")
     assert err <= ATT_TOL
 
 
@@ -84,3 +99,37 @@ def test_prefill_32_heads_split_k():
     # 32 heads (two head tiles per query in the per-tile kernel), a few queries, split over workgroups
     n = 7000
     _run(n, [100, 3000, 6999, 6998, 5555, 17], 32, 128, 6)
+
+
+def test_prefill_local_branch_64_heads():
+    # a chunk of 40 queries spanning the last 300 positions, 128-position
+    # windows, a ring of 300 + 127 slots
+    n = 9000
+    qpos = np.sort(np.random.default_rng(11).choice(np.arange(n - 300, n), 40, replace=False))
+    _run(n, qpos, 64, 64, 7, window=128, slots=300 + 127)
+
+
+def test_prefill_local_branch_16_heads_many_queries():
+    # 600 queries of 16 heads, windows of 100 (not a multiple of 64), ring of 700 slots
+    n = 5000
+    _run(n, np.arange(n - 600, n), 16, 24, 8, window=100, slots=700)
+
+
+def test_prefill_local_branch_window_outside_ring_is_flagged():
+    # a query whose window reaches below the ring's oldest position: the
+    # positions that were overwritten are skipped and the call flags it
+    require_gpu()
+    n, window, slots = 3000, 64, 100
+    oc = oracle_cache(2, 0, [n], cap_for(n))
+    g = to_device(oc)
+    ring = csa2.SwaCache(1, window, slots=slots)
+    ring.seq_len.fill_(n)
+    q = torch.from_numpy(W.queries(2, 7, 9, 1, 16)).cuda()
+    qpos = torch.tensor([n - 80], dtype=torch.int64, device="cuda")     # window from n-143: below n-100
+    idx = torch.tensor([[0, -1]], dtype=torch.int32, device="cuda")
+    out = torch.zeros((1, 16, 512), dtype=torch.float32, device="cuda")
+    csa2.device_error()
+    csa2.prefill_attend(g, 0, q, qpos, idx, 0.05, out, csa2.prefill_workspace(1, 16, 2), swa=ring)
+    torch.cuda.synchronize()
+    assert csa2.device_error() & csa2.FLAG_BAD_INDEX
+    assert torch.isfinite(out).all()
