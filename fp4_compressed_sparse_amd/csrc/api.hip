@@ -69,6 +69,8 @@ csa2_status device_ready() {
         (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, big);
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, big);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&select2_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&rescore_kernel<true>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, big);
       (void)hipGetLastError();
@@ -219,6 +221,12 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
   se.lds_keys = lk;
   se.pool_scores = pool_scores;
   se.hist = sa.hist;
+  if (L.nwords <= SEL2_WORDS && R <= SEL2_KEYS) {
+    // the chosen ids' bitmap fits in one workgroup's LDS
+    dim3 g2(std::max<int64_t>(1, ceil_div(nblk_grid, SEL2_SPAN)), B);
+    select2_kernel<<<g2, SEL2_THREADS, select2_lds(L.nwords), s>>>(se);
+    return launched("select");
+  }
   dim3 g2(grid_for(ceil_div(L.nwords / 2, 4), B, 256), B);
   select_kernel<<<g2, SCAN_THREADS, (size_t)lk * sizeof(uint64_t), s>>>(se);
   return launched("select");

@@ -1052,6 +1052,273 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   if (t < SCAN_GROUPS) ctrl->work[t * 32] = 0;
 }
 
+// ---- select: classification by every workgroup, ranking by the last ------
+//
+// The same choice as select_kernel (pool or top-k by (score desc, id asc),
+// ids ascending, -1 padded).  Every workgroup (1,024 threads) takes 4,096
+// consecutive blocks, finds the threshold digit from the scan's histogram
+// and writes the keys of its blocks at or above that digit into its own
+// region of a key list (no shared counter); the last workgroup to arrive
+// loads the regions into LDS (R plus the digit's blocks: about 5K keys at a
+// 1M-position context), takes the threshold inside the digit by radix
+// digits, marks the chosen ids in an LDS bitmap and writes every chosen
+// block at its rank in ascending id order, its score recovered from the
+// key (the order-preserving score bits invert exactly), so the scores are
+// read once.  One workgroup cannot stream the whole score row fast enough
+// (about 26 GB/s from one compute unit, measured), hence the split.  When
+// the regions hold more keys than LDS, the digits are counted from the
+// regions in global memory (one pass per digit).
+constexpr int SEL2_THREADS = 1024;
+constexpr int SEL2_KEYS = 8192;      // region keys ranked in LDS
+constexpr int SEL2_WORDS = 8192;     // bitmap words in LDS: up to 262,144 blocks
+constexpr int SEL2_U = 4;            // scores per thread
+constexpr int SEL2_SPAN = SEL2_THREADS * SEL2_U;       // blocks per workgroup
+constexpr int SEL2_MAXG = SEL2_WORDS * 32 / SEL2_SPAN;  // workgroups per sequence
+static_assert(SEL2_THREADS == HIST_BINS, "one histogram bin per thread");
+
+// Dynamic LDS bytes of select2_kernel: the keys, the bitmap and its word
+// prefix sums.
+inline size_t select2_lds(int nwords) {
+  return sizeof(uint64_t) * SEL2_KEYS + 2 * sizeof(uint32_t) * (size_t)nwords;
+}
+
+// Digit step of a radix select: s_hist[0..nb) counts the keys under the
+// current prefix by their digit at bit lo; the digit holding the
+// remaining-th largest key is added to *prefix and *remaining becomes the
+// rank inside it.  Returns true when that digit's keys are all taken (the
+// threshold is then the prefix itself).  All threads call.
+__device__ __forceinline__ bool radix_pick(const uint32_t *s_hist, int nb, int lo, uint64_t *prefix,
+                                           int *remaining, uint64_t *s_state, uint32_t *s_wave) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int per = (nb + nt - 1) / nt;
+  uint32_t sum = 0;
+  for (int j = 0; j < per; ++j) {
+    const int bin = nb - 1 - (per * t + j);
+    sum += bin >= 0 ? s_hist[bin] : 0u;
+  }
+  uint32_t total;
+  const uint32_t above = block_exclusive_scan(sum, &total, s_wave);
+  const uint32_t r = (uint32_t)*remaining;
+  if (above < r && r <= above + sum) {
+    uint32_t acc = above;
+    for (int j = 0; j < per; ++j) {
+      const int bin = nb - 1 - (per * t + j);
+      const uint32_t c = bin >= 0 ? s_hist[bin] : 0u;
+      if (acc + c >= r) {
+        s_state[0] = *prefix | ((uint64_t)bin << lo);
+        const uint32_t rem = r - acc;
+        s_state[1] = (uint64_t)rem | ((rem == c) ? (1ull << 63) : 0ull);
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+  *prefix = s_state[0];
+  const uint64_t st = s_state[1];
+  __syncthreads();
+  *remaining = (int)(uint32_t)st;
+  return (st >> 63) != 0;
+}
+
+// The key T such that exactly r of the keys get(0..m) that match `prefix`
+// on the bits of `pmask` (the bits above hi) are >= T; 11-bit digits from
+// bit hi down (keys distinct, 1 <= r <= matching keys).  All threads call.
+template <class F>
+__device__ __forceinline__ uint64_t radix_select_keys(F get, int m, int r, uint64_t prefix, uint64_t pmask,
+                                                      int hi, uint32_t *s_hist, uint64_t *s_state,
+                                                      uint32_t *s_wave) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  int remaining = r;
+  for (; hi >= 0; hi -= 11) {
+    const int lo = hi >= 10 ? hi - 10 : 0;
+    const int nb = 1 << (hi - lo + 1);
+    for (int j = t; j < nb; j += nt) s_hist[j] = 0;
+    __syncthreads();
+    constexpr int U = 8;
+    for (int j0 = 0; j0 < m; j0 += nt * U) {
+      uint64_t kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) kv[u] = get(min(j0 + u * nt + t, m - 1));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (j0 + u * nt + t < m && (kv[u] & pmask) == prefix)
+          atomicAdd(&s_hist[(uint32_t)(kv[u] >> lo) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    const bool whole = radix_pick(s_hist, nb, lo, &prefix, &remaining, s_state, s_wave);
+    pmask |= ((2ull << hi) - 1) & ~((1ull << lo) - 1);
+    if (whole || lo == 0) break;
+  }
+  return prefix;
+}
+
+// grid (ceil(blocks / SEL2_SPAN) <= SEL2_MAXG, batch), SEL2_THREADS threads;
+// nwords <= SEL2_WORDS, R <= SEL2_KEYS; select2_lds(nwords) bytes of
+// dynamic LDS.  Regions live in `cands` (region g at entry g * SEL2_SPAN:
+// it holds keys of its own blocks only, so it stays inside the sequence's
+// cand_stride >= blocks entries); region sizes in the first words of
+// `bitmap` (zero at entry, left zero).
+__global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
+  extern __shared__ uint64_t s_dyn[];
+  uint64_t *s_keys = s_dyn;                                            // [SEL2_KEYS]
+  uint32_t *s_bm = reinterpret_cast<uint32_t *>(s_dyn + SEL2_KEYS);    // [nwords]
+  uint32_t *s_wpre = s_bm + a.nwords;                                  // [nwords]
+  __shared__ uint32_t s_hist[RADIX_BINS];
+  __shared__ uint32_t s_off[SEL2_MAXG + 1];
+  __shared__ uint64_t s_state[2];
+  __shared__ uint32_t s_wave[16];
+  __shared__ uint32_t s_cnt;
+  const int b = blockIdx.y, g = blockIdx.x, G = gridDim.x;
+  const int t = threadIdx.x, nt = SEL2_THREADS;
+  Ctrl *ctrl = a.ctrl + b;
+  const float *scores = a.scores + (int64_t)b * a.score_stride;
+  uint32_t *gh = a.hist + (int64_t)b * HIST_COPIES * HIST_BINS;
+  uint64_t *keys_g = a.cands + (int64_t)b * CAND_COPIES * a.cand_stride;
+  uint32_t *counts = a.bitmap + (int64_t)b * a.nwords;
+  const uint32_t R = (uint32_t)a.R;
+  CSA2_TS(8);
+  // one batch of requests: this thread's histogram bin (8 copies), its
+  // scores, the length
+  const int bin = HIST_BINS - 1 - t;
+  uint32_t hv[HIST_COPIES];
+#pragma unroll
+  for (int k = 0; k < HIST_COPIES; ++k) hv[k] = gh[k * HIST_BINS + bin];
+  const int id0 = g * SEL2_SPAN + t;
+  float sv[SEL2_U];
+#pragma unroll
+  for (int u = 0; u < SEL2_U; ++u) sv[u] = scores[min(id0 + u * nt, (int)a.score_stride - 1)];
+  const int64_t n = clamp_len(a.seq_len[b], a.limit);
+  const int nblk = (int)((n + BLOCK - 1) / BLOCK);
+  if (t == 0) { s_cnt = 0; s_state[0] = 0; }
+  const bool all = R >= (uint32_t)nblk;
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < HIST_COPIES; ++k) c += hv[k];
+  uint32_t total;
+  const uint32_t above = block_exclusive_scan(c, &total, s_wave);    // barriers: s_cnt is clear
+  if (!all && above < R && R <= above + c) s_state[0] = ((uint64_t)bin << 32) | (uint64_t)(R - above);
+  __syncthreads();
+  const uint32_t thr = (uint32_t)(s_state[0] >> 32), need = (uint32_t)s_state[0];
+  // keys of this workgroup's blocks at or above the threshold digit (every
+  // block when R >= blocks)
+  uint64_t *region = keys_g + (int64_t)g * SEL2_SPAN;
+#pragma unroll
+  for (int u = 0; u < SEL2_U; ++u) {
+    const int id = id0 + u * nt;
+    const uint32_t kh = ord_key(sv[u]);
+    if (id < nblk && (all || (kh >> HIST_SHIFT) >= thr)) {
+      const uint32_t pos = atomicAdd(&s_cnt, 1u);
+      st_agent(region + pos, ((uint64_t)kh << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id));
+    }
+  }
+  __syncthreads();
+  if (t == 0) st_agent(counts + g, s_cnt);
+  CSA2_TS(9);
+  if (!arrive_last(ctrl->sel_grp, &ctrl->sel_top, G)) return;
+
+  // ---- the last workgroup: rank the regions' keys ----
+  CSA2_TS(10);
+  const uint32_t rc = t < G ? ld_agent(counts + t) : 0u;
+  uint32_t E;
+  const uint32_t roff = block_exclusive_scan(rc, &E, s_wave);
+  if (t < G) { s_off[t] = roff; counts[t] = 0; }
+  if (t == 0) s_off[G] = E;
+  for (int j = t; j < a.nwords; j += nt) s_bm[j] = 0;
+  __syncthreads();
+  // entry j of the concatenated regions
+  auto key_at = [&](int j) -> uint64_t {
+    int lo = 0, hi = G - 1;                    // largest k with s_off[k] <= j
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= (uint32_t)j) lo = mid; else hi = mid - 1;
+    }
+    return ld_agent(keys_g + (int64_t)lo * SEL2_SPAN + (j - (int)s_off[lo]));
+  };
+  const int m = (int)E;
+  const bool in_lds = m <= SEL2_KEYS;
+  if (in_lds && m > 0) {
+    constexpr int U = SEL2_KEYS / SEL2_THREADS;
+    uint64_t kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kv[u] = key_at(min(t + u * nt, m - 1));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t + u * nt < m) s_keys[t + u * nt] = kv[u];
+  }
+  __syncthreads();
+  auto get_lds = [&](int j) -> uint64_t { return s_keys[j]; };
+  CSA2_TS(11);
+  // threshold: need-th largest key inside the digit (every entry when R >= blocks)
+  uint64_t T = 1ull;                           // keys are never 0
+  if (!all && need > 0 && (uint32_t)m > R) {
+    const uint64_t prefix = (uint64_t)thr << (32 + HIST_SHIFT);
+    const uint64_t pmask = ~((1ull << (32 + HIST_SHIFT)) - 1);
+    T = in_lds ? radix_select_keys(get_lds, m, (int)need, prefix, pmask, 31 + HIST_SHIFT, s_hist, s_state, s_wave)
+               : radix_select_keys(key_at, m, (int)need, prefix, pmask, 31 + HIST_SHIFT, s_hist, s_state, s_wave);
+  }
+  CSA2_TS(12);
+  // chosen ids (keys >= Tc) -> ranks in ascending id order -> out[rank]
+  auto emit = [&](uint64_t Tc, int32_t *out, float *out_scores, int len) {
+    for (int j0 = 0; j0 < m; j0 += nt) {
+      const int j = j0 + t;
+      if (j < m) {
+        const uint64_t k = in_lds ? s_keys[j] : key_at(j);
+        if (k >= Tc) {
+          const uint32_t id = 0xFFFFFFFFu - (uint32_t)k;
+          atomicOr(&s_bm[id >> 5], 1u << (id & 31));
+        }
+      }
+    }
+    __syncthreads();
+    const int per = (a.nwords + nt - 1) / nt;
+    const int w0 = min(a.nwords, t * per), w1 = min(a.nwords, w0 + per);
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(s_bm[w]);
+    uint32_t tot;
+    uint32_t off = block_exclusive_scan(cnt, &tot, s_wave);
+    for (int w = w0; w < w1; ++w) {
+      s_wpre[w] = off;
+      off += __popc(s_bm[w]);
+    }
+    __syncthreads();
+    for (int j0 = 0; j0 < m; j0 += nt) {
+      const int j = j0 + t;
+      if (j < m) {
+        const uint64_t k = in_lds ? s_keys[j] : key_at(j);
+        if (k >= Tc) {
+          const uint32_t id = 0xFFFFFFFFu - (uint32_t)k;
+          const uint32_t rank = s_wpre[id >> 5] + __popc(s_bm[id >> 5] & ((1u << (id & 31)) - 1u));
+          if (rank < (uint32_t)len) {
+            out[rank] = (int32_t)id;
+            if (out_scores) out_scores[rank] = unord_key((uint32_t)(k >> 32));
+          }
+        }
+      }
+    }
+    for (int j = (int)tot + t; j < len; j += nt) out[j] = -1;
+    __syncthreads();
+    for (int j = t; j < a.nwords; j += nt) s_bm[j] = 0;
+    __syncthreads();
+  };
+  const uint32_t chosen = min(R, (uint32_t)m);
+  emit(T, a.first_out + (int64_t)b * R, a.pool_scores ? a.pool_scores + (int64_t)b * R : nullptr, (int)R);
+  CSA2_TS(13);
+  if (a.topk > 0) {
+    // the top-k of the chosen list is the top-k of every entry
+    uint64_t T2 = T;
+    if ((uint32_t)a.topk < chosen)
+      T2 = in_lds ? radix_select_keys(get_lds, m, a.topk, 0ull, 0ull, 63, s_hist, s_state, s_wave)
+                  : radix_select_keys(key_at, m, a.topk, 0ull, 0ull, 63, s_hist, s_state, s_wave);
+    emit(T2, a.idx_out + (int64_t)b * a.topk, nullptr, a.topk);
+  }
+  CSA2_TS(14);
+  // leave the row clean for the next call: the scan's histogram copies and
+  // work counters (the region sizes were cleared above)
+  for (int j = t; j < HIST_COPIES * HIST_BINS; j += nt) gh[j] = 0;
+  if (t < SCAN_GROUPS) ctrl->work[t * 32] = 0;
+}
+
 // ---- rescoring of a candidate list (pool) + top-k --------------------------
 
 struct RescoreArgs {

@@ -133,6 +133,45 @@ def test_ties_lowest_id_and_large_tie_bucket():
         assert idx[0].tolist() == list(range(64))
 
 
+@pytest.mark.parametrize("nblk,ntypes,pool,topk", [
+    (20000, 5, 2048, 64),       # 4,000 blocks per score: the tie digit is ranked in LDS by id
+    (30000, 3, 2048, 256),      # 10,000 tied blocks: more than the LDS list, digits re-counted from the scores
+    (30000, 3, 0, 512),         # the same without a pool
+    (270000, 5, 2048, 256),     # 270,000 blocks: the selection bitmap does not fit in LDS
+])
+def test_selection_with_repeated_block_types(nblk, ntypes, pool, topk):
+    """Blocks drawn from a few distinct 8-row blocks, so whole score levels
+    tie across the threshold: the lowest ids of the level win."""
+    require_gpu()
+    small = Cache(1, 8 * ntypes)
+    small.write(0, 0, W.kv_rows(0, 3, 0, 0, 8 * ntypes))
+    small.seq_len[0] = 8 * ntypes
+    q = W.queries(0, 7, 0, 1, 16)
+    _, type_score = I.block_scores(small.codes[0], small.scales[0], 8 * ntypes, q[0])
+    ids = np.arange(nblk, dtype=np.int64)
+    types = (ids * 7919 + 3) % ntypes
+    scores = type_score[types]
+    log(f"repeated blocks: nblk={nblk} types={ntypes} pool={pool} topk={topk}")
+    g = csa2.KVCache(1, nblk * 8)
+    tt = torch.from_numpy(types).cuda()
+    g.codes[0].copy_(torch.from_numpy(small.codes[0].reshape(ntypes, 8, 256)).cuda()[tt].reshape(-1, 256))
+    g.scales[0].copy_(torch.from_numpy(small.scales[0].reshape(ntypes, 8, 32)).cuda()[tt].reshape(-1, 32))
+    g.seq_len.fill_(nblk * 8)
+    g.max_len = nblk * 8
+    del tt
+    idx, pool_out, ws = _index(g, q, topk, pool)
+    if pool:
+        want_pool = select(ids, scores, pool)
+        assert np.array_equal(pool_out[0], want_pool)
+        keep = np.isin(ids, want_pool)
+        want = select(ids[keep], scores[keep], topk)
+    else:
+        want = select(ids, scores, topk)
+    assert np.array_equal(idx[0], want), (idx[0][:8], want[:8])
+    idx2, _, _ = _index(g, q, topk, pool, ws=ws)
+    assert np.array_equal(idx, idx2)
+
+
 def test_reuse_copies_prior():
     require_gpu()
     prior = torch.arange(3 * 40, dtype=torch.int32, device="cuda").view(3, 40)
