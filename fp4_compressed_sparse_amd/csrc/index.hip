@@ -30,10 +30,11 @@
 // Selection: keys are (order-preserving score bits << 32) | ~block_id, so
 // all keys differ and ties go to the lowest id.  The scan adds the top 10
 // key bits of every block to a histogram (8 copies); every select
-// workgroup finds the digit that holds the R-th largest key from it, marks
-// every block above that digit in a bitmap and collects the digit's blocks;
-// the last select workgroup finishes the choice among them in LDS, then
-// writes the chosen ids in ascending order by compacting the bitmap.
+// workgroup finds the digit that holds the R-th largest key from it and
+// writes the keys of its blocks at or above that digit to its own region;
+// the last select workgroup ranks those keys in LDS and writes the chosen
+// ids in ascending order (select2_kernel; select_kernel, with a global
+// bitmap and tie lists, serves selections whose bitmap exceeds LDS).
 // A block top-k inside LDS (a candidate list) uses linear bins over the
 // score range with an exact pairwise finish (topk_threshold).
 #include "common.hpp"
