@@ -298,8 +298,10 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   if (splits == 1) return CSA2_OK;
   CombineArgs ca;
   ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = splits; ca.heads = heads; ca.out = out;
-  if (splits <= CMB_U)
-    attend_combine_kernel<1><<<dim3((heads / 16) * 32, B), 64, 0, s>>>(ca);
+  if (splits <= 32)
+    attend_combine_regs_kernel<1><<<dim3((heads / 16) * 32, B), 64, 0, s>>>(ca);
+  else if (splits <= 64)
+    attend_combine_regs_kernel<2><<<dim3((heads / 16) * 32, B), 128, 0, s>>>(ca);
   else
     attend_combine_kernel<2><<<dim3((heads / 16) * 32, B), 128, 0, s>>>(ca);
   return launched("combine");
@@ -583,8 +585,10 @@ csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, 
   if (L.att_splits == 1) return CSA2_OK;
   CombineArgs ca;
   ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = L.att_splits; ca.heads = heads; ca.out = out;
-  if (L.att_splits <= CMB_U)
-    attend_combine_kernel<1><<<dim3((heads / 16) * 32, n_q), 64, 0, s>>>(ca);
+  if (L.att_splits <= 32)
+    attend_combine_regs_kernel<1><<<dim3((heads / 16) * 32, n_q), 64, 0, s>>>(ca);
+  else if (L.att_splits <= 64)
+    attend_combine_regs_kernel<2><<<dim3((heads / 16) * 32, n_q), 128, 0, s>>>(ca);
   else
     attend_combine_kernel<2><<<dim3((heads / 16) * 32, n_q), 128, 0, s>>>(ca);
   return launched("prefill combine");

@@ -832,6 +832,79 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_kernel(CombineArgs a) 
   CSA2_TS(10);
 }
 
+// Register-only combine for up to 32 * NW splits: grid (heads/16 * 32,
+// batch), NW waves.  Lane (n16, g) of wave w merges head 16*ht + n16,
+// channels of O^T tile ct, over splits 32w..32w+31: its 32 (max, sum) pairs
+// and 32 partial float4s are requested in one batch (split s of a head tile
+// sits at a fixed stride, so the addresses are a base plus s times it), and
+// the maximum, weights, sum and output are formed in registers; with two
+// waves, wave 1 hands (max, sum, output) to wave 0 through LDS.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) attend_combine_regs_kernel(CombineArgs a) {
+  constexpr int U = 32;
+  __shared__ float4 s_o[NW > 1 ? 64 : 1];
+  __shared__ float s_m[NW > 1 ? 64 : 1], s_l[NW > 1 ? 64 : 1];
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int HT = a.heads >> 4, ht = blockIdx.x >> 5, ct = blockIdx.x & 31;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int ns = a.splits, s0 = U * wv;
+  CSA2_TS(8);
+  const int64_t slot0 = (int64_t)b * ns * HT + ht;                 // slot of split 0
+  const float4 *po = reinterpret_cast<const float4 *>(a.part_o) + slot0 * (16 * D / 4) + ct * 64 + lane;
+  const float2 *pm = reinterpret_cast<const float2 *>(a.part_ml) + slot0 * 16 + n16;
+  const int64_t so = (int64_t)HT * (16 * D / 4), sm = (int64_t)HT * 16;   // per split
+  float2 ml[U];
+  float4 ov[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t sc = min(s0 + u, ns - 1);                        // clamped: one batch, no branch
+    ml[u] = pm[sc * sm];
+    ov[u] = po[sc * so];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float M = -__builtin_huge_valf();
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (s0 + u < ns) M = fmaxf(M, ml[u].x);
+  float L = 0.f;
+  float4 o = {0.f, 0.f, 0.f, 0.f};
+  if (M != -__builtin_huge_valf()) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float e = (s0 + u < ns && ml[u].x != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(ml[u].x - M) : 0.f;
+      L += e * ml[u].y;
+      o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
+    }
+  }
+  CSA2_TS(9);
+  if constexpr (NW > 1) {
+    if (wv == 1) { s_o[lane] = o; s_m[lane] = M; s_l[lane] = L; }
+    __syncthreads();
+    if (wv != 0) return;
+    const float M1 = s_m[lane], L1 = s_l[lane];
+    const float4 o1 = s_o[lane];
+    const float Mx = fmaxf(M, M1);
+    if (Mx == -__builtin_huge_valf()) {
+      L = 0.f;
+      o = float4{0.f, 0.f, 0.f, 0.f};
+    } else {
+      const float e0 = M == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(M - Mx);
+      const float e1 = M1 == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(M1 - Mx);
+      L = e0 * L + e1 * L1;
+      o.x = e0 * o.x + e1 * o1.x; o.y = e0 * o.y + e1 * o1.y;
+      o.z = e0 * o.z + e1 * o1.z; o.w = e0 * o.w + e1 * o1.w;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+  // lane (n16, g) of tile ct holds channels 128*(ct/8) + 4*(ct%8) + 32*g + 0..3
+  const int c0 = 128 * (ct >> 3) + 4 * (ct & 7) + 32 * g;
+  *reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.heads + 16 * ht + n16) * D + c0) = o;
+  CSA2_TS(10);
+}
+
+template __global__ void attend_combine_regs_kernel<1>(CombineArgs);
+template __global__ void attend_combine_regs_kernel<2>(CombineArgs);
 template __global__ void attend_combine_kernel<1>(CombineArgs);
 template __global__ void attend_combine_kernel<2>(CombineArgs);
 
