@@ -246,7 +246,7 @@ csa2_status run_rescore(const csa2_kv *kv, const float *q, int32_t heads, const 
   if (idx_out) {
     rescore_kernel<true><<<g, SCAN_THREADS, (size_t)n_cand * sizeof(uint64_t), s>>>(ra);
   } else {
-    rescore_kernel<false><<<g, SCAN_THREADS, 0, s>>>(ra);
+    rescore32_kernel<<<g, RESCORE32_THREADS, 0, s>>>(ra);
   }
   return launched("rescore");
 }

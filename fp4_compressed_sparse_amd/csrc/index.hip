@@ -198,9 +198,10 @@ __device__ __forceinline__ void load_block32(BlockRows32 &r, const uint8_t *__re
   }
 }
 
-// cnt: rows present (1..8); qb: Qbar[16j..16j+15] (LDS).  As each row is
-// consumed its registers receive the same row of the block at (nrow, nsrow),
-// so the next block's loads are in flight while this one is scored.
+// cnt: rows present (1..8); qb: Qbar[16j..16j+15] (LDS).  RELOAD: as each
+// row is consumed its registers receive the same row of the block at (nrow,
+// nsrow), so the next block's loads are in flight while this one is scored.
+template <bool RELOAD = true>
 __device__ __forceinline__ float block_score32(BlockRows32 &r, int cnt, const float *qb,
                                                const uint8_t *__restrict__ nrow,
                                                const uint8_t *__restrict__ nsrow, int j) {
@@ -228,8 +229,10 @@ __device__ __forceinline__ float block_score32(BlockRows32 &r, int cnt, const fl
         }
       }
     }
-    r.w[t] = *reinterpret_cast<const u32x2 *>(nrow + (int64_t)t * CODE_BYTES + 8 * j);
-    r.sc[t] = nsrow[(int64_t)t * SCALE_BYTES + j];
+    if (RELOAD) {
+      r.w[t] = *reinterpret_cast<const u32x2 *>(nrow + (int64_t)t * CODE_BYTES + 8 * j);
+      r.sc[t] = nsrow[(int64_t)t * SCALE_BYTES + j];
+    }
   }
   float g;
   if (cnt == BLOCK) {
@@ -1430,6 +1433,83 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   CSA2_TS(5);
 }
 
+// Pool rescoring without selection (the decode step's later layers): the
+// full scan's 32-lane layout (lane j owns scale group j), 8 waves of two
+// blocks, so a lane dequantises 8 x 16 values per block instead of the
+// 16-lane layout's 8 x 32.  Thread t forms Qbar channel t (heads in order;
+// 64 head requests per batch).  Same arithmetic, same order.
+constexpr int RESCORE32_THREADS = 512;
+constexpr int RESCORE32_BLOCKS = RESCORE32_THREADS / 32;   // blocks per round
+__global__ void __launch_bounds__(RESCORE32_THREADS) rescore32_kernel(RescoreArgs a) {
+  __shared__ float s_qbar[D];
+  const int b = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int half = lane >> 5, j = lane & 31;
+  const int64_t cap_blocks = a.capacity / BLOCK;   // loads stay inside the cache
+  const uint8_t *codes = a.codes + (int64_t)b * a.capacity * CODE_BYTES;
+  const uint8_t *scales = a.scales + (int64_t)b * a.capacity * SCALE_BYTES;
+  const int32_t *cand = a.cand + (int64_t)b * a.n_cand;
+  float *scores = a.scores + (int64_t)b * a.score_stride;
+  const int iters = (a.n_cand + RESCORE32_BLOCKS - 1) / RESCORE32_BLOCKS;
+  // first round's candidate ids and rows are requested before the query sum
+  int it = blockIdx.x;
+  int jj = it * RESCORE32_BLOCKS + 2 * wv + half;
+  int32_t blk = cand[min(jj, a.n_cand - 1)];          // unconditional: no branch
+  if (!(it < iters && jj < a.n_cand)) blk = -1;
+  BlockRows32 cur;
+  {
+    const int64_t lb = (blk >= 0 && blk < cap_blocks) ? blk : 0;   // block 0 always exists
+    load_block32(cur, codes + lb * BLOCK * CODE_BYTES, scales + lb * BLOCK * SCALE_BYTES, j);
+  }
+  CSA2_TS(0);
+  {
+    const float *qp = a.q + (int64_t)b * a.heads * D + t;
+    float acc = 0.f;
+    constexpr int HB = 64;
+    for (int h0 = 0; h0 < a.heads; h0 += HB) {
+      float v[HB];
+#pragma unroll
+      for (int u = 0; u < HB; ++u) v[u] = qp[(int64_t)min(h0 + u, a.heads - 1) * D];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < HB; ++u) {
+        const int h = h0 + u;
+        if (h == 0) acc = v[u];
+        else if (h < a.heads) acc = acc + v[u];
+      }
+    }
+    if (!__builtin_isfinite(acc)) raise_flag(FLAG_NONFINITE_Q);
+    s_qbar[t] = acc;
+  }
+  __syncthreads();
+  // the length only masks: read after the first rows and the query sum
+  const int64_t n = clamp_len(a.seq_len[b], a.limit);
+  const int64_t nblk = (n + BLOCK - 1) / BLOCK;
+  CSA2_TS(1);
+  const float *qb = s_qbar + 16 * j;
+  for (; it < iters; it += gridDim.x) {
+    if (jj < a.n_cand) {
+      if (blk >= 0 && blk < nblk) {
+        const int cnt = (int)min((int64_t)BLOCK, n - (int64_t)blk * BLOCK);
+        const float sc = block_score32<false>(cur, cnt, qb, nullptr, nullptr, j);
+        if (j == 0) scores[jj] = sc;
+      } else if (j == 0) {
+        scores[jj] = -__builtin_huge_valf();
+        if (blk >= nblk) raise_flag(FLAG_BAD_INDEX);
+      }
+    }
+    const int it_next = it + gridDim.x;
+    jj = it_next * RESCORE32_BLOCKS + 2 * wv + half;
+    blk = cand[min(jj, a.n_cand - 1)];
+    if (!(it_next < iters && jj < a.n_cand)) blk = -1;
+    if (it_next < iters) {
+      const int64_t lb = (blk >= 0 && blk < cap_blocks) ? blk : 0;
+      load_block32(cur, codes + lb * BLOCK * CODE_BYTES, scales + lb * BLOCK * SCALE_BYTES, j);
+    }
+  }
+  CSA2_TS(2);
+}
+
 // Reuse: idx_out = prior (grid-stride copy).
 __global__ void __launch_bounds__(256) copy_idx_kernel(const int32_t *__restrict__ src,
                                                        int32_t *__restrict__ dst, int64_t n) {
@@ -1442,6 +1522,5 @@ __global__ void __launch_bounds__(256) copy_idx_kernel(const int32_t *__restrict
 template __global__ void scan_kernel<true>(ScanArgs);
 template __global__ void scan_kernel<false>(ScanArgs);
 template __global__ void rescore_kernel<true>(RescoreArgs);
-template __global__ void rescore_kernel<false>(RescoreArgs);
 
 }  // namespace csa2
