@@ -116,3 +116,40 @@ def test_local_branch_ragged_batch_separate_selection():
     # pool 0 (every selecting layer scans all blocks), ragged batch, window not a multiple of 64
     w = W.scaled(W.WORKLOADS[1], context=3000, batch=3)
     run_and_compare(w, [3000, 150, 1200], 2, window=200)
+
+
+@pytest.mark.parametrize("ntypes,nblk", [
+    (3, 24000),     # the pool holds one score level: every candidate ties (degenerate range)
+    (8, 16000),     # two score levels, one holding 2,000 of the 2,048 candidates (crowded bin)
+])
+def test_tied_pool_scores_in_attention_selection(ntypes, nblk):
+    """Blocks drawn from a few distinct 8-row blocks: the layer's top-k
+    inside the pool (taken by the attention kernel) meets whole tied score
+    levels, and the lowest ids of the level win."""
+    from oracle.step import Cache, FULL, REINDEX, REUSE
+    require_gpu()
+    small = Cache(1, 8 * ntypes)
+    small.write(0, 0, W.kv_rows(0, 3, 0, 0, 8 * ntypes))
+    types = (np.arange(nblk, dtype=np.int64) * 7919 + 3) % ntypes
+    oc = Cache(1, nblk * 8)
+    oc.codes[0] = small.codes[0].reshape(ntypes, 8, 256)[types].reshape(-1, 256)
+    oc.scales[0] = small.scales[0].reshape(ntypes, 8, 32)[types].reshape(-1, 32)
+    oc.seq_len[0] = nblk * 8
+    g = to_device(oc)
+    H, K, P, scale = 64, 256, 2048, 1 / np.sqrt(512)
+    pattern = (FULL, REINDEX, REUSE)
+    qs = [W.queries(0, 20 + l, 0, 1, H) for l in range(len(pattern))]
+    log(f"tied pool: types={ntypes} blocks={nblk}")
+    ref = oracle_step([oc], [(m, 0, qs[l]) for l, m in enumerate(pattern)], None, K, P, scale)
+    ws = csa2.workspace(1, H, nblk * 8, P, K)
+    pool_out = torch.zeros((1, P), dtype=torch.int32, device="cuda")
+    outs = [torch.zeros((1, H, 512), dtype=torch.float32, device="cuda") for _ in pattern]
+    idxs = [torch.full((1, K), -9, dtype=torch.int32, device="cuda") for _ in pattern]
+    layers = [(m, 0, torch.from_numpy(qs[l]).cuda(), outs[l], idxs[l]) for l, m in enumerate(pattern)]
+    csa2.decode_step([g], layers, H, K, P, scale, ws, pool_out=pool_out)
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    assert np.array_equal(pool_out.cpu().numpy(), ref["pool"])
+    for l in range(len(pattern)):
+        assert np.array_equal(idxs[l].cpu().numpy(), ref["idx"][l]), l
+        assert normwise_err(outs[l].cpu().numpy(), ref["out"][l]) <= ATT_TOL, l
