@@ -77,6 +77,7 @@ def _index(g, q, topk, pool=0, cand=None, ws=None):
     ([4096, 1000, 9, 0], 64, 0),           # ragged batch, fewer blocks than k, empty
     ([65536 + 3], 256, 2048),              # pool + top-k inside it
     ([20000, 16000, 16], 128, 2048),       # pool larger than some sequences
+    ([70000, 20001, 5], 256, 2048),        # ragged batch over several 4,096-block select workgroups
 ])
 def test_full_scan_selection_matches_oracle(lengths, topk, pool):
     require_gpu()
