@@ -205,9 +205,12 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
     if (csa2_status st = launched("qbar")) return st;
   }
   // a workgroup scores 8 blocks per round (4 waves x 2); 1,536 workgroups
-  // fill the 256 compute units at 6 waves per SIMD
+  // fill the 256 compute units at 6 waves per SIMD.  A batch gets 128 per
+  // sequence (two per work group): the dispatcher refills the slots of short
+  // sequences with workgroups of long ones (ragged batch of 64: scan 382 ->
+  // 352 us, measured), where 1,536 spread evenly would leave them idle.
   const int64_t rounds = ceil_div(nblk_grid > 0 ? nblk_grid : 1, 8);
-  dim3 g1(grid_for(rounds, B, 1536), B);
+  dim3 g1(grid_for(rounds, B, B > 1 ? 128 * B : 1536), B);
   if (t_scan_before) (void)hipEventRecord(t_scan_before, s);
   scan_kernel<true><<<g1, SCAN_THREADS, 0, s>>>(sa);
   if (csa2_status st = launched("scan")) return st;
