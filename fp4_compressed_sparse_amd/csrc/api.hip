@@ -205,14 +205,19 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
     if (csa2_status st = launched("qbar")) return st;
   }
   // a workgroup scores 8 blocks per round (4 waves x 2); 1,536 workgroups
-  // fill the 256 compute units at 6 waves per SIMD.  A batch gets 128 per
-  // sequence (two per work group): the dispatcher refills the slots of short
-  // sequences with workgroups of long ones (ragged batch of 64: scan 382 ->
-  // 352 us, measured), where 1,536 spread evenly would leave them idle.
+  // fill the 256 compute units at 6 waves per SIMD.  A batch runs over its
+  // chunks laid end to end (scan_flat_kernel, 1,280 workgroups: 5 per
+  // compute unit, all resident), so ragged lengths leave no slot idle (batch
+  // of 64, 32K-128K: 382 -> 288 us, measured).  Beyond its limits a batch
+  // gets 128 workgroups per sequence, which the dispatcher moves from short
+  // sequences to long ones as they finish.
   const int64_t rounds = ceil_div(nblk_grid > 0 ? nblk_grid : 1, 8);
   dim3 g1(grid_for(rounds, B, B > 1 ? 128 * B : 1536), B);
   if (t_scan_before) (void)hipEventRecord(t_scan_before, s);
-  scan_kernel<true><<<g1, SCAN_THREADS, 0, s>>>(sa);
+  if (B > 1 && B <= SCAN_FLAT_MAXB && (int64_t)B * ((nblk_grid + 1) / 2) < ((int64_t)1 << 31))
+    scan_flat_kernel<<<1280, SCAN_THREADS, 0, s>>>(sa, B);
+  else
+    scan_kernel<true><<<g1, SCAN_THREADS, 0, s>>>(sa);
   if (csa2_status st = launched("scan")) return st;
   if (t_scan_after) (void)hipEventRecord(t_scan_after, s);
   SelectArgs se;

@@ -488,6 +488,126 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
   // kernel's last workgroup clears the copies and the work counters.
 }
 
+// ---- full scan of a batch over the flattened (sequence, chunk) space --------
+//
+// The same scoring and the same per-sequence outputs (scores, the 8 digit
+// histogram copies) as scan_kernel<true>, for batches: the chunks of 2 blocks
+// of every sequence are laid end to end (sequence b's chunks after those of
+// sequences 0..b-1), the whole range is cut into SCAN_GROUPS equal contiguous
+// regions, and the workgroups of group g (blockIdx.x mod SCAN_GROUPS) take the
+// chunks of region g, the first 4 per workgroup fixed, the rest from the
+// group's counter.  So no workgroup idles while long sequences still have
+// chunks, whatever the length mix.  Each wave keeps its current sequence's
+// Qbar in LDS and reloads it when its next chunk lies in another sequence
+// (a region spans one or a few sequences); digit counts go straight to the
+// sequence's histogram copy with no-return atomics.
+constexpr int SCAN_FLAT_MAXB = 512;     // sequences whose chunk prefix fits in LDS
+// Needs batch <= SCAN_FLAT_MAXB and batch * ceil(blocks / 2) < 2^31 (checked
+// by the host), so chunk indices are 32-bit.
+__global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(5)))
+scan_flat_kernel(ScanArgs a, int32_t batch) {
+  __shared__ float s_qbar[4][D];                   // per wave
+  __shared__ int32_t s_pre[SCAN_FLAT_MAXB + 1];    // chunks before sequence b
+  __shared__ int64_t s_len[SCAN_FLAT_MAXB];        // clamped lengths
+  __shared__ uint32_t s_wave[16];
+  const int lane = threadIdx.x & 63, t = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int half = lane >> 5, j = lane & 31;
+  CSA2_TS(0);
+  // lengths -> chunks per sequence -> exclusive prefix, 256 sequences a pass
+  uint32_t carry = 0;
+  for (int b0 = 0; b0 < batch; b0 += SCAN_THREADS) {
+    const int b = b0 + t;
+    int64_t n = 0;
+    if (b < batch) {
+      n = clamp_len(a.seq_len[b], a.limit);
+      s_len[b] = n;
+    }
+    const uint32_t ch = (uint32_t)(((n + BLOCK - 1) / BLOCK + 1) / 2);
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan(ch, &tot, s_wave);
+    if (b < batch) s_pre[b] = (int32_t)(carry + ex);
+    carry += tot;
+  }
+  if (t == 0) s_pre[batch] = (int32_t)carry;
+  __syncthreads();
+  const int total = s_pre[batch];
+  const int ngrp = min(SCAN_GROUPS, (int)gridDim.x);
+  const int grp = blockIdx.x % ngrp;
+  const int in_grp = blockIdx.x / ngrp;                        // workgroup index inside the group
+  const int per_grp = ((int)gridDim.x - grp + ngrp - 1) / ngrp;  // workgroups of this group
+  const int r0 = (int)((int64_t)total * grp / ngrp), r1 = (int)((int64_t)total * (grp + 1) / ngrp);
+  uint32_t *ctr = &a.ctrl[0].work[grp * 32];
+  const int first = 4 * per_grp;                               // fixed chunks of the group
+  auto grab = [&]() {
+    uint32_t k = 0;
+    if (lane == 0) k = atomic_add_agent(ctr, 1u);
+    return k;
+  };
+  // chunk -> sequence: largest b with s_pre[b] <= c (wave-uniform)
+  auto seq_of = [&](int c) {
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    return __builtin_amdgcn_readfirstlane(lo);
+  };
+  // this half-wave's block of chunk c (sequence b) and its first row; row 0
+  // of sequence 0 when past the region or the sequence (valid, never scored)
+  auto rows_of = [&](int c, int b, int &blk) {
+    blk = 2 * (c - s_pre[b]) + half;
+    const bool ok = c < r1 && (int64_t)blk * BLOCK < s_len[b];
+    return ok ? (int64_t)b * a.capacity + (int64_t)blk * BLOCK : (int64_t)0;
+  };
+  int c = r0 + 4 * in_grp + wv;
+  uint32_t pending = grab();
+  int cb = seq_of(c < r1 ? c : r0);
+  int blk;
+  BlockRows32 cur;
+  {
+    const int64_t row = rows_of(c, cb, blk);
+    load_block32(cur, a.codes + row * CODE_BYTES, a.scales + row * SCALE_BYTES, j);
+  }
+  int qb_seq = -1;
+  float *qbw = s_qbar[wv];
+  CSA2_TS(1);
+  while (c < r1) {
+    if (cb != qb_seq) {
+      // this wave's Qbar: 8 floats per lane (wave-local LDS, in order)
+      const float4 *src = reinterpret_cast<const float4 *>(a.qbar + (int64_t)cb * D);
+      const float4 v0 = src[2 * lane], v1 = src[2 * lane + 1];
+      reinterpret_cast<float4 *>(qbw)[2 * lane] = v0;
+      reinterpret_cast<float4 *>(qbw)[2 * lane + 1] = v1;
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      qb_seq = cb;
+    }
+    const int64_t nl = s_len[cb];                               // wave-uniform
+    const int64_t n = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(nl >> 32)) << 32) |
+                                (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)nl));
+    const int cn_raw = r0 + first + (int)__builtin_amdgcn_readlane(pending, 0);
+    pending = grab();
+    const int cn = cn_raw < r1 ? cn_raw : r1;
+    const int nbq = seq_of(cn < r1 ? cn : r0);
+    int blk_next;
+    const int64_t nrow = rows_of(cn, nbq, blk_next);
+    const bool valid = (int64_t)blk * BLOCK < n;
+    const int cnt = (int)max((int64_t)1, min((int64_t)BLOCK, n - (int64_t)blk * BLOCK));
+    const float sc = block_score32(cur, cnt, qbw + 16 * j, a.codes + nrow * CODE_BYTES,
+                                   a.scales + nrow * SCALE_BYTES, j);
+    if (j == 0 && valid) {
+      a.scores[(int64_t)cb * a.score_stride + blk] = sc;
+      uint32_t *gh = a.hist + ((int64_t)cb * HIST_COPIES + (blockIdx.x % HIST_COPIES)) * HIST_BINS;
+      __hip_atomic_fetch_add(&gh[ord_key(sc) >> HIST_SHIFT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    c = cn;
+    cb = nbq;
+    blk = blk_next;
+  }
+  CSA2_TS(2);
+}
+
 // ---- select (after a full scan) ------------------------------------------
 
 struct SelectArgs {
