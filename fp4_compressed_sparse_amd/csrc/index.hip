@@ -499,8 +499,9 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
 // group's counter.  So no workgroup idles while long sequences still have
 // chunks, whatever the length mix.  Each wave keeps its current sequence's
 // Qbar in LDS and reloads it when its next chunk lies in another sequence
-// (a region spans one or a few sequences); digit counts go straight to the
-// sequence's histogram copy with no-return atomics.
+// (a region spans one or a few sequences); its digit counts collect in a
+// per-wave LDS histogram, added to the sequence's copy when the wave moves
+// on and at the end.
 constexpr int SCAN_FLAT_MAXB = 512;     // sequences whose chunk prefix fits in LDS
 // Needs batch <= SCAN_FLAT_MAXB and batch * ceil(blocks / 2) < 2^31 (checked
 // by the host), so chunk indices are 32-bit.
@@ -510,10 +511,30 @@ scan_flat_kernel(ScanArgs a, int32_t batch) {
   __shared__ int32_t s_pre[SCAN_FLAT_MAXB + 1];    // chunks before sequence b
   __shared__ int64_t s_len[SCAN_FLAT_MAXB];        // clamped lengths
   __shared__ uint32_t s_wave[16];
+  __shared__ uint32_t s_hw[4][HIST_BINS];          // per wave: digit counts of its current sequence
   const int lane = threadIdx.x & 63, t = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int half = lane >> 5, j = lane & 31;
   CSA2_TS(0);
+  uint32_t *hw = s_hw[wv];
+#pragma unroll
+  for (int i = 0; i < HIST_BINS / 64; ++i) hw[lane + 64 * i] = 0;
+  // the wave's counts into sequence sb's histogram copy, then cleared
+  auto flush = [&](int sb) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    uint32_t *gh = a.hist + ((int64_t)sb * HIST_COPIES + (blockIdx.x % HIST_COPIES)) * HIST_BINS;
+#pragma unroll
+    for (int i = 0; i < HIST_BINS / 64; ++i) {
+      const uint32_t v = hw[lane + 64 * i];
+      if (v) {
+        __hip_atomic_fetch_add(&gh[lane + 64 * i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hw[lane + 64 * i] = 0;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  };
   // lengths -> chunks per sequence -> exclusive prefix, 256 sequences a pass
   uint32_t carry = 0;
   for (int b0 = 0; b0 < batch; b0 += SCAN_THREADS) {
@@ -574,6 +595,7 @@ scan_flat_kernel(ScanArgs a, int32_t batch) {
   CSA2_TS(1);
   while (c < r1) {
     if (cb != qb_seq) {
+      if (qb_seq >= 0) flush(qb_seq);
       // this wave's Qbar: 8 floats per lane (wave-local LDS, in order)
       const float4 *src = reinterpret_cast<const float4 *>(a.qbar + (int64_t)cb * D);
       const float4 v0 = src[2 * lane], v1 = src[2 * lane + 1];
@@ -598,13 +620,13 @@ scan_flat_kernel(ScanArgs a, int32_t batch) {
                                    a.scales + nrow * SCALE_BYTES, j);
     if (j == 0 && valid) {
       a.scores[(int64_t)cb * a.score_stride + blk] = sc;
-      uint32_t *gh = a.hist + ((int64_t)cb * HIST_COPIES + (blockIdx.x % HIST_COPIES)) * HIST_BINS;
-      __hip_atomic_fetch_add(&gh[ord_key(sc) >> HIST_SHIFT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      atomicAdd(&hw[ord_key(sc) >> HIST_SHIFT], 1u);
     }
     c = cn;
     cb = nbq;
     blk = blk_next;
   }
+  if (qb_seq >= 0) flush(qb_seq);
   CSA2_TS(2);
 }
 
