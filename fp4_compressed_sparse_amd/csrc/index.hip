@@ -1593,14 +1593,26 @@ __global__ void __launch_bounds__(RESCORE32_THREADS) rescore32_kernel(RescoreArg
   const int32_t *cand = a.cand + (int64_t)b * a.n_cand;
   float *scores = a.scores + (int64_t)b * a.score_stride;
   const int iters = (a.n_cand + RESCORE32_BLOCKS - 1) / RESCORE32_BLOCKS;
-  // first round's candidate ids and rows are requested before the query sum
+  // rounds it, it + grid, ...: the ids of the first two rounds and the rows
+  // of the first are requested before the query sum; afterwards each round's
+  // rows are requested as the previous round's rows are consumed and the ids
+  // run one round further ahead (a batch gives a workgroup many rounds)
+  auto id_of = [&](int r, int &jr) {
+    jr = r * RESCORE32_BLOCKS + 2 * wv + half;
+    int32_t v = cand[min(jr, a.n_cand - 1)];           // unconditional: no branch
+    if (!(r < iters && jr < a.n_cand)) v = -1;
+    return v;
+  };
+  auto rows_of = [&](int32_t blkv) {
+    return (blkv >= 0 && blkv < cap_blocks) ? (int64_t)blkv : (int64_t)0;   // block 0 always exists
+  };
   int it = blockIdx.x;
-  int jj = it * RESCORE32_BLOCKS + 2 * wv + half;
-  int32_t blk = cand[min(jj, a.n_cand - 1)];          // unconditional: no branch
-  if (!(it < iters && jj < a.n_cand)) blk = -1;
+  int jj, jj1;
+  int32_t blk = id_of(it, jj);
+  int32_t blk1 = id_of(it + (int)gridDim.x, jj1);
   BlockRows32 cur;
   {
-    const int64_t lb = (blk >= 0 && blk < cap_blocks) ? blk : 0;   // block 0 always exists
+    const int64_t lb = rows_of(blk);
     load_block32(cur, codes + lb * BLOCK * CODE_BYTES, scales + lb * BLOCK * SCALE_BYTES, j);
   }
   CSA2_TS(0);
@@ -1630,24 +1642,27 @@ __global__ void __launch_bounds__(RESCORE32_THREADS) rescore32_kernel(RescoreArg
   CSA2_TS(1);
   const float *qb = s_qbar + 16 * j;
   for (; it < iters; it += gridDim.x) {
-    if (jj < a.n_cand) {
-      if (blk >= 0 && blk < nblk) {
-        const int cnt = (int)min((int64_t)BLOCK, n - (int64_t)blk * BLOCK);
-        const float sc = block_score32<false>(cur, cnt, qb, nullptr, nullptr, j);
-        if (j == 0) scores[jj] = sc;
-      } else if (j == 0) {
+    const bool more = it + (int)gridDim.x < iters;              // uniform
+    const int64_t nb = rows_of(blk1);
+    const bool ok = blk >= 0 && blk < nblk;
+    const int cnt = ok ? (int)min((int64_t)BLOCK, n - (int64_t)blk * BLOCK) : 1;
+    float sc;
+    if (more)
+      sc = block_score32<true>(cur, cnt, qb, codes + nb * BLOCK * CODE_BYTES, scales + nb * BLOCK * SCALE_BYTES, j);
+    else
+      sc = block_score32<false>(cur, cnt, qb, nullptr, nullptr, j);
+    if (jj < a.n_cand && j == 0) {
+      if (ok) {
+        scores[jj] = sc;
+      } else {
         scores[jj] = -__builtin_huge_valf();
         if (blk >= nblk) raise_flag(FLAG_BAD_INDEX);
       }
     }
-    const int it_next = it + gridDim.x;
-    jj = it_next * RESCORE32_BLOCKS + 2 * wv + half;
-    blk = cand[min(jj, a.n_cand - 1)];
-    if (!(it_next < iters && jj < a.n_cand)) blk = -1;
-    if (it_next < iters) {
-      const int64_t lb = (blk >= 0 && blk < cap_blocks) ? blk : 0;
-      load_block32(cur, codes + lb * BLOCK * CODE_BYTES, scales + lb * BLOCK * SCALE_BYTES, j);
-    }
+    int jj2;
+    const int32_t blk2 = id_of(it + 2 * (int)gridDim.x, jj2);
+    blk = blk1; jj = jj1;
+    blk1 = blk2; jj1 = jj2;
   }
   CSA2_TS(2);
 }
