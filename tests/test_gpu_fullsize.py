@@ -265,3 +265,112 @@ def test_decoder20_1m_full_size_with_local_branch():
         log(f"layer {l}: attention with window error {err:.2e} over {pos.size} + {win} positions")
         assert err <= ATT_TOL, (l, err)
     _CHUNKS.clear()
+
+
+def _seq_rows(wid, cache, b, positions, n0, step_row):
+    """Synthetic float32 rows of sequence b at the given positions; position
+    n0 is the step's appended row."""
+    positions = np.asarray(positions, dtype=np.int64)
+    out = np.empty((positions.size, 512), dtype=np.float32)
+    chunks = {c: W._kv_chunk(wid, cache, b, c) for c in sorted(set((positions[positions != n0] // W.CHUNK).tolist()))}
+    for i, p in enumerate(positions.tolist()):
+        out[i] = step_row if p == n0 else chunks[p // W.CHUNK][p % W.CHUNK]
+    return out
+
+
+def test_workload4_ragged_batch64_full_size_sampled():
+    """The batch workload at full size: 64 sequences of 32,768..131,072
+    positions (seeded lengths), [Full, Reindex, Reuse], 16 heads, pool 2,048,
+    top-128, one appended row each, in the launch configuration bench.py
+    times (the batch scan over the sequences' chunks laid end to end).
+    Checks: appended rows byte-equal the oracle's; every sequence's pool is
+    the top 2,048 of its exported full-scan scores and its Reindex selection
+    the top 128 of its exported pool scores; sampled scores bit-exact against
+    the oracle; attention of sampled sequences within 2e-3."""
+    require_gpu()
+    w = W.WORKLOADS[4]
+    lengths = W.lengths(w)
+    B = len(lengths)
+    n = lengths + 1
+    cap = int((int(n.max()) + 7) // 8 * 8)
+    log(f"building the cache: {B} sequences of {int(lengths.min())}..{int(lengths.max())} positions")
+    g = bench.build_caches(w, lengths, cap, log_every=1000)[0]
+    g.max_len = int(n.max())
+    H, K, P = w.heads, w.topk, w.pool
+    L = len(w.pattern)
+    qs = [W.queries(w.wid, l, 0, B, H) for l in range(L)]
+    step_rows = W.append_rows(w.wid, 0, 0, B)                          # [B, 512]
+    qt = [torch.from_numpy(q).cuda() for q in qs]
+    outs = [torch.zeros((B, H, 512), dtype=torch.float32, device="cuda") for _ in range(L)]
+    idxs = []
+    for m in w.pattern:
+        idxs.append(idxs[-1] if m == 2 else torch.full((B, K), -9, dtype=torch.int32, device="cuda"))
+    pool = torch.full((B, P), -9, dtype=torch.int32, device="cuda")
+    ws = csa2.workspace(B, H, g.max_len, P, K)
+    layers = [(m, 0, qt[l], outs[l], idxs[l]) for l, m in enumerate(w.pattern)]
+    csa2.decode_step([g], layers, H, K, P, w.scale, ws, pool_out=pool,
+                     new_rows=torch.from_numpy(step_rows[None]).cuda())
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    log("decode step done")
+
+    assert np.array_equal(g.seq_len.cpu().numpy(), n)
+    oc, osc = quantize_rows(step_rows)
+    for b in range(B):
+        assert np.array_equal(g.codes[b, int(lengths[b])].cpu().numpy(), oc[b])
+        assert np.array_equal(g.scales[b, int(lengths[b])].cpu().numpy(), osc[b])
+    log("appended rows byte-equal")
+
+    nblk = (n + BLOCK - 1) // BLOCK
+    s0 = torch.zeros((B, int(nblk.max())), dtype=torch.float32, device="cuda")
+    csa2.block_scores(g, qt[0], s0)
+    s0 = s0.cpu().numpy()
+    p = pool.cpu().numpy()
+    sel1 = idxs[1].cpu().numpy()
+    pool_t = pool.clone()
+    s1 = torch.zeros((B, P), dtype=torch.float32, device="cuda")
+    csa2.block_scores(g, qt[1], s1, cand=pool_t)
+    s1 = s1.cpu().numpy()
+    for b in range(B):
+        nb = int(nblk[b])
+        assert np.all(np.diff(p[b]) > 0) and p[b][0] >= 0 and p[b][-1] < nb, b
+        assert _top_keys_ok(np.arange(nb), s0[b][:nb], p[b]), b
+        assert _top_keys_ok(p[b], s1[b], sel1[b]), b
+    assert np.array_equal(idxs[2].cpu().numpy(), sel1)
+    log(f"all {B} pools are the top {P} of their scan scores; Reindex selections the top {K} of their pool")
+
+    rng = np.random.default_rng(44)
+    picks = sorted({int(np.argmin(lengths)), int(np.argmax(lengths))} | set(rng.choice(B, 2, replace=False).tolist()))
+    for b in picks:
+        n0, nb = int(lengths[b]), int(nblk[b])
+        qbar0 = collapse_query(qs[0][b])
+        blocks = np.unique(np.concatenate([rng.choice(min(nb - 1, W.CHUNK // BLOCK), 6, replace=False), [nb - 1]]))
+        want = []
+        for beta in blocks.tolist():
+            cnt = min(BLOCK, int(n[b]) - BLOCK * beta)
+            c, s = quantize_rows(_seq_rows(w.wid, 0, b, np.arange(BLOCK * beta, BLOCK * beta + cnt), n0, step_rows[b]))
+            want.append(block_scores_from_keys(qbar0, block_keys(c, s, cnt))[0])
+        assert np.array_equal(s0[b][blocks].view(np.uint32), np.asarray(want, dtype=np.float32).view(np.uint32)), b
+        # the Reindex layer's pool rescoring, sampled on pool blocks of the first chunk
+        qbar1 = collapse_query(qs[1][b])
+        near = np.flatnonzero(p[b] < W.CHUNK // BLOCK)
+        pick = rng.choice(near, min(4, near.size), replace=False)
+        want = []
+        for beta in p[b][pick].tolist():
+            cnt = min(BLOCK, int(n[b]) - BLOCK * beta)
+            c, s = quantize_rows(_seq_rows(w.wid, 0, b, np.arange(BLOCK * beta, BLOCK * beta + cnt), n0, step_rows[b]))
+            want.append(block_scores_from_keys(qbar1, block_keys(c, s, cnt))[0])
+        assert np.array_equal(s1[b][pick].view(np.uint32), np.asarray(want, dtype=np.float32).view(np.uint32)), b
+        for l in (0, 1):
+            idx = idxs[l].cpu().numpy()[b]
+            pos = gather_positions(idx, int(n[b]))
+            codes, scales = quantize_rows(_seq_rows(w.wid, 0, b, pos, n0, step_rows[b]))
+            kept = idx[idx >= 0]
+            ccodes = np.zeros((BLOCK * kept.size, 256), dtype=np.uint8)
+            cscales = np.zeros((BLOCK * kept.size, 32), dtype=np.uint8)
+            ccodes[:pos.size] = codes
+            cscales[:pos.size] = scales
+            ref = sparse_attend(ccodes, cscales, pos.size, qs[l][b], np.arange(kept.size), w.scale)
+            err = normwise_err(outs[l].cpu().numpy()[b][None], ref[None])
+            assert err <= ATT_TOL, (b, l, err)
+        log(f"sequence {b} ({n0} positions): sampled scores bit-exact, attention within {ATT_TOL}")
