@@ -307,9 +307,9 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   CombineArgs ca;
   ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = splits; ca.heads = heads; ca.out = out;
   if (splits <= 32)
-    attend_combine_regs_kernel<1><<<dim3((heads / 16) * 32, B), 64, 0, s>>>(ca);
+    attend_combine_regs_kernel<4, 8><<<dim3((heads / 16) * 32, B), 256, 0, s>>>(ca);
   else if (splits <= 64)
-    attend_combine_regs_kernel<2><<<dim3((heads / 16) * 32, B), 128, 0, s>>>(ca);
+    attend_combine_regs_kernel<4, 16><<<dim3((heads / 16) * 32, B), 256, 0, s>>>(ca);
   else
     attend_combine_kernel<2><<<dim3((heads / 16) * 32, B), 128, 0, s>>>(ca);
   return launched("combine");
@@ -594,9 +594,9 @@ csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, 
   CombineArgs ca;
   ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = L.att_splits; ca.heads = heads; ca.out = out;
   if (L.att_splits <= 32)
-    attend_combine_regs_kernel<1><<<dim3((heads / 16) * 32, n_q), 64, 0, s>>>(ca);
+    attend_combine_regs_kernel<4, 8><<<dim3((heads / 16) * 32, n_q), 256, 0, s>>>(ca);
   else if (L.att_splits <= 64)
-    attend_combine_regs_kernel<2><<<dim3((heads / 16) * 32, n_q), 128, 0, s>>>(ca);
+    attend_combine_regs_kernel<4, 16><<<dim3((heads / 16) * 32, n_q), 256, 0, s>>>(ca);
   else
     attend_combine_kernel<2><<<dim3((heads / 16) * 32, n_q), 128, 0, s>>>(ca);
   return launched("prefill combine");

@@ -832,18 +832,17 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_kernel(CombineArgs a) 
   CSA2_TS(10);
 }
 
-// Register-only combine for up to 32 * NW splits: grid (heads/16 * 32,
+// Register-only combine for up to U * NW splits: grid (heads/16 * 32,
 // batch), NW waves.  Lane (n16, g) of wave w merges head 16*ht + n16,
-// channels of O^T tile ct, over splits 32w..32w+31: its 32 (max, sum) pairs
-// and 32 partial float4s are requested in one batch (split s of a head tile
+// channels of O^T tile ct, over splits Uw..Uw+U-1: its U (max, sum) pairs
+// and U partial float4s are requested in one batch (split s of a head tile
 // sits at a fixed stride, so the addresses are a base plus s times it), and
-// the maximum, weights, sum and output are formed in registers; with two
-// waves, wave 1 hands (max, sum, output) to wave 0 through LDS.
-template <int NW>
+// the maximum, weights, sum and output are formed in registers; with more
+// waves, waves 1.. hand (max, sum, output) to wave 0 through LDS.
+template <int NW, int U>
 __global__ void __launch_bounds__(64 * NW) attend_combine_regs_kernel(CombineArgs a) {
-  constexpr int U = 32;
-  __shared__ float4 s_o[NW > 1 ? 64 : 1];
-  __shared__ float s_m[NW > 1 ? 64 : 1], s_l[NW > 1 ? 64 : 1];
+  __shared__ float4 s_o[NW > 1 ? NW - 1 : 1][64];
+  __shared__ float s_m[NW > 1 ? NW - 1 : 1][64], s_l[NW > 1 ? NW - 1 : 1][64];
   const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int HT = a.heads >> 4, ht = blockIdx.x >> 5, ct = blockIdx.x & 31;
   const int n16 = lane & 15, g = lane >> 4;
@@ -878,21 +877,23 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_regs_kernel(CombineArg
   }
   CSA2_TS(9);
   if constexpr (NW > 1) {
-    if (wv == 1) { s_o[lane] = o; s_m[lane] = M; s_l[lane] = L; }
+    // waves 1.. hand (max, sum, output) to wave 0, which merges them in order
+    if (wv > 0) { s_o[wv - 1][lane] = o; s_m[wv - 1][lane] = M; s_l[wv - 1][lane] = L; }
     __syncthreads();
     if (wv != 0) return;
-    const float M1 = s_m[lane], L1 = s_l[lane];
-    const float4 o1 = s_o[lane];
-    const float Mx = fmaxf(M, M1);
-    if (Mx == -__builtin_huge_valf()) {
-      L = 0.f;
-      o = float4{0.f, 0.f, 0.f, 0.f};
-    } else {
-      const float e0 = M == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(M - Mx);
-      const float e1 = M1 == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(M1 - Mx);
-      L = e0 * L + e1 * L1;
-      o.x = e0 * o.x + e1 * o1.x; o.y = e0 * o.y + e1 * o1.y;
-      o.z = e0 * o.z + e1 * o1.z; o.w = e0 * o.w + e1 * o1.w;
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const float M1 = s_m[w - 1][lane], L1 = s_l[w - 1][lane];
+      const float4 o1 = s_o[w - 1][lane];
+      const float Mx = fmaxf(M, M1);
+      if (Mx != -__builtin_huge_valf()) {
+        const float e0 = M == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(M - Mx);
+        const float e1 = M1 == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(M1 - Mx);
+        L = e0 * L + e1 * L1;
+        o.x = e0 * o.x + e1 * o1.x; o.y = e0 * o.y + e1 * o1.y;
+        o.z = e0 * o.z + e1 * o1.z; o.w = e0 * o.w + e1 * o1.w;
+        M = Mx;
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -903,8 +904,8 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_regs_kernel(CombineArg
   CSA2_TS(10);
 }
 
-template __global__ void attend_combine_regs_kernel<1>(CombineArgs);
-template __global__ void attend_combine_regs_kernel<2>(CombineArgs);
+template __global__ void attend_combine_regs_kernel<4, 8>(CombineArgs);
+template __global__ void attend_combine_regs_kernel<4, 16>(CombineArgs);
 template __global__ void attend_combine_kernel<1>(CombineArgs);
 template __global__ void attend_combine_kernel<2>(CombineArgs);
 
