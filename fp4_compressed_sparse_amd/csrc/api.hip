@@ -693,7 +693,7 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
     }
     // the first layer (Full) scans all blocks: its query sum rides along
     QbarJob qj{st->layers[0].q, st->heads, at<float>(st->ws, L.qbar)};
-    append_kernel<<<dim3(B, nc + nr + 1), 128, 0, s>>>(aa, rr, st->new_rows, B, nc, nr, qj);
+    append_kernel<<<dim3(B, nc + nr + QBAR_SLICES), 128, 0, s>>>(aa, rr, st->new_rows, B, nc, nr, qj);
     if (csa2_status e = launched("append")) return e;
     qbar_ready = true;
   }

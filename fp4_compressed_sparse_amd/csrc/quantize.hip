@@ -219,44 +219,46 @@ struct SwaRings {
 
 // The indexer's query sum of one layer, computed in the same launch as the
 // appends (it only reads the query): Qbar[b] = heads added in order.
+constexpr int QBAR_SLICES = D / 128;   // query-sum workgroups per sequence in append_kernel
+
 struct QbarJob {
   const float *q;           // [batch][heads][512]; NULL = none
   int32_t heads;
   float *qbar;              // [batch][512]
 };
 
-// grid (batch, n_caches + n_rings [+ 1]), 128 threads.  y < n_caches:
-// x[y][b][512] -> position seq_len[b] of cache y.  Then ring y - n_caches:
-// rows[b] -> position seq_len[b], slot seq_len[b] % slots.  A last row of
-// workgroups (when qj.q is set) sums the query heads of sequence b.
+// grid (batch, n_caches + n_rings [+ QBAR_SLICES]), 128 threads.  y <
+// n_caches: x[y][b][512] -> position seq_len[b] of cache y.  Then ring y -
+// n_caches: rows[b] -> position seq_len[b], slot seq_len[b] % slots.  The
+// last QBAR_SLICES rows of workgroups (when qj.q is set) sum the query heads
+// of sequence b, 128 channels each.
 __global__ void __launch_bounds__(128) append_kernel(AppendArgs a, SwaRings r, const float *__restrict__ x,
                                                      int32_t batch, int32_t n_caches, int32_t n_rings,
                                                      QbarJob qj) {
   const int b = blockIdx.x, c = blockIdx.y;
   const int q = threadIdx.x;
   if (c >= n_caches + n_rings) {
-    // channels 4q..4q+3, heads in order, 16 heads per batch of loads
-    constexpr int HB = 16;
-    const float4 *qp = reinterpret_cast<const float4 *>(qj.q + (int64_t)b * qj.heads * D) + q;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    // query sum: slice k of QBAR_SLICES owns channels 128k..128k+127, one
+    // per thread, heads added in order; the heads of a batch of 64 are
+    // requested together (one memory round trip for 64 heads)
+    const int ch = 128 * (c - n_caches - n_rings) + q;
+    constexpr int HB = 64;
+    const float *qp = qj.q + (int64_t)b * qj.heads * D + ch;
+    float acc = 0.f;
     for (int h0 = 0; h0 < qj.heads; h0 += HB) {
-      float4 v[HB];
+      float v[HB];
 #pragma unroll
-      for (int j = 0; j < HB; ++j) v[j] = qp[(int64_t)min(h0 + j, qj.heads - 1) * (D / 4)];
+      for (int j = 0; j < HB; ++j) v[j] = qp[(int64_t)min(h0 + j, qj.heads - 1) * D];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < HB; ++j) {
         const int h = h0 + j;
-        if (h == 0) {
-          acc = v[j];
-        } else if (h < qj.heads) {
-          acc.x = acc.x + v[j].x; acc.y = acc.y + v[j].y;
-          acc.z = acc.z + v[j].z; acc.w = acc.w + v[j].w;
-        }
+        if (h == 0) acc = v[j];
+        else if (h < qj.heads) acc = acc + v[j];
       }
     }
-    if (!finite4(acc)) raise_flag(FLAG_NONFINITE_Q);
-    reinterpret_cast<float4 *>(qj.qbar + (int64_t)b * D)[q] = acc;
+    if (!__builtin_isfinite(acc)) raise_flag(FLAG_NONFINITE_Q);
+    qj.qbar[(int64_t)b * D + ch] = acc;
     return;
   }
   if (c >= n_caches) {
