@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     float csc[KPT];
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
-      const int j = min(tid + ATT_THREADS * k, m - 1);
+      const int j = min(64 * KPT * wv + 64 * k + lane, m - 1);     // wave wv: a quarter of the list
       cid[k] = cb[j];
       csc[k] = sb[j];
     }
@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     uint64_t kr[KPT];
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
-      const int j = tid + ATT_THREADS * k;
+      const int j = 64 * KPT * wv + 64 * k + lane;
       const bool ok = j < m && cid[k] >= 0 && cid[k] < nbs;
       kr[k] = ok ? make_key(csc[k], (uint32_t)cid[k]) : 0ull;
       if (j < m) s_keys[j] = kr[k];

@@ -836,41 +836,38 @@ __device__ __forceinline__ uint64_t topk_threshold(const uint64_t (&kr)[KPT], co
   return s_state[0];
 }
 
-// Register form of the block top-k: thread t holds list entries t + 256k
-// (keys kr, 0 = empty, and their ids); s_keys is the same list in LDS, read
-// only by the radix fallback.
+// Register form of the block top-k (256 threads): wave w holds list
+// entries 64*KPT*w + 64k + lane, k < KPT (a contiguous quarter of the list;
+// keys kr, 0 = empty, and their ids); s_keys is the same list in LDS, read
+// only by the radix fallback.  Ordered compaction: each wave counts its
+// chosen entries by ballots, the four totals give every wave its output
+// offset, and inside a wave the entries follow in list order.
 template <int KPT>
 __device__ __forceinline__ void select_top_regs(const uint64_t (&kr)[KPT], const int32_t (&ids)[KPT],
                                                 const uint64_t *s_keys, int m, int r, int32_t *out,
                                                 int32_t *s_sel, int len, uint32_t *s_hist,
                                                 uint64_t *s_state, uint32_t *s_wave) {
-  static_assert(KPT * 4 <= 128, "entry table holds 128 counts");
-  __shared__ uint32_t s_cnt[128];
+  __shared__ uint32_t s_wtot[4];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   int reff = 0;
   const uint64_t T = topk_threshold<KPT>(kr, s_keys, m, r, &reff, s_hist, s_state, s_wave);
-  uint32_t mine = 0;                             // bit k: entry t + 256k is kept
+  uint32_t wtot = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k)
+    wtot += (uint32_t)__popcll(__ballot(reff > 0 && kr[k] != 0 && kr[k] >= T));
+  if (lane == 0) s_wtot[wv] = wtot;
+  __syncthreads();
+  CSA2_TOPK_TS(6);
+  uint32_t base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t v = s_wtot[w];
+    base += w < wv ? v : 0u;
+    total += v;
+  }
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const bool f = reff > 0 && kr[k] != 0 && kr[k] >= T;
-    const uint64_t mask = __ballot(f);
-    if (f) mine |= 1u << k;
-    if (lane == 0) s_cnt[4 * k + wv] = (uint32_t)__popcll(mask);
-  }
-  if (t >= 4 * KPT && t < 128) s_cnt[t] = 0;
-  __syncthreads();
-  CSA2_TOPK_TS(6);
-  // every wave: exclusive offsets of entry pairs (2 per lane)
-  const uint32_t c0 = s_cnt[2 * lane], c1 = s_cnt[2 * lane + 1];
-  const uint32_t incl = wave_incl_scan(c0 + c1);
-  const uint32_t pair_excl = incl - c0 - c1;
-  const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int e = 4 * k + wv;
-    const uint32_t base = __builtin_amdgcn_readlane(pair_excl, e >> 1) +
-                          ((e & 1) ? __builtin_amdgcn_readlane(c0, e >> 1) : 0u);
-    const bool f = (mine >> k) & 1u;
     const uint64_t mask = __ballot(f);
     if (f) {
       const uint32_t pos = base + lanes_below(mask);
@@ -879,6 +876,7 @@ __device__ __forceinline__ void select_top_regs(const uint64_t (&kr)[KPT], const
         if (out) out[pos] = ids[k];
       }
     }
+    base += (uint32_t)__popcll(mask);
   }
   for (int j = (int)total + t; j < len; j += 256) {
     s_sel[j] = -1;
@@ -890,20 +888,20 @@ __device__ __forceinline__ void select_top_regs(const uint64_t (&kr)[KPT], const
 
 // Top r of the list s_keys[0..m) (LDS, 0 = empty entry, m <= 256 * KPT):
 // the chosen entries' s_ids, in list order, go to s_sel (LDS) and, unless
-// out is NULL, to out[0..len), -1 padded.  Ordered compaction by ballots:
-// entry (round k, wave w) covers list positions 256k + 64w + 0..63; a table
-// of per-entry counts gives each entry's output offset.  All 256 threads.
+// out is NULL, to out[0..len), -1 padded.  All 256 threads; wave w takes the
+// contiguous quarter of the list select_top_regs expects.
 template <int KPT>
 __device__ __forceinline__ void select_top(const uint64_t *s_keys, const int32_t *s_ids, int m, int r, int32_t *out,
                            int32_t *s_sel, int len, uint32_t *s_hist, uint64_t *s_state,
                            uint32_t *s_wave) {
-  const int t = threadIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint64_t kr[KPT];
   int32_t ids[KPT];
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
-    const int j = min(t + 256 * k, m - 1);
-    kr[k] = (t + 256 * k < m) ? s_keys[j] : 0ull;
+    const int e = 64 * KPT * wv + 64 * k + lane;
+    const int j = min(e, m - 1);
+    kr[k] = e < m ? s_keys[j] : 0ull;
     ids[k] = s_ids[j];
   }
   select_top_regs<KPT>(kr, ids, s_keys, m, r, out, s_sel, len, s_hist, s_state, s_wave);
