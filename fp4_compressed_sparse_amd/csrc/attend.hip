@@ -735,9 +735,11 @@ struct CombineArgs {
   float *out;               // [batch][heads][512]
 };
 
+// LDS-staged combine for more than 64 splits (up to MAX_SPLITS; the
+// register-only combine below takes 64 or fewer).
 // grid (heads/16 * 32, batch), NW waves per workgroup: workgroup (ht, ct)
-// merges O^T tile ct (1 KB) of head tile ht over every split, so the 4 MB of
-// partials of a 64-head step spread over 128 compute units.  Wave w takes
+// merges O^T tile ct (1 KB) of head tile ht over every split, so the
+// partials spread over heads/16 * 32 workgroups per sequence.  Wave w takes
 // splits 32w.. of each batch of 32*NW; the (max, sum) pairs of the first
 // 32*NW splits and each wave's first 32 tiles are requested in one batch,
 // before any of them is used (one memory round trip for <= 32*NW splits);
@@ -906,7 +908,6 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_regs_kernel(CombineArg
 
 template __global__ void attend_combine_regs_kernel<4, 8>(CombineArgs);
 template __global__ void attend_combine_regs_kernel<4, 16>(CombineArgs);
-template __global__ void attend_combine_kernel<1>(CombineArgs);
 template __global__ void attend_combine_kernel<2>(CombineArgs);
 
 }  // namespace csa2
