@@ -173,6 +173,36 @@ def test_selection_with_repeated_block_types(nblk, ntypes, pool, topk):
     assert np.array_equal(idx, idx2)
 
 
+@pytest.mark.parametrize("batch", [512, 520])
+def test_many_short_sequences(batch):
+    """512 sequences take the batch scan over the chunks laid end to end;
+    520 exceed its per-workgroup length table and take one scan per
+    sequence.  Short ragged sequences (1..200 positions), top-4 and pool 16."""
+    require_gpu()
+    lengths = np.random.default_rng(batch).integers(1, 201, batch)
+    # 8 source sequences quantised once by the oracle; sequence b holds the
+    # first lengths[b] rows of source b % 8 (its own query keeps its choice
+    # its own)
+    src = Cache(8, 200)
+    for k in range(8):
+        src.write(k, 0, W.kv_rows(1, 2, k, 0, 200))
+    oc = Cache(batch, cap_for(int(lengths.max())))
+    for b, n in enumerate(lengths):
+        oc.codes[b, :n] = src.codes[b % 8, :n]
+        oc.scales[b, :n] = src.scales[b % 8, :n]
+        oc.seq_len[b] = n
+    g = to_device(oc)
+    q = W.queries(1, 9, 0, batch, 4)
+    log(f"many sequences: batch={batch}")
+    ref = [I.block_scores(oc.codes[b], oc.scales[b], int(n), q[b]) for b, n in enumerate(lengths)]
+    for pool in (0, 16):
+        idx, pool_out, _ = _index(g, q, 4, pool)
+        for b, (ids, sc) in enumerate(ref):
+            if pool:
+                assert np.array_equal(pool_out[b], select(ids, sc, pool)), b
+            assert np.array_equal(idx[b], select(ids, sc, 4)), (b, pool)
+
+
 def test_reuse_copies_prior():
     require_gpu()
     prior = torch.arange(3 * 40, dtype=torch.int32, device="cuda").view(3, 40)
