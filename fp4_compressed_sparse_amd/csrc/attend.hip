@@ -43,6 +43,20 @@ constexpr int ATT_SP = 64;                        // gathered positions per stag
 constexpr int ROW_HALVES = D + 8;                 // LDS row stride: 1040 bytes
 constexpr int P_STRIDE = ATT_SP + 8;              // LDS P row stride (halves): no bank conflicts
 
+// A thread dequantises 16 code bytes into 64 bytes of fp16 row, stored as
+// four 16-byte chunks; the 16 threads of a row sit 64 bytes apart, so
+// storing the chunks in the same order for every lane puts lanes 0, 2, 4,
+// ... on the same LDS banks.  Each lane starts at chunk chunk_rot(i16) and
+// wraps: any 8 consecutive lanes (32 banks) and any 16 (64 banks) then
+// write distinct 16-byte bank groups.
+__device__ __forceinline__ int chunk_rot(int i16) { return ((i16 >> 1) + (i16 >> 3)) & 3; }
+// element s of the result is v[(s + rot) & 3]
+__device__ __forceinline__ u32x4 rotate4(u32x4 v, int rot) {
+  if (rot & 1) v = u32x4{v[1], v[2], v[3], v[0]};
+  if (rot & 2) v = u32x4{v[2], v[3], v[0], v[1]};
+  return v;
+}
+
 struct AttendArgs {
   const uint8_t *codes;
   const uint8_t *scales;
@@ -127,6 +141,10 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   // ---- gathered rows of a stage: block ids, then rows (two round trips) --
   constexpr int PASSES = ATT_SP / 16;     // rows per thread per stage
   const int i16 = tid & 15;               // this thread's 16-byte column of a row
+  // (the window variants keep the plain order: the rotation's registers
+  // would halve their occupancy)
+  const int rot = WIN ? 0 : chunk_rot(i16);
+  const bool rhi0 = (rot & 2) != 0, rhi1 = ((rot + 1) & 2) != 0;   // chunk rot, rot + 1 (mod 4) >= 2
   int32_t blkv[PASSES];
   bool okv[PASSES];
   u32x4 wr[PASSES];
@@ -318,13 +336,18 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
       const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
       const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
       u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i16);
+      const u32x4 wrot = rotate4(wr[k], rot);
+      // chunk (s + rot) & 3 takes scale 1 when it is 2 or 3
+      const f16x2 svr[4] = {rhi0 ? sv1 : sv0, rhi1 ? sv1 : sv0, rhi0 ? sv0 : sv1, rhi1 ? sv0 : sv1};
 #pragma unroll
-      for (int dw = 0; dw < 4; ++dw) {
-        const f16x2 sv = dw < 2 ? sv0 : sv1;
-        f16x2 h0 = e2m1x2_to_f16<0>(wr[k][dw]) * sv;
-        f16x2 h1 = e2m1x2_to_f16<1>(wr[k][dw]) * sv;
-        f16x2 h2 = e2m1x2_to_f16<2>(wr[k][dw]) * sv;
-        f16x2 h3 = e2m1x2_to_f16<3>(wr[k][dw]) * sv;
+      for (int s = 0; s < 4; ++s) {
+        const int dw = (s + rot) & 3;
+        const uint32_t w = wrot[s];
+        const f16x2 sv = svr[s];
+        f16x2 h0 = e2m1x2_to_f16<0>(w) * sv;
+        f16x2 h1 = e2m1x2_to_f16<1>(w) * sv;
+        f16x2 h2 = e2m1x2_to_f16<2>(w) * sv;
+        f16x2 h3 = e2m1x2_to_f16<3>(w) * sv;
         dst[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
                         __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
       }
@@ -489,6 +512,8 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
 
   constexpr int PASSES = ATT_SP / 32;     // rows per thread per stage
   const int i16 = tid & 15;
+  const int rot = chunk_rot(i16);
+  const bool rhi0 = (rot & 2) != 0, rhi1 = ((rot + 1) & 2) != 0;   // chunk rot, rot + 1 (mod 4) >= 2
   int32_t blkv[PASSES], nxt[PASSES];
   u32x4 wr[PASSES];
   uint32_t scr[PASSES];
@@ -558,13 +583,17 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
       const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
       const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
       u32x4 *dst = reinterpret_cast<u32x4 *>(sv + pp * ROW_HALVES + 32 * i16);
+      const u32x4 wrot = rotate4(wr[k], rot);
+      const f16x2 svr[4] = {rhi0 ? sv1 : sv0, rhi1 ? sv1 : sv0, rhi0 ? sv0 : sv1, rhi1 ? sv0 : sv1};
 #pragma unroll
-      for (int dw = 0; dw < 4; ++dw) {
-        const f16x2 svs = dw < 2 ? sv0 : sv1;
-        f16x2 h0 = e2m1x2_to_f16<0>(wr[k][dw]) * svs;
-        f16x2 h1 = e2m1x2_to_f16<1>(wr[k][dw]) * svs;
-        f16x2 h2 = e2m1x2_to_f16<2>(wr[k][dw]) * svs;
-        f16x2 h3 = e2m1x2_to_f16<3>(wr[k][dw]) * svs;
+      for (int s = 0; s < 4; ++s) {
+        const int dw = (s + rot) & 3;
+        const uint32_t w = wrot[s];
+        const f16x2 svs = svr[s];
+        f16x2 h0 = e2m1x2_to_f16<0>(w) * svs;
+        f16x2 h1 = e2m1x2_to_f16<1>(w) * svs;
+        f16x2 h2 = e2m1x2_to_f16<2>(w) * svs;
+        f16x2 h3 = e2m1x2_to_f16<3>(w) * svs;
         dst[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
                         __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
       }
