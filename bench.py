@@ -14,6 +14,8 @@ dominant kernel, CPU-oracle baseline).  Progress goes to stderr.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
   python bench.py --copy-probe     (plain copy kernel for counter calibration)
+  python bench.py --prefill 4096   (prefill-side sparse attention, its own JSON line)
+  python bench.py --prefill-write  (FP4 quantisation of 1,048,576 prompt rows, its own JSON line)
 """
 import argparse
 import hashlib
@@ -31,18 +33,25 @@ BLOCK_BYTES = 8 * TOKEN_BYTES  # 2,304
 PMC_FILE = os.path.join(ROOT, "profiles", "scan_kernel_decoder20-1m_pmc.txt")
 SCAN_SOURCES = [os.path.join(ROOT, "fp4_compressed_sparse_amd", "csrc", f)
                 for f in ("index.hip", "common.hpp")]
+QUANT_PMC_FILE = os.path.join(ROOT, "profiles", "quantize_rows_kernel_prefill-write-1m_pmc.txt")
+QUANT_SOURCES = [os.path.join(ROOT, "fp4_compressed_sparse_amd", "csrc", f)
+                 for f in ("quantize.hip", "common.hpp", "api.hip")]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def scan_source_sha():
+def source_sha(paths):
     h = hashlib.sha256()
-    for p in SCAN_SOURCES:
+    for p in paths:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def scan_source_sha():
+    return source_sha(SCAN_SOURCES)
 
 
 def step_bytes(w, n_tokens):
@@ -167,17 +176,17 @@ def cpu_baseline(w, window=0):
     }
 
 
-def pmc_traffic():
-    """HBM bytes per scan launch from the committed rocprofv3 counter runs
-    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), if they
-    were taken on the current scan kernel source; else None."""
+def pmc_traffic(path=PMC_FILE, sources=SCAN_SOURCES):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), if it
+    was taken on the current kernel sources; else None.  Default: the scan."""
     try:
-        with open(PMC_FILE) as f:
+        with open(path) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("source_sha") != scan_source_sha():
+    if kv.get("source_sha") != source_sha(sources):
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -326,6 +335,78 @@ def prefill_bench(args):
     print(json.dumps(result), flush=True)
 
 
+def prefill_write_bench(args):
+    """Prefill write (fp4_quantize_kv): the batch-64 prompt's 64 x 16,384 =
+    1,048,576 fresh fp32 rows, resident in HBM, quantised in one launch into
+    a cache of the same size."""
+    import numpy as np
+    import torch
+
+    import fp4_compressed_sparse_amd as csa2
+    import workloads as W
+
+    csa2.load()
+    torch.cuda.set_device(0)
+    R = 64 * W.PREFILL_WRITE_ROWS
+    t0 = time.perf_counter()
+    x_host = W.kv_rows_threaded(4, 9, 0, R, threads=16)
+    x = torch.from_numpy(x_host).cuda()
+    log(f"rows generated and copied in {time.perf_counter() - t0:.1f} s")
+    codes = torch.empty((R, 256), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((R, 32), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        csa2.fp4_quantize_kv(x, codes, scales)
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    reps = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    t_start = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        csa2.fp4_quantize_kv(x, codes, scales)
+        b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    launch_s = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    per_row = 512 * 4 + TOKEN_BYTES                  # fp32 row read + FP4 codes and scales written
+    gbs = R * per_row / launch_s / 1e9
+    log(f"prefill write: {R} rows, {launch_s * 1e6:.1f} us per launch, {gbs:.0f} GB/s")
+    result = {
+        "metric": "prefill write rows/s (FP4 quantisation of 1,048,576 fp32 KV rows into the cache, 1 GPU)",
+        "value": round(R * reps / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / reps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32 in, FP4 E2M1 + E4M3 out", "data": "synthetic",
+        "config": {"workload": "prefill-write-1m", "rows": R, "sequences": 64,
+                   "rows_per_sequence": W.PREFILL_WRITE_ROWS,
+                   "median_event_launch_us": round(launch_s * 1e6, 2)},
+        "roofline": {"bound": "hbm", "kernel": "quantize_rows_kernel (one lane per 16-channel group)",
+                     "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4), "traffic": pmc_traffic(QUANT_PMC_FILE, QUANT_SOURCES),
+                     "algorithmic_bytes_per_launch": R * per_row},
+    }
+    if not args.no_cpu_baseline:
+        from oracle.quantize import quantize_rows
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:                           # pragma: no cover
+            threadpool_limits = None
+        import contextlib
+        ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+        C = 65536                                     # chunks bound the oracle's float64 temporaries
+        with ctx:
+            t1 = time.perf_counter()
+            for r0 in range(0, R, C):
+                quantize_rows(x_host[r0:r0 + C])
+            cpu_s = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": round(R / cpu_s, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"all {R} rows, {C} at a time, on 1 host thread: {cpu_s:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +419,8 @@ def main():
                     help="instead of the decode step: batched prefill-side sparse attention of T "
                          "queries (the last T positions of a 1M-position cache, 64 heads, top-256 "
                          "blocks each); prints its own JSON line")
+    ap.add_argument("--prefill-write", action="store_true",
+                    help="time fp4_quantize_kv over the batch-64 prompt's 1,048,576 fp32 rows (its own JSON line)")
     ap.add_argument("--swa", type=int, default=0, metavar="W",
                     help="give every layer a local branch: an FP8 sliding-window ring of W positions "
                          "(prefilled, one row appended per layer per step) attended in the same "
@@ -356,6 +439,9 @@ def main():
         return
     if args.prefill:
         prefill_bench(args)
+        return
+    if args.prefill_write:
+        prefill_write_bench(args)
         return
 
     import numpy as np

@@ -93,43 +93,83 @@ __device__ __forceinline__ uint32_t quantize_quad(float4 v, uint32_t *sbyte, boo
   return n0 | (n1 << 4) | (n2 << 8) | (n3 << 12);
 }
 
-// rows x 512 floats -> codes/scales rows dst_row[r] (or r).  Each thread
-// takes QU quads per round, QU grid strides apart, and requests all of them
-// (and their destination rows) before quantising any: QU loads in flight
-// per lane instead of one.  The stride is a multiple of 128 quads (one row),
-// so a wave's 64 lanes always cover half of one row.
-constexpr int QU = 4;
+// E2M1 magnitude code of RNE(a / s) from t[k] = s * midpoint_k, with the
+// tie rule folded into the comparisons: a tie at an odd midpoint (0.75,
+// 1.75, 3.5) goes up to the even code (>=), at an even one (0.25, 1.25,
+// 2.5, 5) it stays down (>).  Same result as mag_code.
+__device__ __forceinline__ uint32_t mag_code_ties(float a, const float *t) {
+  return (uint32_t)(a > t[0]) + (uint32_t)(a >= t[1]) + (uint32_t)(a > t[2]) + (uint32_t)(a >= t[3]) +
+         (uint32_t)(a > t[4]) + (uint32_t)(a >= t[5]) + (uint32_t)(a > t[6]);
+}
+
+// rows x 512 floats -> codes/scales rows dst_row[r] (or r), one lane per
+// 16-channel group: the lane reads the group's 64 bytes, finds the group's
+// scale once (no cross-lane exchange) and writes its 8 code bytes with one
+// store.  Each thread takes GU groups per round, a grid stride apart, and
+// requests all of them (and their destination rows) before quantising any.
+constexpr int GU = 1;
 __global__ void __launch_bounds__(256) quantize_rows_kernel(
     const float *__restrict__ x, int64_t rows, const int64_t *__restrict__ dst_row,
     int64_t dst_rows, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
-  const int64_t total = rows * 128;  // a multiple of 64: whole waves stay together
+  const int64_t total = rows * NGROUPS;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const float4 *x4 = reinterpret_cast<const float4 *>(x);
-  for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < total; i0 += stride * QU) {
-    float4 v[QU];
-    int64_t d[QU];
+  for (int64_t g0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g0 < total; g0 += stride * GU) {
+    float4 v[GU][4];
+    int64_t d[GU];
 #pragma unroll
-    for (int u = 0; u < QU; ++u) {
-      const int64_t i = min(i0 + u * stride, total - 1);      // clamped: no branch
-      v[u] = x4[i];
-      d[u] = dst_row ? dst_row[i >> 7] : (i >> 7);
+    for (int u = 0; u < GU; ++u) {
+      const int64_t gi = min(g0 + u * stride, total - 1);     // clamped: no branch
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[u][j] = x4[gi * 4 + j];
+      d[u] = dst_row ? dst_row[gi / NGROUPS] : gi / NGROUPS;
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < QU; ++u) {
-      const int64_t i = i0 + u * stride;
-      if (i >= total) break;                                  // uniform per wave
-      const int q = (int)(i & 127);
-      uint32_t sb;
-      bool bad;
-      const uint32_t packed = quantize_quad(v[u], &sb, &bad);
+    for (int u = 0; u < GU; ++u) {
+      const int64_t gi = g0 + u * stride;
+      if (gi >= total) break;
+      const int grp = (int)(gi % NGROUPS);
       if (d[u] < 0 || d[u] >= dst_rows) {
-        if (q == 0) raise_flag(FLAG_CAPACITY);
+        if (grp == 0) raise_flag(FLAG_CAPACITY);
         continue;
       }
-      if (bad && (q & 3) == 0) raise_flag(FLAG_NONFINITE_KV);
-      reinterpret_cast<uint16_t *>(codes + d[u] * CODE_BYTES)[q] = (uint16_t)packed;
-      if ((q & 3) == 0) scales[d[u] * SCALE_BYTES + (q >> 2)] = (uint8_t)sb;
+      const float *f = reinterpret_cast<const float *>(v[u]);
+      // |x| as bits: finite magnitudes order like their bit patterns, and
+      // any infinity or NaN is at least 0x7f800000
+      uint32_t mb = 0;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2)
+        mb = max(mb, max(__float_as_uint(f[e]) & 0x7fffffffu, __float_as_uint(f[e + 1]) & 0x7fffffffu));
+      uint32_t w0 = 0, w1 = 0, sc = 0;
+      if (mb >= 0x7f800000u) {
+        raise_flag(FLAG_NONFINITE_KV);               // the group is written as zeros
+      } else {
+        sc = scale_code(__uint_as_float(mb));
+        const float sv = e4m3_pos(sc);
+        uint32_t nib[16];
+        if (sv == 0.0f) {
+          // magnitudes all round to 0; keep the signs
+#pragma unroll
+          for (int e = 0; e < 16; ++e) nib[e] = (__float_as_uint(f[e]) >> 31) << 3;
+        } else {
+          const float t[7] = {sv * 0.25f, sv * 0.75f, sv * 1.25f, sv * 1.75f, sv * 2.5f, sv * 3.5f, sv * 5.0f};
+          // one value's comparisons at a time: hoisting all 112 of them
+          // ahead of their sums runs out of scalar mask registers
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            nib[e] = mag_code_ties(fabsf(f[e]), t) | ((__float_as_uint(f[e]) >> 31) << 3);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          w0 |= nib[e] << (4 * e);
+          w1 |= nib[8 + e] << (4 * e);
+        }
+      }
+      *reinterpret_cast<uint2 *>(codes + d[u] * CODE_BYTES + 8 * grp) = uint2{w0, w1};
+      scales[d[u] * SCALE_BYTES + grp] = (uint8_t)sc;
     }
   }
 }
