@@ -119,20 +119,31 @@ def build_caches(w, lengths, capacity, log_every=8):
     return caches
 
 
-def cpu_baseline(w, window=0):
-    """The oracle's decode step timed on the host (1 thread), on two bounded
-    contexts, extrapolated linearly in context to the workload's context
-    (window > 0: every layer with its local branch, as the GPU step)."""
+def cpu_threads(threads):
+    """Context that limits the host's BLAS/OpenMP pools to `threads` (0: the
+    pools' own size), and the thread count in effect inside it."""
+    import contextlib
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:                               # pragma: no cover
+        return contextlib.nullcontext(), 1
+    if threads > 0:
+        return threadpool_limits(limits=threads), threads
+    n = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return contextlib.nullcontext(), n
+
+
+def cpu_baseline(w, window=0, threads=1):
+    """The oracle's decode step timed on the host (1 thread unless told
+    otherwise), on two bounded contexts, extrapolated linearly in context to
+    the workload's context (window > 0: every layer with its local branch,
+    as the GPU step)."""
     import numpy as np
 
     import workloads as W
     from oracle.step import Cache, decode_step
     from oracle.swa import SwaCache
 
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:                               # pragma: no cover
-        threadpool_limits = None
     samples = (8192, 32768)
     times = []
     for n in samples:
@@ -154,8 +165,7 @@ def cpu_baseline(w, window=0):
                 sw.seq_len[0] = n
                 swa.append(sw)
             srows = np.stack([W.swa_append_rows(w.wid, l, 0, 1) for l in range(len(w.pattern))])
-        import contextlib
-        ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+        ctx, used = cpu_threads(threads)
         with ctx:
             t0 = time.perf_counter()
             decode_step(caches, layers, rows, w.topk, w.pool, w.scale, swa=swa, swa_rows=srows, window=window)
@@ -167,11 +177,11 @@ def cpu_baseline(w, window=0):
     return {
         "value": round(w.batch / t_full, 6),
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": used,
         "kind": "oracle",
         "sample": (f"one decode step of the same 20-layer pattern (64 heads, pool 2048, top-256, batch 1"
                    + (f", a {window}-position window on every layer" if window else "") + ") "
-                   f"at contexts {n1} and {n2}: {t1:.2f} s and {t2:.2f} s on 1 host thread; "
+                   f"at contexts {n1} and {n2}: {t1:.2f} s and {t2:.2f} s on {used} host thread(s); "
                    f"extrapolated linearly in context to {w.context} positions: {t_full:.1f} s per step"),
     }
 
@@ -414,6 +424,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, help="workload id (default 3: 20 layers at 1M)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=1, metavar="N",
+                    help="host threads for the oracle baseline of the decode step (default 1; 0: the BLAS pool's size)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--prefill", type=int, default=0, metavar="T",
                     help="instead of the decode step: batched prefill-side sparse attention of T "
@@ -589,7 +601,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.swa)
+        result["cpu_baseline"] = cpu_baseline(w, args.swa, args.cpu_threads)
     print(json.dumps(result), flush=True)
 
 
