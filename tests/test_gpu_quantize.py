@@ -139,3 +139,29 @@ def test_prefill_write_full_size_sampled():
     gc = cache.codes.view(-1, Q.CODE_BYTES)[sel].cpu().numpy()
     gs = cache.scales.view(-1, Q.SCALE_BYTES)[sel].cpu().numpy()
     assert np.array_equal(gc, oc) and np.array_equal(gs, os_)
+
+
+def test_rows_beyond_one_grid_round():
+    """More rows than one grid round covers (2^20 workgroups x 256 lanes =
+    268,435,456 groups = 8,388,608 rows): the last 4,099 rows are quantised
+    in a second grid-stride round.  65,536 workload rows, quantised once by
+    the oracle, are tiled over the 8,392,707 rows; every row is compared."""
+    require_gpu()
+    S, R = 65536, 8_388_608 + 4_099
+    src = W.kv_rows(4, 2, 0, 0, S)
+    oc, os_ = Q.quantize_rows(src)
+    log(f"quantize {R} rows (two grid rounds)")
+    reps = (R + S - 1) // S
+    x = torch.from_numpy(src).cuda().repeat(reps, 1)[:R]
+    codes = torch.full((R, Q.CODE_BYTES), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((R, Q.SCALE_BYTES), 0xCD, dtype=torch.uint8, device="cuda")
+    csa2.fp4_quantize_kv(x, codes, scales)
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    del x
+    want_c = torch.from_numpy(oc).cuda()
+    want_s = torch.from_numpy(os_).cuda()
+    for r0 in range(0, R, S):
+        n = min(S, R - r0)
+        assert torch.equal(codes[r0:r0 + n], want_c[:n]), r0
+        assert torch.equal(scales[r0:r0 + n], want_s[:n]), r0
