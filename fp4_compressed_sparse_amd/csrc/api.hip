@@ -394,7 +394,7 @@ csa2_status fp4_quantize_kv(const float *x, int64_t rows, const int64_t *dst_row
   if (rows == 0) return CSA2_OK;
   if (!x || !codes || !scales) return fail(CSA2_E_ARG, "NULL pointer");
   if (!aligned(x, 16)) return fail(CSA2_E_ARG, "x must be 16-byte aligned");
-  if (!aligned(codes, 4) || !aligned(scales, 1)) return fail(CSA2_E_ARG, "codes must be 4-byte aligned");
+  if (!aligned(codes, 8)) return fail(CSA2_E_ARG, "codes must be 8-byte aligned (a group's 8 code bytes are one store)");
   if (dst_row && !aligned(dst_row, 8)) return fail(CSA2_E_ARG, "dst_row must be 8-byte aligned");
   if (dst_rows < 0 || (!dst_row && dst_rows < rows))
     return fail(CSA2_E_CAPACITY, "dst_rows %lld too small for %lld rows", (long long)dst_rows, (long long)rows);

@@ -113,7 +113,8 @@ typedef struct {
  *          codes/scales, or NULL for row i -> row i.  Rows outside
  *          [0, dst_rows) are skipped and flag CSA2_FLAG_CAPACITY.
  * dst_rows rows available in codes/scales (>= rows when dst_row is NULL).
- * codes    device uint8 [dst_rows][256]; scales device uint8 [dst_rows][32].
+ * codes    device uint8 [dst_rows][256], 8-byte aligned; scales device uint8
+ *          [dst_rows][32].  Both are written, never read.
  * A group with NaN/Inf is written as zero codes and scale 0 and flags
  * CSA2_FLAG_NONFINITE_KV.
  */

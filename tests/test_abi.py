@@ -63,6 +63,9 @@ def test_quantize_argument_errors(lib):
     assert "NULL" in _err(lib)
     assert lib.fp4_quantize_kv(ctypes.c_void_p(0x1004), 4, None, 4, ctypes.c_void_p(0x2000),
                                ctypes.c_void_p(0x3000), None) == 1          # x misaligned
+    assert lib.fp4_quantize_kv(ctypes.c_void_p(0x1000), 4, None, 4, ctypes.c_void_p(0x2004),
+                               ctypes.c_void_p(0x3000), None) == 1          # codes not 8-byte aligned
+    assert "8-byte" in _err(lib)
     assert lib.fp4_quantize_kv(ctypes.c_void_p(0x1000), 4, None, 3, ctypes.c_void_p(0x2000),
                                ctypes.c_void_p(0x3000), None) == 4          # too few rows
 
