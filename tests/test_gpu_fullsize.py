@@ -42,11 +42,11 @@ def _chunks(wid, cache, chunk_ids):
     """Synthetic prefill chunks of one cache (kept for reuse), drawn on a
     thread pool: each chunk has its own seed."""
     from concurrent.futures import ThreadPoolExecutor
-    need = [c for c in sorted(set(chunk_ids)) if (cache, c) not in _CHUNKS]
+    need = [c for c in sorted(set(chunk_ids)) if (wid, cache, c) not in _CHUNKS]
     with ThreadPoolExecutor(max_workers=8) as ex:
         for c, rows in zip(need, ex.map(lambda c: W._kv_chunk(wid, cache, 0, c), need)):
-            _CHUNKS[(cache, c)] = rows
-    return {c: _CHUNKS[(cache, c)] for c in chunk_ids}
+            _CHUNKS[(wid, cache, c)] = rows
+    return {c: _CHUNKS[(wid, cache, c)] for c in chunk_ids}
 
 
 def _rows(wid, cache, positions, n_prefill, step_rows):
@@ -374,3 +374,52 @@ def test_workload4_ragged_batch64_full_size_sampled():
             err = normwise_err(outs[l].cpu().numpy()[b][None], ref[None])
             assert err <= ATT_TOL, (b, l, err)
         log(f"sequence {b} ({n0} positions): sampled scores bit-exact, attention within {ATT_TOL}")
+
+
+def test_prefill_attend_1m_4096_queries_sampled():
+    """Prefill-side attention in the configuration bench.py --prefill 4096
+    times: 4,096 queries at the last positions of a 1,048,576-position cache
+    (GPU-quantised), 64 heads, 256 blocks per query (its own block and 255
+    seeded-random earlier ones), one workgroup per query normalising its
+    output in-kernel.  Every output finite; twelve sampled queries (the first
+    and last two, the rest spread) against the oracle's float64 attention
+    over their selected positions (rows regenerated and quantised by the
+    oracle), within the 2e-3 normwise bound."""
+    require_gpu()
+    import dataclasses
+    from oracle.prefill import prefill_attend
+    _CHUNKS.clear()
+    w = dataclasses.replace(W.WORKLOADS[3], pattern=(0,))          # one cache
+    n = int(w.context)
+    T, H, K = 4096, w.heads, w.topk
+    log(f"prefill 1M: building the {n}-position cache")
+    cache = bench.build_caches(w, np.array([n]), (n + 7) // 8 * 8)[0]
+    cache.max_len = n
+    rng = np.random.default_rng(4096)
+    qpos = np.arange(n - T, n, dtype=np.int64)
+    idx = np.full((T, K), -1, dtype=np.int32)
+    for t, p in enumerate(qpos.tolist()):
+        own = p // 8
+        idx[t] = np.sort(np.concatenate([rng.choice(own, K - 1, replace=False), [own]]))
+    q = W.queries(w.wid, 100, 0, T, H)
+    out = torch.full((T, H, 512), float("nan"), dtype=torch.float32, device="cuda")
+    ws = csa2.prefill_workspace(T, H, K)
+    csa2.prefill_attend(cache, 0, torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
+                        torch.from_numpy(idx).cuda(), w.scale, out, ws)
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    sample = np.unique(np.concatenate([[0, 1, T - 2, T - 1],
+                                       np.random.default_rng(5).choice(np.arange(2, T - 2), 8, replace=False)]))
+    pos = np.unique((8 * idx[sample].astype(np.int64)[:, :, None] + np.arange(8)).ravel())
+    pos = pos[pos < n]
+    log(f"prefill 1M: oracle rows for {sample.size} queries ({pos.size} positions)")
+    codes = np.zeros((n, 256), dtype=np.uint8)
+    scales = np.zeros((n, 32), dtype=np.uint8)
+    codes[pos], scales[pos] = quantize_rows(_rows(w.wid, 0, pos, -1, None))
+    ref = prefill_attend(codes, scales, qpos[sample], q[sample], idx[sample], w.scale)
+    err = normwise_err(got[sample], ref)
+    log(f"prefill 1M: sampled normwise error {err:.2e}")
+    assert err <= ATT_TOL
+    _CHUNKS.clear()
