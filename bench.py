@@ -443,8 +443,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(sequences shard by batch with no exchange; see DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path (a batch would "
+              "shard by sequence across GPUs with no exchange; one GPU's share is what this measures)",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
