@@ -389,8 +389,9 @@ def prefill_write_bench(args):
         "n_gpus": 1, "steps": reps, "warmup": args.warmup,
         "ms_per_step": round(elapsed * 1e3 / reps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp32 in, FP4 E2M1 + E4M3 out", "data": "synthetic",
+        "dtype": "f32", "data": "synthetic",
         "config": {"workload": "prefill-write-1m", "rows": R, "sequences": 64,
+                   "formats": "float32 rows in; FP4 E2M1 codes + E4M3 scales per 16 channels out",
                    "rows_per_sequence": W.PREFILL_WRITE_ROWS,
                    "median_event_launch_us": round(launch_s * 1e6, 2)},
         "roofline": {"bound": "hbm", "kernel": "quantize_rows_kernel (one lane per 16-channel group)",
