@@ -665,6 +665,13 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
       if (ly.swa_row && !aligned(ly.swa_row, 16)) return fail(CSA2_E_ARG, "layer %d: swa_row misaligned", l);
       if (ly.swa_row && ++n_rings > CSA2_MAX_SWA_LAYERS)
         return fail(CSA2_E_SHAPE, "more than %d layers append SWA rows", CSA2_MAX_SWA_LAYERS);
+      // two appends into one ring would race on its slot and length
+      if (ly.swa_row)
+        for (int k = 0; k < l; ++k) {
+          const csa2_layer &o = st->layers[k];
+          if (o.swa && o.swa_row && (o.swa->seq_len == ly.swa->seq_len || o.swa->codes == ly.swa->codes))
+            return fail(CSA2_E_ARG, "layers %d and %d append into the same SWA ring", k, l);
+        }
     }
   }
   Layout L;

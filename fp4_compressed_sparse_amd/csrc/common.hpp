@@ -84,7 +84,7 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
 // of each workgroup records s_memrealtime (100 MHz) after its wave's memory
 // operations complete.
 #ifdef CSA2_PHASE_TIMING
-constexpr int TS_SLOTS = 16;
+constexpr int TS_SLOTS = 32;
 __device__ unsigned long long g_phase_ts[4096][TS_SLOTS];
 #define CSA2_TS(k)                                                                     \
   do {                                                                                 \

@@ -14,9 +14,9 @@
 //   |x|  <> scale * (midpoint of two E2M1 values) (<= 7 significant bits)
 // so no division is ever rounded.
 //
-// Thread layout: 4 lanes per 16-channel group, 4 channels (one float4) per
-// lane, 128 lanes per row: loads of 1 KB per wave instruction, 128-byte
-// code stores, one scale byte per group.
+// Both the bulk row quantiser and the decode-step append run the same
+// per-group routine (quantize_group): one lane per 16-channel group reads
+// the group's 64 bytes, finds its scale once and packs its 8 code bytes.
 #include "common.hpp"
 
 namespace csa2 {
@@ -53,46 +53,6 @@ __device__ __forceinline__ uint32_t scale_code(float amax) {
   return c;
 }
 
-// E2M1 magnitude code (0..7) of RNE(a / s) given t[k] = s * midpoint_k.
-__device__ __forceinline__ uint32_t mag_code(float a, const float *t) {
-  uint32_t c = 0;
-#pragma unroll
-  for (int k = 0; k < 7; ++k) c += (a > t[k]) ? 1u : 0u;
-  // ties at the midpoints 0.75, 1.75, 3.5 (k odd) go up to the even code
-  c += (a == t[1] || a == t[3] || a == t[5]) ? 1u : 0u;
-  return c;
-}
-
-// Quantise one float4 (channels 4q..4q+3 of a row); all 4 lanes of a group
-// must call together.  Returns the 16-bit packed codes; *sbyte the scale.
-__device__ __forceinline__ uint32_t quantize_quad(float4 v, uint32_t *sbyte, bool *bad) {
-  float ax = fabsf(v.x), ay = fabsf(v.y), az = fabsf(v.z), aw = fabsf(v.w);
-  bool nf = !(__builtin_isfinite(v.x) && __builtin_isfinite(v.y) &&
-              __builtin_isfinite(v.z) && __builtin_isfinite(v.w));
-  float amax = fmaxf(fmaxf(ax, ay), fmaxf(az, aw));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  int nfi = nf ? 1 : 0;
-  nfi |= __shfl_xor(nfi, 1);
-  nfi |= __shfl_xor(nfi, 2);
-  *bad = nfi != 0;
-  if (nfi) { *sbyte = 0; return 0; }
-  uint32_t sc = scale_code(amax);
-  float s = e4m3_pos(sc);
-  *sbyte = sc;
-  if (s == 0.0f) {
-    // magnitudes all round to 0; keep the signs
-    return ((__float_as_uint(v.x) >> 31) << 3) | ((__float_as_uint(v.y) >> 31) << 7) |
-           ((__float_as_uint(v.z) >> 31) << 11) | ((__float_as_uint(v.w) >> 31) << 15);
-  }
-  float t[7] = {s * 0.25f, s * 0.75f, s * 1.25f, s * 1.75f, s * 2.5f, s * 3.5f, s * 5.0f};
-  uint32_t n0 = mag_code(ax, t) | ((__float_as_uint(v.x) >> 31) << 3);
-  uint32_t n1 = mag_code(ay, t) | ((__float_as_uint(v.y) >> 31) << 3);
-  uint32_t n2 = mag_code(az, t) | ((__float_as_uint(v.z) >> 31) << 3);
-  uint32_t n3 = mag_code(aw, t) | ((__float_as_uint(v.w) >> 31) << 3);
-  return n0 | (n1 << 4) | (n2 << 8) | (n3 << 12);
-}
-
 // E2M1 magnitude code of RNE(a / s) from t[k] = s * midpoint_k, with the
 // tie rule folded into the comparisons: a tie at an odd midpoint (0.75,
 // 1.75, 3.5) goes up to the even code (>=), at an even one (0.25, 1.25,
@@ -100,6 +60,44 @@ __device__ __forceinline__ uint32_t quantize_quad(float4 v, uint32_t *sbyte, boo
 __device__ __forceinline__ uint32_t mag_code_ties(float a, const float *t) {
   return (uint32_t)(a > t[0]) + (uint32_t)(a >= t[1]) + (uint32_t)(a > t[2]) + (uint32_t)(a >= t[3]) +
          (uint32_t)(a > t[4]) + (uint32_t)(a >= t[5]) + (uint32_t)(a > t[6]);
+}
+
+// One 16-channel group f[0..15] -> its 8 code bytes (w0: channels 0..7,
+// w1: channels 8..15, channel 2j in the low nibble of byte j) and its scale
+// byte.  Returns false for a group holding NaN or Inf, which is written as
+// zero codes and scale 0.
+__device__ __forceinline__ bool quantize_group(const float *f, uint32_t &w0, uint32_t &w1, uint32_t &sc) {
+  // |x| as bits: finite magnitudes order like their bit patterns, and any
+  // infinity or NaN is at least 0x7f800000
+  uint32_t mb = 0;
+#pragma unroll
+  for (int e = 0; e < 16; e += 2)
+    mb = max(mb, max(__float_as_uint(f[e]) & 0x7fffffffu, __float_as_uint(f[e + 1]) & 0x7fffffffu));
+  w0 = w1 = sc = 0;
+  if (mb >= 0x7f800000u) return false;
+  sc = scale_code(__uint_as_float(mb));
+  const float sv = e4m3_pos(sc);
+  uint32_t nib[16];
+  if (sv == 0.0f) {
+    // magnitudes all round to 0; keep the signs
+#pragma unroll
+    for (int e = 0; e < 16; ++e) nib[e] = (__float_as_uint(f[e]) >> 31) << 3;
+  } else {
+    const float t[7] = {sv * 0.25f, sv * 0.75f, sv * 1.25f, sv * 1.75f, sv * 2.5f, sv * 3.5f, sv * 5.0f};
+    // one value's comparisons at a time: hoisting all 112 of them ahead of
+    // their sums runs out of scalar mask registers
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      nib[e] = mag_code_ties(fabsf(f[e]), t) | ((__float_as_uint(f[e]) >> 31) << 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    w0 |= nib[e] << (4 * e);
+    w1 |= nib[8 + e] << (4 * e);
+  }
+  return true;
 }
 
 // rows x 512 floats -> codes/scales rows dst_row[r] (or r), one lane per
@@ -135,39 +133,8 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(
         continue;
       }
       const float *f = reinterpret_cast<const float *>(v[u]);
-      // |x| as bits: finite magnitudes order like their bit patterns, and
-      // any infinity or NaN is at least 0x7f800000
-      uint32_t mb = 0;
-#pragma unroll
-      for (int e = 0; e < 16; e += 2)
-        mb = max(mb, max(__float_as_uint(f[e]) & 0x7fffffffu, __float_as_uint(f[e + 1]) & 0x7fffffffu));
-      uint32_t w0 = 0, w1 = 0, sc = 0;
-      if (mb >= 0x7f800000u) {
-        raise_flag(FLAG_NONFINITE_KV);               // the group is written as zeros
-      } else {
-        sc = scale_code(__uint_as_float(mb));
-        const float sv = e4m3_pos(sc);
-        uint32_t nib[16];
-        if (sv == 0.0f) {
-          // magnitudes all round to 0; keep the signs
-#pragma unroll
-          for (int e = 0; e < 16; ++e) nib[e] = (__float_as_uint(f[e]) >> 31) << 3;
-        } else {
-          const float t[7] = {sv * 0.25f, sv * 0.75f, sv * 1.25f, sv * 1.75f, sv * 2.5f, sv * 3.5f, sv * 5.0f};
-          // one value's comparisons at a time: hoisting all 112 of them
-          // ahead of their sums runs out of scalar mask registers
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            nib[e] = mag_code_ties(fabsf(f[e]), t) | ((__float_as_uint(f[e]) >> 31) << 3);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          w0 |= nib[e] << (4 * e);
-          w1 |= nib[8 + e] << (4 * e);
-        }
-      }
+      uint32_t w0, w1, sc;
+      if (!quantize_group(f, w0, w1, sc)) raise_flag(FLAG_NONFINITE_KV);   // written as zeros
       *reinterpret_cast<uint2 *>(codes + d[u] * CODE_BYTES + 8 * grp) = uint2{w0, w1};
       scales[d[u] * SCALE_BYTES + grp] = (uint8_t)sc;
     }
@@ -330,20 +297,29 @@ __global__ void __launch_bounds__(128) append_kernel(AppendArgs a, SwaRings r, c
     if (q == 0) *len = pos + 1;
     return;
   }
+  // FP4 cache row: lane g < 32 quantises group g with the row quantiser's
+  // routine (the other lanes only wait for the length update)
   int64_t *len = a.seq_len[c] + b;
   const int64_t pos = *len;
-  float4 v = reinterpret_cast<const float4 *>(x + ((int64_t)c * batch + b) * D)[q];
-  uint32_t sb;
-  bool bad;
-  uint32_t packed = quantize_quad(v, &sb, &bad);
+  uint32_t w0 = 0, w1 = 0, sb = 0;
+  bool ok = true;
+  if (q < NGROUPS) {
+    const float4 *src = reinterpret_cast<const float4 *>(x + ((int64_t)c * batch + b) * D) + 4 * q;
+    float4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = src[j];
+    ok = quantize_group(reinterpret_cast<const float *>(v), w0, w1, sb);
+  }
   if (pos < 0 || pos >= a.capacity[c]) {
     if (q == 0) raise_flag(FLAG_CAPACITY);
     return;
   }
-  if (bad && (q & 3) == 0) raise_flag(FLAG_NONFINITE_KV);
-  const int64_t row = (int64_t)b * a.capacity[c] + pos;
-  reinterpret_cast<uint16_t *>(a.codes[c] + row * CODE_BYTES)[q] = (uint16_t)packed;
-  if ((q & 3) == 0) a.scales[c][row * SCALE_BYTES + (q >> 2)] = (uint8_t)sb;
+  if (q < NGROUPS) {
+    if (!ok) raise_flag(FLAG_NONFINITE_KV);
+    const int64_t row = (int64_t)b * a.capacity[c] + pos;
+    *reinterpret_cast<uint2 *>(a.codes[c] + row * CODE_BYTES + 8 * q) = uint2{w0, w1};
+    a.scales[c][row * SCALE_BYTES + q] = (uint8_t)sb;
+  }
   __syncthreads();
   if (q == 0) *len = pos + 1;
 }

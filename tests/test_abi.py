@@ -154,6 +154,13 @@ def test_swa_argument_errors(lib):
     st = csa2._Step(kv, 1, arr, 1, None, 16, 64, 0, 0.04, None, 0x100000, need)
     assert lib.csa2_decode_step(ctypes.byref(st), None) == 2
     assert "window" in _err(lib)
+    # two layers appending into one ring (same length word) would race: rejected
+    ring = _swa()
+    arr2 = (csa2._Layer * 2)(csa2._Layer(0, 0, 0x50000, 0x70000, 0x40000, ctypes.pointer(ring), 0x58000),
+                             csa2._Layer(2, 0, 0x50000, 0x74000, 0x40000, ctypes.pointer(ring), 0x5c000))
+    st2 = csa2._Step(kv, 1, arr2, 2, None, 16, 64, 0, 0.04, None, 0x100000, need)
+    assert lib.csa2_decode_step(ctypes.byref(st2), None) == 1
+    assert "same SWA ring" in _err(lib)
 
 
 def test_prefill_attend_argument_errors(lib):

@@ -120,25 +120,113 @@ def test_append_and_full_cache():
     assert np.array_equal(codes[1, 7], oc[1]) and np.array_equal(scales[1, 7], os_[1])
 
 
-def test_prefill_write_full_size_sampled():
+def test_prefill_write_full_size():
     """The batch-64 prefill write: 16,384 fresh rows per sequence (1,048,576
-    rows); oracle on a sample of 4,096 rows spread over every sequence."""
+    rows) in one launch; every 65,536-row chunk's codes and scales hash to
+    the oracle's (tests/golden/prefill_write_1m.json, written by
+    tests/golden/make_fullsize.py from the oracle alone)."""
     require_gpu()
+    import hashlib
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "prefill_write_1m.json")) as f:
+        gold = json.load(f)
     B, N = 64, W.PREFILL_WRITE_ROWS
+    R, C = B * N, gold["chunk_rows"]
+    assert gold["rows"] == R
     cache = csa2.KVCache(B, N)
-    xs_all = W.kv_rows_threaded(4, 9, 0, B * N)          # sequence b = rows b*N .. b*N+N-1
+    xs_all = W.kv_rows_threaded(4, 9, 0, R)              # sequence b = rows b*N .. b*N+N-1
     log("prefill write: rows generated")
     x = torch.from_numpy(xs_all).cuda()
     csa2.fp4_quantize_kv(x, cache.codes.view(-1, Q.CODE_BYTES), cache.scales.view(-1, Q.SCALE_BYTES))
     torch.cuda.synchronize()
     assert csa2.device_error() == 0
-    rng = np.random.default_rng(11)
-    rows = np.sort(rng.choice(B * N, 4096, replace=False))
-    oc, os_ = Q.quantize_rows(xs_all[rows])
-    sel = torch.from_numpy(rows).cuda()
-    gc = cache.codes.view(-1, Q.CODE_BYTES)[sel].cpu().numpy()
-    gs = cache.scales.view(-1, Q.SCALE_BYTES)[sel].cpu().numpy()
-    assert np.array_equal(gc, oc) and np.array_equal(gs, os_)
+    codes = cache.codes.view(-1, Q.CODE_BYTES).cpu().numpy()
+    scales = cache.scales.view(-1, Q.SCALE_BYTES).cpu().numpy()
+    for k in range(R // C):
+        assert hashlib.sha256(codes[k * C:(k + 1) * C].tobytes()).hexdigest() == gold["codes_sha256"][k], k
+        assert hashlib.sha256(scales[k * C:(k + 1) * C].tobytes()).hexdigest() == gold["scales_sha256"][k], k
+    log(f"prefill write: all {R} rows byte-equal to the oracle's")
+
+
+def test_append_edge_rows_bit_exact():
+    """csa2_append_kv on rows on every rounding boundary of both formats (one
+    row per sequence, at varied positions): the decode-step append path runs
+    the same quantiser as fp4_quantize_kv; bytes equal the oracle's."""
+    require_gpu()
+    x = _edge_rows()
+    B = x.shape[0]
+    log(f"append edge rows: {B} sequences")
+    cache = csa2.KVCache(B, 16)
+    start = (np.arange(B) * 5 % 9).astype(np.int64)              # positions 0..8
+    cache.seq_len.copy_(torch.from_numpy(start))
+    cache.codes.fill_(0xAB)
+    cache.scales.fill_(0xCD)
+    csa2.append_kv(cache, torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    assert np.array_equal(cache.seq_len.cpu().numpy(), start + 1)
+    oc, os_ = Q.quantize_rows(x)
+    codes, scales = cache.codes.cpu().numpy(), cache.scales.cpu().numpy()
+    b = np.arange(B)
+    assert np.array_equal(codes[b, start], oc), np.argwhere(codes[b, start] != oc)[:5]
+    assert np.array_equal(scales[b, start], os_), np.argwhere(scales[b, start] != os_)[:5]
+    other = np.ones((B, 16), dtype=bool)
+    other[b, start] = False
+    assert np.all(codes[other] == 0xAB) and np.all(scales[other] == 0xCD)
+
+
+def test_decode_step_appends_edge_rows():
+    """A decode step whose appended rows (two Full caches) are the edge rows:
+    appended bytes equal the oracle's quantisation and every layer's
+    selection equals the oracle's decode step on the same inputs.  Outputs
+    are compared where the appended row lies in the latent's range (|x| <=
+    sqrt(512), the bound the RMSNorm'd latent obeys): the attention rounds q
+    to fp16, so a logit moves by up to 2^-11 * scale * sum_c |q_c k_c|, which
+    for rows near the format maximum (2688 in every channel) is far outside
+    the 2e-3 output bound, and inside it for rows of the latent's range."""
+    require_gpu()
+    from oracle.step import Cache, decode_step
+    from tests._gpu import ATT_TOL, normwise_err
+    x = _edge_rows()
+    B, n0, H, K = x.shape[0], 21, 16, 2
+    prefill = W.kv_rows(0, 0, 0, 0, n0)                           # the same 21 rows in every sequence
+    pc, ps = Q.quantize_rows(prefill)
+    ocs, gcs = [], []
+    for c in range(2):
+        oc = Cache(B, 24)
+        oc.codes[:, :n0], oc.scales[:, :n0] = pc, ps
+        oc.seq_len[:] = n0
+        ocs.append(oc)
+        g = csa2.KVCache(B, 24)
+        g.codes.copy_(torch.from_numpy(oc.codes))
+        g.scales.copy_(torch.from_numpy(oc.scales))
+        g.seq_len.fill_(n0)
+        g.max_len = n0 + 1
+        gcs.append(g)
+    rows = np.stack([x, x[::-1].copy()])                          # [2, B, 512]
+    qs = [W.queries(0, l, 0, B, H) for l in range(3)]
+    pattern = [(0, 0), (0, 1), (2, 1)]                            # Full, Full, Reuse
+    ref = decode_step(ocs, [(m, c, qs[l]) for l, (m, c) in enumerate(pattern)], rows, K, 0, 1 / np.sqrt(512))
+    outs = [torch.zeros((B, H, 512), dtype=torch.float32, device="cuda") for _ in range(3)]
+    idxs = [torch.full((B, K), -9, dtype=torch.int32, device="cuda") for _ in range(3)]
+    ws = csa2.workspace(B, H, n0 + 1, 0, K)
+    csa2.decode_step(gcs, [(m, c, torch.from_numpy(qs[l]).cuda(), outs[l], idxs[l])
+                           for l, (m, c) in enumerate(pattern)], H, K, 0, 1 / np.sqrt(512), ws,
+                     new_rows=torch.from_numpy(rows).cuda())
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    for c in range(2):
+        assert np.array_equal(gcs[c].seq_len.cpu().numpy(), np.full(B, n0 + 1))
+        assert np.array_equal(gcs[c].codes.cpu().numpy(), ocs[c].codes), c
+        assert np.array_equal(gcs[c].scales.cpu().numpy(), ocs[c].scales), c
+    bound = np.sqrt(512.0)
+    for l, (m, c) in enumerate(pattern):
+        assert np.array_equal(idxs[l].cpu().numpy(), ref["idx"][l]), l
+        ok = np.abs(rows[c]).max(axis=1) <= bound
+        assert ok.sum() >= 100
+        err = normwise_err(outs[l].cpu().numpy()[ok], ref["out"][l][ok])
+        assert err <= ATT_TOL, (l, err)
 
 
 def test_rows_beyond_one_grid_round():

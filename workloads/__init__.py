@@ -101,11 +101,17 @@ def rotation(wid):
 
 
 def shape_rows(z, wid):
-    """RMSNorm (weight 1) then the workload's rotation; float32 out."""
+    """RMSNorm (weight 1) then the workload's rotation; float32 out.
+
+    The rotation is applied in float64 and rounded once to float32, so the
+    rows do not depend on the host's matrix-multiply kernel: a float32
+    product's summation order varies with the BLAS build and CPU, a float64
+    one changes the rounded float32 value only with a ~1e-9 chance per value.
+    """
     z = np.asarray(z, dtype=np.float32)
     rms = np.sqrt(np.mean(z.astype(np.float64) ** 2, axis=-1, keepdims=True) + 1e-6)
     zn = (z / rms).astype(np.float32)
-    return (zn @ rotation(wid).astype(np.float32)).astype(np.float32)
+    return (zn.astype(np.float64) @ rotation(wid)).astype(np.float32)
 
 
 def _kv_chunk(wid, cache, seq, chunk):
