@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libcsa2.so")
 FULL, REINDEX, REUSE = 0, 1, 2
 D, BLOCK, CODE_BYTES, SCALE_BYTES = 512, 8, 256, 32
 MAX_POOL, MAX_TOPK, MAX_CACHES = 8192, 2048, 16
-FLAG_NONFINITE_KV, FLAG_CAPACITY, FLAG_NONFINITE_Q, FLAG_BAD_INDEX, FLAG_SWA_RANGE = 1, 2, 4, 8, 16
+FLAG_NONFINITE_KV, FLAG_CAPACITY, FLAG_NONFINITE_Q, FLAG_BAD_INDEX, FLAG_SWA_RANGE, FLAG_Q_RANGE = 1, 2, 4, 8, 16, 32
 MAX_WINDOW, MAX_SWA_LAYERS, MAX_SWA_SLOTS = 1024, 64, 1 << 22
 
 EXPORTED = ("fp4_quantize_kv", "csa2_append_kv", "fp8_quantize_kv", "csa2_swa_append",

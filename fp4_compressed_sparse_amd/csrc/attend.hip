@@ -28,6 +28,11 @@
 //  * Prefill side with 64 heads (many queries, each with its own
 //    selection): attend64_kernel below covers all four head tiles of a
 //    query in one workgroup, so each gathered row is dequantised once.
+//  * The query is rounded to fp16 for the matrix cores: a logit moves by at
+//    most 2^-11 * scale * sum_c |q_c k_c|, far inside the output bound for
+//    rows of the latent's range (|x| <= sqrt(512) after RMSNorm); a query
+//    value of magnitude 65520 or more (or not finite) has no fp16 value and
+//    raises FLAG_Q_RANGE.
 //
 // MFMA 16x16x32 f16 lane layout (checked on gfx950): A row = lane%16 with
 // k = 8*(lane/16)..+7; B column = lane%16, same k; C column = lane%16,
@@ -111,8 +116,9 @@ constexpr int SEL_CAND_MAX = 2048;  // candidates of the in-kernel top-k (8 per 
 // 8w..8w+7 over all 64 positions.
 template <bool SELECT, bool WIN>
 __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs a) {
-  extern __shared__ _Float16 s_v[];               // [ATT_SP][ROW_HALVES]; first holds q
-  __shared__ _Float16 s_p[16 * P_STRIDE];         // P: [16 heads][64 positions]
+  // 16-byte aligned: rows are read and written as 128-bit vectors
+  extern __shared__ __attribute__((aligned(16))) _Float16 s_v[];   // [ATT_SP][ROW_HALVES]; first holds q
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[16 * P_STRIDE];   // P: [16 heads][64 positions]
   __shared__ float s_max[4][16], s_sum[4][16];
   __shared__ uint8_t s_ok[ATT_SP];
   __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX : 1];   // in-kernel selection
@@ -263,13 +269,18 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     }
     fetch_rows(st0);
     if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);
+    uint32_t mb = 0;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int e = tid + u * ATT_THREADS;                    // head e/128, channels 4*(e%128)
+      mb = max(mb, max(max(__float_as_uint(v[u].x) & 0x7fffffffu, __float_as_uint(v[u].y) & 0x7fffffffu),
+                       max(__float_as_uint(v[u].z) & 0x7fffffffu, __float_as_uint(v[u].w) & 0x7fffffffu)));
       f16x2 lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
       *reinterpret_cast<u32x2 *>(s_v + (e >> 7) * ROW_HALVES + 4 * (e & 127)) =
           u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
     }
+    // no fp16 value for |q| >= 65520 (or NaN/Inf): flag it
+    if (__builtin_amdgcn_ballot_w64(mb >= 0x477ff000u) && lane == 0) raise_flag(FLAG_Q_RANGE);
     __syncthreads();
     const _Float16 *qrow = s_v + n16 * ROW_HALVES + 8 * g;
 #pragma unroll
@@ -493,8 +504,9 @@ template __global__ void attend_partial_kernel<true, true>(AttendArgs);
 constexpr int ATT64_THREADS = 512;
 constexpr size_t ATT64_LDS = (size_t)2 * ATT_SP * ROW_HALVES * sizeof(_Float16);
 __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
-  extern __shared__ _Float16 s_v[];               // [2][ATT_SP][ROW_HALVES]; first holds q (64 heads)
-  __shared__ _Float16 s_p[64 * P_STRIDE];         // P: [64 heads][64 positions]
+  // 16-byte aligned: rows are read and written as 128-bit vectors
+  extern __shared__ __attribute__((aligned(16))) _Float16 s_v[];   // [2][ATT_SP][ROW_HALVES]; first holds q (64 heads)
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[64 * P_STRIDE];   // P: [64 heads][64 positions]
   __shared__ float s_max[2][64], s_corr[64], s_fin[2][64];
   __shared__ uint8_t s_ok[2][ATT_SP];
 
@@ -551,13 +563,18 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     fetch_rows(st0);
     if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);
+    uint32_t mb = 0;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int e = tid + u * ATT64_THREADS;                  // head e/128, channels 4*(e%128)
+      mb = max(mb, max(max(__float_as_uint(v[u].x) & 0x7fffffffu, __float_as_uint(v[u].y) & 0x7fffffffu),
+                       max(__float_as_uint(v[u].z) & 0x7fffffffu, __float_as_uint(v[u].w) & 0x7fffffffu)));
       f16x2 lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
       *reinterpret_cast<u32x2 *>(s_v + (e >> 7) * ROW_HALVES + 4 * (e & 127)) =
           u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
     }
+    // no fp16 value for |q| >= 65520 (or NaN/Inf): flag it
+    if (__builtin_amdgcn_ballot_w64(mb >= 0x477ff000u) && lane == 0) raise_flag(FLAG_Q_RANGE);
     __syncthreads();
     const _Float16 *qrow = s_v + (16 * ht + n16) * ROW_HALVES + 8 * g;
 #pragma unroll

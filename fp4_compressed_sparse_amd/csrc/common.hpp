@@ -27,7 +27,7 @@ constexpr int MAX_GRID_X = 2048;  // workgroups per grid row of a hand-off kerne
 
 // Device flag bits (mirrors include/csa2.h).
 constexpr uint32_t FLAG_NONFINITE_KV = 1, FLAG_CAPACITY = 2, FLAG_NONFINITE_Q = 4,
-                   FLAG_BAD_INDEX = 8;
+                   FLAG_BAD_INDEX = 8, FLAG_Q_RANGE = 32;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

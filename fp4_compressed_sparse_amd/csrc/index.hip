@@ -935,7 +935,7 @@ __device__ __forceinline__ uint64_t threshold_in_lds(const uint64_t *s_keys, int
 }
 
 __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
-  extern __shared__ uint64_t s_keys[];                 // lds_keys
+  extern __shared__ __attribute__((aligned(16))) uint64_t s_keys[];                 // lds_keys
   __shared__ int32_t s_ids[LDS_KEYS];
   __shared__ int32_t s_sel[CSA2_TOPK_MAX];
   __shared__ uint32_t s_hist[RADIX_BINS];
@@ -1304,7 +1304,7 @@ __device__ __forceinline__ uint64_t radix_select_keys(F get, int m, int r, uint6
 // cand_stride >= blocks entries); region sizes in the first words of
 // `bitmap` (zero at entry, left zero).
 __global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
-  extern __shared__ uint64_t s_dyn[];
+  extern __shared__ __attribute__((aligned(16))) uint64_t s_dyn[];
   uint64_t *s_keys = s_dyn;                                            // [SEL2_KEYS]
   uint32_t *s_bm = reinterpret_cast<uint32_t *>(s_dyn + SEL2_KEYS);    // [nwords]
   uint32_t *s_wpre = s_bm + a.nwords;                                  // [nwords]
@@ -1484,7 +1484,7 @@ struct RescoreArgs {
 
 template <bool SELECT>
 __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
-  extern __shared__ uint64_t s_keys[];
+  extern __shared__ __attribute__((aligned(16))) uint64_t s_keys[];
   __shared__ float s_qbar[D];
   __shared__ int32_t s_ids[SELECT ? LDS_KEYS : 1];
   __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX : 1];

@@ -73,8 +73,11 @@ enum {
   CSA2_FLAG_CAPACITY = 2,       /* append into a full sequence, or dst_row out of range */
   CSA2_FLAG_NONFINITE_Q = 4,    /* an indexer query sum held NaN/Inf (scores unspecified) */
   CSA2_FLAG_BAD_INDEX = 8,      /* a candidate/selected block id was >= the block count */
-  CSA2_FLAG_SWA_RANGE = 16      /* an SWA row's largest magnitude exceeded 65504, the
+  CSA2_FLAG_SWA_RANGE = 16,     /* an SWA row's largest magnitude exceeded 65504, the
                                    attention's fp16 operand range (stored as given)      */
+  CSA2_FLAG_Q_RANGE = 32        /* an attention query value had magnitude >= 65520 or was
+                                   NaN/Inf: it has no fp16 value (the matrix-core operand),
+                                   so the outputs of its sequence are unspecified         */
 };
 
 #define CSA2_D 512              /* latent channels                 */
@@ -248,6 +251,11 @@ csa2_status csa2_index_topk(int32_t mode, const csa2_kv *kv, const float *q, int
  * out   device float32 [batch][heads][512].
  * Accumulates in float32 with fp16 matrix-core operands (the FP4 values
  * are exact in fp16; q and the SWA values e4m3 * scale are rounded to fp16).
+ * Rounding q moves a logit by at most 2^-11 * scale * sum_c |q_c k_c|: far
+ * inside the 2e-3 output bound for rows of the latent's range (|x| <=
+ * sqrt(512) after RMSNorm), not for rows near the format's maximum (2688 in
+ * every channel).  A q value with |q| >= 65520, NaN or Inf flags
+ * CSA2_FLAG_Q_RANGE.
  */
 csa2_status csa2_sparse_attend(const csa2_kv *kv, const float *q, int32_t heads,
                                const int32_t *idx, int32_t topk, float scale,
