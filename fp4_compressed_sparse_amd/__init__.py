@@ -7,7 +7,8 @@ the binding's entry points raises.
 
 Names follow the C ABI: fp4_quantize_kv, append_kv, fp8_quantize_kv,
 swa_append, index_topk, sparse_attend, prefill_attend, decode_step,
-block_scores, device_error, workspace_bytes, workspace_init.
+decode_step_noalloc, block_scores, device_error, workspace_bytes,
+workspace_init.
 """
 import ctypes
 import os
@@ -24,7 +25,7 @@ MAX_WINDOW, MAX_SWA_LAYERS, MAX_SWA_SLOTS = 1024, 64, 1 << 22
 EXPORTED = ("fp4_quantize_kv", "csa2_append_kv", "fp8_quantize_kv", "csa2_swa_append",
             "csa2_workspace_bytes", "csa2_workspace_init",
             "csa2_index_topk", "csa2_sparse_attend", "csa2_prefill_workspace_bytes",
-            "csa2_prefill_attend", "csa2_decode_step", "csa2_block_scores",
+            "csa2_prefill_attend", "csa2_decode_step", "csa2_decode_step_noalloc", "csa2_block_scores",
             "csa2_device_error", "csa2_set_scan_events", "csa2_status_string", "csa2_last_error")
 
 
@@ -85,6 +86,7 @@ def load():
         "csa2_prefill_attend": (i32, [ctypes.POINTER(_Kv), i32, vp, i32, i32, vp, vp, i32, ctypes.c_float,
                                       ctypes.POINTER(_Swa), vp, vp, sz, vp]),
         "csa2_decode_step": (i32, [ctypes.POINTER(_Step), vp]),
+        "csa2_decode_step_noalloc": (i32, [ctypes.POINTER(_Step), vp]),
         "csa2_block_scores": (i32, [ctypes.POINTER(_Kv), vp, i32, vp, i32, vp, vp]),
         "csa2_device_error": (i32, [ctypes.POINTER(ctypes.c_int32), vp]),
         "csa2_set_scan_events": (i32, [vp, vp]),
@@ -284,7 +286,7 @@ class StepPlan:
         self._step = _Step(self._kv, len(caches), self._layers, len(layers),
                            new_rows.data_ptr() if new_rows is not None else None, heads, topk, pool,
                            float(scale), pool_out.data_ptr() if pool_out is not None else None,
-                           ws.data_ptr(), ws.numel())
+                           ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0)
 
     def refresh_lengths(self):
         """Copy each cache's host max_len bound into the C views."""
@@ -294,9 +296,19 @@ class StepPlan:
     def run(self, stream=None):
         _check(load().csa2_decode_step(ctypes.byref(self._step), _stream(stream)))
 
+    def run_noalloc(self, stream=None):
+        """The same step through csa2_decode_step_noalloc (the library's own
+        per-device workspace; this plan's ws is ignored)."""
+        _check(load().csa2_decode_step_noalloc(ctypes.byref(self._step), _stream(stream)))
+
 
 def decode_step(caches, layers, heads, topk, pool, scale, ws, pool_out=None, new_rows=None, stream=None):
     StepPlan(caches, layers, heads, topk, pool, scale, ws, pool_out, new_rows).run(stream)
+
+
+def decode_step_noalloc(caches, layers, heads, topk, pool, scale, pool_out=None, new_rows=None, stream=None):
+    """decode_step on the library's own per-device workspace (no allocation)."""
+    StepPlan(caches, layers, heads, topk, pool, scale, None, pool_out, new_rows).run_noalloc(stream)
 
 
 def set_scan_events(before=None, after=None):

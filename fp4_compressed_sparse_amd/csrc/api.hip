@@ -20,6 +20,12 @@
 
 using namespace csa2;
 
+// The library's own workspace for csa2_decode_step_noalloc (callers that
+// cannot allocate): one copy per device, held until the process ends.  Host
+// code never uses this name as an address: the device address comes from
+// hipGetSymbolAddress, per device (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_WORKSPACE_BYTES];
+
 namespace {
 
 thread_local std::string t_last_error;
@@ -768,6 +774,56 @@ int csa2_debug_phase_clear(void) {
   return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_phase_ts), zero, sizeof(zero), 0, hipMemcpyHostToDevice);
 }
 #endif
+
+// Device address of this device's scratch array, found once per device
+// (with that device current) and zero-filled then on `stream` by a kernel;
+// every call leaves the workspace's control words zero again, so later calls
+// need no clearing.
+static csa2_status noalloc_scratch(void **out, hipStream_t s) {
+  static std::mutex mu;
+  static void *addr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(CSA2_E_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(CSA2_E_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(CSA2_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    const int64_t words = (int64_t)(CSA2_NOALLOC_WORKSPACE_BYTES / 4);
+    zero_kernel<<<2048, 256, 0, s>>>(static_cast<uint32_t *>(p), words);
+    if (csa2_status st = launched("scratch init")) return st;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return CSA2_OK;
+}
+
+csa2_status csa2_decode_step_noalloc(const csa2_step *st, void *stream) {
+  t_last_error.clear();
+  if (!st) return fail(CSA2_E_ARG, "step is NULL");
+  if (!st->caches || st->n_caches < 1 || st->n_caches > CSA2_MAX_CACHES)
+    return fail(CSA2_E_ARG, "n_caches %d outside [1, %d]", st->n_caches, CSA2_MAX_CACHES);
+  int64_t max_len = 0;
+  for (int c = 0; c < st->n_caches; ++c) {
+    if (csa2_status e = check_kv(&st->caches[c])) return e;
+    if (st->caches[c].max_len > max_len) max_len = st->caches[c].max_len;
+  }
+  Layout L;
+  if (!make_layout(st->caches[0].batch, st->heads, max_len, st->pool, st->topk, &L))
+    return fail(CSA2_E_SHAPE, "bad sizes");
+  if (L.total > (size_t)CSA2_NOALLOC_WORKSPACE_BYTES)
+    return fail(CSA2_E_WORKSPACE, "this step needs a %zu-byte workspace, more than the %zu-byte scratch of "
+                "csa2_decode_step_noalloc (use csa2_decode_step with a workspace)",
+                L.total, (size_t)CSA2_NOALLOC_WORKSPACE_BYTES);
+  if (csa2_status e = device_ready()) return e;
+  void *ws = nullptr;
+  if (csa2_status e = noalloc_scratch(&ws, as_stream(stream))) return e;
+  csa2_step own = *st;
+  own.ws = ws;
+  own.ws_bytes = CSA2_NOALLOC_WORKSPACE_BYTES;
+  return csa2_decode_step(&own, stream);
+}
 
 csa2_status csa2_device_error(int32_t *flags_host, void *stream) {
   t_last_error.clear();

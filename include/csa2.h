@@ -341,6 +341,23 @@ typedef struct {
 csa2_status csa2_decode_step(const csa2_step *step, void *stream);
 
 /*
+ * csa2_decode_step_noalloc — csa2_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same computation, but step->ws and
+ * step->ws_bytes are ignored: the workspace is the library's own array of
+ * CSA2_NOALLOC_WORKSPACE_BYTES (16 MiB) per device, held until the process
+ * ends and zero-filled by a kernel on `stream` at the first call on each
+ * device.  Enough for batch 1 with 64 heads up to about 1.1M positions
+ * (csa2_workspace_bytes gives the need); a larger step returns
+ * CSA2_E_WORKSPACE before anything is queued.  The call allocates and frees
+ * nothing.  Every call on a device shares that device's array: calls that
+ * overlap on one device (different streams or threads) race and must be
+ * ordered by the caller.
+ */
+#define CSA2_NOALLOC_WORKSPACE_BYTES (16u << 20)
+csa2_status csa2_decode_step_noalloc(const csa2_step *step, void *stream);
+
+/*
  * csa2_block_scores — diagnostic export of the indexer's float32 scores
  * (the same arithmetic as csa2_index_topk).
  * cand == NULL: scores[b][j] for every block j < ceil(max_len/8) (blocks at

@@ -133,6 +133,17 @@ def test_decode_step_pattern_errors(lib):
     assert step([(0, 0)], pool=64) == 1         # pool > 0 without pool_out
 
 
+def test_noalloc_step_rejects_oversize_workspace(lib):
+    # the batch-64 workload needs about 87 MiB, more than the library's scratch
+    need = lib.csa2_workspace_bytes(64, 16, 131072 + 64, 2048, 128)
+    assert need > (16 << 20)
+    kv = (csa2._Kv * 1)(_kv(batch=64, capacity=131136, max_len=131072 + 64))
+    arr = (csa2._Layer * 1)(csa2._Layer(0, 0, 0x50000, 0x70000, 0x40000, None, None))
+    st = csa2._Step(kv, 1, arr, 1, None, 16, 128, 2048, 0.04, 0x80000, None, 0)
+    assert lib.csa2_decode_step_noalloc(ctypes.byref(st), None) == 3
+    assert "scratch" in _err(lib)
+
+
 def test_swa_argument_errors(lib):
     x = ctypes.c_void_p(0x50000)
     assert lib.fp8_quantize_kv(None, 0, None, 0, None, None, None) == 0     # no-op
