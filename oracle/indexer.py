@@ -23,12 +23,25 @@ Readings taken (the pages are silent on every step below):
       level 1; five levels in all.
       s_b = (tree result) + 0.0, which turns -0 into +0.
     No 1/sqrt(512) factor: it does not change the ranking.
+
+Per-head variant (score = SCORE_HEADMAX).  The pages do not say how the
+indexer turns many query heads into one block score.  The reading above sums
+the heads first; the other plain reading scores every head on its own and
+keeps the best head's score:
+      s_b = max over h of S_h,b,  S_h,b = the pinned-order score above with
+      q_h in place of Qbar
+(the maximum is exact).  It costs one 512-term dot product per head and
+block, heads times the collapsed scan's arithmetic; the pages put the whole
+decode step's FLOPs at roughly a quarter more for a 256x longer context [P2
+"why it matters"], which leaves room for indexer arithmetic that grows with
+the context.
 """
 import numpy as np
 
 from .quantize import D, GROUP, NGROUPS, dequantize_rows
 
 BLOCK = 8   # positions per block
+SCORE_SUM, SCORE_HEADMAX = 0, 1   # heads summed into Qbar / best per-head score
 
 
 def num_blocks(n: int) -> int:
@@ -110,15 +123,34 @@ def block_scores_from_keys(qbar, keys):
     return acc[:, 0] + np.float32(0.0)
 
 
-def block_scores(codes, scales, n, q, cand=None):
+def headmax_scores_from_keys(q, keys):
+    """Per-head variant: for every key, the largest over the heads q [H, 512]
+    of that head's pinned-order score (block_scores_from_keys with q_h in
+    place of Qbar) -> float32 [nblk]."""
+    q = np.asarray(q, dtype=np.float32)
+    if not np.all(np.isfinite(q)):
+        raise ValueError("non-finite query")
+    best = block_scores_from_keys(q[0], keys)
+    for h in range(1, q.shape[0]):
+        best = np.maximum(best, block_scores_from_keys(q[h], keys))
+    return best
+
+
+def block_scores(codes, scales, n, q, cand=None, score=SCORE_SUM):
     """Scores of one sequence's blocks for the query heads q [H, 512].
 
-    cand: block ids to score (None = all blocks).  Returns (ids, scores).
+    cand: block ids to score (None = all blocks).  score: SCORE_SUM (heads
+    summed into Qbar) or SCORE_HEADMAX (best per-head score).
+    Returns (ids, scores).
     """
     keys = block_keys(codes, scales, n)
     ids = np.arange(keys.shape[0], dtype=np.int64) if cand is None else \
         np.asarray([c for c in cand if c >= 0], dtype=np.int64)
     if ids.size and (ids.max() >= keys.shape[0]):
         raise ValueError("candidate block id out of range")
+    if score == SCORE_HEADMAX:
+        return ids, headmax_scores_from_keys(q, keys[ids])
+    if score != SCORE_SUM:
+        raise ValueError(f"unknown score rule {score}")
     qbar = collapse_query(q)
     return ids, block_scores_from_keys(qbar, keys[ids])

@@ -71,7 +71,8 @@ class Cache:
             self.seq_len[b] += 1
 
 
-def decode_step(caches, layers, new_rows, topk, pool, scale, swa=None, swa_rows=None, window=0):
+def decode_step(caches, layers, new_rows, topk, pool, scale, swa=None, swa_rows=None, window=0,
+                score=_indexer.SCORE_SUM):
     """Run one decode step.
 
     caches:   list of Cache (one per Full layer); mutated by the append.
@@ -80,6 +81,8 @@ def decode_step(caches, layers, new_rows, topk, pool, scale, swa=None, swa_rows=
     swa:      None, or one swa.SwaCache (or None) per layer: the layer's local
               branch, window positions wide; swa_rows float32 [n_layers, B, 512]
               (rows of layers without a cache are ignored) are appended first.
+    score:    the indexer's head rule, SCORE_SUM (heads summed) or
+              SCORE_HEADMAX (best per-head score) (oracle/indexer.py).
     Returns dict with 'idx' (list of int32 [B, topk]), 'out' (list of float64
     [B, H, 512]) and 'pool' (int32 [B, pool] or None).
     """
@@ -116,7 +119,7 @@ def decode_step(caches, layers, new_rows, topk, pool, scale, swa=None, swa_rows=
                     cand = pool_ids[b]
                 else:
                     cand = None
-                ids, sc = _indexer.block_scores(cache.codes[b], cache.scales[b], n, q[b], cand)
+                ids, sc = _indexer.block_scores(cache.codes[b], cache.scales[b], n, q[b], cand, score)
                 if build_pool:
                     pool_ids[b] = select(ids, sc, pool)
                     keep = np.isin(ids, pool_ids[b])
