@@ -16,6 +16,12 @@ dominant kernel, CPU-oracle baseline).  Progress goes to stderr.
   python bench.py --copy-probe     (plain copy kernel for counter calibration)
   python bench.py --prefill 4096   (prefill-side sparse attention, its own JSON line)
   python bench.py --prefill-write  (FP4 quantisation of 1,048,576 prompt rows, its own JSON line)
+  python bench.py --cpu-only [--cpu-steps N] [--cpu-threads N]   (the oracle baseline alone)
+  python bench.py --launch-floor   (a chain of dependent tiny launches: the per-launch floor)
+
+By default the 256 MB last-level cache is flushed (a 512 MB read) between
+the timed steps and the step time is the mean of the events around each
+step; --warm runs them back to back.
 """
 import argparse
 import hashlib
@@ -133,56 +139,104 @@ def cpu_threads(threads):
     return contextlib.nullcontext(), n
 
 
-def cpu_baseline(w, window=0, threads=1):
-    """The oracle's decode step timed on the host (1 thread unless told
-    otherwise), on two bounded contexts, extrapolated linearly in context to
-    the workload's context (window > 0: every layer with its local branch,
-    as the GPU step)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_chunk(job):
+    """One chunk of a workload cache's prefill rows, quantised by the oracle."""
+    import workloads as W
+    from oracle.quantize import quantize_rows
+    wid, cache, seq, chunk, count = job
+    return job, quantize_rows(W.kv_rows(wid, cache, seq, chunk * W.CHUNK, count))
+
+
+def oracle_caches(w, lengths, capacity, workers=16):
+    """The workload's Full caches holding its prefill rows quantised by the
+    oracle's own quantiser (chunks in worker processes).  Call it before
+    anything touches the GPU: the workers are forked from this process."""
+    from concurrent.futures import ProcessPoolExecutor
+
+    import workloads as W
+    from oracle.step import Cache
+
+    caches = [Cache(len(lengths), capacity) for _ in range(w.n_caches)]
+    jobs = [(w.wid, c, b, k, min(W.CHUNK, int(n) - k * W.CHUNK))
+            for c in range(w.n_caches) for b, n in enumerate(lengths)
+            for k in range((int(n) + W.CHUNK - 1) // W.CHUNK)]
+    with ProcessPoolExecutor(max_workers=min(workers, os.cpu_count() or 1)) as ex:
+        for (_, c, b, k, cnt), (codes, scales) in ex.map(_oracle_chunk, jobs):
+            caches[c].codes[b, k * W.CHUNK:k * W.CHUNK + cnt] = codes
+            caches[c].scales[b, k * W.CHUNK:k * W.CHUNK + cnt] = scales
+    for cache in caches:
+        cache.seq_len[:] = lengths
+    return caches
+
+
+def cpu_baseline(w, window=0, threads=1, steps=1):
+    """The oracle's decode step timed on the host at the workload's full size:
+    its caches quantised by the oracle (not timed), then `steps` decode steps
+    of the same layer pattern, each appending one row per Full cache as the
+    GPU steps do, at `threads` host threads (0: the BLAS pool's size).
+    window > 0: every layer with its local branch, as the GPU step."""
+    import dataclasses
+
     import numpy as np
 
     import workloads as W
-    from oracle.step import Cache, decode_step
+    from oracle.step import decode_step
     from oracle.swa import SwaCache
 
-    samples = (8192, 32768)
+    full_batch = w.batch
+    if w.batch > 4:
+        # a bounded sample: the first 4 sequences (the same seeded lengths)
+        w = dataclasses.replace(w, batch=4)
+    lengths = W.lengths(w)
+    t0 = time.perf_counter()
+    caches = oracle_caches(w, lengths, int((int(lengths.max()) + steps + 7) // 8 * 8))
+    log(f"cpu oracle: caches quantised by the oracle in {time.perf_counter() - t0:.1f} s")
+    lc = w.layer_caches()
+    L = len(w.pattern)
+    swa = None
+    if window:
+        swa = []
+        for l in range(L):
+            sw = SwaCache(w.batch, int(lengths.max()) + steps)
+            for b, n in enumerate(lengths):
+                n = int(n)
+                sw.write(b, n - window, W.swa_rows(w.wid, l, b, n - window, window))
+                sw.seq_len[b] = n
+            swa.append(sw)
+    ctx, used = cpu_threads(threads)
     times = []
-    for n in samples:
-        caches = []
-        for c in range(w.n_caches):
-            oc = Cache(1, n + 8)
-            oc.write(0, 0, W.kv_rows(w.wid, c, 0, 0, n))
-            oc.seq_len[0] = n
-            caches.append(oc)
-        lc = w.layer_caches()
-        layers = [(m, lc[l], W.queries(w.wid, l, 0, 1, w.heads)) for l, m in enumerate(w.pattern)]
-        rows = np.stack([W.append_rows(w.wid, c, 0, 1) for c in range(w.n_caches)])
-        swa = srows = None
-        if window:
-            swa = []
-            for l in range(len(w.pattern)):
-                sw = SwaCache(1, n + 1)
-                sw.write(0, n - window, W.swa_rows(w.wid, l, 0, n - window, window))
-                sw.seq_len[0] = n
-                swa.append(sw)
-            srows = np.stack([W.swa_append_rows(w.wid, l, 0, 1) for l in range(len(w.pattern))])
-        ctx, used = cpu_threads(threads)
-        with ctx:
-            t0 = time.perf_counter()
+    with ctx:
+        for s in range(steps):
+            layers = [(m, lc[l], W.queries(w.wid, l, s, w.batch, w.heads)) for l, m in enumerate(w.pattern)]
+            rows = np.stack([W.append_rows(w.wid, c, s, w.batch) for c in range(w.n_caches)]) if w.append else None
+            srows = np.stack([W.swa_append_rows(w.wid, l, s, w.batch) for l in range(L)]) if window else None
+            t1 = time.perf_counter()
             decode_step(caches, layers, rows, w.topk, w.pool, w.scale, swa=swa, swa_rows=srows, window=window)
-            times.append(time.perf_counter() - t0)
-        log(f"cpu oracle: context {n}: {times[-1]:.2f} s per step")
-    (n1, n2), (t1, t2) = samples, times
-    slope = (t2 - t1) / (n2 - n1)
-    t_full = t2 + slope * (w.context - n2)
+            times.append(time.perf_counter() - t1)
+            log(f"cpu oracle: step {s}: {times[-1]:.2f} s on {used} host thread(s)")
+    total = sum(times)
     return {
-        "value": round(w.batch / t_full, 6),
+        "value": round(w.batch * steps / total, 6),
         "unit": "tokens/s",
         "cores": used,
         "kind": "oracle",
-        "sample": (f"one decode step of the same 20-layer pattern (64 heads, pool 2048, top-256, batch 1"
-                   + (f", a {window}-position window on every layer" if window else "") + ") "
-                   f"at contexts {n1} and {n2}: {t1:.2f} s and {t2:.2f} s on {used} host thread(s); "
-                   f"extrapolated linearly in context to {w.context} positions: {t_full:.1f} s per step"),
+        "sample": (f"{steps} decode step(s) of the workload ({w.name}: batch {w.batch}"
+                   + (f" of its {full_batch} sequences" if full_batch != w.batch else "") + ", "
+                   f"{int(lengths.max())} positions, {L} layers, {w.heads} heads, pool {w.pool}, top-{w.topk}"
+                   + (f", a {window}-position window on every layer" if window else "") + ") on "
+                   f"{used} host thread(s) of a {cpu_model()}: " + ", ".join(f"{t:.2f}" for t in times)
+                   + " s per step (caches quantised by the oracle beforehand, not timed)"),
     }
 
 
@@ -232,6 +286,31 @@ class HipEvents:
 
     def destroy(self, ev):
         self.hip.hipEventDestroy(ev)
+
+
+def launch_floor(args):
+    """A chain of dependent tiny launches (torch's in-place add on 32K
+    floats, 128 workgroups) timed with events: the per-launch floor of any
+    chain of dependent kernels on this GPU."""
+    import numpy as np
+    import torch
+    torch.cuda.set_device(0)
+    x = torch.zeros(128 * 256, dtype=torch.float32, device="cuda")
+    n = 40
+    for _ in range(n):
+        x.add_(1.0)
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(max(args.steps, 5)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            x.add_(1.0)
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) * 1e3 / n)
+    print(json.dumps({"launch_floor_us_per_dependent_launch": round(float(np.median(per)), 3),
+                      "chain": n, "repeats": len(per), "kernel": "torch add_ on 32,768 floats"}))
 
 
 def copy_probe():
@@ -427,6 +506,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=1, metavar="N",
                     help="host threads for the oracle baseline of the decode step (default 1; 0: the BLAS pool's size)")
+    ap.add_argument("--cpu-steps", type=int, default=1, metavar="N",
+                    help="oracle decode steps timed for the CPU baseline (default 1)")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="print only the CPU baseline of the decode step (no GPU work)")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="time a chain of dependent tiny launches (its own JSON line)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--prefill", type=int, default=0, metavar="T",
                     help="instead of the decode step: batched prefill-side sparse attention of T "
@@ -438,9 +523,11 @@ def main():
                     help="give every layer a local branch: an FP8 sliding-window ring of W positions "
                          "(prefilled, one row appended per layer per step) attended in the same "
                          "softmax; reported as its own configuration")
-    ap.add_argument("--mall-flush", action="store_true",
-                    help="read a 512 MB scratch buffer between steps (cold last-level cache, no "
-                         "dirty lines left to write back); step time from the events around each step")
+    ap.add_argument("--warm", action="store_true",
+                    help="run the steps back to back; by default a 512 MB scratch buffer is read between "
+                         "steps (cold last-level cache, as after a model's weights stream through it; no "
+                         "dirty lines left to write back) and the step time comes from the events around "
+                         "each step")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -451,6 +538,9 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
+    if args.launch_floor:
+        launch_floor(args)
+        return
     if args.prefill:
         prefill_bench(args)
         return
@@ -459,14 +549,25 @@ def main():
         return
 
     import numpy as np
+
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    # the oracle baseline first: its worker processes are forked before
+    # anything touches the GPU
+    cpu = None
+    if args.cpu_only or not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.swa, args.cpu_threads, args.cpu_steps)
+    if args.cpu_only:
+        print(json.dumps({"workload": w.name, "cpu_baseline": cpu}), flush=True)
+        return
+
     import torch
 
     import fp4_compressed_sparse_amd as csa2
-    import workloads as W
 
     csa2.load()
     torch.cuda.set_device(0)
-    w = W.WORKLOADS[args.workload]
     K, WU = args.steps, args.warmup
     total_steps = K + WU
     lengths = W.lengths(w)
@@ -521,7 +622,7 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     hev = HipEvents()
     sev = [(hev.create(), hev.create()) for _ in range(K)]
-    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda") if args.mall_flush else None
+    flush = None if args.warm else torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     flush_sink = torch.zeros((), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -547,8 +648,8 @@ def main():
         hev.destroy(b)
 
     ms_per_step = elapsed * 1e3 / K
-    if flush is not None:                          # the flush writes are not part of a step
-        ms_per_step = float(np.median(step_ms))
+    if flush is not None:                          # the flush reads are not part of a step
+        ms_per_step = float(np.mean(step_ms))
         elapsed = ms_per_step * 1e-3 * K
     n_mid = [int(n) + (WU + K // 2 + 1 if w.append else 0) for n in lengths]
     uniq, touched = step_bytes(w, n_mid)
@@ -576,18 +677,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "fp16",
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": B, "context": int(lengths.max()), "heads": H,
             "topk_blocks": w.topk, "pool_blocks": w.pool, "layers": L,
             "pattern": "[Full,Reindex,Reuse,Reuse,Reindex]x4" if w.wid == 3 else str(w.pattern),
             "kv_format": "FP4 E2M1 + E4M3/16ch, 288 B/position",
+            "arithmetic": "indexer scores float32; attention on fp16 matrix-core operands with float32 accumulation",
             "effective_kv_gbs": round(eff_gbs, 1),
             "effective_kv_frac_of_peak": round(eff_gbs / PEAK_HBM_GBS, 4),
             "unique_kv_bytes_per_step": uniq, "touched_kv_bytes_per_step": touched,
             "median_event_step_us": round(float(np.median(step_ms)) * 1e3, 2),
-            "mall_flush_between_steps": bool(args.mall_flush),
+            "mall_flush_between_steps": flush is not None,
             "swa_window": args.swa,
         },
         "roofline": {
@@ -602,8 +704,8 @@ def main():
             "avg_launch_us": round(scan_avg_s * 1e6, 2),
         },
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.swa, args.cpu_threads)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
