@@ -18,6 +18,8 @@ dominant kernel, CPU-oracle baseline).  Progress goes to stderr.
   python bench.py --prefill-write  (FP4 quantisation of 1,048,576 prompt rows, its own JSON line)
   python bench.py --cpu-only [--cpu-steps N] [--cpu-threads N]   (the oracle baseline alone)
   python bench.py --launch-floor   (a chain of dependent tiny launches: the per-launch floor)
+  python bench.py --score headmax  (the per-head indexer score rule: every head scores each block
+                                    in the pinned float32 order, the best head's score ranks it)
 
 By default the 256 MB last-level cache is flushed (a 512 MB read) between
 the timed steps and the step time is the mean of the events around each
@@ -34,6 +36,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+# Vector ALU peak for float32 work that may use neither FMA nor packed math
+# (the per-head score's pinned order multiplies and adds separately): 256
+# compute units x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T operations/s, each
+# multiply or add one operation (the published 157.3 TFLOP/s counts packed
+# FMAs, 4 flops per lane per clock).
+PEAK_VALU_TOPS = 256 * 64 * 2.4e9 / 1e12
 TOKEN_BYTES = 288              # 256 code bytes + 32 scale bytes per position
 BLOCK_BYTES = 8 * TOKEN_BYTES  # 2,304
 PMC_FILE = os.path.join(ROOT, "profiles", "scan_kernel_decoder20-1m_pmc.txt")
@@ -180,7 +188,7 @@ def oracle_caches(w, lengths, capacity, workers=16):
     return caches
 
 
-def cpu_baseline(w, window=0, threads=1, steps=1):
+def cpu_baseline(w, window=0, threads=1, steps=1, score=0):
     """The oracle's decode step timed on the host at the workload's full size:
     its caches quantised by the oracle (not timed), then `steps` decode steps
     of the same layer pattern, each appending one row per Full cache as the
@@ -222,7 +230,8 @@ def cpu_baseline(w, window=0, threads=1, steps=1):
             rows = np.stack([W.append_rows(w.wid, c, s, w.batch) for c in range(w.n_caches)]) if w.append else None
             srows = np.stack([W.swa_append_rows(w.wid, l, s, w.batch) for l in range(L)]) if window else None
             t1 = time.perf_counter()
-            decode_step(caches, layers, rows, w.topk, w.pool, w.scale, swa=swa, swa_rows=srows, window=window)
+            decode_step(caches, layers, rows, w.topk, w.pool, w.scale, swa=swa, swa_rows=srows, window=window,
+                        score=score)
             times.append(time.perf_counter() - t1)
             log(f"cpu oracle: step {s}: {times[-1]:.2f} s on {used} host thread(s)")
     total = sum(times)
@@ -234,7 +243,8 @@ def cpu_baseline(w, window=0, threads=1, steps=1):
         "sample": (f"{steps} decode step(s) of the workload ({w.name}: batch {w.batch}"
                    + (f" of its {full_batch} sequences" if full_batch != w.batch else "") + ", "
                    f"{int(lengths.max())} positions, {L} layers, {w.heads} heads, pool {w.pool}, top-{w.topk}"
-                   + (f", a {window}-position window on every layer" if window else "") + ") on "
+                   + (f", a {window}-position window on every layer" if window else "")
+                   + (", per-head score rule" if score else "") + ") on "
                    f"{used} host thread(s) of a {cpu_model()}: " + ", ".join(f"{t:.2f}" for t in times)
                    + " s per step (caches quantised by the oracle beforehand, not timed)"),
     }
@@ -523,6 +533,9 @@ def main():
                     help="give every layer a local branch: an FP8 sliding-window ring of W positions "
                          "(prefilled, one row appended per layer per step) attended in the same "
                          "softmax; reported as its own configuration")
+    ap.add_argument("--score", choices=("sum", "headmax"), default="sum",
+                    help="indexer score rule: heads summed into one query (default) or the best per-head "
+                         "score (vector-ALU bound; reported as its own configuration)")
     ap.add_argument("--warm", action="store_true",
                     help="run the steps back to back; by default a 512 MB scratch buffer is read between "
                          "steps (cold last-level cache, as after a model's weights stream through it; no "
@@ -553,11 +566,12 @@ def main():
     import workloads as W
 
     w = W.WORKLOADS[args.workload]
+    rule = 1 if args.score == "headmax" else 0
     # the oracle baseline first: its worker processes are forked before
     # anything touches the GPU
     cpu = None
     if args.cpu_only or not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.swa, args.cpu_threads, args.cpu_steps)
+        cpu = cpu_baseline(w, args.swa, args.cpu_threads, args.cpu_steps, rule)
     if args.cpu_only:
         print(json.dumps({"workload": w.name, "cpu_baseline": cpu}), flush=True)
         return
@@ -610,7 +624,7 @@ def main():
                      for s in range(total_steps)]
     plans = [csa2.StepPlan(caches, [(m, lc[l], q_all[s][l], outs[l], idxs[l], rings[l], srows_all[s][l])
                                     for l, m in enumerate(w.pattern)],
-                           H, w.topk, w.pool, w.scale, ws, pool_out=pool_out, new_rows=rows_all[s])
+                           H, w.topk, w.pool, w.scale, ws, pool_out=pool_out, new_rows=rows_all[s], score=rule)
              for s in range(total_steps)]
     stream = torch.cuda.current_stream()
 
@@ -691,6 +705,7 @@ def main():
             "median_event_step_us": round(float(np.median(step_ms)) * 1e3, 2),
             "mall_flush_between_steps": flush is not None,
             "swa_window": args.swa,
+            "score_rule": args.score,
         },
         "roofline": {
             "bound": "hbm",
@@ -704,6 +719,26 @@ def main():
             "avg_launch_us": round(scan_avg_s * 1e6, 2),
         },
     }
+    if rule:
+        # the per-head scan: H dot products of 512 unfused multiplies and 511
+        # adds (plus the +0.0) per block, and the block key (8 rows x 512
+        # multiply-adds, the x 1/8): vector-ALU bound
+        nblk = sum((n + 7) // 8 for n in n_mid)
+        ops = nblk * (H * 1024 + 8 * 512 * 2 + 512)
+        tops = ops / scan_avg_s / 1e12
+        result["roofline"] = {
+            "bound": "alu",
+            "kernel": "headmax_kernel (first Full layer per-head full-range scan)",
+            "achieved": round(tops, 2),
+            "peak": round(PEAK_VALU_TOPS, 2),
+            "unit": "TFLOP/s",
+            "frac": round(tops / PEAK_VALU_TOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": ops,
+            "avg_launch_us": round(scan_avg_s * 1e6, 2),
+        }
+        log(f"per-head scan: {ops / 1e9:.2f} G float32 ops in {scan_avg_s * 1e6:.1f} us = {tops:.2f} T ops/s "
+            f"({tops / PEAK_VALU_TOPS * 100:.1f}% of the {PEAK_VALU_TOPS:.1f} T ops/s unfused vector peak)")
     if cpu is not None:
         result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)

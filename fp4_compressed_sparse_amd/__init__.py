@@ -17,6 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa2.so")
 
 FULL, REINDEX, REUSE = 0, 1, 2
+SCORE_SUM, SCORE_HEADMAX = 0, 1     # indexer score rules: heads summed / best head
+MODE_HEADMAX = 0x100                # OR-ed into an index_topk mode: the per-head rule
 D, BLOCK, CODE_BYTES, SCALE_BYTES = 512, 8, 256, 32
 MAX_POOL, MAX_TOPK, MAX_CACHES = 8192, 2048, 16
 FLAG_NONFINITE_KV, FLAG_CAPACITY, FLAG_NONFINITE_Q, FLAG_BAD_INDEX, FLAG_SWA_RANGE, FLAG_Q_RANGE = 1, 2, 4, 8, 16, 32
@@ -56,7 +58,7 @@ class _Step(ctypes.Structure):
                 ("layers", ctypes.POINTER(_Layer)), ("n_layers", ctypes.c_int32),
                 ("new_rows", ctypes.c_void_p), ("heads", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("pool", ctypes.c_int32), ("scale", ctypes.c_float), ("pool_out", ctypes.c_void_p),
-                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("score_rule", ctypes.c_int32)]
 
 
 _lib = None
@@ -87,7 +89,7 @@ def load():
                                       ctypes.POINTER(_Swa), vp, vp, sz, vp]),
         "csa2_decode_step": (i32, [ctypes.POINTER(_Step), vp]),
         "csa2_decode_step_noalloc": (i32, [ctypes.POINTER(_Step), vp]),
-        "csa2_block_scores": (i32, [ctypes.POINTER(_Kv), vp, i32, vp, i32, vp, vp]),
+        "csa2_block_scores": (i32, [ctypes.POINTER(_Kv), vp, i32, vp, i32, vp, i32, vp]),
         "csa2_device_error": (i32, [ctypes.POINTER(ctypes.c_int32), vp]),
         "csa2_set_scan_events": (i32, [vp, vp]),
         "csa2_status_string": (ctypes.c_char_p, [i32]),
@@ -216,8 +218,13 @@ def workspace_init(ws, stream=None):
 
 
 def index_topk(mode, cache, q, topk, idx_out, ws, cand=None, pool=0, pool_out=None, prior_idx=None,
-               max_len=None, stream=None):
+               max_len=None, stream=None, score=SCORE_SUM):
+    """score: SCORE_SUM or SCORE_HEADMAX (Full/Reindex only)."""
     lib = load()
+    if score == SCORE_HEADMAX and mode != REUSE:
+        mode |= MODE_HEADMAX
+    elif score not in (SCORE_SUM, SCORE_HEADMAX):
+        raise ValueError(f"unknown score rule {score}")
     kv = cache.view(max_len) if cache is not None else _Kv(None, None, None, 8, 0, idx_out.shape[0])
     heads = q.shape[1] if q is not None else 0
     n_cand = cand.shape[1] if cand is not None else 0
@@ -256,21 +263,23 @@ def prefill_workspace(n_q, heads, topk, device="cuda"):
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
-def block_scores(cache, q, scores, cand=None, max_len=None, stream=None):
+def block_scores(cache, q, scores, cand=None, max_len=None, stream=None, score=SCORE_SUM):
     lib = load()
     kv = cache.view(max_len)
     n_cand = cand.shape[1] if cand is not None else 0
     _check(lib.csa2_block_scores(ctypes.byref(kv), _ptr(q), q.shape[1], _ptr(cand), n_cand,
-                                 _ptr(scores), _stream(stream)))
+                                 _ptr(scores), int(score), _stream(stream)))
 
 
 class StepPlan:
     """A decode step's C structures, built once and reusable (e.g. for
     repeated launches or graph capture).  layers: list of (mode, cache, q,
     out, idx) or (mode, cache, q, out, idx, swa, swa_row) with torch tensors
-    (swa: the layer's SwaCache or None; swa_row float32 [B, 512] or None)."""
+    (swa: the layer's SwaCache or None; swa_row float32 [B, 512] or None).
+    score: SCORE_SUM or SCORE_HEADMAX for every selecting layer."""
 
-    def __init__(self, caches, layers, heads, topk, pool, scale, ws, pool_out=None, new_rows=None):
+    def __init__(self, caches, layers, heads, topk, pool, scale, ws, pool_out=None, new_rows=None,
+                 score=SCORE_SUM):
         self.caches = caches
         self._kv = (_Kv * len(caches))(*[c.view() for c in caches])
         self._swa = [ly[5].view() if len(ly) > 5 and ly[5] is not None else None for ly in layers]
@@ -286,7 +295,8 @@ class StepPlan:
         self._step = _Step(self._kv, len(caches), self._layers, len(layers),
                            new_rows.data_ptr() if new_rows is not None else None, heads, topk, pool,
                            float(scale), pool_out.data_ptr() if pool_out is not None else None,
-                           ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0)
+                           ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+                           int(score))
 
     def refresh_lengths(self):
         """Copy each cache's host max_len bound into the C views."""
@@ -302,13 +312,15 @@ class StepPlan:
         _check(load().csa2_decode_step_noalloc(ctypes.byref(self._step), _stream(stream)))
 
 
-def decode_step(caches, layers, heads, topk, pool, scale, ws, pool_out=None, new_rows=None, stream=None):
-    StepPlan(caches, layers, heads, topk, pool, scale, ws, pool_out, new_rows).run(stream)
+def decode_step(caches, layers, heads, topk, pool, scale, ws, pool_out=None, new_rows=None, stream=None,
+                score=SCORE_SUM):
+    StepPlan(caches, layers, heads, topk, pool, scale, ws, pool_out, new_rows, score).run(stream)
 
 
-def decode_step_noalloc(caches, layers, heads, topk, pool, scale, pool_out=None, new_rows=None, stream=None):
+def decode_step_noalloc(caches, layers, heads, topk, pool, scale, pool_out=None, new_rows=None, stream=None,
+                        score=SCORE_SUM):
     """decode_step on the library's own per-device workspace (no allocation)."""
-    StepPlan(caches, layers, heads, topk, pool, scale, None, pool_out, new_rows).run_noalloc(stream)
+    StepPlan(caches, layers, heads, topk, pool, scale, None, pool_out, new_rows, score).run_noalloc(stream)
 
 
 def set_scan_events(before=None, after=None):

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["api.hip", "quantize.hip", "index.hip", "attend.hip", "common.hpp"]
+SOURCES = ["api.hip", "quantize.hip", "index.hip", "headmax.hip", "attend.hip", "common.hpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

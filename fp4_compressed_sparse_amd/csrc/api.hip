@@ -8,6 +8,7 @@
 // search) and the mode table of ailily.cc "890 bytes per token", section 二.
 #include "quantize.hip"
 #include "index.hip"
+#include "headmax.hip"
 #include "attend.hip"
 
 #include <cstdarg>
@@ -78,6 +79,8 @@ csa2_status device_ready() {
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&select2_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, big);
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&rescore_kernel<true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, big);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&select_cand_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, big);
       (void)hipGetLastError();
       state[dev] = 1;
@@ -190,14 +193,50 @@ int grid_for(int64_t items, int batch, int target) {
 
 // ---- launches (arguments already validated) -----------------------------
 
+// Per-head score rule: tile sizes and grid (headmax.hip; 4 waves of 128
+// channels, about 190 registers: two workgroups per compute unit).  The full
+// scan gives each of 512 workgroups 16 blocks at a time; the candidate
+// rescoring gives each
+// workgroup one tile of 8 candidates, so a 2,048-block pool spreads over 256
+// workgroups, one wave per SIMD.
+constexpr int HM_SCAN_NT = 16;
+constexpr int HM_SCAN_GRID = 512;
+constexpr int HM_CAND_NT = 8;
+
+HeadmaxArgs headmax_args(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *cand,
+                         int32_t n_cand, float *scores, int64_t score_stride) {
+  HeadmaxArgs ha;
+  memset(&ha, 0, sizeof ha);
+  ha.codes = kv->codes; ha.scales = kv->scales; ha.seq_len = kv->seq_len; ha.capacity = kv->capacity;
+  ha.limit = kv->max_len;
+  ha.q = q; ha.heads = heads; ha.cand = cand; ha.n_cand = n_cand;
+  ha.scores = scores; ha.score_stride = score_stride;
+  return ha;
+}
+
+csa2_status run_select(const csa2_kv *kv, int32_t R, int32_t *first_out, int32_t topk2, int32_t *idx_out,
+                       void *ws, const Layout &L, hipStream_t s, float *pool_scores);
+
 // qbar_ready: the query sum is already in the workspace (computed in the
 // decode step's append launch for this same query).
 csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, int32_t R,
                             int32_t *first_out, int32_t topk2, int32_t *idx_out, void *ws,
                             const Layout &L, hipStream_t s, float *pool_scores = nullptr,
-                            bool qbar_ready = false) {
+                            bool qbar_ready = false, int32_t rule = CSA2_SCORE_SUM) {
   const int B = kv->batch;
   const int64_t nblk_grid = ceil_div(kv->max_len, BLOCK);
+  if (rule == CSA2_SCORE_HEADMAX) {
+    // per-head scores and their digit counts, then the same selection
+    HeadmaxArgs ha = headmax_args(kv, q, heads, nullptr, 0, at<float>(ws, L.scores), L.score_stride);
+    ha.nblk_grid = (int32_t)nblk_grid;
+    ha.hist = at<uint32_t>(ws, L.hist);
+    if (t_scan_before) (void)hipEventRecord(t_scan_before, s);
+    const int64_t tiles = ceil_div(nblk_grid > 0 ? nblk_grid : 1, HM_SCAN_NT);
+    headmax_kernel<4, HM_SCAN_NT, false, true><<<dim3(grid_for(tiles, B, HM_SCAN_GRID), B), 256, 0, s>>>(ha);
+    if (csa2_status st = launched("headmax scan")) return st;
+    if (t_scan_after) (void)hipEventRecord(t_scan_after, s);
+    return run_select(kv, R, first_out, topk2, idx_out, ws, L, s, pool_scores);
+  }
   ScanArgs sa;
   sa.codes = kv->codes; sa.scales = kv->scales; sa.seq_len = kv->seq_len; sa.capacity = kv->capacity;
   sa.limit = kv->max_len;
@@ -226,15 +265,25 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
     scan_kernel<true><<<g1, SCAN_THREADS, 0, s>>>(sa);
   if (csa2_status st = launched("scan")) return st;
   if (t_scan_after) (void)hipEventRecord(t_scan_after, s);
+  return run_select(kv, R, first_out, topk2, idx_out, ws, L, s, pool_scores);
+}
+
+// Selection of the top-R scored blocks (and their top-topk2) from the
+// workspace's scores and digit counts, as the full scan left them.
+csa2_status run_select(const csa2_kv *kv, int32_t R, int32_t *first_out, int32_t topk2, int32_t *idx_out,
+                       void *ws, const Layout &L, hipStream_t s, float *pool_scores) {
+  const int B = kv->batch;
+  const int64_t nblk_grid = ceil_div(kv->max_len, BLOCK);
   SelectArgs se;
-  se.seq_len = kv->seq_len; se.limit = kv->max_len; se.scores = sa.scores; se.score_stride = L.score_stride;
-  se.ctrl = sa.ctrl; se.bitmap = at<uint32_t>(ws, L.bitmap); se.nwords = L.nwords;
+  se.seq_len = kv->seq_len; se.limit = kv->max_len; se.scores = at<float>(ws, L.scores);
+  se.score_stride = L.score_stride;
+  se.ctrl = at<Ctrl>(ws, L.ctrl); se.bitmap = at<uint32_t>(ws, L.bitmap); se.nwords = L.nwords;
   se.cands = at<uint64_t>(ws, L.cands); se.cand_stride = L.cand_stride;
   se.R = R; se.first_out = first_out; se.topk = topk2; se.idx_out = idx_out;
   int lk = R > 4096 ? R : 4096;
   se.lds_keys = lk;
   se.pool_scores = pool_scores;
-  se.hist = sa.hist;
+  se.hist = at<uint32_t>(ws, L.hist);
   if (L.nwords <= SEL2_WORDS && R <= SEL2_KEYS) {
     // the chosen ids' bitmap fits in one workgroup's LDS
     dim3 g2(std::max<int64_t>(1, ceil_div(nblk_grid, SEL2_SPAN)), B);
@@ -248,8 +297,22 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
 
 csa2_status run_rescore(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *cand,
                         int32_t n_cand, int32_t topk, int32_t *idx_out, float *scores,
-                        int64_t score_stride, Ctrl *ctrl, hipStream_t s) {
+                        int64_t score_stride, Ctrl *ctrl, hipStream_t s, int32_t rule = CSA2_SCORE_SUM) {
   const int B = kv->batch;
+  if (rule == CSA2_SCORE_HEADMAX) {
+    // per-head scores of the list (one tile per workgroup), then, when a
+    // selection is wanted, its top-k in one workgroup per sequence
+    HeadmaxArgs ha = headmax_args(kv, q, heads, cand, n_cand, scores, score_stride);
+    headmax_kernel<4, HM_CAND_NT, true, false><<<dim3((int)ceil_div(n_cand, HM_CAND_NT), B), 256, 0, s>>>(ha);
+    if (csa2_status st = launched("headmax rescore")) return st;
+    if (!idx_out) return CSA2_OK;
+    RescoreArgs ra;
+    memset(&ra, 0, sizeof ra);
+    ra.seq_len = kv->seq_len; ra.limit = kv->max_len; ra.cand = cand; ra.n_cand = n_cand;
+    ra.scores = scores; ra.score_stride = score_stride; ra.topk = topk; ra.idx_out = idx_out;
+    select_cand_kernel<<<dim3(1, B), SCAN_THREADS, (size_t)n_cand * sizeof(uint64_t), s>>>(ra);
+    return launched("candidate select");
+  }
   RescoreArgs ra;
   ra.codes = kv->codes; ra.scales = kv->scales; ra.seq_len = kv->seq_len; ra.capacity = kv->capacity;
   ra.limit = kv->max_len;
@@ -469,8 +532,10 @@ csa2_status csa2_index_topk(int32_t mode, const csa2_kv *kv, const float *q, int
                             int32_t pool, int32_t *pool_out, const int32_t *prior_idx, void *ws,
                             size_t ws_bytes, void *stream) {
   t_last_error.clear();
+  const int32_t rule = (mode & CSA2_MODE_HEADMAX) ? CSA2_SCORE_HEADMAX : CSA2_SCORE_SUM;
+  mode &= ~CSA2_MODE_HEADMAX;
   if (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)
-    return fail(CSA2_E_ARG, "mode %d is not Full/Reindex/Reuse", mode);
+    return fail(CSA2_E_ARG, "mode %d is not Full/Reindex/Reuse (optionally | CSA2_MODE_HEADMAX)", mode);
   if (!idx_out || !aligned(idx_out, 4)) return fail(CSA2_E_ARG, "idx_out must be non-NULL");
   if (topk < 1 || topk > CSA2_MAX_TOPK) return fail(CSA2_E_SHAPE, "topk %d outside [1, %d]", topk, CSA2_MAX_TOPK);
   hipStream_t s = as_stream(stream);
@@ -496,13 +561,13 @@ csa2_status csa2_index_topk(int32_t mode, const csa2_kv *kv, const float *q, int
     if (n_cand < 1 || n_cand > CSA2_MAX_POOL) return fail(CSA2_E_SHAPE, "n_cand %d outside [1, %d]", n_cand, CSA2_MAX_POOL);
     if (!aligned(cand, 4)) return fail(CSA2_E_ARG, "cand misaligned");
     return run_rescore(kv, q, heads, cand, n_cand, topk, idx_out, at<float>(ws, L.scores),
-                       L.score_stride, at<Ctrl>(ws, L.ctrl), s);
+                       L.score_stride, at<Ctrl>(ws, L.ctrl), s, rule);
   }
   if (pool > 0) {
     if (!pool_out || !aligned(pool_out, 4)) return fail(CSA2_E_ARG, "pool > 0 needs pool_out");
-    return run_scan_select(kv, q, heads, pool, pool_out, topk, idx_out, ws, L, s);
+    return run_scan_select(kv, q, heads, pool, pool_out, topk, idx_out, ws, L, s, nullptr, false, rule);
   }
-  return run_scan_select(kv, q, heads, topk, idx_out, 0, nullptr, ws, L, s);
+  return run_scan_select(kv, q, heads, topk, idx_out, 0, nullptr, ws, L, s, nullptr, false, rule);
 }
 
 csa2_status csa2_sparse_attend(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *idx,
@@ -611,8 +676,10 @@ csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, 
 }
 
 csa2_status csa2_block_scores(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *cand,
-                              int32_t n_cand, float *scores, void *stream) {
+                              int32_t n_cand, float *scores, int32_t score_rule, void *stream) {
   t_last_error.clear();
+  if (score_rule != CSA2_SCORE_SUM && score_rule != CSA2_SCORE_HEADMAX)
+    return fail(CSA2_E_ARG, "score_rule %d is not CSA2_SCORE_SUM or CSA2_SCORE_HEADMAX", score_rule);
   if (csa2_status st = check_kv(kv)) return st;
   if (!q || !aligned(q, 16) || !scores || !aligned(scores, 4))
     return fail(CSA2_E_ARG, "q/scores must be non-NULL and aligned");
@@ -621,10 +688,19 @@ csa2_status csa2_block_scores(const csa2_kv *kv, const float *q, int32_t heads, 
   hipStream_t s = as_stream(stream);
   if (cand) {
     if (n_cand < 1 || n_cand > CSA2_MAX_POOL) return fail(CSA2_E_SHAPE, "n_cand %d outside [1, %d]", n_cand, CSA2_MAX_POOL);
-    return run_rescore(kv, q, heads, cand, n_cand, 0, nullptr, scores, n_cand, nullptr, s);
+    return run_rescore(kv, q, heads, cand, n_cand, 0, nullptr, scores, n_cand, nullptr, s, score_rule);
   }
   const int64_t nblk_grid = ceil_div(kv->max_len, BLOCK);
   if (nblk_grid == 0) return CSA2_OK;
+  if (score_rule == CSA2_SCORE_HEADMAX) {
+    HeadmaxArgs ha = headmax_args(kv, q, heads, nullptr, 0, scores, nblk_grid);
+    ha.nblk_grid = (int32_t)nblk_grid;
+    ha.fill_invalid = 1;
+    const int64_t tiles = ceil_div(nblk_grid, HM_SCAN_NT);
+    headmax_kernel<4, HM_SCAN_NT, false, false>
+        <<<dim3(grid_for(tiles, kv->batch, HM_SCAN_GRID), kv->batch), 256, 0, s>>>(ha);
+    return launched("headmax scores");
+  }
   ScanArgs sa;
   sa.codes = kv->codes; sa.scales = kv->scales; sa.seq_len = kv->seq_len; sa.capacity = kv->capacity;
   sa.limit = kv->max_len;
@@ -654,6 +730,9 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
   if (csa2_status e = check_select_args(st->topk, st->pool)) return e;
   if (st->pool > 0 && (!st->pool_out || !aligned(st->pool_out, 4))) return fail(CSA2_E_ARG, "pool > 0 needs pool_out");
   if (st->new_rows && !aligned(st->new_rows, 16)) return fail(CSA2_E_ARG, "new_rows misaligned");
+  const int32_t rule = st->score_rule;
+  if (rule != CSA2_SCORE_SUM && rule != CSA2_SCORE_HEADMAX)
+    return fail(CSA2_E_ARG, "score_rule %d is not CSA2_SCORE_SUM or CSA2_SCORE_HEADMAX", rule);
   // mode pattern: layer 0 Full; Reindex/Reuse use the latest Full cache
   int latest = -1, n_rings = 0;
   for (int l = 0; l < st->n_layers; ++l) {
@@ -707,10 +786,14 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
       ++nr;
     }
     // the first layer (Full) scans all blocks: its query sum rides along
+    // (the summed score rule only)
     QbarJob qj{st->layers[0].q, st->heads, at<float>(st->ws, L.qbar)};
-    append_kernel<<<dim3(B, nc + nr + QBAR_SLICES), 128, 0, s>>>(aa, rr, st->new_rows, B, nc, nr, qj);
-    if (csa2_status e = launched("append")) return e;
-    qbar_ready = true;
+    const int slices = rule == CSA2_SCORE_SUM ? QBAR_SLICES : 0;
+    if (nc + nr + slices > 0) {
+      append_kernel<<<dim3(B, nc + nr + slices), 128, 0, s>>>(aa, rr, st->new_rows, B, nc, nr, qj);
+      if (csa2_status e = launched("append")) return e;
+    }
+    qbar_ready = slices > 0;
   }
   bool pool_built = false;
   const int32_t *prev_idx = nullptr;
@@ -732,10 +815,10 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
       float *cs = at<float>(st->ws, L.cscores);
       if (!pool_built) {
         e = run_scan_select(kv, ly.q, st->heads, st->pool, st->pool_out, 0, nullptr, st->ws, L, s, cs,
-                            qbar_ready && l == 0);
+                            qbar_ready && l == 0, rule);
         pool_built = true;
       } else {
-        e = run_rescore(kv, ly.q, st->heads, st->pool_out, st->pool, 0, nullptr, cs, st->pool, nullptr, s);
+        e = run_rescore(kv, ly.q, st->heads, st->pool_out, st->pool, 0, nullptr, cs, st->pool, nullptr, s, rule);
       }
       if (e) return e;
       e = run_attend(kv, ly.q, st->heads, nullptr, st->topk, st->scale, ly.out, st->ws, L, s,
@@ -745,14 +828,14 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
       continue;
     } else if (st->pool > 0 && !pool_built) {
       e = run_scan_select(kv, ly.q, st->heads, st->pool, st->pool_out, st->topk, ly.idx, st->ws, L, s,
-                          nullptr, qbar_ready && l == 0);
+                          nullptr, qbar_ready && l == 0, rule);
       pool_built = true;
     } else if (st->pool > 0) {
       e = run_rescore(kv, ly.q, st->heads, st->pool_out, st->pool, st->topk, ly.idx,
-                      at<float>(st->ws, L.scores), L.score_stride, at<Ctrl>(st->ws, L.ctrl), s);
+                      at<float>(st->ws, L.scores), L.score_stride, at<Ctrl>(st->ws, L.ctrl), s, rule);
     } else {
       e = run_scan_select(kv, ly.q, st->heads, st->topk, ly.idx, 0, nullptr, st->ws, L, s, nullptr,
-                          qbar_ready && l == 0);
+                          qbar_ready && l == 0, rule);
     }
     if (e) return e;
     e = run_attend(kv, ly.q, st->heads, ly.idx, st->topk, st->scale, ly.out, st->ws, L, s, nullptr,

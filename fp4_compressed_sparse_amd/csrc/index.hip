@@ -1482,6 +1482,37 @@ struct RescoreArgs {
   int32_t *idx_out;         // [batch][topk]; NULL = scores only
 };
 
+// Selection keys of a scored candidate list into LDS (all threads call):
+// s_ids[j] = cand[j]; s_keys[j] = key of (scores[j], cand[j]), 0 for an id
+// outside [0, nblk).  AGENT: other workgroups of the running kernel wrote
+// the scores.
+template <bool AGENT>
+__device__ __forceinline__ void cand_keys_to_lds(const int32_t *cand, const float *scores, int m, int64_t nblk,
+                                                 uint64_t *s_keys, int32_t *s_ids) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  constexpr int U = 8;
+  for (int j0 = t; j0 < m; j0 += nt * U) {
+    int32_t idv[U];
+    float sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = min(j0 + u * nt, m - 1);         // clamped: no branch
+      idv[u] = cand[jj];
+      sv[u] = AGENT ? ld_agent(scores + jj) : scores[jj];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = j0 + u * nt;
+      if (jj < m) {
+        const bool ok = idv[u] >= 0 && idv[u] < nblk;
+        s_ids[jj] = idv[u];
+        s_keys[jj] = ok ? make_key(sv[u], (uint32_t)idv[u]) : 0ull;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 template <bool SELECT>
 __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint64_t s_keys[];
@@ -1544,31 +1575,9 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   Ctrl *ctrl = a.ctrl + b;
   if (!arrive_last(ctrl->sel_grp, &ctrl->sel_top, gridDim.x)) return;
   CSA2_TS(3);
-  const int t = threadIdx.x, nt = blockDim.x;
-  const int m = a.n_cand;
-  constexpr int U = 8;
-  for (int j0 = t; j0 < m; j0 += nt * U) {
-    int32_t idv[U];
-    float sv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int jj = j0 + u * nt;
-      idv[u] = cand[min(jj, m - 1)];                  // clamped: no branch
-      sv[u] = ld_agent(scores + min(jj, m - 1));
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int jj = j0 + u * nt;
-      if (jj < m) {
-        const bool ok = idv[u] >= 0 && idv[u] < nblk;
-        s_ids[jj] = idv[u];
-        s_keys[jj] = ok ? make_key(sv[u], (uint32_t)idv[u]) : 0ull;
-      }
-    }
-  }
-  __syncthreads();
+  cand_keys_to_lds<true>(cand, scores, a.n_cand, nblk, s_keys, s_ids);
   CSA2_TS(4);
-  select_in_lds(s_keys, s_ids, m, a.topk, a.idx_out + (int64_t)b * a.topk, s_sel, a.topk,
+  select_in_lds(s_keys, s_ids, a.n_cand, a.topk, a.idx_out + (int64_t)b * a.topk, s_sel, a.topk,
                 s_hist, s_state, s_wave);
   CSA2_TS(5);
 }

@@ -67,6 +67,23 @@ enum {
 /* Layer modes [P2 CSA2 section; P3 section 二, mode table]. */
 enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 };
 
+/*
+ * Indexer score rules.  The pages say the indexer keeps the top-k most
+ * relevant blocks [P2 CSA2 section] but not how many query heads become one
+ * block score; two plain readings are built, both in a pinned float32 order
+ * so the selected indices are reproducible bit for bit:
+ *   CSA2_SCORE_SUM      heads added in order into one query Qbar, score =
+ *                       Qbar . key (memory-bound scan; the default);
+ *   CSA2_SCORE_HEADMAX  score = the largest over the heads of q_h . key, each
+ *                       head in the same order as Qbar . key (64 dot products
+ *                       per block at 64 heads: bound by the vector ALU).
+ * csa2_index_topk takes the rule as a flag OR-ed into its mode
+ * (CSA2_FULL | CSA2_MODE_HEADMAX); csa2_step and csa2_block_scores take it
+ * as a field / argument.
+ */
+enum { CSA2_SCORE_SUM = 0, CSA2_SCORE_HEADMAX = 1 };
+#define CSA2_MODE_HEADMAX 0x100
+
 /* Bits of the device flag word (csa2_device_error). */
 enum {
   CSA2_FLAG_NONFINITE_KV = 1,   /* a quantised group held NaN/Inf: written as zeros     */
@@ -205,6 +222,9 @@ csa2_status csa2_workspace_init(void *ws, size_t ws_bytes, void *stream);
  *     pointers are equal); kv, q, cand and pool_out are not used.
  *   mode CSA2_FULL / CSA2_REINDEX: identical computation; the caller passes
  *     the layer's own cache (Full) or the latest Full cache (Reindex).
+ *     OR-ing CSA2_MODE_HEADMAX into the mode selects the per-head score
+ *     rule (CSA2_SCORE_HEADMAX, described above); the rest of this
+ *     paragraph describes the default rule.
  *     Block key = mean of the block's dequantised rows (rows added in
  *     ascending order in float32, then divided by the row count); indexer
  *     query Qbar = heads added in order in float32; score = Qbar . key in a
@@ -324,6 +344,8 @@ typedef struct {
   int32_t *pool_out;         /* device int32 [batch][pool] (pool > 0)            */
   void *ws;
   size_t ws_bytes;
+  int32_t score_rule;        /* CSA2_SCORE_SUM or CSA2_SCORE_HEADMAX, for every
+                                selecting layer                                 */
 } csa2_step;
 
 /*
@@ -359,7 +381,8 @@ csa2_status csa2_decode_step_noalloc(const csa2_step *step, void *stream);
 
 /*
  * csa2_block_scores — diagnostic export of the indexer's float32 scores
- * (the same arithmetic as csa2_index_topk).
+ * (the same arithmetic as csa2_index_topk) under score_rule
+ * (CSA2_SCORE_SUM or CSA2_SCORE_HEADMAX).
  * cand == NULL: scores[b][j] for every block j < ceil(max_len/8) (blocks at
  * or past a shorter sequence's end get -inf); else scores[b][j] for
  * cand[b][j], j < n_cand (-inf for -1 entries).
@@ -367,7 +390,7 @@ csa2_status csa2_decode_step_noalloc(const csa2_step *step, void *stream);
  */
 csa2_status csa2_block_scores(const csa2_kv *kv, const float *q, int32_t heads,
                               const int32_t *cand, int32_t n_cand, float *scores,
-                              void *stream);
+                              int32_t score_rule, void *stream);
 
 /*
  * csa2_device_error — synchronise `stream`, copy the device flag word of
