@@ -178,6 +178,48 @@ csa2_status check_ws(void *ws, size_t ws_bytes, const Layout &L) {
   return CSA2_OK;
 }
 
+// The words that must be zero when a call starts (control words, digit
+// counts, the fallback selection's bitmap) sit at offsets that depend on the
+// call's bounds, and every call leaves only its own ones zero.  So the
+// library remembers, per workspace, where the last call's were; a call
+// whose layout differs zero-fills [0, cands) first (a kernel on its stream).
+// A workspace seen for the first time is taken as zero-filled, as the ABI
+// requires; csa2_workspace_init forgets it.
+struct WsStamp {
+  const void *ws;
+  int32_t batch, nwords;
+  size_t ctrl, hist, scores, bitmap, cands;
+};
+std::mutex g_ws_mu;
+WsStamp g_ws_tab[256];
+int g_ws_next = 0;
+
+void ws_forget(const void *ws) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  for (WsStamp &e : g_ws_tab)
+    if (e.ws == ws) e.ws = nullptr;
+}
+
+csa2_status ws_ready(void *ws, int32_t batch, const Layout &L, hipStream_t s) {
+  const WsStamp now{ws, batch, L.nwords, L.ctrl, L.hist, L.scores, L.bitmap, L.cands};
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  for (WsStamp &e : g_ws_tab) {
+    if (e.ws != ws) continue;
+    if (e.batch == now.batch && e.nwords == now.nwords && e.ctrl == now.ctrl && e.hist == now.hist &&
+        e.scores == now.scores && e.bitmap == now.bitmap && e.cands == now.cands)
+      return CSA2_OK;
+    const int64_t words = (int64_t)(L.cands / sizeof(uint32_t));
+    zero_kernel<<<(int)std::min<int64_t>(2048, ceil_div(words, 256)), 256, 0, s>>>(static_cast<uint32_t *>(ws),
+                                                                                    words);
+    if (csa2_status st = launched("workspace re-zero")) return st;
+    e = now;
+    return CSA2_OK;
+  }
+  g_ws_tab[g_ws_next] = now;
+  g_ws_next = (g_ws_next + 1) % (int)(sizeof(g_ws_tab) / sizeof(g_ws_tab[0]));
+  return CSA2_OK;
+}
+
 template <typename T>
 T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
 
@@ -196,12 +238,11 @@ int grid_for(int64_t items, int batch, int target) {
 // Per-head score rule: tile sizes and grid (headmax.hip; 4 waves of 128
 // channels, about 190 registers: two workgroups per compute unit).  The full
 // scan gives each of 512 workgroups 16 blocks at a time; the candidate
-// rescoring gives each
-// workgroup one tile of 8 candidates, so a 2,048-block pool spreads over 256
-// workgroups, one wave per SIMD.
+// rescoring gives each workgroup one tile of 4 candidates, so a 2,048-block
+// pool spreads over 512 workgroups.
 constexpr int HM_SCAN_NT = 16;
 constexpr int HM_SCAN_GRID = 512;
-constexpr int HM_CAND_NT = 8;
+constexpr int HM_CAND_NT = 4;
 
 HeadmaxArgs headmax_args(const csa2_kv *kv, const float *q, int32_t heads, const int32_t *cand,
                          int32_t n_cand, float *scores, int64_t score_stride) {
@@ -287,6 +328,7 @@ csa2_status run_select(const csa2_kv *kv, int32_t R, int32_t *first_out, int32_t
   if (L.nwords <= SEL2_WORDS && R <= SEL2_KEYS) {
     // the chosen ids' bitmap fits in one workgroup's LDS
     dim3 g2(std::max<int64_t>(1, ceil_div(nblk_grid, SEL2_SPAN)), B);
+    se.lds_keys = select2_keys(L.nwords);
     select2_kernel<<<g2, SEL2_THREADS, select2_lds(L.nwords), s>>>(se);
     return launched("select");
   }
@@ -453,6 +495,7 @@ csa2_status csa2_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   const int64_t words = (int64_t)(ws_bytes / 4);
   const int grid = (int)(ceil_div(words, 256) < 2048 ? ceil_div(words, 256) : 2048);
   zero_kernel<<<grid, 256, 0, as_stream(stream)>>>(static_cast<uint32_t *>(ws), words);
+  ws_forget(ws);
   return launched("workspace_init");
 }
 
@@ -556,6 +599,7 @@ csa2_status csa2_index_topk(int32_t mode, const csa2_kv *kv, const float *q, int
   if (!make_layout(kv->batch, heads, kv->max_len, pool, topk, &L)) return fail(CSA2_E_SHAPE, "bad sizes");
   if (csa2_status st = check_ws(ws, ws_bytes, L)) return st;
   if (csa2_status st = device_ready()) return st;
+  if (csa2_status st = ws_ready(ws, kv->batch, L, s)) return st;
   if (cand) {
     if (pool != 0) return fail(CSA2_E_ARG, "pool must be 0 with a candidate list");
     if (n_cand < 1 || n_cand > CSA2_MAX_POOL) return fail(CSA2_E_SHAPE, "n_cand %d outside [1, %d]", n_cand, CSA2_MAX_POOL);
@@ -764,6 +808,7 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
   if (csa2_status e = check_ws(st->ws, st->ws_bytes, L)) return e;
   if (csa2_status e = device_ready()) return e;
   hipStream_t s = as_stream(stream);
+  if (csa2_status e = ws_ready(st->ws, B, L, s)) return e;
 
   bool qbar_ready = false;                // layer 0's query sum is in the workspace
   if (st->new_rows || n_rings) {

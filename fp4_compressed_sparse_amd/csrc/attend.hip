@@ -209,10 +209,17 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     __builtin_amdgcn_sched_barrier(0);
   };
   CSA2_TS(0);
+  // the tile's 16 query rows (32 KB), 8 float4 per thread: requested first
+  // by the selecting variant, so their latency hides behind the block top-k
+  constexpr int NV = 16 * D / 4 / ATT_THREADS;
+  const float4 *qsrc = reinterpret_cast<const float4 *>(a.q + ((int64_t)b * a.heads + 16 * ht) * D);
+  float4 v[NV];
   // Selecting variant: candidates, their scores and the sequence length in
   // one batch, then the block top-k in LDS (the key/id/bin arrays borrow the
   // row buffer, which is free until the query is staged).
   if constexpr (SELECT) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) v[u] = qsrc[tid + u * ATT_THREADS];
     constexpr int KPT = SEL_CAND_MAX / ATT_THREADS;
     const int m = a.n_cand;
     const int32_t *cb = a.cand + (int64_t)b * m;
@@ -252,11 +259,10 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   // batch of coalesced float4 loads per thread, then read into registers.
   f16x8 qop[16];
   {
-    constexpr int NV = 16 * D / 4 / ATT_THREADS;            // 8 float4 per thread
-    const float4 *src = reinterpret_cast<const float4 *>(a.q + ((int64_t)b * a.heads + 16 * ht) * D);
-    float4 v[NV];
+    if constexpr (!SELECT) {
 #pragma unroll
-    for (int u = 0; u < NV; ++u) v[u] = src[tid + u * ATT_THREADS];
+      for (int u = 0; u < NV; ++u) v[u] = qsrc[tid + u * ATT_THREADS];
+    }
     __builtin_amdgcn_sched_barrier(0);    // query loads go out before the ids are awaited
     if (WIN) {
       wrl = wlen_raw < 0 ? 0 : wlen_raw;                      // positions in the ring

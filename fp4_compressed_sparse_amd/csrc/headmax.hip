@@ -282,7 +282,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_cand_kernel(RescoreArgs a
   extern __shared__ __attribute__((aligned(16))) uint64_t s_keys[];
   __shared__ int32_t s_ids[LDS_KEYS];
   __shared__ int32_t s_sel[CSA2_TOPK_MAX];
-  __shared__ uint32_t s_hist[RADIX_BINS];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[RADIX_BINS];   // also 64-bit keys (radix_select_keys)
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;
@@ -296,6 +296,6 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_cand_kernel(RescoreArgs a
 
 template __global__ void headmax_kernel<4, 16, false, true>(HeadmaxArgs);
 template __global__ void headmax_kernel<4, 16, false, false>(HeadmaxArgs);
-template __global__ void headmax_kernel<4, 8, true, false>(HeadmaxArgs);
+template __global__ void headmax_kernel<4, 4, true, false>(HeadmaxArgs);
 
 }  // namespace csa2

@@ -938,7 +938,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint64_t s_keys[];                 // lds_keys
   __shared__ int32_t s_ids[LDS_KEYS];
   __shared__ int32_t s_sel[CSA2_TOPK_MAX];
-  __shared__ uint32_t s_hist[RADIX_BINS];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[RADIX_BINS];   // also 64-bit keys (radix_select_keys)
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;
@@ -1220,19 +1220,31 @@ constexpr int SEL2_SPAN = SEL2_THREADS * SEL2_U;       // blocks per workgroup
 constexpr int SEL2_MAXG = SEL2_WORDS * 32 / SEL2_SPAN;  // workgroups per sequence
 static_assert(SEL2_THREADS == HIST_BINS, "one histogram bin per thread");
 
+// The finisher's LDS key capacity for a bitmap of nwords words: what fits in
+// SEL2_LDS_BYTES of dynamic LDS beside the bitmap and its word prefix sums
+// (a multiple of 1,024; at least SEL2_KEYS for nwords <= SEL2_WORDS).
+constexpr int64_t SEL2_LDS_BYTES = 136 * 1024;
+inline int select2_keys(int nwords) {
+  const int64_t k = (SEL2_LDS_BYTES - 2 * (int64_t)sizeof(uint32_t) * nwords) / (int64_t)sizeof(uint64_t);
+  return (int)(k / 1024 * 1024);
+}
+static_assert((SEL2_LDS_BYTES - 8 * SEL2_WORDS) / 8 >= SEL2_KEYS, "finisher capacity");
+
 // Dynamic LDS bytes of select2_kernel: the keys, the bitmap and its word
 // prefix sums.
 inline size_t select2_lds(int nwords) {
-  return sizeof(uint64_t) * SEL2_KEYS + 2 * sizeof(uint32_t) * (size_t)nwords;
+  return sizeof(uint64_t) * (size_t)select2_keys(nwords) + 2 * sizeof(uint32_t) * (size_t)nwords;
 }
 
 // Digit step of a radix select: s_hist[0..nb) counts the keys under the
 // current prefix by their digit at bit lo; the digit holding the
-// remaining-th largest key is added to *prefix and *remaining becomes the
-// rank inside it.  Returns true when that digit's keys are all taken (the
-// threshold is then the prefix itself).  All threads call.
+// remaining-th largest key is added to *prefix, *remaining becomes the rank
+// inside it and *bucket (if given) that digit's key count.  Returns true
+// when that digit's keys are all taken (the threshold is then the prefix
+// itself).  All threads call.
 __device__ __forceinline__ bool radix_pick(const uint32_t *s_hist, int nb, int lo, uint64_t *prefix,
-                                           int *remaining, uint64_t *s_state, uint32_t *s_wave) {
+                                           int *remaining, uint64_t *s_state, uint32_t *s_wave,
+                                           uint32_t *bucket = nullptr) {
   const int t = threadIdx.x, nt = blockDim.x;
   const int per = (nb + nt - 1) / nt;
   uint32_t sum = 0;
@@ -1251,7 +1263,7 @@ __device__ __forceinline__ bool radix_pick(const uint32_t *s_hist, int nb, int l
       if (acc + c >= r) {
         s_state[0] = *prefix | ((uint64_t)bin << lo);
         const uint32_t rem = r - acc;
-        s_state[1] = (uint64_t)rem | ((rem == c) ? (1ull << 63) : 0ull);
+        s_state[1] = (uint64_t)rem | ((uint64_t)c << 32) | ((rem == c) ? (1ull << 63) : 0ull);
         break;
       }
       acc += c;
@@ -1262,17 +1274,23 @@ __device__ __forceinline__ bool radix_pick(const uint32_t *s_hist, int nb, int l
   const uint64_t st = s_state[1];
   __syncthreads();
   *remaining = (int)(uint32_t)st;
+  if (bucket) *bucket = (uint32_t)(st >> 32) & 0x7FFFFFFFu;
   return (st >> 63) != 0;
 }
 
 // The key T such that exactly r of the keys get(0..m) that match `prefix`
 // on the bits of `pmask` (the bits above hi) are >= T; 11-bit digits from
-// bit hi down (keys distinct, 1 <= r <= matching keys).  All threads call.
+// bit hi down (keys distinct, 1 <= r <= matching keys).  Once a digit's
+// bucket holds at most one key per thread (and no more than s_hist holds as
+// 64-bit keys), its keys are gathered and ranked pairwise instead of taking
+// further digits.  All threads call.
 template <class F>
 __device__ __forceinline__ uint64_t radix_select_keys(F get, int m, int r, uint64_t prefix, uint64_t pmask,
                                                       int hi, uint32_t *s_hist, uint64_t *s_state,
                                                       uint32_t *s_wave) {
   const int t = threadIdx.x, nt = blockDim.x;
+  constexpr int TIE_CAP = RADIX_BINS / 2;     // 64-bit keys that fit in s_hist
+  __shared__ uint32_t s_ntie;
   int remaining = r;
   for (; hi >= 0; hi -= 11) {
     const int lo = hi >= 10 ? hi - 10 : 0;
@@ -1290,9 +1308,35 @@ __device__ __forceinline__ uint64_t radix_select_keys(F get, int m, int r, uint6
           atomicAdd(&s_hist[(uint32_t)(kv[u] >> lo) & (uint32_t)(nb - 1)], 1u);
     }
     __syncthreads();
-    const bool whole = radix_pick(s_hist, nb, lo, &prefix, &remaining, s_state, s_wave);
+    uint32_t bucket = 0;
+    const bool whole = radix_pick(s_hist, nb, lo, &prefix, &remaining, s_state, s_wave, &bucket);
     pmask |= ((2ull << hi) - 1) & ~((1ull << lo) - 1);
     if (whole || lo == 0) break;
+    if ((int)bucket <= min(nt, TIE_CAP)) {
+      // the bucket's keys into s_hist (as 64-bit keys), then each one's rank
+      uint64_t *s_tie = reinterpret_cast<uint64_t *>(s_hist);
+      if (t == 0) s_ntie = 0;
+      __syncthreads();
+      for (int j0 = 0; j0 < m; j0 += nt * 8) {
+        uint64_t kv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kv[u] = get(min(j0 + u * nt + t, m - 1));
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j0 + u * nt + t < m && (kv[u] & pmask) == prefix) s_tie[atomicAdd(&s_ntie, 1u)] = kv[u];
+      }
+      __syncthreads();
+      if (t < (int)bucket) {
+        const uint64_t k = s_tie[t];
+        uint32_t gt = 0;
+        for (uint32_t i2 = 0; i2 < bucket; ++i2) gt += s_tie[i2] > k ? 1u : 0u;
+        if (gt == (uint32_t)remaining - 1) s_state[0] = k;   // the remaining-th largest
+      }
+      __syncthreads();
+      prefix = s_state[0];
+      __syncthreads();
+      break;
+    }
   }
   return prefix;
 }
@@ -1305,10 +1349,10 @@ __device__ __forceinline__ uint64_t radix_select_keys(F get, int m, int r, uint6
 // `bitmap` (zero at entry, left zero).
 __global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint64_t s_dyn[];
-  uint64_t *s_keys = s_dyn;                                            // [SEL2_KEYS]
-  uint32_t *s_bm = reinterpret_cast<uint32_t *>(s_dyn + SEL2_KEYS);    // [nwords]
+  uint64_t *s_keys = s_dyn;                                            // [lds_keys]
+  uint32_t *s_bm = reinterpret_cast<uint32_t *>(s_dyn + a.lds_keys);  // [nwords]
   uint32_t *s_wpre = s_bm + a.nwords;                                  // [nwords]
-  __shared__ uint32_t s_hist[RADIX_BINS];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[RADIX_BINS];   // also 64-bit keys (radix_select_keys)
   __shared__ uint32_t s_off[SEL2_MAXG + 1];
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
@@ -1363,13 +1407,33 @@ __global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
 
   // ---- the last workgroup: rank the regions' keys ----
   CSA2_TS(10);
-  const uint32_t rc = t < G ? ld_agent(counts + t) : 0u;
-  uint32_t E;
-  const uint32_t roff = block_exclusive_scan(rc, &E, s_wave);
-  if (t < G) { s_off[t] = roff; counts[t] = 0; }
-  if (t == 0) s_off[G] = E;
+  // One batch of requests: every region's key count and, speculatively, its
+  // first SU * tpr entries (tpr threads per region); entries past a count
+  // are dropped, and a longer region's remaining entries are read after.
+  int lg = 0;
+  while ((1 << lg) < G) ++lg;                  // G <= SEL2_MAXG
+  const int tpr = SEL2_THREADS >> lg;          // threads per region
+  const int rg = t / tpr, rl = t - rg * tpr;
+  const int64_t rbase = (int64_t)rg * SEL2_SPAN;
+  const int64_t rlim = rg < G ? min((int64_t)SEL2_SPAN, a.cand_stride - rbase) : 1;   // >= 1: inside the row
+  constexpr int SU = 8;
+  const uint32_t rc = (rg < G && rl == 0) ? ld_agent(counts + rg) : 0u;
+  uint64_t kv[SU];
+#pragma unroll
+  for (int u = 0; u < SU; ++u)
+    kv[u] = rg < G ? ld_agent(keys_g + rbase + min((int64_t)(rl + u * tpr), rlim - 1)) : 0ull;
+  if (rg < G && rl == 0) { s_off[rg] = rc; counts[rg] = 0; }
   for (int j = t; j < a.nwords; j += nt) s_bm[j] = 0;
   __syncthreads();
+  if (t < 64) {                                // region offsets: exclusive prefix of the counts
+    const uint32_t c = t < G ? s_off[t] : 0u;
+    const uint32_t incl = wave_incl_scan(c);
+    if (t < G) s_off[t] = incl - c;
+    if (t == 63) s_off[G] = incl;
+  }
+  __syncthreads();
+  const int cap = a.lds_keys;
+  const uint32_t E = s_off[G];
   // entry j of the concatenated regions
   auto key_at = [&](int j) -> uint64_t {
     int lo = 0, hi = G - 1;                    // largest k with s_off[k] <= j
@@ -1380,15 +1444,14 @@ __global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
     return ld_agent(keys_g + (int64_t)lo * SEL2_SPAN + (j - (int)s_off[lo]));
   };
   const int m = (int)E;
-  const bool in_lds = m <= SEL2_KEYS;
-  if (in_lds && m > 0) {
-    constexpr int U = SEL2_KEYS / SEL2_THREADS;
-    uint64_t kv[U];
+  const bool in_lds = m <= cap;
+  if (in_lds && rg < G) {
+    const uint32_t off = s_off[rg], cnt = s_off[rg + 1] - off;
 #pragma unroll
-    for (int u = 0; u < U; ++u) kv[u] = key_at(min(t + u * nt, m - 1));
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (t + u * nt < m) s_keys[t + u * nt] = kv[u];
+    for (int u = 0; u < SU; ++u)
+      if ((uint32_t)(rl + u * tpr) < cnt) s_keys[off + rl + u * tpr] = kv[u];
+    for (uint32_t j = (uint32_t)(SU * tpr + rl); j < cnt; j += (uint32_t)tpr)
+      s_keys[off + j] = ld_agent(keys_g + rbase + j);
   }
   __syncthreads();
   auto get_lds = [&](int j) -> uint64_t { return s_keys[j]; };
@@ -1519,7 +1582,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   __shared__ float s_qbar[D];
   __shared__ int32_t s_ids[SELECT ? LDS_KEYS : 1];
   __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX : 1];
-  __shared__ uint32_t s_hist[SELECT ? RADIX_BINS : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[SELECT ? RADIX_BINS : 1];
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;

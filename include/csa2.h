@@ -22,7 +22,9 @@
  *   - Pointers marked "device" are HIP device memory owned by the caller;
  *     "host" pointers are read during the call only.  The library never
  *     allocates, frees or synchronises (except csa2_device_error) and keeps
- *     no state besides its loaded kernels and one device flag word.
+ *     no state besides its loaded kernels, one device flag word and a host
+ *     table of the workspace layout each of the last 256 workspaces was
+ *     used with (see csa2_workspace_init).
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *     enqueued on it in order; a call returns once its kernels are queued.
  *   - Host-checkable errors return a non-zero status before anything is
@@ -212,6 +214,11 @@ size_t csa2_workspace_bytes(int32_t batch, int32_t heads, int64_t max_len,
  * csa2_workspace_init — zero-fill a workspace (with a kernel, so it can be
  * recorded in a HIP graph).  A workspace must be zero before its first use;
  * every call leaves its control words zero again when its kernels finish.
+ * Where those words sit depends on the call's bounds (batch, max_len, pool,
+ * topk): when a call's layout differs from the previous call's on the same
+ * workspace, the library first zero-fills the part that holds them (a
+ * kernel on the call's stream, up to the candidate area: about 4 bytes per
+ * block per sequence plus 36 KB per sequence).
  */
 csa2_status csa2_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
@@ -368,8 +375,9 @@ csa2_status csa2_decode_step(const csa2_step *step, void *stream);
  * harnesses that forbid hipMalloc).  The same computation, but step->ws and
  * step->ws_bytes are ignored: the workspace is the library's own array of
  * CSA2_NOALLOC_WORKSPACE_BYTES (16 MiB) per device, held until the process
- * ends and zero-filled by a kernel on `stream` at the first call on each
- * device.  Enough for batch 1 with 64 heads up to about 1.1M positions
+ * ends, zero-filled by a kernel on `stream` at the first call on each
+ * device and re-zeroed like any workspace when the bounds change.  Enough
+ * for batch 1 with 64 heads up to about 1.1M positions
  * (csa2_workspace_bytes gives the need); a larger step returns
  * CSA2_E_WORKSPACE before anything is queued.  The call allocates and frees
  * nothing.  Every call on a device shares that device's array: calls that
