@@ -14,7 +14,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libcsa2.so")
+# CSA2_LIB_PATH: another build of the same library (the tests' host-sanitizer build)
+LIB_PATH = os.environ.get("CSA2_LIB_PATH") or os.path.join(HERE, "libcsa2.so")
 
 FULL, REINDEX, REUSE = 0, 1, 2
 SCORE_SUM, SCORE_HEADMAX = 0, 1     # indexer score rules: heads summed / best head

@@ -209,17 +209,17 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     __builtin_amdgcn_sched_barrier(0);
   };
   CSA2_TS(0);
-  // the tile's 16 query rows (32 KB), 8 float4 per thread: requested first
-  // by the selecting variant, so their latency hides behind the block top-k
+  // the tile's 16 query rows (32 KB), 8 float4 per thread
   constexpr int NV = 16 * D / 4 / ATT_THREADS;
   const float4 *qsrc = reinterpret_cast<const float4 *>(a.q + ((int64_t)b * a.heads + 16 * ht) * D);
   float4 v[NV];
   // Selecting variant: candidates, their scores and the sequence length in
   // one batch, then the block top-k in LDS (the key/id/bin arrays borrow the
-  // row buffer, which is free until the query is staged).
+  // row buffer, which is free until the query is staged).  The query rows
+  // are requested right behind the candidates: the in-order memory counter
+  // lets the top-k start once the candidates are in, and the query's latency
+  // hides behind the selection.
   if constexpr (SELECT) {
-#pragma unroll
-    for (int u = 0; u < NV; ++u) v[u] = qsrc[tid + u * ATT_THREADS];
     constexpr int KPT = SEL_CAND_MAX / ATT_THREADS;
     const int m = a.n_cand;
     const int32_t *cb = a.cand + (int64_t)b * m;
@@ -233,6 +233,8 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
       csc[k] = sb[j];
     }
     const int64_t nsel = clamp_len(a.seq_len[b] + a.len_add, a.limit);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) v[u] = qsrc[tid + u * ATT_THREADS];
     __builtin_amdgcn_sched_barrier(0);
     const int64_t nbs = (nsel + BLOCK - 1) / BLOCK;
     uint64_t *s_keys = reinterpret_cast<uint64_t *>(s_v);     // for the radix fallback only
