@@ -45,6 +45,7 @@ PEAK_VALU_TOPS = 256 * 64 * 2.4e9 / 1e12
 TOKEN_BYTES = 288              # 256 code bytes + 32 scale bytes per position
 BLOCK_BYTES = 8 * TOKEN_BYTES  # 2,304
 PMC_FILE = os.path.join(ROOT, "profiles", "scan_kernel_decoder20-1m_pmc.txt")
+PMC_FILE_FLAT = os.path.join(ROOT, "profiles", "scan_flat_kernel_ragged-b64_pmc.txt")
 SCAN_SOURCES = [os.path.join(ROOT, "fp4_compressed_sparse_amd", "csrc", f)
                 for f in ("index.hip", "common.hpp")]
 QUANT_PMC_FILE = os.path.join(ROOT, "profiles", "quantize_rows_kernel_prefill-write-1m_pmc.txt")
@@ -709,12 +710,13 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "scan_kernel (first Full layer full-range scan)",
+            # a batch scans its sequences' chunks laid end to end (scan_flat_kernel)
+            "kernel": ("scan_flat_kernel" if 1 < B <= 512 else "scan_kernel") + " (first Full layer full-range scan)",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": pmc_traffic(),
+            "traffic": pmc_traffic(PMC_FILE_FLAT if 1 < B <= 512 else PMC_FILE),
             "algorithmic_bytes_per_launch": scan_bytes,
             "avg_launch_us": round(scan_avg_s * 1e6, 2),
         },
