@@ -417,7 +417,11 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   if (splits == 1) return CSA2_OK;
   CombineArgs ca;
   ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.splits = splits; ca.heads = heads; ca.out = out;
-  if (splits <= 32)
+  // up to 8 splits (batches): one wave per output tile merges them all;
+  // more: four waves of 8 or 16 splits each (one wave idles less than four)
+  if (splits <= 8)
+    attend_combine_regs_kernel<1, 8><<<dim3((heads / 16) * 32, B), 64, 0, s>>>(ca);
+  else if (splits <= 32)
     attend_combine_regs_kernel<4, 8><<<dim3((heads / 16) * 32, B), 256, 0, s>>>(ca);
   else if (splits <= 64)
     attend_combine_regs_kernel<4, 16><<<dim3((heads / 16) * 32, B), 256, 0, s>>>(ca);

@@ -960,6 +960,7 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_regs_kernel(CombineArg
   CSA2_TS(10);
 }
 
+template __global__ void attend_combine_regs_kernel<1, 8>(CombineArgs);
 template __global__ void attend_combine_regs_kernel<4, 8>(CombineArgs);
 template __global__ void attend_combine_regs_kernel<4, 16>(CombineArgs);
 template __global__ void attend_combine_kernel<2>(CombineArgs);

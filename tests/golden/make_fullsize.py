@@ -26,12 +26,15 @@ Outputs (in this directory):
         idx         int32 [3, 64, 128]
         scan_sha    per sequence: sha256 of its full-scan float32 scores
         pool_sha    per sequence: sha256 of the Reindex layer's pool scores
+  fullsize_decoder20_1m_headmax.npz   the same step with the per-head score
+      rule (score = the best head's pinned-order score): the same fields,
+      the scores being per-head ones
   prefill_write_1m.json       the prefill write (1,048,576 rows of workload
       4, cache stream 9): sha256 of the oracle's codes bytes then scales
       bytes of every 65,536-row chunk.
 
 Run from the repository root (takes several minutes on 8 cores):
-    python tests/golden/make_fullsize.py [decoder20|ragged|prefill|all]
+    python tests/golden/make_fullsize.py [decoder20|decoder20-headmax|ragged|prefill|all]
 """
 import hashlib
 import json
@@ -47,7 +50,8 @@ ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
 import workloads as W  # noqa: E402
-from oracle.indexer import block_keys, block_scores_from_keys, collapse_query  # noqa: E402
+from oracle.indexer import (SCORE_HEADMAX, SCORE_SUM, block_keys, block_scores_from_keys,  # noqa: E402
+                            collapse_query, headmax_scores_from_keys)
 from oracle.quantize import quantize_rows  # noqa: E402
 from oracle.step import Cache, decode_step  # noqa: E402
 
@@ -84,7 +88,14 @@ def fill_cache(wid, cache_id, lengths, capacity):
     return oc
 
 
-def decoder20():
+def _scores(q, keys, score):
+    """The indexer's scores of `keys` for the query heads q [H, 512] under the rule."""
+    if score == SCORE_HEADMAX:
+        return headmax_scores_from_keys(q, keys)
+    return block_scores_from_keys(collapse_query(q), keys)
+
+
+def decoder20(score=SCORE_SUM):
     w = W.WORKLOADS[3]
     n0 = int(w.context)
     cap = (n0 + 1 + 7) // 8 * 8
@@ -98,21 +109,22 @@ def decoder20():
     qs = [W.queries(w.wid, l, 0, 1, H) for l in range(L)]
     rows = np.stack([W.append_rows(w.wid, c, 0, 1) for c in range(w.n_caches)])
     layers = [(m, lc[l], qs[l]) for l, m in enumerate(w.pattern)]
-    res = decode_step(caches, layers, rows, w.topk, w.pool, w.scale)
+    res = decode_step(caches, layers, rows, w.topk, w.pool, w.scale, score=score)
     log(f"decoder20: decode step done ({time.perf_counter() - t0:.0f} s)")
     n = n0 + 1
     pool = res["pool"][0]
     keys = {}
     for c in sorted(set(lc)):
         keys[c] = block_keys(caches[c].codes[0], caches[c].scales[0], n)
-    scan = block_scores_from_keys(collapse_query(qs[0][0]), keys[lc[0]])
+    scan = _scores(qs[0][0], keys[lc[0]], score)
     pool_sha = []
     for l, m in enumerate(w.pattern):
         if l == 0 or m == 2:
             pool_sha.append("")
             continue
-        pool_sha.append(sha(block_scores_from_keys(collapse_query(qs[l][0]), keys[lc[l]][pool])))
-    np.savez_compressed(os.path.join(HERE, "fullsize_decoder20_1m.npz"),
+        pool_sha.append(sha(_scores(qs[l][0], keys[lc[l]][pool], score)))
+    name = "fullsize_decoder20_1m_headmax.npz" if score == SCORE_HEADMAX else "fullsize_decoder20_1m.npz"
+    np.savez_compressed(os.path.join(HERE, name),
                         pool=pool.astype(np.int32), idx=np.stack([i[0] for i in res["idx"]]).astype(np.int32),
                         scan_sha=np.array(sha(scan)), pool_sha=np.array(pool_sha))
     log(f"decoder20: written ({time.perf_counter() - t0:.0f} s)")
@@ -170,5 +182,7 @@ if __name__ == "__main__":
         prefill()
     if what in ("decoder20", "all"):
         decoder20()
+    if what in ("decoder20-headmax", "all"):
+        decoder20(SCORE_HEADMAX)
     if what in ("ragged", "all"):
         ragged()

@@ -190,6 +190,73 @@ def test_decoder20_1m_full_size():
     _CHUNKS.clear()
 
 
+def test_decoder20_1m_full_size_per_head_rule():
+    """The 20-layer step at 1,048,576 positions with the per-head score rule,
+    in bench.py's launch configuration: the pool and all 20 selections
+    byte-equal to the oracle's, the full scan's per-head scores and every
+    pool layer's scores bit-equal (sha256), and two layers' attention
+    against the oracle."""
+    require_gpu()
+    _CHUNKS.clear()
+    w = W.WORKLOADS[3]
+    n0 = int(w.context)
+    n = n0 + 1
+    cap = (n + 7) // 8 * 8
+    log(f"building 4 caches of {n0} positions (per-head rule)")
+    caches = bench.build_caches(w, np.array([n0]), cap, log_every=1000)
+    for c in caches:
+        c.max_len = n
+    L, H, K, P = len(w.pattern), w.heads, w.topk, w.pool
+    lc = w.layer_caches()
+    qs = [W.queries(w.wid, l, 0, 1, H) for l in range(L)]
+    step_rows = np.stack([W.append_rows(w.wid, c, 0, 1) for c in range(w.n_caches)])
+    qt = [torch.from_numpy(q).cuda() for q in qs]
+    outs = [torch.zeros((1, H, 512), dtype=torch.float32, device="cuda") for _ in range(L)]
+    idxs = []
+    for m in w.pattern:
+        idxs.append(idxs[-1] if m == 2 else torch.full((1, K), -9, dtype=torch.int32, device="cuda"))
+    pool = torch.full((1, P), -9, dtype=torch.int32, device="cuda")
+    ws = csa2.workspace(1, H, n, P, K)
+    layers = [(m, lc[l], qt[l], outs[l], idxs[l]) for l, m in enumerate(w.pattern)]
+    csa2.decode_step(caches, layers, H, K, P, w.scale, ws, pool_out=pool,
+                     new_rows=torch.from_numpy(step_rows).cuda(), score=csa2.SCORE_HEADMAX)
+    torch.cuda.synchronize()
+    assert csa2.device_error() == 0
+    gold = _golden("fullsize_decoder20_1m_headmax.npz")
+    nblk = (n + BLOCK - 1) // BLOCK
+    p = pool.cpu().numpy()[0]
+    assert np.array_equal(p, gold["pool"]), "pool differs from the oracle's"
+    for l in range(L):
+        assert np.array_equal(idxs[l].cpu().numpy()[0], gold["idx"][l]), f"layer {l}: selection differs"
+    log(f"per-head rule: pool and all {L} selections byte-equal to the oracle's")
+    s0 = torch.zeros((1, nblk), dtype=torch.float32, device="cuda")
+    csa2.block_scores(caches[lc[0]], qt[0], s0, score=csa2.SCORE_HEADMAX)
+    s0 = s0.cpu().numpy()[0]
+    assert _sha(s0) == str(gold["scan_sha"]), "per-head full-scan scores differ from the oracle's"
+    pool_t = pool.clone()
+    for l, m in enumerate(w.pattern):
+        if l == 0 or m == 2:
+            continue
+        sl = torch.zeros((1, P), dtype=torch.float32, device="cuda")
+        csa2.block_scores(caches[lc[l]], qt[l], sl, cand=pool_t, score=csa2.SCORE_HEADMAX)
+        assert _sha(sl.cpu().numpy()[0]) == str(gold["pool_sha"][l]), f"layer {l}: pool scores differ"
+    log(f"per-head rule: all {nblk} scan scores and every layer's pool scores bit-equal")
+    for l in (1, L - 1):
+        idx = idxs[l].cpu().numpy()[0]
+        pos = gather_positions(idx, n)
+        codes, scales = quantize_rows(_rows(w.wid, lc[l], pos, n0, step_rows[:, 0]))
+        kept = idx[idx >= 0]
+        ccodes = np.zeros((BLOCK * kept.size, 256), dtype=np.uint8)
+        cscales = np.zeros((BLOCK * kept.size, 32), dtype=np.uint8)
+        ccodes[:pos.size] = codes
+        cscales[:pos.size] = scales
+        ref = sparse_attend(ccodes, cscales, pos.size, qs[l][0], np.arange(kept.size), w.scale)
+        err = normwise_err(outs[l].cpu().numpy()[0][None], ref[None])
+        log(f"layer {l}: attention error {err:.2e} over {pos.size} positions")
+        assert err <= ATT_TOL, (l, err)
+    _CHUNKS.clear()
+
+
 def test_decoder20_1m_full_size_with_local_branch():
     """The same 20-layer step at 1,048,576 positions with a 128-position FP8
     window on every layer (ring bytes from the oracle's quantiser): the
