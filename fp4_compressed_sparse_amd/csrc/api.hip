@@ -290,18 +290,21 @@ csa2_status run_scan_select(const csa2_kv *kv, const float *q, int32_t heads, in
     qbar_kernel<<<B, SCAN_THREADS, 0, s>>>(q, heads, at<float>(ws, L.qbar));
     if (csa2_status st = launched("qbar")) return st;
   }
-  // a workgroup scores 8 blocks per round (4 waves x 2); 1,536 workgroups
-  // fill the 256 compute units at 6 waves per SIMD.  A batch runs over its
-  // chunks laid end to end (scan_flat_kernel, 1,280 workgroups: 5 per
-  // compute unit, all resident), so ragged lengths leave no slot idle (batch
-  // of 64, 32K-128K: 382 -> 288 us, measured).  Beyond its limits a batch
-  // gets 128 workgroups per sequence, which the dispatcher moves from short
+  // a workgroup scores 8 blocks per round (4 waves x 2).  512 workgroups
+  // (two per compute unit) stream the cache faster than more: at 1M, cold,
+  // 56.6 us against 61.8 with 1,536 (six waves per SIMD) and 60.2 with
+  // 1,024; 384 or 256 leave compute units idle (62.7, 77.8 us).  A batch
+  // runs over its chunks laid end to end (scan_flat_kernel, 768 workgroups:
+  // 279 us at batch 64 against 285 with 1,280 and 301 with 512), so ragged
+  // lengths leave no slot idle (batch of 64, 32K-128K: 382 -> 288 us
+  // against a per-sequence split).  Beyond its limits a batch gets 128
+  // workgroups per sequence, which the dispatcher moves from short
   // sequences to long ones as they finish.
   const int64_t rounds = ceil_div(nblk_grid > 0 ? nblk_grid : 1, 8);
-  dim3 g1(grid_for(rounds, B, B > 1 ? 128 * B : 1536), B);
+  dim3 g1(grid_for(rounds, B, B > 1 ? 128 * B : 512), B);
   if (t_scan_before) (void)hipEventRecord(t_scan_before, s);
   if (B > 1 && B <= SCAN_FLAT_MAXB && (int64_t)B * ((nblk_grid + 1) / 2) < ((int64_t)1 << 31))
-    scan_flat_kernel<<<1280, SCAN_THREADS, 0, s>>>(sa, B);
+    scan_flat_kernel<<<768, SCAN_THREADS, 0, s>>>(sa, B);
   else
     scan_kernel<true><<<g1, SCAN_THREADS, 0, s>>>(sa);
   if (csa2_status st = launched("scan")) return st;

@@ -355,8 +355,10 @@ __global__ void __launch_bounds__(SCAN_THREADS) qbar_kernel(const float *__restr
 
 // ---- full scan ----------------------------------------------------------
 
-// 80 registers: six waves per SIMD (24 per compute unit) keep the stream
-// of row requests going while other waves score.
+// 80 registers (room for six waves per SIMD).  The host launches two
+// workgroups per compute unit, which streamed the rows faster than six
+// waves per SIMD; a second block of prefetched rows per wave (114
+// registers) did not help either (57.9 against 56.6 us at 1M, cold).
 template <bool HIST>
 __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(6))) scan_kernel(ScanArgs a) {
   __shared__ float s_qbar[D];
