@@ -150,9 +150,17 @@ __global__ void __launch_bounds__(64 * NW) headmax_kernel(HeadmaxArgs a) {
   constexpr int NG = C / 16;           // scale groups per wave
   constexpr int NTHR = 64 * NW;
   constexpr int KPASS = NTHR / 32;     // blocks whose keys one pass builds
-  static_assert(C % 64 == 0 && (NG & (NG - 1)) == 0 && NT % 4 == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) float s_key[NT][D];
-  __shared__ float s_part[NW][NT][64];
+  constexpr int NPASS = (NT + KPASS - 1) / KPASS;
+  constexpr int QR = 32;               // query channels per staging round and wave
+  constexpr int QPAD = 65;             // heads per staged row (one more: stores spread over the banks)
+  static_assert(C % 64 == 0 && (NG & (NG - 1)) == 0 && NT % 4 == 0 && C % QR == 0, "tile shape");
+  // The tile arrays (keys, partial scores) and the query staging area share
+  // one LDS buffer: the query is staged once, before the first tile.
+  constexpr int TILE_FLOATS = NT * D + NW * NT * 64;
+  constexpr int STAGE_FLOATS = NW * (QR / 4) * QPAD * 4;
+  __shared__ __attribute__((aligned(16))) float s_buf[TILE_FLOATS > STAGE_FLOATS ? TILE_FLOATS : STAGE_FLOATS];
+  float (*s_key)[D] = reinterpret_cast<float (*)[D]>(s_buf);
+  float (*s_part)[NT][64] = reinterpret_cast<float (*)[NT][64]>(s_buf + NT * D);
   __shared__ uint32_t s_hist[HIST ? HIST_BINS : 1];
   const int b = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63;
@@ -174,48 +182,92 @@ __global__ void __launch_bounds__(64 * NW) headmax_kernel(HeadmaxArgs a) {
   const int32_t *cand = CAND ? a.cand + (int64_t)b * a.n_cand : nullptr;
   float *scores = a.scores + (int64_t)b * a.score_stride;
 
-  // this lane's query values: head h, channels w*C .. w*C + C - 1 (zeros for
-  // a lane past the last head; its scores are dropped at the max)
+  // Rows of a tile's blocks: pass p, thread t holds the rows of block
+  // p * KPASS + t / 32 (an item without a block reads block 0, which always
+  // exists; its score is never written).
+  const int j32 = t & 31;
+  auto block_of = [&](int64_t tile, int bl) -> int64_t {
+    const int64_t item = tile * NT + bl;
+    if (CAND) return item < a.n_cand ? (int64_t)cand[item] : -1;
+    return item;
+  };
+  BlockRows32 rows[NPASS];
+  auto load_tile = [&](int64_t tile) {
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int bl = p * KPASS + (t >> 5);
+      if (bl < NT) {
+        const int64_t blk = block_of(tile, bl);
+        const int64_t lb = (blk >= 0 && blk < cap_blocks) ? blk : 0;
+        load_block32(rows[p], codes + lb * BLOCK * CODE_BYTES, scales + lb * BLOCK * SCALE_BYTES, j32);
+      }
+    }
+  };
+  int64_t tile = blockIdx.x;
+  if (tile < ntiles) load_tile(tile);     // the first tile's rows overlap the query staging
+
+  // This lane's query values: head h, channels w*C .. w*C + C - 1 (zeros for
+  // a lane past the last head; its scores are dropped at the max).  Staged
+  // through LDS in rounds of QR channels: a load instruction reads 8 heads'
+  // QR-channel runs (8 lanes x 16 bytes each, so a few cache lines per
+  // instruction instead of one per lane), stored as [channel quad][head], and
+  // each lane then reads its head's QR channels back.
   float qv[C];
   {
-    const bool hv = h < H;
-    const f32x4 *qp = reinterpret_cast<const f32x4 *>(a.q + ((int64_t)b * H + (hv ? h : 0)) * D + w * C);
+    float *sq = s_buf + w * (QR / 4) * QPAD * 4;
+    const int cq = lane & 7, hl0 = lane >> 3;
     bool fin = true;
+    f32x4 v[C / QR][8];                   // every round's loads in one batch
 #pragma unroll
-    for (int i = 0; i < C / 4; ++i) {
-      f32x4 v = qp[i];
-      if (!hv) v = f32x4{0.f, 0.f, 0.f, 0.f};
-      fin = fin && __builtin_isfinite(v[0]) && __builtin_isfinite(v[1]) && __builtin_isfinite(v[2]) &&
-            __builtin_isfinite(v[3]);
-      qv[4 * i] = v[0]; qv[4 * i + 1] = v[1]; qv[4 * i + 2] = v[2]; qv[4 * i + 3] = v[3];
+    for (int r = 0; r < C / QR; ++r) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int hl = hl0 + 8 * i;
+        v[r][i] = *reinterpret_cast<const f32x4 *>(a.q + ((int64_t)b * H + min(hl, H - 1)) * D + w * C + r * QR +
+                                                   4 * cq);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < C / QR; ++r) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int hl = hl0 + 8 * i;
+        if (hl >= H) v[r][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4 *>(sq + (cq * QPAD + hl) * 4) = v[r][i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < QR / 4; ++k) {
+        const f32x4 u = *reinterpret_cast<const f32x4 *>(sq + (k * QPAD + h) * 4);
+        fin = fin && __builtin_isfinite(u[0]) && __builtin_isfinite(u[1]) && __builtin_isfinite(u[2]) &&
+              __builtin_isfinite(u[3]);
+        qv[r * QR + 4 * k] = u[0]; qv[r * QR + 4 * k + 1] = u[1];
+        qv[r * QR + 4 * k + 2] = u[2]; qv[r * QR + 4 * k + 3] = u[3];
+      }
+      __syncthreads();                    // the area is refilled next round, then holds the tiles
     }
     if (__builtin_amdgcn_ballot_w64(!fin) && lane == 0) raise_flag(FLAG_NONFINITE_Q);
   }
 
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  for (; tile < ntiles; tile += gridDim.x) {
     const int64_t base = tile * NT;
-    // 1. keys of the tile's blocks (an item without a block reads block 0,
-    //    which always exists; its score is never written)
+    // 1. keys of the tile's blocks into LDS, then the next tile's rows are
+    //    requested (in flight during phases 2 and 3)
 #pragma unroll
-    for (int p = 0; p < NT; p += KPASS) {
-      const int bl = p + (t >> 5), j = t & 31;
+    for (int p = 0; p < NPASS; ++p) {
+      const int bl = p * KPASS + (t >> 5);
       if (bl < NT) {
-        const int64_t item = base + bl;
-        int64_t blk;
-        if (CAND) blk = item < a.n_cand ? (int64_t)cand[item] : -1;
-        else blk = item;
+        const int64_t blk = block_of(tile, bl);
         const bool ok = blk >= 0 && blk < nblk;
-        const int64_t lb = (blk >= 0 && blk < cap_blocks) ? blk : 0;
-        BlockRows32 r;
-        load_block32(r, codes + lb * BLOCK * CODE_BYTES, scales + lb * BLOCK * SCALE_BYTES, j);
         const int cnt = ok ? (int)min((int64_t)BLOCK, n - blk * BLOCK) : BLOCK;
         float key[16];
-        block_key32(r, cnt, key);
-        f32x4 *dst = reinterpret_cast<f32x4 *>(&s_key[bl][16 * j]);
+        block_key32(rows[p], cnt, key);
+        f32x4 *dst = reinterpret_cast<f32x4 *>(&s_key[bl][16 * j32]);
 #pragma unroll
         for (int k = 0; k < 4; ++k) dst[k] = f32x4{key[4 * k], key[4 * k + 1], key[4 * k + 2], key[4 * k + 3]};
       }
     }
+    if (tile + gridDim.x < ntiles) load_tile(tile + gridDim.x);
     __syncthreads();
     // 2. per-head subtree of this wave's groups, bpw blocks per step
     for (int st = 0; st < NT / bpw; ++st) {
