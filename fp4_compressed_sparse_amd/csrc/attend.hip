@@ -121,7 +121,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   __shared__ __attribute__((aligned(16))) _Float16 s_p[16 * P_STRIDE];   // P: [16 heads][64 positions]
   __shared__ float s_max[4][16], s_sum[4][16];
   __shared__ uint8_t s_ok[ATT_SP];
-  __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX : 1];   // in-kernel selection
+  __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX + SEL_PAD : 1];   // in-kernel selection
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
 
@@ -239,6 +239,9 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     const int64_t nbs = (nsel + BLOCK - 1) / BLOCK;
     uint64_t *s_keys = reinterpret_cast<uint64_t *>(s_v);     // for the radix fallback only
     uint32_t *s_hist = reinterpret_cast<uint32_t *>(s_keys + SEL_CAND_MAX);
+    static_assert(SEL_CAND_MAX * sizeof(uint64_t) + TOPK_HIST_BINS * sizeof(uint32_t) <=
+                      (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16),
+                  "the selection's keys and bins fit in the row buffer");
     uint64_t kr[KPT];
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
@@ -248,7 +251,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
       if (j < m) s_keys[j] = kr[k];
     }
     int32_t *io = blockIdx.x == 0 ? a.idx_out + (int64_t)b * a.topk : nullptr;
-    select_top_regs<KPT>(kr, cid, s_keys, m, a.topk, io, s_sel, a.topk, s_hist, s_state, s_wave);
+    select_top_regs<KPT>(kr, csc, cid, s_keys, m, a.topk, io, s_sel, a.topk, s_hist, s_state, s_wave);
   }
   // request order: the first stage's block ids, the query tile, then (once
   // the ids are in) the rows, so the query and id latencies overlap

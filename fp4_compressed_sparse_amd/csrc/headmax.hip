@@ -333,8 +333,8 @@ __global__ void __launch_bounds__(64 * NW) headmax_kernel(HeadmaxArgs a) {
 __global__ void __launch_bounds__(SCAN_THREADS) select_cand_kernel(RescoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint64_t s_keys[];
   __shared__ int32_t s_ids[LDS_KEYS];
-  __shared__ int32_t s_sel[CSA2_TOPK_MAX];
-  __shared__ __attribute__((aligned(16))) uint32_t s_hist[RADIX_BINS];   // also 64-bit keys (radix_select_keys)
+  __shared__ int32_t s_sel[CSA2_TOPK_MAX + SEL_PAD];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[TOPK_HIST_BINS];
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;

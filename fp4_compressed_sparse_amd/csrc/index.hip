@@ -838,28 +838,23 @@ __device__ __forceinline__ uint64_t topk_threshold(const uint64_t (&kr)[KPT], co
   return s_state[0];
 }
 
-// Register form of the block top-k (256 threads): wave w holds list
-// entries 64*KPT*w + 64k + lane, k < KPT (a contiguous quarter of the list;
-// keys kr, 0 = empty, and their ids); s_keys is the same list in LDS, read
-// only by the radix fallback.  Ordered compaction: each wave counts its
-// chosen entries by ballots, the four totals give every wave its output
-// offset, and inside a wave the entries follow in list order.
+constexpr int SEL_PAD = 64;          // s_sel slots past len: unchosen lanes' stores land there
+constexpr int TOPK_HIST_BINS = RADIX_BINS + 64;   // block top-k bins; the last 64 take empty entries
+
+// Ordered compaction of the keys >= T (nonzero; none when reff <= 0): the
+// four wave totals are exchanged through LDS, then each wave's chosen
+// entries follow in list order.  Ids to s_sel[0..len) (-1 padded) and,
+// unless out is NULL, to out.
 template <int KPT>
-__device__ __forceinline__ void select_top_regs(const uint64_t (&kr)[KPT], const int32_t (&ids)[KPT],
-                                                const uint64_t *s_keys, int m, int r, int32_t *out,
-                                                int32_t *s_sel, int len, uint32_t *s_hist,
-                                                uint64_t *s_state, uint32_t *s_wave) {
-  __shared__ uint32_t s_wtot[4];
+__device__ __forceinline__ void compact_ge(const uint64_t (&kr)[KPT], const int32_t (&ids)[KPT], uint64_t T,
+                                           int reff, int32_t *out, int32_t *s_sel, int len, uint32_t *s_wtot) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  int reff = 0;
-  const uint64_t T = topk_threshold<KPT>(kr, s_keys, m, r, &reff, s_hist, s_state, s_wave);
   uint32_t wtot = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k)
     wtot += (uint32_t)__popcll(__ballot(reff > 0 && kr[k] != 0 && kr[k] >= T));
   if (lane == 0) s_wtot[wv] = wtot;
   __syncthreads();
-  CSA2_TOPK_TS(6);
   uint32_t base = 0, total = 0;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -871,42 +866,208 @@ __device__ __forceinline__ void select_top_regs(const uint64_t (&kr)[KPT], const
   for (int k = 0; k < KPT; ++k) {
     const bool f = reff > 0 && kr[k] != 0 && kr[k] >= T;
     const uint64_t mask = __ballot(f);
-    if (f) {
-      const uint32_t pos = base + lanes_below(mask);
-      if (pos < (uint32_t)len) {
-        s_sel[pos] = ids[k];
-        if (out) out[pos] = ids[k];
-      }
-    }
+    const uint32_t pos = base + lanes_below(mask);
+    s_sel[(f && pos < (uint32_t)len) ? pos : len + lane] = ids[k];
     base += (uint32_t)__popcll(mask);
   }
-  for (int j = (int)total + t; j < len; j += 256) {
-    s_sel[j] = -1;
-    if (out) out[j] = -1;
+  for (int j = (int)total + t; j < len; j += 256) s_sel[j] = -1;
+  __syncthreads();
+  if (out)
+    for (int j = t; j < len; j += 256) out[j] = s_sel[j];
+}
+
+// Register form of the block top-k (256 threads): wave w holds list
+// entries 64*KPT*w + 64k + lane, k < KPT (a contiguous quarter of the list:
+// keys kr, 0 = empty, their float scores sc and ids); s_keys is the same
+// list in LDS, read only by the radix fallback.  The chosen entries' ids,
+// in list order, go to s_sel[0..len) (-1 padded; s_sel holds len + SEL_PAD
+// entries) and, unless out is NULL, to out.  s_hist holds TOPK_HIST_BINS
+// counters.
+//
+// One pass of RADIX_BINS linear bins over the scores' range [lo, hi]
+// (monotone in the score, equal scores share a bin; empty entries count in
+// the extra bins).  Every wave then finds the bin holding the r-th largest
+// key on its own (lane sums of 32 bins, a wave scan, then the found lane's
+// 32 bins), so no exchange is needed for it.  The bin's members, a handful,
+// are ranked pairwise; each chosen member counts itself for its wave and
+// each wave counts its keys above the bin, so every wave knows its output
+// offset when the threshold is published and the ordered compaction
+// follows without another exchange (five workgroup barriers in all).  A
+// NaN or infinite score, a degenerate range or a crowded bin falls back to
+// the radix select above.
+template <int KPT>
+__device__ __forceinline__ void select_top_regs(const uint64_t (&kr)[KPT], const float (&sc)[KPT],
+                                                const int32_t (&ids)[KPT], const uint64_t *s_keys, int m, int r,
+                                                int32_t *out, int32_t *s_sel, int len, uint32_t *s_hist,
+                                                uint64_t *s_state, uint32_t *s_wave) {
+  __shared__ uint32_t s_red[12];
+  __shared__ uint32_t s_cnt[12];     // [w]: keys above the threshold bin; [4 + w]: chosen members; [8]: member slots
+  __shared__ __attribute__((aligned(16))) uint64_t s_tie[TIE_MAX];
+  __shared__ uint8_t s_tiew[TIE_MAX];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  // ---- valid count and the range of the keys' score halves
+  uint32_t hmax = 0u, hmin1 = 0xFFFFFFFFu, cnt = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const uint32_t h = (uint32_t)(kr[k] >> 32);
+    hmax = max(hmax, h);
+    hmin1 = min(hmin1, h - 1u);                    // an empty entry (0) wraps to the top
+    cnt += (uint32_t)__popcll(__ballot(kr[k] != 0));
+  }
+#pragma unroll
+  for (int k = 0; k < RADIX_BINS / 256; ++k) s_hist[t + 256 * k] = 0;
+  if (t < TOPK_HIST_BINS - RADIX_BINS) s_hist[RADIX_BINS + t] = 0;
+  if (t < 9) s_cnt[t] = 0;
+  hmax = wave_umax(hmax);
+  hmin1 = wave_umin(hmin1);
+  if (lane == 0) { s_red[wv] = cnt; s_red[4 + wv] = hmin1; s_red[8 + wv] = hmax; }
+  __syncthreads();
+  CSA2_TOPK_TS(1);
+  const uint32_t nvalid = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  const uint32_t umin = min(min(s_red[4], s_red[5]), min(s_red[6], s_red[7])) + 1u;
+  const uint32_t umax = max(max(s_red[8], s_red[9]), max(s_red[10], s_red[11]));
+  r = min(r, (int)nvalid);
+  if (r <= 0 || r == (int)nvalid) {                // none, or every valid key
+    compact_ge<KPT>(kr, ids, r <= 0 ? ~0ull : 0ull, r, out, s_sel, len, s_wave);
+    return;
+  }
+  // finite scores only: a NaN's or an infinity's key lies at or beyond
+  // key(-inf) = 0x007FFFFF and key(+inf) = 0xFF800000
+  const float lo = unord_key(umin), hi = unord_key(umax);
+  const float inv = (float)RADIX_BINS * __builtin_amdgcn_rcpf(hi - lo);   // any positive scale keeps bins monotone
+  if (umin >= umax || umin <= 0x007FFFFFu || umax >= 0xFF800000u || !(inv < __builtin_huge_valf()) ||
+      !(inv > 0.f)) {
+    const uint64_t T = radix_threshold(s_keys, m, r, 63, s_hist, s_state, s_wave);
+    compact_ge<KPT>(kr, ids, T, r, out, s_sel, len, s_wave);
+    return;
+  }
+  uint32_t bin[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int bf = min(RADIX_BINS - 1, (int)((sc[k] - lo) * inv));
+    bin[k] = kr[k] != 0 ? (uint32_t)bf : (uint32_t)(RADIX_BINS + lane);   // empty: a lane's own spare bin
+    atomicAdd(&s_hist[bin[k]], 1u);
   }
   __syncthreads();
+  CSA2_TOPK_TS(2);
+  // ---- the bin holding the r-th largest key, found by every wave alone:
+  // lane l sums bins [2016 - 32 l, 2047 - 32 l] (read in a rotated order,
+  // so eight neighbouring lanes cover all banks), a wave scan finds the
+  // lane, and lanes 0..31 scan that lane's bins
+  uint32_t bstar, rem, cbin;
+  bool ok;
+  {
+    const uint32_t *hb = s_hist + (RADIX_BINS - 32 - 32 * lane);
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(hb + 4 * ((i + lane) & 7));
+      sum += v.x + v.y + v.z + v.w;
+    }
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint64_t fm = __ballot(incl - sum < (uint32_t)r && (uint32_t)r <= incl);
+    const int L = fm ? __builtin_ctzll(fm) : 0;
+    const uint32_t aboveL = __builtin_amdgcn_readlane(incl - sum, L);
+    const uint32_t cc = lane < 32 ? s_hist[RADIX_BINS - 1 - 32 * L - lane] : 0u;
+    const uint32_t ic = wave_incl_scan(cc);
+    const uint64_t bm = __ballot(lane < 32 && aboveL + ic - cc < (uint32_t)r && (uint32_t)r <= aboveL + ic);
+    ok = fm != 0 && bm != 0;
+    const int B = bm ? __builtin_ctzll(bm) : 0;
+    bstar = (uint32_t)(RADIX_BINS - 1 - 32 * L - B);
+    rem = (uint32_t)r - aboveL - __builtin_amdgcn_readlane(ic - cc, B);   // keys still needed from the bin
+    cbin = __builtin_amdgcn_readlane(cc, B);                                // keys in the bin
+  }
+  CSA2_TOPK_TS(3);
+  if (!ok || cbin > (uint32_t)TIE_MAX) {           // uniform: every wave read the same bins
+    const uint64_t T = radix_threshold(s_keys, m, r, 63, s_hist, s_state, s_wave);
+    compact_ge<KPT>(kr, ids, T, r, out, s_sel, len, s_wave);
+    return;
+  }
+  // ---- the bin's members into LDS; each wave's count of keys above the bin
+  uint32_t above_w = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    above_w += (uint32_t)__popcll(__ballot(bin[k] - bstar - 1u < (uint32_t)RADIX_BINS - 1u - bstar));
+    if (bin[k] == bstar) {
+      const uint32_t slot = atomicAdd(&s_cnt[8], 1u);
+      s_tie[slot] = kr[k];
+      s_tiew[slot] = (uint8_t)wv;
+    }
+  }
+  if (lane == 0) s_cnt[wv] = above_w;
+  __syncthreads();
+  CSA2_TOPK_TS(4);
+  // ---- rank the members pairwise: the rem-th largest is the threshold T;
+  // a member is chosen when fewer than rem members beat it (that is, when
+  // it is >= T), and counts itself for its wave
+  if (t < (int)cbin) {
+    const uint64_t k = s_tie[t];
+    uint32_t gt = 0, ge = 0;
+    uint32_t i2 = 0;
+    for (; i2 + 2 <= cbin; i2 += 2) {             // two members per 16-byte read
+      const uint64_t o0 = s_tie[i2], o1 = s_tie[i2 + 1];
+      gt += (o0 > k ? 1u : 0u) + (o1 > k ? 1u : 0u);
+      ge += (o0 >= k ? 1u : 0u) + (o1 >= k ? 1u : 0u);
+    }
+    if (i2 < cbin) {
+      const uint64_t o = s_tie[i2];
+      gt += o > k ? 1u : 0u;
+      ge += o >= k ? 1u : 0u;
+    }
+    if (gt < rem) {
+      atomicAdd(&s_cnt[4 + s_tiew[t]], 1u);
+      if (rem <= ge) s_state[0] = k;
+    }
+  }
+  __syncthreads();
+  CSA2_TOPK_TS(5);
+  const uint64_t T = s_state[0];
+  // ---- ordered compaction at the offsets the counts give
+  uint32_t base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t v = s_cnt[w] + s_cnt[4 + w];
+    base += w < wv ? v : 0u;
+    total += v;
+  }
+  CSA2_TOPK_TS(6);
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const bool f = kr[k] >= T;                     // T is a real key, so f implies nonzero
+    const uint64_t mask = __ballot(f);
+    const uint32_t pos = base + lanes_below(mask);
+    s_sel[(f && pos < (uint32_t)len) ? pos : len + lane] = ids[k];
+    base += (uint32_t)__popcll(mask);
+  }
+  for (int j = (int)total + t; j < len; j += 256) s_sel[j] = -1;
+  __syncthreads();
   CSA2_TOPK_TS(7);
+  if (out)
+    for (int j = t; j < len; j += 256) out[j] = s_sel[j];
 }
 
 // Top r of the list s_keys[0..m) (LDS, 0 = empty entry, m <= 256 * KPT):
-// the chosen entries' s_ids, in list order, go to s_sel (LDS) and, unless
-// out is NULL, to out[0..len), -1 padded.  All 256 threads; wave w takes the
-// contiguous quarter of the list select_top_regs expects.
+// the chosen entries' s_ids, in list order, go to s_sel (LDS, len +
+// SEL_PAD entries) and, unless out is NULL, to out[0..len), -1 padded.  All
+// 256 threads; wave w takes the contiguous quarter of the list
+// select_top_regs expects; s_hist holds TOPK_HIST_BINS counters.
 template <int KPT>
 __device__ __forceinline__ void select_top(const uint64_t *s_keys, const int32_t *s_ids, int m, int r, int32_t *out,
                            int32_t *s_sel, int len, uint32_t *s_hist, uint64_t *s_state,
                            uint32_t *s_wave) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint64_t kr[KPT];
+  float sc[KPT];
   int32_t ids[KPT];
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const int e = 64 * KPT * wv + 64 * k + lane;
     const int j = min(e, m - 1);
     kr[k] = e < m ? s_keys[j] : 0ull;
+    sc[k] = unord_key((uint32_t)(kr[k] >> 32));
     ids[k] = s_ids[j];
   }
-  select_top_regs<KPT>(kr, ids, s_keys, m, r, out, s_sel, len, s_hist, s_state, s_wave);
+  select_top_regs<KPT>(kr, sc, ids, s_keys, m, r, out, s_sel, len, s_hist, s_state, s_wave);
 }
 
 // Runtime dispatch on the list length (up to 8,192 entries).
@@ -939,8 +1100,8 @@ __device__ __forceinline__ uint64_t threshold_in_lds(const uint64_t *s_keys, int
 __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint64_t s_keys[];                 // lds_keys
   __shared__ int32_t s_ids[LDS_KEYS];
-  __shared__ int32_t s_sel[CSA2_TOPK_MAX];
-  __shared__ __attribute__((aligned(16))) uint32_t s_hist[RADIX_BINS];   // also 64-bit keys (radix_select_keys)
+  __shared__ int32_t s_sel[CSA2_TOPK_MAX + SEL_PAD];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[TOPK_HIST_BINS];   // also 64-bit keys (radix_select_keys)
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;
@@ -1583,8 +1744,8 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint64_t s_keys[];
   __shared__ float s_qbar[D];
   __shared__ int32_t s_ids[SELECT ? LDS_KEYS : 1];
-  __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX : 1];
-  __shared__ __attribute__((aligned(16))) uint32_t s_hist[SELECT ? RADIX_BINS : 1];
+  __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX + SEL_PAD : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[SELECT ? TOPK_HIST_BINS : 1];
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;
