@@ -131,7 +131,7 @@ bool make_layout(int32_t batch, int32_t heads, int64_t max_len, int32_t pool, in
     // to CSA2_MAX_WINDOW / ATT_SP stages; one split normalises in-kernel
     const int cap = att_splits(batch * (heads / 16), L->att_stages + CSA2_MAX_WINDOW / ATT_SP);
     const size_t slots = cap > 1 ? (size_t)batch * cap * (heads / 16) * 16 : 0;
-    L->part_o = off;  off = align256(off + sizeof(float) * slots * D);
+    L->part_o = off;  off = align256(off + sizeof(_Float16) * slots * D);
     L->part_ml = off; off = align256(off + sizeof(float) * slots * 2);
   }
   L->total = off;
@@ -402,7 +402,7 @@ csa2_status run_attend(const csa2_kv *kv, const float *q, int32_t heads, const i
   int splits = att_splits(B * (heads / 16), aa.n_stages);
   if (splits > room) splits = room;
   aa.splits = splits;
-  aa.part_o = at<float>(ws, L.part_o); aa.part_ml = at<float>(ws, L.part_ml);
+  aa.part_o = at<_Float16>(ws, L.part_o); aa.part_ml = at<float>(ws, L.part_ml);
   aa.heads = heads;
   aa.cand = cand; aa.cand_scores = cand_scores; aa.n_cand = n_cand; aa.idx_out = idx_out;
   aa.seq_stride = kv->capacity; aa.len_add = 0; aa.out = out;
@@ -455,7 +455,7 @@ bool prefill_layout(int32_t n_q, int32_t heads, int32_t topk, int32_t window, La
   L->att_splits = att_splits(heads == 64 && window == 0 ? n_q : n_q * (heads / 16), L->att_stages + wstages);
   const size_t slots = L->att_splits > 1 ? (size_t)n_q * L->att_splits * (heads / 16) * 16 : 0;
   size_t off = 0;
-  L->part_o = off;  off = align256(off + sizeof(float) * slots * D);
+  L->part_o = off;  off = align256(off + sizeof(_Float16) * slots * D);
   L->part_ml = off; off = align256(off + sizeof(float) * slots * 2);
   L->total = slots ? off : 0;
   return true;
@@ -702,7 +702,7 @@ csa2_status csa2_prefill_attend(const csa2_kv *kv, int32_t seq, const float *q, 
     aa.swa_slots = 1; aa.swa_stride = 0; aa.win_at_query = 0;
     aa.swa_codes = aa.codes; aa.swa_scales = nullptr; aa.swa_len = qpos;
   }
-  aa.part_o = L.total ? at<float>(ws, L.part_o) : nullptr;
+  aa.part_o = L.total ? at<_Float16>(ws, L.part_o) : nullptr;
   aa.part_ml = L.total ? at<float>(ws, L.part_ml) : nullptr;
   aa.out = out;
   const size_t lds = (size_t)ATT_SP * ROW_HALVES * sizeof(_Float16);

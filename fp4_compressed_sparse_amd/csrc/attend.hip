@@ -62,6 +62,23 @@ __device__ __forceinline__ u32x4 rotate4(u32x4 v, int rot) {
   return v;
 }
 
+// A split's O^T accumulators (four channels of one head) divided by that
+// head's sum, as fp16: the normalised values are averages of V rows, so they
+// stay within fp16 range, and the combine re-weights them by the sums.
+__device__ __forceinline__ u32x2 pack_partial(f32x4 v, float inv) {
+  const f16x2 lo = {(_Float16)(v[0] * inv), (_Float16)(v[1] * inv)};
+  const f16x2 hi = {(_Float16)(v[2] * inv), (_Float16)(v[3] * inv)};
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+// (the words are copied to scalars before the bit casts: this compiler
+// turned a bit cast of a vector element u[1] into a read of u[0])
+__device__ __forceinline__ float4 unpack_partial(u32x2 u) {
+  const uint32_t w0 = u.x, w1 = u.y;
+  const f16x2 lo = __builtin_bit_cast(f16x2, w0);
+  const f16x2 hi = __builtin_bit_cast(f16x2, w1);
+  return float4{(float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y};
+}
+
 struct AttendArgs {
   const uint8_t *codes;
   const uint8_t *scales;
@@ -75,8 +92,9 @@ struct AttendArgs {
   float scale_log2;         // scale * log2(e)
   int32_t n_stages;         // n_sparse + ceil(window / ATT_SP)
   int32_t splits;           // workgroups per (sequence, head tile)
-  float *part_o;            // [batch][splits][heads/16][32 tiles][64 lanes][4]: O^T accumulators
-                            // in lane order (contiguous stores)
+  _Float16 *part_o;         // [batch][splits][heads/16][32 tiles][64 lanes][4]: O^T of the split
+                            // divided by its sum (so |O| <= max |V|), fp16, in lane order
+                            // (contiguous stores)
   float *part_ml;           // [batch][splits][heads/16][16 heads][2]: running max (log2) and sum
   // selecting variant only: the top-k is taken inside the kernel from a
   // scored candidate list (every workgroup takes the same, deterministic
@@ -258,6 +276,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   // every split owns at least one stage (splits <= stages)
   fetch_ids(st0);
   __builtin_amdgcn_sched_barrier(0);
+  CSA2_TS(24);
 
   // ---- Q^T operand: head 16*ht + n16, channels 32*kc + 8*g + 0..7.  The
   // tile's 16 query rows (32 KB) are staged through LDS as fp16 with one
@@ -280,6 +299,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     }
     fetch_rows(st0);
     if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);
+    CSA2_TS(25);
     uint32_t mb = 0;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -292,7 +312,9 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     }
     // no fp16 value for |q| >= 65520 (or NaN/Inf): flag it
     if (__builtin_amdgcn_ballot_w64(mb >= 0x477ff000u) && lane == 0) raise_flag(FLAG_Q_RANGE);
+    CSA2_TS(26);
     __syncthreads();
+    CSA2_TS(27);
     const _Float16 *qrow = s_v + n16 * ROW_HALVES + 8 * g;
 #pragma unroll
     for (int kc = 0; kc < 16; ++kc) qop[kc] = *reinterpret_cast<const f16x8 *>(qrow + 32 * kc);
@@ -478,12 +500,15 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     return;
   }
   // ---- partial of this (sequence, split, head tile) ----
-  // streaming stores: the partials are read once, by the combine kernel
-  // (measured: 4 us per 20-layer step less than ordinary stores)
+  // fp16, normalised by the split's sum: half the bytes of float32
+  // accumulators to write here and to read in the combine (a 20-layer step
+  // at 1M: 0.420 -> 0.402 ms).  Ordinary stores for them (0.399 ms; streaming
+  // stores helped while they were float32); the (max, sum) pairs stream.
   const int64_t slot = ((int64_t)b * a.splits + split) * HT + ht;
-  f32x4 *po = reinterpret_cast<f32x4 *>(a.part_o + slot * (16 * D)) + lane;
+  u32x2 *po = reinterpret_cast<u32x2 *>(a.part_o) + slot * (16 * D / 4) + lane;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) __builtin_nontemporal_store(acc[t], &po[(8 * wv + t) * 64]);
+  for (int t = 0; t < 8; ++t) po[(8 * wv + t) * 64] = pack_partial(acc[t], inv);
   if (wv == 0 && g == 0) {
     float *pm = a.part_ml + (slot * 16 + n16) * 2;
     __builtin_nontemporal_store(m_run, &pm[0]);
@@ -771,9 +796,11 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     const int64_t slot = ((int64_t)b * a.splits + split) * 4 + h;
-    f32x4 *po = reinterpret_cast<f32x4 *>(a.part_o + slot * (16 * D)) + lane;
+    u32x2 *po = reinterpret_cast<u32x2 *>(a.part_o) + slot * (16 * D / 4) + lane;
+    const float l = s_fin[0][16 * h + n16] + s_fin[1][16 * h + n16];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) po[(4 * wv + t) * 64] = acc[h][t];
+    for (int t = 0; t < 4; ++t) po[(4 * wv + t) * 64] = pack_partial(acc[h][t], inv);
   }
   if (g == 0 && ph == 0) {
     const int64_t slot = ((int64_t)b * a.splits + split) * 4 + ht;
@@ -785,7 +812,7 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
 }
 
 struct CombineArgs {
-  const float *part_o;
+  const _Float16 *part_o;   // as AttendArgs::part_o
   const float *part_ml;
   int32_t splits;
   int32_t heads;
@@ -817,7 +844,7 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_kernel(CombineArgs a) 
   constexpr int MLV = BATCH * 16 / (64 * NW);
   CSA2_TS(8);
   const float2 *pml = reinterpret_cast<const float2 *>(a.part_ml);
-  const float4 *po = reinterpret_cast<const float4 *>(a.part_o) + ct * 64 + lane;
+  const u32x2 *po = reinterpret_cast<const u32x2 *>(a.part_o) + ct * 64 + lane;
   auto slot_of = [&](int s) { return ((int64_t)b * a.splits + s) * HT + ht; };
   // (max, sum) of the first BATCH splits: entry tid + 64*NW*u is split
   // (tid + 64*NW*u) / 16, head (tid + 64*NW*u) % 16 (slots are contiguous in
@@ -828,7 +855,7 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_kernel(CombineArgs a) 
     const int e = min(tid + 64 * NW * u, nml - 1);
     mlv[u] = pml[slot_of(e >> 4) * 16 + (e & 15)];
   }
-  float4 ov[CMB_U];
+  u32x2 ov[CMB_U];
 #pragma unroll
   for (int u = 0; u < CMB_U; ++u) ov[u] = po[slot_of(min(CMB_U * wv + u, nslots - 1)) * (16 * D / 4)];
   __builtin_amdgcn_sched_barrier(0);
@@ -870,8 +897,10 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_kernel(CombineArgs a) 
         const int su = min(sw + u, nslots - 1);
         const float2 ml = s_ml[su * 16 + n16];
         const float e = (sw + u < nslots && ml.x != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
-        L += e * ml.y;
-        o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
+        const float we = e * ml.y;          // the partial is O / sum
+        const float4 v = unpack_partial(ov[u]);
+        L += we;
+        o.x += we * v.x; o.y += we * v.y; o.z += we * v.z; o.w += we * v.w;
       }
     }
   }
@@ -908,11 +937,11 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_regs_kernel(CombineArg
   const int ns = a.splits, s0 = U * wv;
   CSA2_TS(8);
   const int64_t slot0 = (int64_t)b * ns * HT + ht;                 // slot of split 0
-  const float4 *po = reinterpret_cast<const float4 *>(a.part_o) + slot0 * (16 * D / 4) + ct * 64 + lane;
+  const u32x2 *po = reinterpret_cast<const u32x2 *>(a.part_o) + slot0 * (16 * D / 4) + ct * 64 + lane;
   const float2 *pm = reinterpret_cast<const float2 *>(a.part_ml) + slot0 * 16 + n16;
   const int64_t so = (int64_t)HT * (16 * D / 4), sm = (int64_t)HT * 16;   // per split
   float2 ml[U];
-  float4 ov[U];
+  u32x2 ov[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t sc = min(s0 + u, ns - 1);                        // clamped: one batch, no branch
@@ -930,8 +959,10 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_regs_kernel(CombineArg
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float e = (s0 + u < ns && ml[u].x != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(ml[u].x - M) : 0.f;
-      L += e * ml[u].y;
-      o.x += e * ov[u].x; o.y += e * ov[u].y; o.z += e * ov[u].z; o.w += e * ov[u].w;
+      const float we = e * ml[u].y;         // the partial is O / sum
+      const float4 v = unpack_partial(ov[u]);
+      L += we;
+      o.x += we * v.x; o.y += we * v.y; o.z += we * v.z; o.w += we * v.w;
     }
   }
   CSA2_TS(9);

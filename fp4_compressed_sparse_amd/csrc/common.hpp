@@ -82,16 +82,26 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
 // Phase timestamps for profiling builds only (compiled with
 // -DCSA2_PHASE_TIMING; the normal build compiles the hook away).  Thread 0
 // of each workgroup records s_memrealtime (100 MHz) after its wave's memory
-// operations complete.
+// operations complete; with -DCSA2_PHASE_TIMING_LIGHT it records the
+// core-clock counter (s_memtime) as the wave reaches the hook, without
+// waiting for outstanding memory operations (progress, not arrival).
 #ifdef CSA2_PHASE_TIMING
 constexpr int TS_SLOTS = 32;
 __device__ unsigned long long g_phase_ts[4096][TS_SLOTS];
+#ifdef CSA2_PHASE_TIMING_LIGHT
+#define CSA2_TS(k)                                                                     \
+  do {                                                                                 \
+    const unsigned wg_ = blockIdx.x + blockIdx.y * gridDim.x;                          \
+    if (threadIdx.x == 0 && wg_ < 4096) g_phase_ts[wg_][k] = __builtin_amdgcn_s_memtime(); \
+  } while (0)
+#else
 #define CSA2_TS(k)                                                                     \
   do {                                                                                 \
     __builtin_amdgcn_s_waitcnt(0);                                                     \
     const unsigned wg_ = blockIdx.x + blockIdx.y * gridDim.x;                          \
     if (threadIdx.x == 0 && wg_ < 4096) g_phase_ts[wg_][k] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
+#endif
 #else
 #define CSA2_TS(k) \
   do {             \
