@@ -339,6 +339,39 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
 
 
+def read_probe(args):
+    """The achievable HBM read rate for the full scan's byte count at 1M
+    (301,990,608 B): csa2_read_probe (16-byte loads, the scan's 512
+    workgroups) timed with events, cold (a 512 MB read before each run, as
+    in the decode bench) and back to back."""
+    import numpy as np
+    import torch
+    import fp4_compressed_sparse_amd as csa2
+    torch.cuda.set_device(0)
+    nbytes = 301990608 // 16 * 16
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(512 * 256, dtype=torch.int32, device="cuda")
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    flush_sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for mode in ("cold", "warm"):
+        us = []
+        for i in range(max(args.steps, 5) + 2):
+            if mode == "cold":
+                torch.sum(flush, dim=0, out=flush_sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            csa2.read_probe(buf, sink, stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                us.append(a.elapsed_time(b) * 1e3)
+        med = float(np.median(us))
+        res[mode] = {"median_us": round(med, 2), "tb_s": round(nbytes / med / 1e6, 3), "runs": len(us)}
+    print(json.dumps({"read_probe_bytes": nbytes, "workgroups": 512, **res}))
+
+
 def prefill_bench(args):
     """Batched prefill-side sparse attention (csa2_prefill_attend): T queries
     at the last T positions of one 1,048,576-position cache, each with its
@@ -524,6 +557,8 @@ def main():
     ap.add_argument("--launch-floor", action="store_true",
                     help="time a chain of dependent tiny launches (its own JSON line)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="achievable read rate for the 1M scan's bytes (csa2_read_probe), cold and warm")
     ap.add_argument("--prefill", type=int, default=0, metavar="T",
                     help="instead of the decode step: batched prefill-side sparse attention of T "
                          "queries (the last T positions of a 1M-position cache, 64 heads, top-256 "
@@ -549,6 +584,9 @@ def main():
               "shard by sequence across GPUs with no exchange; one GPU's share is what this measures)",
               file=sys.stderr)
         sys.exit(2)
+    if args.read_probe:
+        read_probe(args)
+        return
     if args.copy_probe:
         copy_probe()
         return

@@ -29,7 +29,8 @@ EXPORTED = ("fp4_quantize_kv", "csa2_append_kv", "fp8_quantize_kv", "csa2_swa_ap
             "csa2_workspace_bytes", "csa2_workspace_init",
             "csa2_index_topk", "csa2_sparse_attend", "csa2_prefill_workspace_bytes",
             "csa2_prefill_attend", "csa2_decode_step", "csa2_decode_step_noalloc", "csa2_block_scores",
-            "csa2_device_error", "csa2_set_scan_events", "csa2_status_string", "csa2_last_error")
+            "csa2_device_error", "csa2_set_scan_events", "csa2_read_probe", "csa2_status_string",
+            "csa2_last_error")
 
 
 class Csa2Error(RuntimeError):
@@ -93,6 +94,7 @@ def load():
         "csa2_block_scores": (i32, [ctypes.POINTER(_Kv), vp, i32, vp, i32, vp, i32, vp]),
         "csa2_device_error": (i32, [ctypes.POINTER(ctypes.c_int32), vp]),
         "csa2_set_scan_events": (i32, [vp, vp]),
+        "csa2_read_probe": (i32, [vp, i64, vp, vp]),
         "csa2_status_string": (ctypes.c_char_p, [i32]),
         "csa2_last_error": (ctypes.c_char_p, []),
     }
@@ -328,6 +330,14 @@ def set_scan_events(before=None, after=None):
     """Record hipEvent_t handles `before`/`after` (ctypes c_void_p) around
     every full-scan kernel launched from this thread (None, None clears)."""
     _check(load().csa2_set_scan_events(before, after))
+
+
+def read_probe(buf, sink, stream=None):
+    """csa2_read_probe: read every byte of the device tensor `buf` once (the
+    read-rate yardstick for the full scan); `sink` is a device int32 tensor
+    of at least 512 * 256 entries."""
+    assert buf.is_cuda and sink.is_cuda and sink.numel() >= 512 * 256 and sink.element_size() == 4
+    _check(load().csa2_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 def device_error(stream=None):

@@ -463,6 +463,25 @@ bool prefill_layout(int32_t n_q, int32_t heads, int32_t topk, int32_t window, La
 
 }  // namespace
 
+namespace csa2 {
+// Plain streaming read (the read-rate yardstick for the full scan): four
+// 16-byte loads per thread per round, grid-stride over 512 workgroups.
+__global__ void __launch_bounds__(256) read_probe_kernel(const u32x4 *__restrict__ p, int64_t n,
+                                                         uint32_t *__restrict__ sink) {
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 * 4 + threadIdx.x; i < n; i += stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = p[min(i + 256 * u, n - 1)];   // clamped: one batch, in bounds
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= (i + 256 * u < n) ? (v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3]) : 0u;
+  }
+  sink[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+}  // namespace csa2
+
 extern "C" {
 
 const char *csa2_status_string(csa2_status s) {
@@ -896,6 +915,17 @@ csa2_status csa2_decode_step(const csa2_step *st, void *stream) {
     prev_idx = ly.idx;
   }
   return CSA2_OK;
+}
+
+csa2_status csa2_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {
+  t_last_error.clear();
+  if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4))
+    return fail(CSA2_E_ARG, "read probe: NULL or misaligned pointer");
+  if (bytes <= 0 || bytes % 16 != 0) return fail(CSA2_E_ARG, "read probe: bytes %lld not a positive multiple of 16",
+                                                 (long long)bytes);
+  if (csa2_status st = device_ready()) return st;
+  csa2::read_probe_kernel<<<512, 256, 0, as_stream(stream)>>>(static_cast<const u32x4 *>(buf), bytes / 16, sink);
+  return launched("read probe");
 }
 
 #ifdef CSA2_PHASE_TIMING

@@ -414,6 +414,17 @@ csa2_status csa2_device_error(int32_t *flags_host, void *stream);
  */
 csa2_status csa2_set_scan_events(void *before, void *after);
 
+/*
+ * csa2_read_probe — measurement aid: the achievable HBM read rate that the
+ * full scan's rate is judged against.  Reads bytes (a multiple of 16, > 0)
+ * of device memory at buf (16-byte aligned) once, with 16-byte loads
+ * spread over 512 workgroups of 256 threads (the full scan's grid), and
+ * writes 512 * 256 uint32 xor-reductions of what it read to sink (device,
+ * 4-byte aligned; their values mean nothing) so no load is dropped.
+ * Errors: CSA2_E_ARG for NULL or misaligned pointers or a bad size.
+ */
+csa2_status csa2_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
 const char *csa2_status_string(csa2_status s);
 /* Message of the last failing call on this thread ("" if none). */
 const char *csa2_last_error(void);

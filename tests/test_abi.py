@@ -197,3 +197,14 @@ def test_prefill_attend_argument_errors(lib):
     assert call(kv=_kv(capacity=4092)) == 2
     assert call(sw=_swa(window=0)) == 2                          # bad local branch
     assert call(sw=_swa(batch=3)) == 1
+
+
+def test_read_probe_argument_errors(lib):
+    buf, sink = ctypes.c_void_p(0x50000), ctypes.c_void_p(0x60000)
+    assert lib.csa2_read_probe(None, 16, sink, None) == 1
+    assert lib.csa2_read_probe(buf, 16, None, None) == 1
+    assert lib.csa2_read_probe(ctypes.c_void_p(0x50008), 16, sink, None) == 1   # buf not 16-byte aligned
+    assert lib.csa2_read_probe(buf, 16, ctypes.c_void_p(0x60002), None) == 1    # sink misaligned
+    assert lib.csa2_read_probe(buf, 0, sink, None) == 1
+    assert lib.csa2_read_probe(buf, 24, sink, None) == 1                       # not a multiple of 16
+    assert "read probe" in _err(lib)
