@@ -35,8 +35,9 @@
 // the last select workgroup ranks those keys in LDS and writes the chosen
 // ids in ascending order (select2_kernel; select_kernel, with a global
 // bitmap and tie lists, serves selections whose bitmap exceeds LDS).
-// A block top-k inside LDS (a candidate list) uses linear bins over the
-// score range with an exact pairwise finish (topk_threshold).
+// A top-k inside one workgroup (a candidate list, the finishers' ranks)
+// uses linear bins over the score range with an exact pairwise finish
+// (select_top_regs, threshold_linear).
 #include "common.hpp"
 
 namespace csa2 {
@@ -727,117 +728,6 @@ constexpr int TIE_MAX = 256;     // threshold-bin members ranked pairwise
 #define CSA2_TOPK_TS(k) do { } while (0)
 #endif
 
-// Threshold of a top-r choice among the nonzero keys held in registers:
-// thread t holds entries t, t + 256, ..., t + 256 (KPT - 1) of a list of
-// 256 * KPT keys (0 = empty; make_key never yields 0).  Returns T such that
-// exactly min(r, #nonzero) nonzero keys are >= T (0 when r >= #nonzero, ~0
-// when r <= 0 or the list is empty); *r_eff = min(r, #nonzero).  All 256
-// threads call; s_keys is the same list in LDS (read only by the fallback),
-// s_hist holds RADIX_BINS counters.
-//
-// One pass of linear bins over the scores' range [lo, hi]:
-// bin(s) = min(2047, floor((s - lo) * 2048 / (hi - lo))) is monotone in s,
-// so every key of a higher bin beats every key of a lower one and equal
-// scores share a bin (their order is the id part of the key).  The bin
-// holding the r-th largest key usually has a handful of members, ranked
-// pairwise; a degenerate range or a crowded bin falls back to the radix
-// select above.
-template <int KPT>
-__device__ __forceinline__ uint64_t topk_threshold(const uint64_t (&kr)[KPT], const uint64_t *s_keys, int m, int r,
-                                   int *r_eff, uint32_t *s_hist, uint64_t *s_state,
-                                   uint32_t *s_wave) {
-  __shared__ uint32_t s_red[12];
-  __shared__ uint32_t s_tot[4];
-  __shared__ uint32_t s_find[4];
-  __shared__ uint64_t s_tie[TIE_MAX];
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0u;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const uint32_t u = (uint32_t)(kr[k] >> 32);
-    if (kr[k]) { ++cnt; umin = min(umin, u); umax = max(umax, u); }
-  }
-#pragma unroll
-  for (int k = 0; k < RADIX_BINS / 256; ++k) s_hist[t + 256 * k] = 0;
-  if (t == 0) s_find[3] = 0;                    // gather counter
-  cnt = wave_sum(cnt);
-  umin = wave_umin(umin);
-  umax = wave_umax(umax);
-  if (lane == 0) { s_red[wv] = cnt; s_red[4 + wv] = umin; s_red[8 + wv] = umax; }
-  __syncthreads();
-  CSA2_TOPK_TS(1);
-  const uint32_t nvalid = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-  umin = min(min(s_red[4], s_red[5]), min(s_red[6], s_red[7]));
-  umax = max(max(s_red[8], s_red[9]), max(s_red[10], s_red[11]));
-  r = min(r, (int)nvalid);
-  *r_eff = r;
-  if (r <= 0) return ~0ull;
-  if (r == (int)nvalid) return 0ull;
-  const float lo = unord_key(umin), hi = unord_key(umax);
-  const float range = hi - lo;
-  const float inv = (float)RADIX_BINS / range;
-  if (umin == umax || !(range < __builtin_huge_valf()) || !(inv < __builtin_huge_valf()) || !(inv > 0.f))
-    return radix_threshold(s_keys, m, r, 63, s_hist, s_state, s_wave);
-  int bin[KPT];
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const float sc = unord_key((uint32_t)(kr[k] >> 32));
-    bin[k] = kr[k] ? min(RADIX_BINS - 1, (int)((sc - lo) * inv)) : -1;
-    if (kr[k]) atomicAdd(&s_hist[bin[k]], 1u);
-  }
-  __syncthreads();
-  CSA2_TOPK_TS(2);
-  // counts above each thread's 8 bins (thread 0 owns the top 8)
-  constexpr int PER = RADIX_BINS / 256;
-  uint32_t c8[PER], sum = 0;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) { c8[k] = s_hist[RADIX_BINS - 1 - (PER * t + k)]; sum += c8[k]; }
-  const uint32_t incl = wave_incl_scan(sum);
-  if (lane == 63) s_tot[wv] = incl;
-  __syncthreads();
-  uint32_t above = incl - sum;
-  above += (wv > 0 ? s_tot[0] : 0u) + (wv > 1 ? s_tot[1] : 0u) + (wv > 2 ? s_tot[2] : 0u);
-  if (above < (uint32_t)r && (uint32_t)r <= above + sum) {
-    uint32_t acc = above;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      if (acc < (uint32_t)r && (uint32_t)r <= acc + c8[k]) {
-        s_find[0] = (uint32_t)(RADIX_BINS - 1 - (PER * t + k));
-        s_find[1] = (uint32_t)r - acc;          // keys still needed from the bin
-        s_find[2] = c8[k];                      // keys in the bin
-      }
-      acc += c8[k];
-    }
-  }
-  __syncthreads();
-  CSA2_TOPK_TS(3);
-  const int bstar = (int)s_find[0];
-  const uint32_t rem = s_find[1], c = s_find[2];
-  if (c > (uint32_t)TIE_MAX) return radix_threshold(s_keys, m, r, 63, s_hist, s_state, s_wave);
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    if (bin[k] == bstar) {
-      const uint32_t slot = atomicAdd(&s_find[3], 1u);
-      if (slot < (uint32_t)TIE_MAX) s_tie[slot] = kr[k];
-    }
-  }
-  __syncthreads();
-  CSA2_TOPK_TS(4);
-  if (t < (int)c) {
-    const uint64_t k = s_tie[t];
-    uint32_t gt = 0, ge = 0;                    // bin members above / not below k
-    for (uint32_t i2 = 0; i2 < c; ++i2) {
-      const uint64_t o = s_tie[i2];
-      gt += o > k ? 1u : 0u;
-      ge += o >= k ? 1u : 0u;
-    }
-    if (gt < rem && rem <= ge) s_state[0] = k;  // k is the rem-th largest
-  }
-  __syncthreads();
-  CSA2_TOPK_TS(5);
-  return s_state[0];
-}
-
 constexpr int SEL_PAD = 64;          // s_sel slots past len: unchosen lanes' stores land there
 constexpr int TOPK_HIST_BINS = RADIX_BINS + 64;   // block top-k bins; the last 64 take empty entries
 
@@ -874,6 +764,39 @@ __device__ __forceinline__ void compact_ge(const uint64_t (&kr)[KPT], const int3
   __syncthreads();
   if (out)
     for (int j = t; j < len; j += 256) out[j] = s_sel[j];
+}
+
+// The bin of s_hist[0..RADIX_BINS) (counts, bin RADIX_BINS - 1 the highest)
+// holding the r-th largest key, found by one wave on its own (every wave of
+// a workgroup gets the same answer from the same counts, so no exchange is
+// needed): lane l sums bins [2016 - 32 l, 2047 - 32 l] (read in a rotated
+// order, so eight neighbouring lanes cover all banks), a wave scan finds the
+// lane, and lanes 0..31 scan that lane's bins.  *rem: keys still needed from
+// the bin, *cbin: keys in it, *total: keys in all bins.  Returns false when
+// the bins hold fewer than r keys.
+__device__ __forceinline__ bool find_threshold_bin(const uint32_t *s_hist, int r, uint32_t *bstar, uint32_t *rem,
+                                                   uint32_t *cbin, uint32_t *total) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t *hb = s_hist + (RADIX_BINS - 32 - 32 * lane);
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(hb + 4 * ((i + lane) & 7));
+    sum += v.x + v.y + v.z + v.w;
+  }
+  const uint32_t incl = wave_incl_scan(sum);
+  *total = __builtin_amdgcn_readlane(incl, 63);
+  const uint64_t fm = __ballot(incl - sum < (uint32_t)r && (uint32_t)r <= incl);
+  const int L = fm ? __builtin_ctzll(fm) : 0;
+  const uint32_t aboveL = __builtin_amdgcn_readlane(incl - sum, L);
+  const uint32_t cc = lane < 32 ? s_hist[RADIX_BINS - 1 - 32 * L - lane] : 0u;
+  const uint32_t ic = wave_incl_scan(cc);
+  const uint64_t bm = __ballot(lane < 32 && aboveL + ic - cc < (uint32_t)r && (uint32_t)r <= aboveL + ic);
+  const int B = bm ? __builtin_ctzll(bm) : 0;
+  *bstar = (uint32_t)(RADIX_BINS - 1 - 32 * L - B);
+  *rem = (uint32_t)r - aboveL - __builtin_amdgcn_readlane(ic - cc, B);
+  *cbin = __builtin_amdgcn_readlane(cc, B);
+  return fm != 0 && bm != 0;
 }
 
 // Register form of the block top-k (256 threads): wave w holds list
@@ -950,33 +873,9 @@ __device__ __forceinline__ void select_top_regs(const uint64_t (&kr)[KPT], const
   }
   __syncthreads();
   CSA2_TOPK_TS(2);
-  // ---- the bin holding the r-th largest key, found by every wave alone:
-  // lane l sums bins [2016 - 32 l, 2047 - 32 l] (read in a rotated order,
-  // so eight neighbouring lanes cover all banks), a wave scan finds the
-  // lane, and lanes 0..31 scan that lane's bins
-  uint32_t bstar, rem, cbin;
-  bool ok;
-  {
-    const uint32_t *hb = s_hist + (RADIX_BINS - 32 - 32 * lane);
-    uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(hb + 4 * ((i + lane) & 7));
-      sum += v.x + v.y + v.z + v.w;
-    }
-    const uint32_t incl = wave_incl_scan(sum);
-    const uint64_t fm = __ballot(incl - sum < (uint32_t)r && (uint32_t)r <= incl);
-    const int L = fm ? __builtin_ctzll(fm) : 0;
-    const uint32_t aboveL = __builtin_amdgcn_readlane(incl - sum, L);
-    const uint32_t cc = lane < 32 ? s_hist[RADIX_BINS - 1 - 32 * L - lane] : 0u;
-    const uint32_t ic = wave_incl_scan(cc);
-    const uint64_t bm = __ballot(lane < 32 && aboveL + ic - cc < (uint32_t)r && (uint32_t)r <= aboveL + ic);
-    ok = fm != 0 && bm != 0;
-    const int B = bm ? __builtin_ctzll(bm) : 0;
-    bstar = (uint32_t)(RADIX_BINS - 1 - 32 * L - B);
-    rem = (uint32_t)r - aboveL - __builtin_amdgcn_readlane(ic - cc, B);   // keys still needed from the bin
-    cbin = __builtin_amdgcn_readlane(cc, B);                                // keys in the bin
-  }
+  // ---- the bin holding the r-th largest key, found by every wave alone
+  uint32_t bstar, rem, cbin, binned;
+  const bool ok = find_threshold_bin(s_hist, r, &bstar, &rem, &cbin, &binned);
   CSA2_TOPK_TS(3);
   if (!ok || cbin > (uint32_t)TIE_MAX) {           // uniform: every wave read the same bins
     const uint64_t T = radix_threshold(s_keys, m, r, 63, s_hist, s_state, s_wave);
@@ -1080,21 +979,110 @@ __device__ __forceinline__ void select_in_lds(const uint64_t *s_keys, const int3
     select_top<32>(s_keys, s_ids, m, r, out, s_sel, len, s_hist, s_state, s_wave);
 }
 
-// Threshold only, over an LDS list of up to 8,192 entries.
-__device__ __forceinline__ uint64_t threshold_in_lds(const uint64_t *s_keys, int m, int r, uint32_t *s_hist,
-                                     uint64_t *s_state, uint32_t *s_wave) {
-  const int t = threadIdx.x;
-  int reff = 0;
-  if (m <= 2048) {
-    uint64_t kr[8];
+// Threshold of a top-r choice over the LDS list s_keys[0..m) (0 = empty
+// entry; keys distinct), for any workgroup of up to 16 waves: T such that
+// exactly min(r, #nonzero) nonzero keys are >= T (0 when r >= #nonzero, ~0
+// when r <= 0).  Thread t holds entries t + nt k, k < KPT (m <= nt KPT).
+// The block top-k's method without its compaction: one pass of RADIX_BINS
+// linear bins over the keys' score range, the threshold bin found by every
+// wave alone, its members ranked pairwise (four workgroup barriers); a NaN
+// or infinite score, a degenerate range or a crowded bin falls back to the
+// radix select.  s_hist holds TOPK_HIST_BINS counters.
+struct LinearLds {
+  uint32_t red[3 * 16];   // per wave: valid count, min key - 1, max key
+  uint32_t ntie;
+  uint64_t tie[TIE_MAX];
+};
+__device__ __forceinline__ LinearLds &linear_lds() {
+  __shared__ LinearLds s;   // one object, whatever KPT the caller picks
+  return s;
+}
+
+template <int KPT>
+__device__ __forceinline__ uint64_t threshold_linear(const uint64_t *s_keys, int m, int r, uint32_t *s_hist,
+                                                     uint64_t *s_state, uint32_t *s_wave) {
+  LinearLds &L = linear_lds();
+  uint32_t *s_red = L.red;
+  uint32_t &s_nt = L.ntie;
+  uint64_t *s_tie = L.tie;
+  const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wv = t >> 6, nw = nt >> 6;
+  uint64_t kr[KPT];
+  uint32_t hmax = 0u, hmin1 = 0xFFFFFFFFu, cnt = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) kr[k] = (t + 256 * k < m) ? s_keys[t + 256 * k] : 0ull;
-    return topk_threshold<8>(kr, s_keys, m, r, &reff, s_hist, s_state, s_wave);
+  for (int k = 0; k < KPT; ++k) {
+    kr[k] = t + nt * k < m ? s_keys[t + nt * k] : 0ull;
+    const uint32_t h = (uint32_t)(kr[k] >> 32);
+    hmax = max(hmax, h);
+    hmin1 = min(hmin1, h - 1u);                    // an empty entry (0) wraps to the top
+    cnt += (uint32_t)__popcll(__ballot(kr[k] != 0));
   }
-  uint64_t kr[32];
+  for (int j = t; j < TOPK_HIST_BINS; j += nt) s_hist[j] = 0;
+  if (t == 0) s_nt = 0;
+  hmax = wave_umax(hmax);
+  hmin1 = wave_umin(hmin1);
+  if (lane == 0) { s_red[wv] = cnt; s_red[16 + wv] = hmin1; s_red[32 + wv] = hmax; }
+  __syncthreads();
+  uint32_t nvalid = 0, umin = 0xFFFFFFFFu, umax = 0u;
+  for (int w = 0; w < nw; ++w) {
+    nvalid += s_red[w];
+    umin = min(umin, s_red[16 + w]);
+    umax = max(umax, s_red[32 + w]);
+  }
+  umin += 1u;
+  r = min(r, (int)nvalid);
+  if (r <= 0 || r == (int)nvalid) {
+    __syncthreads();                               // every wave has read s_red: a next call may write it
+    return r <= 0 ? ~0ull : 0ull;
+  }
+  const float lo = unord_key(umin), hi = unord_key(umax);
+  const float inv = (float)RADIX_BINS * __builtin_amdgcn_rcpf(hi - lo);
+  if (umin >= umax || umin <= 0x007FFFFFu || umax >= 0xFF800000u || !(inv < __builtin_huge_valf()) ||
+      !(inv > 0.f))
+    return radix_threshold(s_keys, m, r, 63, s_hist, s_state, s_wave);
+  uint32_t bin[KPT];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) kr[k] = (t + 256 * k < m) ? s_keys[t + 256 * k] : 0ull;
-  return topk_threshold<32>(kr, s_keys, m, r, &reff, s_hist, s_state, s_wave);
+  for (int k = 0; k < KPT; ++k) {
+    const float sc = unord_key((uint32_t)(kr[k] >> 32));
+    const int bf = min(RADIX_BINS - 1, (int)((sc - lo) * inv));
+    bin[k] = kr[k] != 0 ? (uint32_t)bf : (uint32_t)(RADIX_BINS + lane);
+    atomicAdd(&s_hist[bin[k]], 1u);
+  }
+  __syncthreads();
+  uint32_t bstar, rem, cbin, binned;
+  const bool ok = find_threshold_bin(s_hist, r, &bstar, &rem, &cbin, &binned);
+  if (!ok || cbin > (uint32_t)TIE_MAX)             // uniform: every wave read the same bins
+    return radix_threshold(s_keys, m, r, 63, s_hist, s_state, s_wave);
+#pragma unroll
+  for (int k = 0; k < KPT; ++k)
+    if (bin[k] == bstar) s_tie[atomicAdd(&s_nt, 1u)] = kr[k];
+  __syncthreads();
+  if (t < (int)cbin) {
+    const uint64_t k = s_tie[t];
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t i2 = 0; i2 < cbin; ++i2) {
+      const uint64_t o = s_tie[i2];
+      gt += o > k ? 1u : 0u;
+      ge += o >= k ? 1u : 0u;
+    }
+    if (gt < rem && rem <= ge) s_state[0] = k;  // k is the rem-th largest of the bin
+  }
+  __syncthreads();
+  const uint64_t T = s_state[0];
+  __syncthreads();                                 // s_state and s_hist are free again
+  return T;
+}
+
+// Threshold only, over an LDS list of up to MAXK * blockDim entries
+// (MAXK = 16 or 32): the fewest registers per thread that hold it.
+template <int MAXK>
+__device__ __forceinline__ uint64_t threshold_in_lds(const uint64_t *s_keys, int m, int r, uint32_t *s_hist,
+                                                     uint64_t *s_state, uint32_t *s_wave) {
+  static_assert(MAXK == 16 || MAXK == 32, "list size class");
+  const int nt = blockDim.x;
+  if (m <= 4 * nt) return threshold_linear<4>(s_keys, m, r, s_hist, s_state, s_wave);
+  if (m <= 8 * nt) return threshold_linear<8>(s_keys, m, r, s_hist, s_state, s_wave);
+  if (MAXK == 16 || m <= 16 * nt) return threshold_linear<16>(s_keys, m, r, s_hist, s_state, s_wave);
+  return threshold_linear<MAXK>(s_keys, m, r, s_hist, s_state, s_wave);
 }
 
 __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
@@ -1247,7 +1235,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
       __syncthreads();
       CSA2_TS(11);
       // the candidates share the top 10 key bits (the tie digit)
-      const uint64_t T = threshold_in_lds(s_keys, c, (int)need, s_hist, s_state, s_wave);
+      const uint64_t T = threshold_in_lds<32>(s_keys, c, (int)need, s_hist, s_state, s_wave);
       CSA2_TS(12);
       for (int j = t; j < c; j += nt) {
         uint64_t k = s_keys[j];
@@ -1515,7 +1503,7 @@ __global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
   uint64_t *s_keys = s_dyn;                                            // [lds_keys]
   uint32_t *s_bm = reinterpret_cast<uint32_t *>(s_dyn + a.lds_keys);  // [nwords]
   uint32_t *s_wpre = s_bm + a.nwords;                                  // [nwords]
-  __shared__ __attribute__((aligned(16))) uint32_t s_hist[RADIX_BINS];   // also 64-bit keys (radix_select_keys)
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[TOPK_HIST_BINS];   // also 64-bit keys (radix_select_keys)
   __shared__ uint32_t s_off[SEL2_MAXG + 1];
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
@@ -1608,6 +1596,7 @@ __global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
   };
   const int m = (int)E;
   const bool in_lds = m <= cap;
+  const bool fast = in_lds && m <= 16 * SEL2_THREADS;   // within the linear threshold's registers
   if (in_lds && rg < G) {
     const uint32_t off = s_off[rg], cnt = s_off[rg + 1] - off;
 #pragma unroll
@@ -1624,6 +1613,9 @@ __global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
   if (!all && need > 0 && (uint32_t)m > R) {
     const uint64_t prefix = (uint64_t)thr << (32 + HIST_SHIFT);
     const uint64_t pmask = ~((1ull << (32 + HIST_SHIFT)) - 1);
+    // one digit of the radix select inside the threshold digit (its keys
+    // alone) leaves a bucket small enough to rank; the linear threshold
+    // over every key measured no faster here (8,700-10,200 cycles at 1M)
     T = in_lds ? radix_select_keys(get_lds, m, (int)need, prefix, pmask, 31 + HIST_SHIFT, s_hist, s_state, s_wave)
                : radix_select_keys(key_at, m, (int)need, prefix, pmask, 31 + HIST_SHIFT, s_hist, s_state, s_wave);
   }
@@ -1678,8 +1670,11 @@ __global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
     // the top-k of the chosen list is the top-k of every entry
     uint64_t T2 = T;
     if ((uint32_t)a.topk < chosen)
-      T2 = in_lds ? radix_select_keys(get_lds, m, a.topk, 0ull, 0ull, 63, s_hist, s_state, s_wave)
-                  : radix_select_keys(key_at, m, a.topk, 0ull, 0ull, 63, s_hist, s_state, s_wave);
+      // no digit is known here: linear bins over the keys' range (11,000
+      // cycles at 1M against 34,500 for a radix select from the top bit)
+      T2 = fast ? threshold_in_lds<16>(s_keys, m, a.topk, s_hist, s_state, s_wave)
+           : in_lds ? radix_select_keys(get_lds, m, a.topk, 0ull, 0ull, 63, s_hist, s_state, s_wave)
+                    : radix_select_keys(key_at, m, a.topk, 0ull, 0ull, 63, s_hist, s_state, s_wave);
     emit(T2, a.idx_out + (int64_t)b * a.topk, nullptr, a.topk);
   }
   CSA2_TS(14);
