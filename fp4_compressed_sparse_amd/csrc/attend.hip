@@ -45,15 +45,53 @@ namespace csa2 {
 
 constexpr int ATT_THREADS = 256;
 constexpr int ATT_SP = 64;                        // gathered positions per stage
-constexpr int ROW_HALVES = D + 8;                 // LDS row stride: 1040 bytes
+constexpr int ROW_HALVES = D;                     // LDS row stride: 1,024 bytes (swizzled chunks)
 constexpr int P_STRIDE = ATT_SP + 8;              // LDS P row stride (halves): no bank conflicts
 
-// A thread dequantises 16 code bytes into 64 bytes of fp16 row, stored as
-// four 16-byte chunks; the 16 threads of a row sit 64 bytes apart, so
-// storing the chunks in the same order for every lane puts lanes 0, 2, 4,
-// ... on the same LDS banks.  Each lane starts at chunk chunk_rot(i16) and
-// wraps: any 8 consecutive lanes (32 banks) and any 16 (64 banks) then
-// write distinct 16-byte bank groups.
+// LDS rows of a stage (and the staged query) are 64 chunks of 8 channels
+// (16 bytes); chunk c of row p sits at chunk slot (c & ~15) | ((c ^ p) & 15)
+// of the row.  Measured on gfx950 with the LDS bank-conflict counter: a
+// 128-bit read by 16 lanes runs without conflict when the lanes hit 16
+// distinct 16-byte slots of one 256-byte window (address bits 4-9; with a
+// padded 1,040-byte row, the reads of 16 rows at one chunk straddle two
+// windows and take twice as long), and a transposing 64-bit read by 32 lanes
+// when they hit 32 distinct 8-byte slots of one window.  Rows of a
+// 16-aligned group then put any one chunk in 16 distinct slots of the same
+// window (the matrix operands' reads), and the two chunks c and c ^ 8 of
+// eight rows fill a window (the V^T reads).  Returns the row's element
+// offset in halves.
+__device__ __forceinline__ int row_chunk(int p, int c) { return p * ROW_HALVES + 8 * ((c & ~15) | ((c ^ p) & 15)); }
+
+// The matrix operands' 16-byte read: chunk 4 * kc + g of row p (channels
+// 32 * kc + 8 * g .. +7), i.e. row_chunk(p, 4 * kc + g) written so that
+// the four values of kc & 3 give four per-lane bases and kc >> 2 an
+// immediate offset.
+__device__ __forceinline__ int k_offset(int p, int kc, int g) {
+  return p * ROW_HALVES + 128 * (kc >> 2) + 8 * ((4 * (kc & 3) + g) ^ (p & 15));
+}
+
+// The O^T tile ct (16 channels) covers chunks tile_chunk(ct) and
+// tile_chunk(ct) ^ 8 of window ct & 3; its matrix row m holds channel
+// 8 * (tile_chunk(ct) ^ (8 * (m / 8))) + m % 8, so lane (n16, g) of the
+// accumulator holds the four channels from tile_channel(ct, g).  Tiles
+// ct and ct + 1 sit in neighbouring windows at the same slots, so a wave's
+// V^T reads of consecutive tiles differ by an immediate offset.
+__device__ __forceinline__ int tile_chunk(int ct) { return 16 * (ct & 3) + (ct >> 2); }
+__device__ __forceinline__ int tile_channel(int ct, int g) { return 8 * (tile_chunk(ct) ^ (8 * (g >> 1))) + 4 * (g & 1); }
+// The transposing read of tile ct by the lane that points at row p and
+// quarter q (channels 4 * (q & 1) .. +3 of chunk tile_chunk(ct) ^ (8 * (q >> 1))):
+// row_chunk(p, tile_chunk(ct) ^ (8 * (q >> 1))) + 4 * (q & 1).
+__device__ __forceinline__ int vt_offset(int p, int ct, int q) {
+  return p * ROW_HALVES + 128 * (ct & 3) + 8 * ((((ct >> 2) | (8 * (q >> 1))) ^ p) & 15) + 4 * (q & 1);
+}
+
+// A thread dequantises 16 code bytes (chunks 4 * i16 .. 4 * i16 + 3 of its
+// row) and stores them as four 16-byte chunks.  A 128-bit LDS write serves 8
+// lanes at a time, without conflict when they hit 8 distinct 16-byte slots
+// modulo 128 bytes; chunk 4 * i16 + s of row p falls in slot
+// ((4 * i16 + s) ^ p) & 7, so each lane starts at chunk chunk_rot(i16) and
+// wraps, which keeps the even lanes of any 8 on distinct slots, and the odd
+// ones too.
 __device__ __forceinline__ int chunk_rot(int i16) { return ((i16 >> 1) + (i16 >> 3)) & 3; }
 // element s of the result is v[(s + rot) & 3]
 __device__ __forceinline__ u32x4 rotate4(u32x4 v, int rot) {
@@ -133,7 +171,7 @@ constexpr int SEL_CAND_MAX = 2048;  // candidates of the in-kernel top-k (8 per 
 // written to LDS as fp16; wave w then accumulates O^T for channel tiles
 // 8w..8w+7 over all 64 positions.
 template <bool SELECT, bool WIN>
-__global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs a) {
+__global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))) attend_partial_kernel(AttendArgs a) {
   // 16-byte aligned: rows are read and written as 128-bit vectors
   extern __shared__ __attribute__((aligned(16))) _Float16 s_v[];   // [ATT_SP][ROW_HALVES]; first holds q
   __shared__ __attribute__((aligned(16))) _Float16 s_p[16 * P_STRIDE];   // P: [16 heads][64 positions]
@@ -307,7 +345,7 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
       mb = max(mb, max(max(__float_as_uint(v[u].x) & 0x7fffffffu, __float_as_uint(v[u].y) & 0x7fffffffu),
                        max(__float_as_uint(v[u].z) & 0x7fffffffu, __float_as_uint(v[u].w) & 0x7fffffffu)));
       f16x2 lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
-      *reinterpret_cast<u32x2 *>(s_v + (e >> 7) * ROW_HALVES + 4 * (e & 127)) =
+      *reinterpret_cast<u32x2 *>(s_v + row_chunk(e >> 7, (e & 127) >> 1) + 4 * (e & 1)) =
           u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
     }
     // no fp16 value for |q| >= 65520 (or NaN/Inf): flag it
@@ -315,9 +353,8 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     CSA2_TS(26);
     __syncthreads();
     CSA2_TS(27);
-    const _Float16 *qrow = s_v + n16 * ROW_HALVES + 8 * g;
 #pragma unroll
-    for (int kc = 0; kc < 16; ++kc) qop[kc] = *reinterpret_cast<const f16x8 *>(qrow + 32 * kc);
+    for (int kc = 0; kc < 16; ++kc) qop[kc] = *reinterpret_cast<const f16x8 *>(s_v + k_offset(n16, kc, g));
   }
 
   const int64_t n = clamp_len(a.seq_len[b] + a.len_add, a.limit);
@@ -331,9 +368,8 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
 
   // V^T operand: rows (k) of chunk kk are positions 32*kk + 4g + 0..3 then
   // 32*kk + 16 + 4g + 0..3; source lane s = 4r + q points at row k0 + r,
-  // channel n0 + 32q, so row m of O^T tile ct holds channel
-  // 128*(ct/8) + 4*(ct%8) + 32*(m/4) + m%4 (4 lanes of a group read 8 bytes
-  // 64 bytes apart: no LDS bank conflict).
+  // channels 4 * (q & 1) .. +3 of chunk tile_chunk(ct) ^ (8 * (q >> 1)), so
+  // row m of O^T tile ct holds channel 8 * (tile_chunk(ct) ^ (8 * (m / 8))) + m % 8.
   const int r_src = n16 >> 2, q_src = n16 & 3;
 
 #pragma unroll 1
@@ -348,7 +384,6 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
         const int pp = (tid >> 4) + 16 * k;
         if (!okv[k]) { wr[k] = u32x4{0u, 0u, 0u, 0u}; wr2[k] = wr[k]; }   // masked: finite zeros
         const float sc = okv[k] ? __uint_as_float(scr[k]) : 0.f;
-        u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i16);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const u32x4 w = h ? wr2[k] : wr[k];
@@ -362,8 +397,8 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
             o[2 * dw] = __builtin_bit_cast(uint32_t, a0);
             o[2 * dw + 1] = __builtin_bit_cast(uint32_t, a1);
           }
-          dst[2 * h] = u32x4{o[0], o[1], o[2], o[3]};
-          dst[2 * h + 1] = u32x4{o[4], o[5], o[6], o[7]};
+          *reinterpret_cast<u32x4 *>(s_v + row_chunk(pp, 4 * i16 + 2 * h)) = u32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<u32x4 *>(s_v + row_chunk(pp, 4 * i16 + 2 * h + 1)) = u32x4{o[4], o[5], o[6], o[7]};
         }
         if (i16 == 0) s_ok[pp] = okv[k] ? 1 : 0;
       }
@@ -379,7 +414,6 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
       const _Float16 s0 = (_Float16)e4m3_to_f32(scr[k] & 0xffu);
       const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
       const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
-      u32x4 *dst = reinterpret_cast<u32x4 *>(s_v + pp * ROW_HALVES + 32 * i16);
       const u32x4 wrot = rotate4(wr[k], rot);
       // chunk (s + rot) & 3 takes scale 1 when it is 2 or 3
       const f16x2 svr[4] = {rhi0 ? sv1 : sv0, rhi1 ? sv1 : sv0, rhi0 ? sv0 : sv1, rhi1 ? sv0 : sv1};
@@ -392,8 +426,9 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
         f16x2 h1 = e2m1x2_to_f16<1>(w) * sv;
         f16x2 h2 = e2m1x2_to_f16<2>(w) * sv;
         f16x2 h3 = e2m1x2_to_f16<3>(w) * sv;
-        dst[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
-                        __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
+        *reinterpret_cast<u32x4 *>(s_v + row_chunk(pp, 4 * i16 + dw)) =
+            u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                  __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
       }
       if (i16 == 0) s_ok[pp] = okv[k] ? 1 : 0;
     }
@@ -412,10 +447,9 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
     // ---- S^T for positions 16*wv .. 16*wv+15 ----
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
     {
-      const _Float16 *krow = s_v + (16 * wv + n16) * ROW_HALVES + 8 * g;
 #pragma unroll
       for (int kc = 0; kc < 16; ++kc) {
-        f16x8 kop = *reinterpret_cast<const f16x8 *>(krow + 32 * kc);
+        f16x8 kop = *reinterpret_cast<const f16x8 *>(s_v + k_offset(16 * wv + n16, kc, g));
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kc], sacc, 0, 0, 0);
       }
     }
@@ -468,16 +502,15 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
       const u32x2 p_lo = *reinterpret_cast<const u32x2 *>(s_p + n16 * P_STRIDE + base + 4 * g);
       const u32x2 p_hi = *reinterpret_cast<const u32x2 *>(s_p + n16 * P_STRIDE + base + 16 + 4 * g);
       const f16x8 pop = __builtin_bit_cast(f16x8, u32x4{p_lo[0], p_lo[1], p_hi[0], p_hi[1]});
-      const _Float16 *v0 = s_v + (base + 4 * g + r_src) * ROW_HALVES + 32 * q_src;
-      const _Float16 *v1 = v0 + 16 * ROW_HALVES;
+      const int vrow = base + 4 * g + r_src;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int ct = 8 * wv + t;
-        const int n0 = 128 * (ct >> 3) + 4 * (ct & 7);
+        const _Float16 *v0 = s_v + vt_offset(vrow, ct, q_src);
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(v0 + n0));
+            (__attribute__((address_space(3))) i16x4 *)(v0));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(v1 + n0));
+            (__attribute__((address_space(3))) i16x4 *)(v0 + 16 * ROW_HALVES));
         f16x8 vop = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, acc[t], 0, 0, 0);
       }
@@ -487,13 +520,13 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_partial_kernel(AttendArgs 
   CSA2_TS(4);
   if (a.splits == 1) {
     // one workgroup holds the whole softmax of its heads: normalise here.
-    // lane (n16, g) of tile ct holds channels 128*(ct/8) + 4*(ct%8) + 32*g + 0..3
+    // lane (n16, g) of tile ct holds channels tile_channel(ct, g) + 0..3
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float *orow = a.out + ((int64_t)b * a.heads + 16 * ht + n16) * D + 32 * g;
+    float *orow = a.out + ((int64_t)b * a.heads + 16 * ht + n16) * D;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int ct = 8 * wv + t;
-      *reinterpret_cast<float4 *>(orow + 128 * (ct >> 3) + 4 * (ct & 7)) =
+      *reinterpret_cast<float4 *>(orow + tile_channel(ct, g)) =
           float4{acc[t][0] * inv, acc[t][1] * inv, acc[t][2] * inv, acc[t][3] * inv};
     }
     CSA2_TS(5);
@@ -606,15 +639,15 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
       mb = max(mb, max(max(__float_as_uint(v[u].x) & 0x7fffffffu, __float_as_uint(v[u].y) & 0x7fffffffu),
                        max(__float_as_uint(v[u].z) & 0x7fffffffu, __float_as_uint(v[u].w) & 0x7fffffffu)));
       f16x2 lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
-      *reinterpret_cast<u32x2 *>(s_v + (e >> 7) * ROW_HALVES + 4 * (e & 127)) =
+      *reinterpret_cast<u32x2 *>(s_v + row_chunk(e >> 7, (e & 127) >> 1) + 4 * (e & 1)) =
           u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
     }
     // no fp16 value for |q| >= 65520 (or NaN/Inf): flag it
     if (__builtin_amdgcn_ballot_w64(mb >= 0x477ff000u) && lane == 0) raise_flag(FLAG_Q_RANGE);
     __syncthreads();
-    const _Float16 *qrow = s_v + (16 * ht + n16) * ROW_HALVES + 8 * g;
 #pragma unroll
-    for (int kc = 0; kc < 16; ++kc) qop[kc] = *reinterpret_cast<const f16x8 *>(qrow + 32 * kc);
+    for (int kc = 0; kc < 16; ++kc)
+      qop[kc] = *reinterpret_cast<const f16x8 *>(s_v + k_offset(16 * ht + n16, kc, g));
   }
 
   const int64_t n = clamp_len(a.seq_len[b] + a.len_add, a.limit);
@@ -635,7 +668,6 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
       const _Float16 s0 = (_Float16)e4m3_to_f32(scr[k] & 0xffu);
       const _Float16 s1 = (_Float16)e4m3_to_f32(scr[k] >> 8);
       const f16x2 sv0 = {s0, s0}, sv1 = {s1, s1};
-      u32x4 *dst = reinterpret_cast<u32x4 *>(sv + pp * ROW_HALVES + 32 * i16);
       const u32x4 wrot = rotate4(wr[k], rot);
       const f16x2 svr[4] = {rhi0 ? sv1 : sv0, rhi1 ? sv1 : sv0, rhi0 ? sv0 : sv1, rhi1 ? sv0 : sv1};
 #pragma unroll
@@ -647,8 +679,9 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
         f16x2 h1 = e2m1x2_to_f16<1>(w) * svs;
         f16x2 h2 = e2m1x2_to_f16<2>(w) * svs;
         f16x2 h3 = e2m1x2_to_f16<3>(w) * svs;
-        dst[dw] = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
-                        __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
+        *reinterpret_cast<u32x4 *>(sv + row_chunk(pp, 4 * i16 + dw)) =
+            u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                  __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
       }
       if (i16 == 0) s_ok[buf][pp] = ok ? 1 : 0;
     }
@@ -684,8 +717,7 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
     for (int kc = 0; kc < 16; ++kc) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const f16x8 kop = *reinterpret_cast<const f16x8 *>(
-            sv + (32 * ph + 16 * u + n16) * ROW_HALVES + 8 * g + 32 * kc);
+        const f16x8 kop = *reinterpret_cast<const f16x8 *>(sv + k_offset(32 * ph + 16 * u + n16, kc, g));
         sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kc], sacc[u], 0, 0, 0);
       }
     }
@@ -753,16 +785,15 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
         const u32x2 p_hi = *reinterpret_cast<const u32x2 *>(pr + 16);
         pop[h] = __builtin_bit_cast(f16x8, u32x4{p_lo[0], p_lo[1], p_hi[0], p_hi[1]});
       }
-      const _Float16 *v0 = sv + (base + 4 * g + r_src) * ROW_HALVES + 32 * q_src;
-      const _Float16 *v1 = v0 + 16 * ROW_HALVES;
+      const int vrow = base + 4 * g + r_src;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int ct = 4 * wv + t;
-        const int n0 = 128 * (ct >> 3) + 4 * (ct & 7);
+        const _Float16 *v0 = sv + vt_offset(vrow, ct, q_src);
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(v0 + n0));
+            (__attribute__((address_space(3))) i16x4 *)(v0));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(v1 + n0));
+            (__attribute__((address_space(3))) i16x4 *)(v0 + 16 * ROW_HALVES));
         f16x8 vop = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int h = 0; h < 4; ++h)
@@ -781,11 +812,11 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
     for (int h = 0; h < 4; ++h) {
       const float l = s_fin[0][16 * h + n16] + s_fin[1][16 * h + n16];
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      float *orow = a.out + ((int64_t)b * 64 + 16 * h + n16) * D + 32 * g;
+      float *orow = a.out + ((int64_t)b * 64 + 16 * h + n16) * D;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int ct = 4 * wv + t;
-        *reinterpret_cast<float4 *>(orow + 128 * (ct >> 3) + 4 * (ct & 7)) =
+        *reinterpret_cast<float4 *>(orow + tile_channel(ct, g)) =
             float4{acc[h][t][0] * inv, acc[h][t][1] * inv, acc[h][t][2] * inv, acc[h][t][3] * inv};
       }
     }
@@ -914,8 +945,8 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_kernel(CombineArgs a) 
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
-  // lane (n16, g) of tile ct holds channels 128*(ct/8) + 4*(ct%8) + 32*g + 0..3
-  const int c0 = 128 * (ct >> 3) + 4 * (ct & 7) + 32 * g;
+  // lane (n16, g) of tile ct holds channels tile_channel(ct, g) + 0..3
+  const int c0 = tile_channel(ct, g);
   *reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.heads + 16 * ht + n16) * D + c0) = o;
   CSA2_TS(10);
 }
@@ -988,8 +1019,8 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_regs_kernel(CombineArg
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
-  // lane (n16, g) of tile ct holds channels 128*(ct/8) + 4*(ct%8) + 32*g + 0..3
-  const int c0 = 128 * (ct >> 3) + 4 * (ct & 7) + 32 * g;
+  // lane (n16, g) of tile ct holds channels tile_channel(ct, g) + 0..3
+  const int c0 = tile_channel(ct, g);
   *reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.heads + 16 * ht + n16) * D + c0) = o;
   CSA2_TS(10);
 }
