@@ -46,7 +46,17 @@ namespace csa2 {
 constexpr int ATT_THREADS = 256;
 constexpr int ATT_SP = 64;                        // gathered positions per stage
 constexpr int ROW_HALVES = D;                     // LDS row stride: 1,024 bytes (swizzled chunks)
-constexpr int P_STRIDE = ATT_SP + 8;              // LDS P row stride (halves): no bank conflicts
+
+// P (fp16, heads x the stage's 64 positions) in LDS, laid out as the P.V
+// matrix operand is read: lane (n16, g) of position chunk kk takes the 8
+// values of positions 32 kk + 4 g + 0..3 and 32 kk + 16 + 4 g + 0..3 of
+// head 16 * tile + n16, stored as one 16-byte vector, and the 16 heads of a
+// (kk, g, tile) fill one 256-byte block: one conflict-free 128-bit read per
+// operand (two 64-bit reads 32 or 144 bytes apart took twice as long).
+// Returns the element offset (halves) of position pos of head 16 * tile + n16.
+__device__ __forceinline__ int p_offset(int tile, int ntiles, int n16, int pos) {
+  return ((((pos >> 5) * 4 + ((pos >> 2) & 3)) * ntiles + tile) * 16 + n16) * 8 + 4 * ((pos >> 4) & 1) + (pos & 3);
+}
 
 // LDS rows of a stage (and the staged query) are 64 chunks of 8 channels
 // (16 bytes); chunk c of row p sits at chunk slot (c & ~15) | ((c ^ p) & 15)
@@ -174,7 +184,7 @@ template <bool SELECT, bool WIN>
 __global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))) attend_partial_kernel(AttendArgs a) {
   // 16-byte aligned: rows are read and written as 128-bit vectors
   extern __shared__ __attribute__((aligned(16))) _Float16 s_v[];   // [ATT_SP][ROW_HALVES]; first holds q
-  __shared__ __attribute__((aligned(16))) _Float16 s_p[16 * P_STRIDE];   // P: [16 heads][64 positions]
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[16 * ATT_SP];   // P of 16 heads (p_offset)
   __shared__ float s_max[4][16], s_sum[4][16];
   __shared__ uint8_t s_ok[ATT_SP];
   __shared__ int32_t s_sel[SELECT ? CSA2_TOPK_MAX + SEL_PAD : 1];   // in-kernel selection
@@ -480,7 +490,7 @@ __global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_e
         psum += (float)ph[r];
       }
     }
-    *reinterpret_cast<u32x2 *>(s_p + n16 * P_STRIDE + 16 * wv + 4 * g) =
+    *reinterpret_cast<u32x2 *>(s_p + p_offset(0, 1, n16, 16 * wv + 4 * g)) =
         u32x2{__builtin_bit_cast(uint32_t, f16x2{ph[0], ph[1]}),
               __builtin_bit_cast(uint32_t, f16x2{ph[2], ph[3]})};
     psum += __shfl_xor(psum, 16);
@@ -499,9 +509,7 @@ __global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int base = 32 * kk;
-      const u32x2 p_lo = *reinterpret_cast<const u32x2 *>(s_p + n16 * P_STRIDE + base + 4 * g);
-      const u32x2 p_hi = *reinterpret_cast<const u32x2 *>(s_p + n16 * P_STRIDE + base + 16 + 4 * g);
-      const f16x8 pop = __builtin_bit_cast(f16x8, u32x4{p_lo[0], p_lo[1], p_hi[0], p_hi[1]});
+      const f16x8 pop = *reinterpret_cast<const f16x8 *>(s_p + p_offset(0, 1, n16, base + 4 * g));
       const int vrow = base + 4 * g + r_src;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -575,7 +583,7 @@ constexpr size_t ATT64_LDS = (size_t)2 * ATT_SP * ROW_HALVES * sizeof(_Float16);
 __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
   // 16-byte aligned: rows are read and written as 128-bit vectors
   extern __shared__ __attribute__((aligned(16))) _Float16 s_v[];   // [2][ATT_SP][ROW_HALVES]; first holds q (64 heads)
-  __shared__ __attribute__((aligned(16))) _Float16 s_p[64 * P_STRIDE];   // P: [64 heads][64 positions]
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[64 * ATT_SP];   // P of 64 heads (p_offset)
   __shared__ float s_max[2][64], s_corr[64], s_fin[2][64];
   __shared__ uint8_t s_ok[2][ATT_SP];
 
@@ -738,11 +746,9 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
     __syncthreads();
     const float m_new = fmaxf(m_run, fmaxf(s_max[0][16 * ht + n16], s_max[1][16 * ht + n16]));
     float psum = 0.f, corr = 1.f;
-    _Float16 *prow = s_p + (16 * ht + n16) * P_STRIDE + 32 * ph + 4 * g;
-    if (m_new == -__builtin_huge_valf()) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x2 *>(prow + 16 * u) = u32x2{0u, 0u};
-    } else {
+    // positions 32 ph + 16 u + 4 g + 0..3 (u = 0, 1): one 16-byte P vector
+    u32x4 pw = {0u, 0u, 0u, 0u};
+    if (m_new != -__builtin_huge_valf()) {
       corr = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -752,11 +758,11 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
           pv[r] = (_Float16)__builtin_amdgcn_exp2f(sacc[u][r] - m_new);
           psum += (float)pv[r];
         }
-        *reinterpret_cast<u32x2 *>(prow + 16 * u) =
-            u32x2{__builtin_bit_cast(uint32_t, f16x2{pv[0], pv[1]}),
-                  __builtin_bit_cast(uint32_t, f16x2{pv[2], pv[3]})};
+        pw[2 * u] = __builtin_bit_cast(uint32_t, f16x2{pv[0], pv[1]});
+        pw[2 * u + 1] = __builtin_bit_cast(uint32_t, f16x2{pv[2], pv[3]});
       }
     }
+    *reinterpret_cast<u32x4 *>(s_p + p_offset(ht, 4, n16, 32 * ph + 4 * g)) = pw;
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
     l_run = l_run * corr + psum;
@@ -779,12 +785,7 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
       const int base = 32 * kk;
       f16x8 pop[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const _Float16 *pr = s_p + (16 * h + n16) * P_STRIDE + base + 4 * g;
-        const u32x2 p_lo = *reinterpret_cast<const u32x2 *>(pr);
-        const u32x2 p_hi = *reinterpret_cast<const u32x2 *>(pr + 16);
-        pop[h] = __builtin_bit_cast(f16x8, u32x4{p_lo[0], p_lo[1], p_hi[0], p_hi[1]});
-      }
+      for (int h = 0; h < 4; ++h) pop[h] = *reinterpret_cast<const f16x8 *>(s_p + p_offset(h, 4, n16, base + 4 * g));
       const int vrow = base + 4 * g + r_src;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
