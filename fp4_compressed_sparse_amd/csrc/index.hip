@@ -66,11 +66,21 @@ struct ScanArgs {
                             // or NULL (computed in-kernel)
 };
 
+// Qbar in LDS for the 32-lane scorers: channel 16 j + 4 k + e (group j,
+// quarter k) at float 256 (j >> 4) + 64 k + 4 (j & 15) + e, so that when
+// lane j reads quarter k of its group (a 128-bit read), 16 lanes hit 16
+// distinct 16-byte slots of one 256-byte window (in channel order, lanes 64
+// bytes apart met four to a slot and the read took four times as long).
+__device__ __forceinline__ int qbar32_index(int c) {
+  return 256 * (c >> 8) + 64 * ((c >> 2) & 3) + 4 * ((c >> 4) & 15) + (c & 3);
+}
+__device__ __forceinline__ int qbar32_base(int j) { return 256 * (j >> 4) + 4 * (j & 15); }
+
 // Qbar of sequence b into LDS; all 256 threads call.  Each thread owns two
 // channels and adds the heads in order; the loads of HB heads are issued
 // together so the sum costs heads/HB memory round trips, not one per head
 // (HB = 16 keeps the scan's register budget; the pool rescoring uses 64).
-template <int HB>
+template <int HB, bool QB32 = false>
 __device__ __forceinline__ void compute_qbar(const float *__restrict__ q, int heads, int b,
                                              float *s_qbar) {
   const int t = threadIdx.x;
@@ -95,7 +105,10 @@ __device__ __forceinline__ void compute_qbar(const float *__restrict__ q, int he
     }
   }
   if (!(__builtin_isfinite(acc.x) && __builtin_isfinite(acc.y))) raise_flag(FLAG_NONFINITE_Q);
-  reinterpret_cast<float2 *>(s_qbar)[t] = acc;
+  if (QB32)
+    *reinterpret_cast<float2 *>(s_qbar + qbar32_index(2 * t)) = acc;   // QB32: the 32-lane scorers' layout
+  else
+    reinterpret_cast<float2 *>(s_qbar)[t] = acc;
   __syncthreads();
 }
 
@@ -199,7 +212,8 @@ __device__ __forceinline__ void load_block32(BlockRows32 &r, const uint8_t *__re
   }
 }
 
-// cnt: rows present (1..8); qb: Qbar[16j..16j+15] (LDS).  RELOAD: as each
+// cnt: rows present (1..8); qb: s_qbar + qbar32_base(j), so that channel
+// 16 j + c is qb[64 * (c >> 2) + (c & 3)] (LDS).  RELOAD: as each
 // row is consumed its registers receive the same row of the block at (nrow,
 // nsrow), so the next block's loads are in flight while this one is scored.
 template <bool RELOAD = true>
@@ -239,11 +253,11 @@ __device__ __forceinline__ float block_score32(BlockRows32 &r, int cnt, const fl
   if (cnt == BLOCK) {
     g = qb[0] * (S[0] * 0.125f);
 #pragma unroll
-    for (int c = 1; c < 16; ++c) g = g + qb[c] * (S[c] * 0.125f);
+    for (int c = 1; c < 16; ++c) g = g + qb[64 * (c >> 2) + (c & 3)] * (S[c] * 0.125f);
   } else {
     const float fc = (float)cnt;
     g = qb[0] * __fdiv_rn(S[0], fc);
-    for (int c = 1; c < 16; ++c) g = g + qb[c] * __fdiv_rn(S[c], fc);
+    for (int c = 1; c < 16; ++c) g = g + qb[64 * (c >> 2) + (c & 3)] * __fdiv_rn(S[c], fc);
   }
   g = g + __shfl_xor(g, 1);             // tree level 1: groups 2k, 2k+1
   g = g + __shfl_xor(g, 2);
@@ -362,7 +376,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) qbar_kernel(const float *__restr
 // registers) did not help either (57.9 against 56.6 us at 1M, cold).
 template <bool HIST>
 __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(6))) scan_kernel(ScanArgs a) {
-  __shared__ float s_qbar[D];
+  __shared__ __attribute__((aligned(16))) float s_qbar[D];   // qbar32_index layout
   __shared__ uint32_t s_hist[HIST ? HIST_BINS : 1];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;
@@ -415,10 +429,10 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
     __builtin_amdgcn_sched_barrier(0);
     n = clamp_len(seq, a.limit);
     nblk = (n + BLOCK - 1) / BLOCK;
-    reinterpret_cast<float2 *>(s_qbar)[threadIdx.x] = qv;
+    *reinterpret_cast<float2 *>(s_qbar + qbar32_index(2 * threadIdx.x)) = qv;
     __syncthreads();
     CSA2_TS(1);
-    const float *qb = s_qbar + 16 * j;
+    const float *qb = s_qbar + qbar32_base(j);
     while (c < nchunks) {
       const int64_t blk = 2 * c + half;
       const int64_t cn = first + grp + (int64_t)ngrp * __builtin_amdgcn_readlane(pending, 0);
@@ -450,14 +464,14 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
     n = clamp_len(a.seq_len[b], a.limit);
     nblk = (n + BLOCK - 1) / BLOCK;
     if (a.qbar) {
-      reinterpret_cast<float2 *>(s_qbar)[threadIdx.x] =
+      *reinterpret_cast<float2 *>(s_qbar + qbar32_index(2 * threadIdx.x)) =
           reinterpret_cast<const float2 *>(a.qbar + (int64_t)b * D)[threadIdx.x];
       __syncthreads();
     } else {
-      compute_qbar<16>(a.q, a.heads, b, s_qbar);
+      compute_qbar<16, true>(a.q, a.heads, b, s_qbar);
     }
     CSA2_TS(1);
-    const float *qb = s_qbar + 16 * j;
+    const float *qb = s_qbar + qbar32_base(j);
     for (; c < nchunks; c += step) {
       const int64_t blk = 2 * c + half;
       int64_t nb = 2 * (c + step) + half;
@@ -510,7 +524,7 @@ constexpr int SCAN_FLAT_MAXB = 512;     // sequences whose chunk prefix fits in 
 // by the host), so chunk indices are 32-bit.
 __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(5)))
 scan_flat_kernel(ScanArgs a, int32_t batch) {
-  __shared__ float s_qbar[4][D];                   // per wave
+  __shared__ __attribute__((aligned(16))) float s_qbar[4][D];   // per wave, qbar32_index layout
   __shared__ int32_t s_pre[SCAN_FLAT_MAXB + 1];    // chunks before sequence b
   __shared__ int64_t s_len[SCAN_FLAT_MAXB];        // clamped lengths
   __shared__ uint32_t s_wave[16];
@@ -599,11 +613,11 @@ scan_flat_kernel(ScanArgs a, int32_t batch) {
   while (c < r1) {
     if (cb != qb_seq) {
       if (qb_seq >= 0) flush(qb_seq);
-      // this wave's Qbar: 8 floats per lane (wave-local LDS, in order)
+      // this wave's Qbar: 8 floats per lane (wave-local LDS, qbar32_index layout)
       const float4 *src = reinterpret_cast<const float4 *>(a.qbar + (int64_t)cb * D);
       const float4 v0 = src[2 * lane], v1 = src[2 * lane + 1];
-      reinterpret_cast<float4 *>(qbw)[2 * lane] = v0;
-      reinterpret_cast<float4 *>(qbw)[2 * lane + 1] = v1;
+      *reinterpret_cast<float4 *>(qbw + qbar32_index(8 * lane)) = v0;
+      *reinterpret_cast<float4 *>(qbw + qbar32_index(8 * lane + 4)) = v1;
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
       qb_seq = cb;
@@ -619,7 +633,7 @@ scan_flat_kernel(ScanArgs a, int32_t batch) {
     const int64_t nrow = rows_of(cn, nbq, blk_next);
     const bool valid = (int64_t)blk * BLOCK < n;
     const int cnt = (int)max((int64_t)1, min((int64_t)BLOCK, n - (int64_t)blk * BLOCK));
-    const float sc = block_score32(cur, cnt, qbw + 16 * j, a.codes + nrow * CODE_BYTES,
+    const float sc = block_score32(cur, cnt, qbw + qbar32_base(j), a.codes + nrow * CODE_BYTES,
                                    a.scales + nrow * SCALE_BYTES, j);
     if (j == 0 && valid) {
       a.scores[(int64_t)cb * a.score_stride + blk] = sc;
@@ -1811,7 +1825,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
 constexpr int RESCORE32_THREADS = 512;
 constexpr int RESCORE32_BLOCKS = RESCORE32_THREADS / 32;   // blocks per round
 __global__ void __launch_bounds__(RESCORE32_THREADS) rescore32_kernel(RescoreArgs a) {
-  __shared__ float s_qbar[D];
+  __shared__ __attribute__((aligned(16))) float s_qbar[D];   // qbar32_index layout
   const int b = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int half = lane >> 5, j = lane & 31;
@@ -1861,14 +1875,14 @@ __global__ void __launch_bounds__(RESCORE32_THREADS) rescore32_kernel(RescoreArg
       }
     }
     if (!__builtin_isfinite(acc)) raise_flag(FLAG_NONFINITE_Q);
-    s_qbar[t] = acc;
+    s_qbar[qbar32_index(t)] = acc;
   }
   __syncthreads();
   // the length only masks: read after the first rows and the query sum
   const int64_t n = clamp_len(a.seq_len[b], a.limit);
   const int64_t nblk = (n + BLOCK - 1) / BLOCK;
   CSA2_TS(1);
-  const float *qb = s_qbar + 16 * j;
+  const float *qb = s_qbar + qbar32_base(j);
   for (; it < iters; it += gridDim.x) {
     const bool more = it + (int)gridDim.x < iters;              // uniform
     const int64_t nb = rows_of(blk1);
