@@ -567,30 +567,36 @@ template __global__ void attend_partial_kernel<true, true>(AttendArgs);
 //
 // Many queries, each with its own selection: one workgroup takes one query
 // and a range of stages for all four 16-head tiles, so a gathered row is
-// dequantised once for 64 heads (the kernel above dequantises it once per
-// tile, and the FP4 convert then outweighs the matrix work).  Eight waves,
-// two per SIMD: wave w computes S^T = K Q^T for head tile w%4 over
-// positions 32*(w/4)..+31 of the stage (its 16 query rows stay in registers
-// as fp16; K fragments come from LDS); the two halves of a head exchange
-// their stage maxima through LDS and keep their own partial sums; P of all
-// 64 heads and each head's rescale factor go through LDS, and wave w then
-// accumulates O^T channel tiles 4w..4w+3 of all four head tiles (each V^T
-// fragment read once, used for the four tiles).  The stage rows are double
-// buffered: the next stage is dequantised right after this stage's S
-// matrix instructions are issued, so the convert overlaps them.
+// dequantised once for 64 heads.  Eight waves in two roles, one of each per
+// SIMD, so that one role's matrix instructions run beside the other's vector
+// work:
+//  * producer wave w < 4 (head tile w): S^T = K Q^T of its 16 heads over
+//    all 64 positions of the stage (its query rows in registers as fp16,
+//    K fragments from LDS), masked and scaled, to LDS; then it dequantises
+//    a quarter of the next stage's rows into the other stage buffer and
+//    requests the rows of the stage after;
+//  * consumer wave 4 + w (head tile w): the online softmax of its 16 heads
+//    over the stage (the S values a lane reads are exactly the P.V operand
+//    it needs, so P stays in registers) and O^T for all 32 channel tiles,
+//    V^T read with the transposing read.
+// Two workgroup barriers per stage: stage ready (and the S buffer free),
+// then S ready.  The consumers' P.V and the producers' dequantisation of the
+// next stage overlap.
 constexpr int ATT64_THREADS = 512;
 constexpr size_t ATT64_LDS = (size_t)2 * ATT_SP * ROW_HALVES * sizeof(_Float16);
 __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
   // 16-byte aligned: rows are read and written as 128-bit vectors
   extern __shared__ __attribute__((aligned(16))) _Float16 s_v[];   // [2][ATT_SP][ROW_HALVES]; first holds q (64 heads)
-  __shared__ __attribute__((aligned(16))) _Float16 s_p[64 * ATT_SP];   // P of 64 heads (p_offset)
-  __shared__ float s_max[2][64], s_corr[64], s_fin[2][64];
+  // S of the stage: [head tile][position tile u][lane][4], in the matrix
+  // accumulator's lane order (lane (n16, g): head n16, positions 16 u + 4 g + 0..3)
+  __shared__ __attribute__((aligned(16))) float s_s[4 * 4 * 64 * 4];
   __shared__ uint8_t s_ok[2][ATT_SP];
 
   const int b = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;
-  const int ht = wv & 3, ph = wv >> 2;            // S: head tile, position half
+  const bool producer = wv < 4;                   // wave-uniform role
+  const int ht = wv & 3;                          // the wave's head tile
   const int64_t cap_blocks = a.capacity / BLOCK;
   const int32_t *idx = a.idx + (int64_t)b * a.topk;
   const uint8_t *codes = a.codes + (int64_t)b * a.seq_stride * CODE_BYTES;
@@ -599,7 +605,8 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
   const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
   const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
 
-  constexpr int PASSES = ATT_SP / 32;     // rows per thread per stage
+  // producers: rows (tid >> 4) + 16 k of a stage, 16 code bytes each
+  constexpr int PASSES = ATT_SP / 16;
   const int i16 = tid & 15;
   const int rot = chunk_rot(i16);
   const bool rhi0 = (rot & 2) != 0, rhi1 = ((rot + 1) & 2) != 0;   // chunk rot, rot + 1 (mod 4) >= 2
@@ -609,28 +616,32 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
   auto fetch_ids_into = [&](int st, int32_t (&dst)[PASSES]) {
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      const int j = st * ATT_SP + (tid >> 4) + 32 * k;
+      const int j = st * ATT_SP + (tid >> 4) + 16 * k;
       dst[k] = idx[min(j, total_pos - 1) >> 3];
     }
   };
   auto fetch_rows = [&](int st) {
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      if (st * ATT_SP + (tid >> 4) + 32 * k >= total_pos) blkv[k] = -1;
+      if (st * ATT_SP + (tid >> 4) + 16 * k >= total_pos) blkv[k] = -1;
       const bool ok = blkv[k] >= 0 && blkv[k] < cap_blocks;
-      const int64_t pos = ok ? (int64_t)blkv[k] * BLOCK + (((tid >> 4) + 32 * k) & 7) : 0;
+      const int64_t pos = ok ? (int64_t)blkv[k] * BLOCK + (((tid >> 4) + 16 * k) & 7) : 0;
       wr[k] = *reinterpret_cast<const u32x4 *>(codes + pos * CODE_BYTES + 16 * i16);
       scr[k] = *reinterpret_cast<const uint16_t *>(scales + pos * SCALE_BYTES + 2 * i16);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   CSA2_TS(0);
-  fetch_ids_into(st0, blkv);
+  if (producer) fetch_ids_into(st0, blkv);
   __builtin_amdgcn_sched_barrier(0);
 
+  // One register array serves both roles (a wave uses one branch only, but
+  // the compiler allocates for both): a consumer's O^T accumulators, tiles
+  // 0..31; a producer's query operand, 16 steps of 8 channels as fp16
+  // (reg[kc], bit-cast).
+  f32x4 reg[32];
   // ---- the query's 64 x 512 tile -> fp16 in LDS (one batch of 16 float4
-  // per thread), then wave w's 16 rows of head tile w%4 into registers
-  f16x8 qop[16];
+  // per thread), then each producer's 16 rows of its head tile into registers
   {
     constexpr int NV = 16;
     const float4 *src = reinterpret_cast<const float4 *>(a.q + (int64_t)b * 64 * D);
@@ -638,8 +649,10 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) v[u] = src[tid + u * ATT64_THREADS];
     __builtin_amdgcn_sched_barrier(0);
-    fetch_rows(st0);
-    if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);
+    if (producer) {
+      fetch_rows(st0);
+      if (st0 + 1 < st1) fetch_ids_into(st0 + 1, nxt);
+    }
     uint32_t mb = 0;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -654,20 +667,25 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
     if (__builtin_amdgcn_ballot_w64(mb >= 0x477ff000u) && lane == 0) raise_flag(FLAG_Q_RANGE);
     __syncthreads();
 #pragma unroll
-    for (int kc = 0; kc < 16; ++kc)
-      qop[kc] = *reinterpret_cast<const f16x8 *>(s_v + k_offset(16 * ht + n16, kc, g));
+    for (int t = 0; t < 32; ++t) reg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (producer) {
+#pragma unroll
+      for (int kc = 0; kc < 16; ++kc)
+        reg[kc] = *reinterpret_cast<const f32x4 *>(s_v + k_offset(16 * ht + n16, kc, g));
+    }
   }
 
   const int64_t n = clamp_len(a.seq_len[b] + a.len_add, a.limit);
   const int64_t nblk = (n + BLOCK - 1) / BLOCK;
 
-  // dequantise stage st (its rows are in wr/scr) into buffer `buf`, then
-  // request the rows of stage st + 1 (ids in nxt) and the ids of st + 2
+  // producers: dequantise stage st (its rows are in wr/scr) into buffer
+  // `buf`, then request the rows of stage st + 1 (ids in nxt) and the ids of
+  // st + 2
   auto dequant_and_fetch = [&](int st, int buf) {
     _Float16 *sv = s_v + buf * (ATT_SP * ROW_HALVES);
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      const int pp = (tid >> 4) + 32 * k;
+      const int pp = (tid >> 4) + 16 * k;
       const int j = st * ATT_SP + pp;
       const int32_t blk = blkv[k];
       if ((j & 7) == 0 && i16 == 0 && blk >= nblk) raise_flag(FLAG_BAD_INDEX);
@@ -700,145 +718,161 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
       if (st + 2 < st1) fetch_ids_into(st + 2, nxt);
     }
   };
-  __syncthreads();                        // every wave has its query rows: buffer 0 is free
-  dequant_and_fetch(st0, 0);
+  __syncthreads();                        // the producers hold their query rows: buffer 0 is free
+  if (producer) dequant_and_fetch(st0, 0);
 
   CSA2_TS(1);
-  f32x4 acc[4][4];                        // [head tile][O^T tile 4*wv + t]
-#pragma unroll
-  for (int h = 0; h < 4; ++h)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_huge_valf();   // head 16*ht + n16 (log2 domain), same in both halves
-  float l_run = 0.f;                      // this half's share of the head's sum
+  f32x4 (&acc)[32] = reg;                 // consumers: O^T tiles 0..31 of head tile ht
+  float m_run = -__builtin_huge_valf();   // consumers: head 16*ht + n16 (log2 domain)
+  float l_run = 0.f;
   const int r_src = n16 >> 2, q_src = n16 & 3;
+  f32x4 *s_mine = reinterpret_cast<f32x4 *>(s_s) + (ht * 4) * 64 + lane;   // [u * 64]
 
 #pragma unroll 1
   for (int st = st0; st < st1; ++st) {
     const int cur = (st - st0) & 1;
     const _Float16 *sv = s_v + cur * (ATT_SP * ROW_HALVES);
-    __syncthreads();                      // stage st is in buffer cur; buffer cur^1 is free
+    __syncthreads();                      // stage st is in buffer cur; buffer cur^1 and s_s are free
     CSA2_TS(2);
-    // ---- S^T of head tile ht over position tiles 2*ph, 2*ph+1 ----
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (producer) {
+      // ---- S^T of head tile ht over the stage's 4 position tiles ----
+      // (the K fragments of step kc + 2 are requested before step kc's four
+      // matrix instructions; the scheduling barriers keep the register
+      // footprint to three steps)
+      f32x4 sacc[4];
 #pragma unroll
-    for (int kc = 0; kc < 16; ++kc) {
+      for (int u = 0; u < 4; ++u) sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f16x8 k0[4], k1[4], k2[4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const f16x8 kop = *reinterpret_cast<const f16x8 *>(sv + k_offset(32 * ph + 16 * u + n16, kc, g));
-        sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kc], sacc[u], 0, 0, 0);
+      for (int u = 0; u < 4; ++u) {
+        k0[u] = *reinterpret_cast<const f16x8 *>(sv + k_offset(16 * u + n16, 0, g));
+        k1[u] = *reinterpret_cast<const f16x8 *>(sv + k_offset(16 * u + n16, 1, g));
       }
-    }
-    // the next stage's rows, while the matrix instructions run
-    if (st + 1 < st1) dequant_and_fetch(st + 1, cur ^ 1);
-    // lane (head n16 of tile ht, group g) holds positions 32*ph + 16*u + 4g + r
-    float mx = -__builtin_huge_valf();
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int kc = 0; kc < 16; ++kc) {
+        if (kc + 2 < 16) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sacc[u][r] = s_ok[cur][32 * ph + 16 * u + 4 * g + r] ? sacc[u][r] * a.scale_log2 : -__builtin_huge_valf();
-        mx = fmaxf(mx, sacc[u][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (g == 0) s_max[ph][16 * ht + n16] = mx;
-    __syncthreads();
-    const float m_new = fmaxf(m_run, fmaxf(s_max[0][16 * ht + n16], s_max[1][16 * ht + n16]));
-    float psum = 0.f, corr = 1.f;
-    // positions 32 ph + 16 u + 4 g + 0..3 (u = 0, 1): one 16-byte P vector
-    u32x4 pw = {0u, 0u, 0u, 0u};
-    if (m_new != -__builtin_huge_valf()) {
-      corr = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        _Float16 pv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pv[r] = (_Float16)__builtin_amdgcn_exp2f(sacc[u][r] - m_new);
-          psum += (float)pv[r];
+          for (int u = 0; u < 4; ++u)
+            k2[u] = *reinterpret_cast<const f16x8 *>(sv + k_offset(16 * u + n16, kc + 2, g));
         }
-        pw[2 * u] = __builtin_bit_cast(uint32_t, f16x2{pv[0], pv[1]});
-        pw[2 * u + 1] = __builtin_bit_cast(uint32_t, f16x2{pv[2], pv[3]});
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0[u], __builtin_bit_cast(f16x8, reg[kc]), sacc[u], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { k0[u] = k1[u]; k1[u] = k2[u]; }
+      }
+      // lane (head n16, group g) holds positions 16 u + 4 g + r
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sacc[u][r] = s_ok[cur][16 * u + 4 * g + r] ? sacc[u][r] * a.scale_log2 : -__builtin_huge_valf();
+        s_mine[u * 64] = sacc[u];
       }
     }
-    *reinterpret_cast<u32x4 *>(s_p + p_offset(ht, 4, n16, 32 * ph + 4 * g)) = pw;
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-    if (g == 0 && ph == 0) s_corr[16 * ht + n16] = corr;
-    __syncthreads();
+    __syncthreads();                      // S of the stage is in s_s
     CSA2_TS(3);
-
-    // ---- O^T tiles 4*wv .. 4*wv+3 of the four head tiles ----
+    if (producer) {
+      // the next stage's rows, while the consumers run P.V
+      if (st + 1 < st1) dequant_and_fetch(st + 1, cur ^ 1);
+    } else {
+      // ---- online softmax of head 16*ht + n16 over the stage ----
+      f32x4 sl[4];
+      float mx = -__builtin_huge_valf();
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float c = s_corr[16 * h + n16];
-      if (c != 1.f) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[h][t] *= c;
+      for (int u = 0; u < 4; ++u) {
+        sl[u] = s_mine[u * 64];
+        mx = fmaxf(mx, fmaxf(fmaxf(sl[u][0], sl[u][1]), fmaxf(sl[u][2], sl[u][3])));
       }
-    }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // The reference moves only when the stage's max exceeds it by more
+      // than 8 (log2 domain), so P <= 256 (fp16-safe) and the 128
+      // accumulators are rescaled only on such jumps (with the exact running
+      // max they were rescaled almost every stage); the output and the
+      // partials are relative to the same reference, so the result is the
+      // same up to rounding.
+      const float m_new = mx > m_run + 8.f ? mx : m_run;
+      float psum = 0.f, corr = 1.f;
+      u32x4 pw[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+      if (m_new != -__builtin_huge_valf()) {
+        corr = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int base = 32 * kk;
-      f16x8 pop[4];
+        for (int u = 0; u < 4; ++u) {
+          _Float16 pv[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) pop[h] = *reinterpret_cast<const f16x8 *>(s_p + p_offset(h, 4, n16, base + 4 * g));
-      const int vrow = base + 4 * g + r_src;
+          for (int r = 0; r < 4; ++r) {
+            pv[r] = (_Float16)__builtin_amdgcn_exp2f(sl[u][r] - m_new);
+            psum += (float)pv[r];
+          }
+          // P.V operand of position chunk u / 2: positions 32 kk + 4 g + 0..3
+          // (tile 2 kk) then 32 kk + 16 + 4 g + 0..3 (tile 2 kk + 1)
+          pw[u >> 1][2 * (u & 1)] = __builtin_bit_cast(uint32_t, f16x2{pv[0], pv[1]});
+          pw[u >> 1][2 * (u & 1) + 1] = __builtin_bit_cast(uint32_t, f16x2{pv[2], pv[3]});
+        }
+      }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      l_run = l_run * corr + psum;
+      m_run = m_new;
+      if (corr != 1.f) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int ct = 4 * wv + t;
-        const _Float16 *v0 = sv + vt_offset(vrow, ct, q_src);
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        for (int t = 0; t < 32; ++t) acc[t] *= corr;
+      }
+      // ---- O^T tiles 0..31 of head tile ht over the stage's 64 positions ----
+      // (the V^T fragments of the next 4 tiles are requested before this
+      // group's 4 matrix instructions; scheduling barriers bound the
+      // registers held in flight)
+      auto read_vt = [&](int kk, int ct) -> f16x8 {
+        const _Float16 *v0 = sv + vt_offset(32 * kk + 4 * g + r_src, ct, q_src);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4 *)(v0));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4 *)(v0 + 16 * ROW_HALVES));
-        f16x8 vop = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      f16x8 vcur[4], vnext[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-          acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[h], acc[h][t], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) vcur[i] = read_vt(0, i);
+#pragma unroll
+      for (int grp = 0; grp < 16; ++grp) {          // 8 groups of 4 tiles per position chunk kk
+        const int kk = grp >> 3, ct0 = 4 * (grp & 7);
+        if (grp + 1 < 16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vnext[i] = read_vt((grp + 1) >> 3, 4 * ((grp + 1) & 7) + i);
+        }
+        const f16x8 pop = __builtin_bit_cast(f16x8, pw[kk]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[ct0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vcur[i], pop, acc[ct0 + i], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vcur[i] = vnext[i];
       }
     }
   }
 
   CSA2_TS(4);
-  // a head's max is the same in both halves; its sum is the two halves' sum
-  if (g == 0) s_fin[ph][16 * ht + n16] = l_run;
-  if (g == 0 && ph == 0) s_max[0][16 * ht + n16] = m_run;
-  __syncthreads();
+  if (producer) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   if (a.splits == 1) {
+    float *orow = a.out + ((int64_t)b * 64 + 16 * ht + n16) * D;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float l = s_fin[0][16 * h + n16] + s_fin[1][16 * h + n16];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      float *orow = a.out + ((int64_t)b * 64 + 16 * h + n16) * D;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int ct = 4 * wv + t;
-        *reinterpret_cast<float4 *>(orow + tile_channel(ct, g)) =
-            float4{acc[h][t][0] * inv, acc[h][t][1] * inv, acc[h][t][2] * inv, acc[h][t][3] * inv};
-      }
-    }
+    for (int ct = 0; ct < 32; ++ct)
+      *reinterpret_cast<float4 *>(orow + tile_channel(ct, g)) =
+          float4{acc[ct][0] * inv, acc[ct][1] * inv, acc[ct][2] * inv, acc[ct][3] * inv};
     CSA2_TS(5);
     return;
   }
-  // partials in the 16-head kernel's layout: slot (b, split, tile h)
+  // partials in the 16-head kernel's layout: slot (b, split, tile ht)
+  const int64_t slot = ((int64_t)b * a.splits + split) * 4 + ht;
+  u32x2 *po = reinterpret_cast<u32x2 *>(a.part_o) + slot * (16 * D / 4) + lane;
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int64_t slot = ((int64_t)b * a.splits + split) * 4 + h;
-    u32x2 *po = reinterpret_cast<u32x2 *>(a.part_o) + slot * (16 * D / 4) + lane;
-    const float l = s_fin[0][16 * h + n16] + s_fin[1][16 * h + n16];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) po[(4 * wv + t) * 64] = pack_partial(acc[h][t], inv);
-  }
-  if (g == 0 && ph == 0) {
-    const int64_t slot = ((int64_t)b * a.splits + split) * 4 + ht;
+  for (int ct = 0; ct < 32; ++ct) po[ct * 64] = pack_partial(acc[ct], inv);
+  if (g == 0) {
     float *pm = a.part_ml + (slot * 16 + n16) * 2;
-    pm[0] = s_max[0][16 * ht + n16];
-    pm[1] = s_fin[0][16 * ht + n16] + s_fin[1][16 * ht + n16];
+    pm[0] = m_run;
+    pm[1] = l_run;
   }
   CSA2_TS(5);
 }
