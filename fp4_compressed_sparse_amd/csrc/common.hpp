@@ -169,11 +169,6 @@ __device__ __forceinline__ void st_agent(T *p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
-
 // ---- wave64 primitives on DPP lane moves (no LDS round trip) --------------
 // update_dpp(old, src, ctrl, row_mask, bank_mask, bound_ctrl): lanes whose
 // source is outside the 16-lane row, or whose row is masked off, keep `old`.
@@ -191,11 +186,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   x += CSA2_DPP(x, 0x142, 0xa);
   x += CSA2_DPP(x, 0x143, 0xc);
   return x;
-}
-
-// Sum over the wave, uniform (in a scalar register).
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
 }
 
 // Minimum / maximum over the wave, uniform: butterflies inside each row
