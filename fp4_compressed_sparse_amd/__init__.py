@@ -14,8 +14,10 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# CSA2_LIB_PATH: another build of the same library (the tests' host-sanitizer build)
+# CSA2_LIB_PATH: another build of the same library (the tests' host-sanitizer
+# build, or libcsa2_checked.so)
 LIB_PATH = os.environ.get("CSA2_LIB_PATH") or os.path.join(HERE, "libcsa2.so")
+CHECKED_LIB_PATH = os.path.join(HERE, "libcsa2_checked.so")
 
 FULL, REINDEX, REUSE = 0, 1, 2
 SCORE_SUM, SCORE_HEADMAX = 0, 1     # indexer score rules: heads summed / best head
@@ -23,6 +25,7 @@ MODE_HEADMAX = 0x100                # OR-ed into an index_topk mode: the per-hea
 D, BLOCK, CODE_BYTES, SCALE_BYTES = 512, 8, 256, 32
 MAX_POOL, MAX_TOPK, MAX_CACHES = 8192, 2048, 16
 FLAG_NONFINITE_KV, FLAG_CAPACITY, FLAG_NONFINITE_Q, FLAG_BAD_INDEX, FLAG_SWA_RANGE, FLAG_Q_RANGE = 1, 2, 4, 8, 16, 32
+FLAG_CHECK = 64                     # checked build (libcsa2_checked.so) only
 MAX_WINDOW, MAX_SWA_LAYERS, MAX_SWA_SLOTS = 1024, 64, 1 << 22
 
 EXPORTED = ("fp4_quantize_kv", "csa2_append_kv", "fp8_quantize_kv", "csa2_swa_append",

@@ -12,6 +12,7 @@
 #include "attend.hip"
 
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -83,6 +84,16 @@ csa2_status device_ready() {
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&select_cand_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, big);
       (void)hipGetLastError();
+#ifdef CSA2_CHECKED
+      {
+        // checked build: the workgroup-order salt (a blocking copy, once per
+        // device; this build is not meant for graph capture)
+        const char *env = getenv("CSA2_WG_ORDER");
+        const uint32_t salt = env ? (uint32_t)strtoul(env, nullptr, 10) : 0u;
+        const hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_wg_salt), &salt, sizeof salt, 0, hipMemcpyHostToDevice);
+        if (e != hipSuccess) return fail(CSA2_E_HIP, "set workgroup order: %s", hipGetErrorString(e));
+      }
+#endif
       state[dev] = 1;
     }
   }

@@ -193,7 +193,8 @@ __global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_e
 
   const int b = blockIdx.y;
   const int HT = a.heads >> 4;
-  const int ht = blockIdx.x % HT, split = blockIdx.x / HT;
+  const uint32_t wx = wg_x();
+  const int ht = wx % HT, split = wx / HT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;
   // The sequence length is only needed to mask positions: loads are bounded
@@ -205,6 +206,7 @@ __global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_e
   const int total_pos = a.topk * BLOCK;
   const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
   const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
+  CSA2_CHECK(split < a.splits && st0 < st1 && st1 <= a.n_stages && a.topk <= CSA2_TOPK_MAX);
   // local branch: read now, with the first ids, so that the window rows'
   // addresses are known when the first window stage is fetched
   const int64_t wlen_raw = WIN ? a.swa_len[(int64_t)b * a.swa_stride] : 0;
@@ -253,6 +255,7 @@ __global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_e
         okv[k] = blkv[k] < nw && p >= wlo && p < wrl;
         int64_t slot = wbase + blkv[k];
         slot = okv[k] ? (slot >= a.swa_slots ? slot - a.swa_slots : slot) : 0;
+        CSA2_CHECK(slot >= 0 && slot < a.swa_slots);
         const uint8_t *row = wcodes + slot * D + 32 * i16;
         wr[k] = *reinterpret_cast<const u32x4 *>(row);
         wr2[k] = *reinterpret_cast<const u32x4 *>(row + 16);
@@ -288,6 +291,7 @@ __global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_e
   if constexpr (SELECT) {
     constexpr int KPT = SEL_CAND_MAX / ATT_THREADS;
     const int m = a.n_cand;
+    CSA2_CHECK(m >= 1 && m <= SEL_CAND_MAX);
     const int32_t *cb = a.cand + (int64_t)b * m;
     const float *sb = a.cand_scores + (int64_t)b * m;
     int32_t cid[KPT];
@@ -316,7 +320,7 @@ __global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_e
       kr[k] = ok ? make_key(csc[k], (uint32_t)cid[k]) : 0ull;
       if (j < m) s_keys[j] = kr[k];
     }
-    int32_t *io = blockIdx.x == 0 ? a.idx_out + (int64_t)b * a.topk : nullptr;
+    int32_t *io = wx == 0 ? a.idx_out + (int64_t)b * a.topk : nullptr;
     select_top_regs<KPT>(kr, csc, cid, s_keys, m, a.topk, io, s_sel, a.topk, s_hist, s_state, s_wave);
   }
   // request order: the first stage's block ids, the query tile, then (once
@@ -592,7 +596,7 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) float s_s[4 * 4 * 64 * 4];
   __shared__ uint8_t s_ok[2][ATT_SP];
 
-  const int b = blockIdx.y, split = blockIdx.x;
+  const int b = blockIdx.y, split = wg_x();
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;
   const bool producer = wv < 4;                   // wave-uniform role
@@ -604,6 +608,7 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
   const int total_pos = a.topk * BLOCK;
   const int st0 = (int)((int64_t)a.n_stages * split / a.splits);
   const int st1 = (int)((int64_t)a.n_stages * (split + 1) / a.splits);
+  CSA2_CHECK(split < a.splits && st0 < st1 && st1 <= a.n_stages && a.topk <= CSA2_TOPK_MAX);
 
   // producers: rows (tid >> 4) + 16 k of a stage, 16 code bytes each
   constexpr int PASSES = ATT_SP / 16;
@@ -903,7 +908,8 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_kernel(CombineArgs a) 
   __shared__ float4 s_o[NW > 1 ? 64 : 1];
   __shared__ float s_l[NW > 1 ? 64 : 1];
   const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int HT = a.heads / 16, ht = blockIdx.x >> 5, ct = blockIdx.x & 31;
+  const int HT = a.heads / 16, ht = wg_x() >> 5, ct = wg_x() & 31;
+  CSA2_CHECK(ht < HT);
   const int nslots = a.splits, nml = nslots * 16;
   const int n16 = lane & 15, g = lane >> 4;
   constexpr int BATCH = CMB_U * NW;       // splits per batch
@@ -998,7 +1004,8 @@ __global__ void __launch_bounds__(64 * NW) attend_combine_regs_kernel(CombineArg
   __shared__ float4 s_o[NW > 1 ? NW - 1 : 1][64];
   __shared__ float s_m[NW > 1 ? NW - 1 : 1][64], s_l[NW > 1 ? NW - 1 : 1][64];
   const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int HT = a.heads >> 4, ht = blockIdx.x >> 5, ct = blockIdx.x & 31;
+  const int HT = a.heads >> 4, ht = wg_x() >> 5, ct = wg_x() & 31;
+  CSA2_CHECK(ht < HT);
   const int n16 = lane & 15, g = lane >> 4;
   const int ns = a.splits, s0 = U * wv;
   CSA2_TS(8);

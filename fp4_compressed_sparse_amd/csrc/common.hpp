@@ -27,7 +27,7 @@ constexpr int MAX_GRID_X = 2048;  // workgroups per grid row of a hand-off kerne
 
 // Device flag bits (mirrors include/csa2.h).
 constexpr uint32_t FLAG_NONFINITE_KV = 1, FLAG_CAPACITY = 2, FLAG_NONFINITE_Q = 4,
-                   FLAG_BAD_INDEX = 8, FLAG_Q_RANGE = 32;
+                   FLAG_BAD_INDEX = 8, FLAG_Q_RANGE = 32, FLAG_CHECK = 64;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -113,6 +113,40 @@ extern __device__ uint32_t g_flags;
 __device__ __forceinline__ void raise_flag(uint32_t bit) {
   __hip_atomic_fetch_or(&g_flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// ---- checked build (-DCSA2_CHECKED: libcsa2_checked.so) -------------------
+//
+// Two debugging aids that the product library compiles away:
+// * wg_x(), the workgroup's logical index along x, from which every kernel
+//   derives the work it takes.  The product build returns blockIdx.x.  The
+//   checked build returns (blockIdx.x * p + salt) mod gridDim.x, with p the
+//   first of three primes that does not divide gridDim.x (a bijection), so
+//   the hardware's in-order dispatch hands the work to other physical
+//   workgroups and every cross-workgroup hand-off sees another arrival
+//   order.  The salt is the CSA2_WG_ORDER environment variable, read at the
+//   library's first call on a device (0 keeps the identity order).
+// * CSA2_CHECK(cond): an index bound that a kernel's memory accesses rely
+//   on.  The checked build raises FLAG_CHECK when it does not hold; it only
+//   records (the access still goes ahead), so it is for runs on valid
+//   inputs, whose flag word must stay zero.
+#ifdef CSA2_CHECKED
+extern __device__ uint32_t g_wg_salt;
+__device__ __forceinline__ uint32_t wg_x() {
+  const uint32_t n = gridDim.x, salt = g_wg_salt;
+  if (salt == 0 || n < 2) return blockIdx.x;
+  const uint32_t p = (n % 65521u) ? 65521u : (n % 40009u) ? 40009u : 7919u;
+  return (uint32_t)(((uint64_t)blockIdx.x * p + salt) % n);
+}
+#define CSA2_CHECK(cond)                         \
+  do {                                           \
+    if (!(cond)) raise_flag(::csa2::FLAG_CHECK); \
+  } while (0)
+#else
+__device__ __forceinline__ uint32_t wg_x() { return blockIdx.x; }
+#define CSA2_CHECK(cond) \
+  do {                   \
+  } while (0)
+#endif
 
 // Load of a value another workgroup of the same kernel wrote (after the
 // arrive_last hand-off): agent-scope atomic load, coherent across XCDs.

@@ -203,7 +203,8 @@ __global__ void __launch_bounds__(64 * NW) headmax_kernel(HeadmaxArgs a) {
       }
     }
   };
-  int64_t tile = blockIdx.x;
+  const uint32_t wx = wg_x();
+  int64_t tile = wx;
   if (tile < ntiles) load_tile(tile);     // the first tile's rows overlap the query staging
 
   // This lane's query values: head h, channels w*C .. w*C + C - 1 (zeros for
@@ -321,7 +322,7 @@ __global__ void __launch_bounds__(64 * NW) headmax_kernel(HeadmaxArgs a) {
   }
   if (!HIST) return;
   __syncthreads();
-  uint32_t *mine = a.hist + ((int64_t)b * HIST_COPIES + (blockIdx.x % HIST_COPIES)) * HIST_BINS;
+  uint32_t *mine = a.hist + ((int64_t)b * HIST_COPIES + (wx % HIST_COPIES)) * HIST_BINS;
   for (int j = t; j < HIST_BINS; j += NTHR) {
     const uint32_t c = s_hist[j];
     if (c) atomic_add_agent(mine + j, c);

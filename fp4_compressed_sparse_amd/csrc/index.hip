@@ -363,8 +363,9 @@ __device__ __forceinline__ uint64_t radix_threshold(const uint64_t *keys, int m,
 __global__ void __launch_bounds__(SCAN_THREADS) qbar_kernel(const float *__restrict__ q, int heads,
                                                             float *__restrict__ qbar) {
   __shared__ float s_qbar[D];
-  compute_qbar<64>(q, heads, blockIdx.x, s_qbar);
-  reinterpret_cast<float2 *>(qbar + (int64_t)blockIdx.x * D)[threadIdx.x] =
+  const uint32_t b = wg_x();
+  compute_qbar<64>(q, heads, b, s_qbar);
+  reinterpret_cast<float2 *>(qbar + (int64_t)b * D)[threadIdx.x] =
       reinterpret_cast<const float2 *>(s_qbar)[threadIdx.x];
 }
 
@@ -380,6 +381,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
   __shared__ uint32_t s_hist[HIST ? HIST_BINS : 1];
   __shared__ uint32_t s_wave[16];
   const int b = blockIdx.y;
+  const uint32_t wx = wg_x();
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   CSA2_TS(0);
   if (HIST) {
@@ -395,8 +397,8 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
   int64_t n, nblk;
   if constexpr (HIST) {
     // Dynamic schedule.  Each wave scores chunks of 2 blocks (one per half
-    // wave): its first chunk is fixed (blockIdx.x * 4 + wave); later ones
-    // come from its group's counter, group g of the workgroups (blockIdx.x =
+    // wave): its first chunk is fixed (wg_x() * 4 + wave); later ones
+    // come from its group's counter, group g of the workgroups (wg_x() =
     // g mod G, G = min(64, grid), spanning every dispatch slot of the compute
     // units) sharing chunks first + g, first + g + G, ...  Older workgroups
     // win the issue arbiter, so a static split leaves the youngest finishing
@@ -405,7 +407,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
     // scored, and so are the next chunk's rows.
     const int half = lane >> 5, j = lane & 31;
     const int ngrp = min(SCAN_GROUPS, (int)gridDim.x);   // every group has a workgroup
-    const int grp = blockIdx.x % ngrp;
+    const int grp = wx % ngrp;
     uint32_t *ctr = &ctrl->work[grp * 32];
     const int64_t nchunks = (a.nblk_grid + 1) / 2;
     const int64_t first = (int64_t)gridDim.x * 4;
@@ -419,7 +421,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
     // request
     const int64_t seq = a.seq_len[b];
     const float2 qv = reinterpret_cast<const float2 *>(a.qbar + (int64_t)b * D)[threadIdx.x];
-    int64_t c = (int64_t)blockIdx.x * 4 + wv;
+    int64_t c = (int64_t)wx * 4 + wv;
     uint32_t pending = grab();
     BlockRows32 cur;
     {
@@ -429,6 +431,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
     __builtin_amdgcn_sched_barrier(0);
     n = clamp_len(seq, a.limit);
     nblk = (n + BLOCK - 1) / BLOCK;
+    CSA2_CHECK((int64_t)a.nblk_grid * BLOCK <= a.capacity && nblk <= a.score_stride);
     *reinterpret_cast<float2 *>(s_qbar + qbar32_index(2 * threadIdx.x)) = qv;
     __syncthreads();
     CSA2_TS(1);
@@ -450,12 +453,12 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
       c = cn;
     }
   } else {
-    // static schedule (score export): wave chunks blockIdx.x * 4 + wave,
+    // static schedule (score export): wave chunks wg_x() * 4 + wave,
     // then every gridDim.x * 4 chunks
     const int half = lane >> 5, j = lane & 31;
     const int64_t nchunks = (a.nblk_grid + 1) / 2;
     const int64_t step = (int64_t)gridDim.x * 4;
-    int64_t c = (int64_t)blockIdx.x * 4 + wv;
+    int64_t c = (int64_t)wx * 4 + wv;
     BlockRows32 cur;
     {
       const int64_t blk = max((int64_t)0, min(2 * c + half, (int64_t)a.nblk_grid - 1));
@@ -463,6 +466,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
     }
     n = clamp_len(a.seq_len[b], a.limit);
     nblk = (n + BLOCK - 1) / BLOCK;
+    CSA2_CHECK((int64_t)a.nblk_grid * BLOCK <= a.capacity && nblk <= a.score_stride);
     if (a.qbar) {
       *reinterpret_cast<float2 *>(s_qbar + qbar32_index(2 * threadIdx.x)) =
           reinterpret_cast<const float2 *>(a.qbar + (int64_t)b * D)[threadIdx.x];
@@ -494,7 +498,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
   CSA2_TS(2);
   uint32_t *gh = a.hist + (int64_t)b * HIST_COPIES * HIST_BINS;
   {
-    uint32_t *mine = gh + (blockIdx.x % HIST_COPIES) * HIST_BINS;
+    uint32_t *mine = gh + (wx % HIST_COPIES) * HIST_BINS;
     for (int j = threadIdx.x; j < HIST_BINS; j += SCAN_THREADS) {
       uint32_t c = s_hist[j];
       if (c) atomic_add_agent(mine + j, c);
@@ -511,7 +515,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_
 // histogram copies) as scan_kernel<true>, for batches: the chunks of 2 blocks
 // of every sequence are laid end to end (sequence b's chunks after those of
 // sequences 0..b-1), the whole range is cut into SCAN_GROUPS equal contiguous
-// regions, and the workgroups of group g (blockIdx.x mod SCAN_GROUPS) take the
+// regions, and the workgroups of group g (wg_x() mod SCAN_GROUPS) take the
 // chunks of region g, the first 4 per workgroup fixed, the rest from the
 // group's counter.  So no workgroup idles while long sequences still have
 // chunks, whatever the length mix.  Each wave keeps its current sequence's
@@ -532,6 +536,7 @@ scan_flat_kernel(ScanArgs a, int32_t batch) {
   const int lane = threadIdx.x & 63, t = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int half = lane >> 5, j = lane & 31;
+  const uint32_t wx = wg_x();
   CSA2_TS(0);
   uint32_t *hw = s_hw[wv];
 #pragma unroll
@@ -540,7 +545,7 @@ scan_flat_kernel(ScanArgs a, int32_t batch) {
   auto flush = [&](int sb) {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    uint32_t *gh = a.hist + ((int64_t)sb * HIST_COPIES + (blockIdx.x % HIST_COPIES)) * HIST_BINS;
+    uint32_t *gh = a.hist + ((int64_t)sb * HIST_COPIES + (wx % HIST_COPIES)) * HIST_BINS;
 #pragma unroll
     for (int i = 0; i < HIST_BINS / 64; ++i) {
       const uint32_t v = hw[lane + 64 * i];
@@ -552,6 +557,7 @@ scan_flat_kernel(ScanArgs a, int32_t batch) {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
   };
+  CSA2_CHECK(batch <= SCAN_FLAT_MAXB);
   // lengths -> chunks per sequence -> exclusive prefix, 256 sequences a pass
   uint32_t carry = 0;
   for (int b0 = 0; b0 < batch; b0 += SCAN_THREADS) {
@@ -571,8 +577,8 @@ scan_flat_kernel(ScanArgs a, int32_t batch) {
   __syncthreads();
   const int total = s_pre[batch];
   const int ngrp = min(SCAN_GROUPS, (int)gridDim.x);
-  const int grp = blockIdx.x % ngrp;
-  const int in_grp = blockIdx.x / ngrp;                        // workgroup index inside the group
+  const int grp = wx % ngrp;
+  const int in_grp = wx / ngrp;                        // workgroup index inside the group
   const int per_grp = ((int)gridDim.x - grp + ngrp - 1) / ngrp;  // workgroups of this group
   const int r0 = (int)((int64_t)total * grp / ngrp), r1 = (int)((int64_t)total * (grp + 1) / ngrp);
   uint32_t *ctr = &a.ctrl[0].work[grp * 32];
@@ -1121,7 +1127,8 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   // with the histogram copies: one memory round trip for both.
   constexpr int PRE = 4;
   const int chunks = a.nwords / 2;
-  const int ch0 = blockIdx.x * 4 + wv, chs = gridDim.x * 4;
+  const uint32_t wx = wg_x();
+  const int ch0 = wx * 4 + wv, chs = gridDim.x * 4;
   float sv[PRE];
 #pragma unroll
   for (int k = 0; k < PRE; ++k) {
@@ -1169,8 +1176,8 @@ __global__ void __launch_bounds__(SCAN_THREADS) select_kernel(SelectArgs a) {
   // 64 ids per chunk: the ballot of ids above the tie digit is OR-ed into
   // the (zeroed) bitmap; ids in the tie digit go to one of 8 lists, with one
   // counter reservation per wave for all its chunks
-  uint64_t *mylist = cands + (blockIdx.x % CAND_COPIES) * a.cand_stride;
-  uint32_t *mycount = &ctrl->ncand[blockIdx.x % CAND_COPIES];
+  uint64_t *mylist = cands + (wx % CAND_COPIES) * a.cand_stride;
+  uint32_t *mycount = &ctrl->ncand[wx % CAND_COPIES];
   for (int base_ch = ch0; base_ch < chunks; base_ch += PRE * chs) {
     if (base_ch != ch0) {
 #pragma unroll
@@ -1488,7 +1495,11 @@ __device__ __forceinline__ uint64_t radix_select_keys(F get, int m, int r, uint6
         for (int u = 0; u < 8; ++u) kv[u] = get(min(j0 + u * nt + t, m - 1));
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (j0 + u * nt + t < m && (kv[u] & pmask) == prefix) s_tie[atomicAdd(&s_ntie, 1u)] = kv[u];
+          if (j0 + u * nt + t < m && (kv[u] & pmask) == prefix) {
+            const uint32_t k = atomicAdd(&s_ntie, 1u);
+            CSA2_CHECK(k < (uint32_t)min(nt, TIE_CAP));
+            s_tie[k] = kv[u];
+          }
       }
       __syncthreads();
       if (t < (int)bucket) {
@@ -1522,7 +1533,7 @@ __global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
   __shared__ uint64_t s_state[2];
   __shared__ uint32_t s_wave[16];
   __shared__ uint32_t s_cnt;
-  const int b = blockIdx.y, g = blockIdx.x, G = gridDim.x;
+  const int b = blockIdx.y, g = wg_x(), G = gridDim.x;
   const int t = threadIdx.x, nt = SEL2_THREADS;
   Ctrl *ctrl = a.ctrl + b;
   const float *scores = a.scores + (int64_t)b * a.score_stride;
@@ -1653,6 +1664,7 @@ __global__ void __launch_bounds__(SEL2_THREADS) select2_kernel(SelectArgs a) {
     for (int w = w0; w < w1; ++w) cnt += __popc(s_bm[w]);
     uint32_t tot;
     uint32_t off = block_exclusive_scan(cnt, &tot, s_wave);
+    CSA2_CHECK(tot <= (uint32_t)len);   // the threshold admits at most len keys
     for (int w = w0; w < w1; ++w) {
       s_wpre[w] = off;
       off += __popc(s_bm[w]);
@@ -1767,7 +1779,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) rescore_kernel(RescoreArgs a) {
   float *scores = a.scores + (int64_t)b * a.score_stride;
   const int iters = (a.n_cand + BLOCKS_PER_ITER - 1) / BLOCKS_PER_ITER;
   // first group's candidate ids and rows are requested before the query sum
-  int it = blockIdx.x;
+  int it = wg_x();
   int j = it * BLOCKS_PER_ITER + wv * 4 + slot;
   int32_t blk = cand[min(j, a.n_cand - 1)];          // unconditional: no branch
   if (!(it < iters && j < a.n_cand)) blk = -1;
@@ -1835,6 +1847,7 @@ __global__ void __launch_bounds__(RESCORE32_THREADS) rescore32_kernel(RescoreArg
   const int32_t *cand = a.cand + (int64_t)b * a.n_cand;
   float *scores = a.scores + (int64_t)b * a.score_stride;
   const int iters = (a.n_cand + RESCORE32_BLOCKS - 1) / RESCORE32_BLOCKS;
+  CSA2_CHECK(a.n_cand <= a.score_stride);
   // rounds it, it + grid, ...: the ids of the first two rounds and the rows
   // of the first are requested before the query sum; afterwards each round's
   // rows are requested as the previous round's rows are consumed and the ids
@@ -1848,7 +1861,7 @@ __global__ void __launch_bounds__(RESCORE32_THREADS) rescore32_kernel(RescoreArg
   auto rows_of = [&](int32_t blkv) {
     return (blkv >= 0 && blkv < cap_blocks) ? (int64_t)blkv : (int64_t)0;   // block 0 always exists
   };
-  int it = blockIdx.x;
+  int it = wg_x();
   int jj, jj1;
   int32_t blk = id_of(it, jj);
   int32_t blk1 = id_of(it + (int)gridDim.x, jj1);
@@ -1912,7 +1925,7 @@ __global__ void __launch_bounds__(RESCORE32_THREADS) rescore32_kernel(RescoreArg
 // Reuse: idx_out = prior (grid-stride copy).
 __global__ void __launch_bounds__(256) copy_idx_kernel(const int32_t *__restrict__ src,
                                                        int32_t *__restrict__ dst, int64_t n) {
-  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n;
+  for (int64_t j = (int64_t)wg_x() * blockDim.x + threadIdx.x; j < n;
        j += (int64_t)gridDim.x * blockDim.x)
     dst[j] = src[j];
 }

@@ -22,6 +22,9 @@
 namespace csa2 {
 
 __device__ uint32_t g_flags = 0;
+#ifdef CSA2_CHECKED
+__device__ uint32_t g_wg_salt = 0;   // workgroup-order salt of the checked build
+#endif
 
 // E4M3 value of a non-negative code 0..126.
 __device__ __forceinline__ float e4m3_pos(uint32_t c) { return e4m3_to_f32(c); }
@@ -112,7 +115,7 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(
   const int64_t total = rows * NGROUPS;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const float4 *x4 = reinterpret_cast<const float4 *>(x);
-  for (int64_t g0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g0 < total; g0 += stride * GU) {
+  for (int64_t g0 = (int64_t)wg_x() * blockDim.x + threadIdx.x; g0 < total; g0 += stride * GU) {
     float4 v[GU][4];
     int64_t d[GU];
 #pragma unroll
@@ -185,7 +188,7 @@ __global__ void __launch_bounds__(256) fp8_quantize_kernel(
     int64_t dst_rows, uint8_t *__restrict__ codes, float *__restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows; r += waves) {
+  for (int64_t r = (int64_t)wg_x() * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows; r += waves) {
     const float4 *src = reinterpret_cast<const float4 *>(x + r * D) + 2 * lane;
     const float4 v0 = src[0], v1 = src[1];
     const int64_t d = dst_row ? dst_row[r] : r;
@@ -242,7 +245,7 @@ struct QbarJob {
 __global__ void __launch_bounds__(128) append_kernel(AppendArgs a, SwaRings r, const float *__restrict__ x,
                                                      int32_t batch, int32_t n_caches, int32_t n_rings,
                                                      QbarJob qj) {
-  const int b = blockIdx.x, c = blockIdx.y;
+  const int b = wg_x(), c = blockIdx.y;
   const int q = threadIdx.x;
   if (c >= n_caches + n_rings) {
     // query sum: slice k of QBAR_SLICES owns channels 128k..128k+127, one
@@ -327,7 +330,7 @@ __global__ void __launch_bounds__(128) append_kernel(AppendArgs a, SwaRings r, c
 // Zero fill (graph-safe replacement for memset).
 __global__ void __launch_bounds__(256) zero_kernel(uint32_t *__restrict__ p, int64_t words) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride) p[i] = 0;
+  for (int64_t i = (int64_t)wg_x() * blockDim.x + threadIdx.x; i < words; i += stride) p[i] = 0;
 }
 
 }  // namespace csa2

@@ -94,9 +94,15 @@ enum {
   CSA2_FLAG_BAD_INDEX = 8,      /* a candidate/selected block id was >= the block count */
   CSA2_FLAG_SWA_RANGE = 16,     /* an SWA row's largest magnitude exceeded 65504, the
                                    attention's fp16 operand range (stored as given)      */
-  CSA2_FLAG_Q_RANGE = 32        /* an attention query value had magnitude >= 65520 or was
+  CSA2_FLAG_Q_RANGE = 32,       /* an attention query value had magnitude >= 65520 or was
                                    NaN/Inf: it has no fp16 value (the matrix-core operand),
                                    so the outputs of its sequence are unspecified         */
+  CSA2_FLAG_CHECK = 64          /* checked build only (libcsa2_checked.so, compiled with
+                                   -DCSA2_CHECKED): an index bound that a kernel relies on
+                                   failed.  That build also scrambles the order in which
+                                   workgroups take their work (environment variable
+                                   CSA2_WG_ORDER, an unsigned salt; 0 = identity), and its
+                                   results must equal the product library's bit for bit  */
 };
 
 #define CSA2_D 512              /* latent channels                 */

@@ -33,6 +33,16 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_checked_build_exports_the_same_symbols():
+    # the checked build (workgroup order scrambled, device index checks) is
+    # the same ABI: the GPU comparison loads it in place of libcsa2.so
+    if not os.path.exists(csa2.CHECKED_LIB_PATH):
+        pytest.fail("libcsa2_checked.so is not built; run __graft_entry__.build()")
+    chk = ctypes.CDLL(csa2.CHECKED_LIB_PATH)
+    for n in _declared():
+        assert hasattr(chk, n), n
+
+
 def test_status_strings(lib):
     assert lib.csa2_status_string(0) == b"ok"
     assert lib.csa2_status_string(3) == b"workspace too small"
