@@ -5,7 +5,7 @@ has loaded (the product libcsa2.so, or libcsa2_checked.so when CSA2_LIB_PATH
 names it) and returns every output as numpy arrays, plus the device flag
 word.  Inputs are seeded: random FP4 cache bytes with valid E4M3 scales,
 workload queries and rows.  The cases reach every kernel: the quantisers,
-the append, the single-sequence and batched full scans, the pool select,
+the append, the single-sequence (up to 1,048,576 positions) and batched full scans, the pool select,
 pool rescoring, both score rules, the decode attention with and without
 in-kernel selection and window rows, the combines and the 64-head prefill
 kernel.
@@ -132,6 +132,8 @@ def run_cases():
     w3 = W.scaled(W.WORKLOADS[3], context=20000)
     _steps(csa2, torch, W, res, "w3", w3, [20000], 2)
     _steps(csa2, torch, W, res, "w3win", w3, [20000], 2, window=96)
+    # the same 20 layers at 1,048,576 positions (the scan's dynamic schedule over all its work counters)
+    _steps(csa2, torch, W, res, "w3full", W.WORKLOADS[3], [1 << 20], 2)
     # a ragged batch of 8 (3,000-60,000 positions): the batched scan, pool 2,048, 16 heads, top-128
     w4 = W.Workload(4, "ragged-b8", 8, 0, 16, 128, 2048, (0, 1, 2), 2, True)
     lens = np.random.default_rng(44).integers(3000, 60000, size=8)
