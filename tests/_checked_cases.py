@@ -8,7 +8,8 @@ workload queries and rows.  The cases reach every kernel: the quantisers,
 the append, the single-sequence (up to 1,048,576 positions) and batched full scans, the pool select,
 pool rescoring, both score rules, the decode attention with and without
 in-kernel selection and window rows, the combines and the 64-head prefill
-kernel.
+kernel, and the entry points on their own (selection, pool rescoring, score
+export, attention).
 
 As a script: python tests/_checked_cases.py OUT.npz (the child process of
 the comparison test)."""
@@ -107,6 +108,36 @@ def _prefill(csa2, torch, W, res, tag, n, qpos, heads, topk, seed):
     res[f"{tag}/out"] = out.cpu().numpy()
 
 
+def _standalone(csa2, torch, W, res):
+    # the entry points on their own: a Full selection into a pool, pool
+    # rescoring with its top-k, score export (every block and the pool's
+    # blocks) and attention, under both score rules; batch 2, 70,000 and
+    # 50,001 positions, 64 heads
+    rng = np.random.default_rng(77)
+    B, n, H = 2, 70000, 64
+    g = _cache(csa2, torch, rng, [n, 50001], n)
+    g.max_len = n
+    q0 = torch.from_numpy(W.queries(2, 0, 0, B, H)).cuda()
+    q1 = torch.from_numpy(W.queries(2, 1, 0, B, H)).cuda()
+    for hm in (0, 1):
+        ws = csa2.workspace(B, H, n, 2048, 256)
+        idx0 = torch.full((B, 256), -7, dtype=torch.int32, device="cuda")
+        pool = torch.full((B, 2048), -7, dtype=torch.int32, device="cuda")
+        csa2.index_topk(csa2.FULL, g, q0, 256, idx0, ws, pool=2048, pool_out=pool, score=hm)
+        idx1 = torch.full((B, 256), -7, dtype=torch.int32, device="cuda")
+        csa2.index_topk(csa2.FULL, g, q1, 256, idx1, ws, cand=pool, score=hm)
+        sc = torch.zeros((B, n // 8), dtype=torch.float32, device="cuda")
+        csa2.block_scores(g, q0, sc, score=hm)
+        scp = torch.zeros((B, 2048), dtype=torch.float32, device="cuda")
+        csa2.block_scores(g, q1, scp, cand=pool, score=hm)
+        out = torch.zeros((B, H, 512), dtype=torch.float32, device="cuda")
+        csa2.sparse_attend(g, q1, idx1, 1 / np.sqrt(512), out, ws)
+        torch.cuda.synchronize()
+        for k, v in (("idx0", idx0), ("pool", pool), ("idx1", idx1), ("scores", sc), ("pool_scores", scp),
+                     ("out", out)):
+            res[f"alone{hm}/{k}"] = v.cpu().numpy()
+
+
 def run_cases():
     import torch
 
@@ -148,6 +179,7 @@ def run_cases():
     _prefill(csa2, torch, W, res, "pre64", 12000, np.arange(12000 - 64, 12000), 64, 256, 12)
     _prefill(csa2, torch, W, res, "pre16", 4096, [0, 1, 7, 8, 63, 64, 200, 511, 1000, 4093, 4094, 4095],
              16, 64, 3)
+    _standalone(csa2, torch, W, res)
     res["flags"] = np.asarray([csa2.device_error()], dtype=np.int64)
     return res
 
