@@ -174,6 +174,29 @@ struct AttendArgs {
 
 constexpr int SEL_CAND_MAX = 2048;  // candidates of the in-kernel top-k (8 per thread)
 
+// A lane's value combined with that of lane ^ 16 (or lane ^ 32) by the
+// permlane swap instructions: VALU lane moves, no LDS round trip as with a
+// bpermute.  With the value in both operands the two results hold the lane's
+// own value and its partner's (in an order that differs between lanes; max
+// and sum are symmetric, so every lane gets the same result as own (op) partner).
+template <int X>
+__device__ __forceinline__ f32x2 xor_lanes_pair(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto s = X == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return f32x2{__uint_as_float(s[0]), __uint_as_float(s[1])};
+}
+template <int X>
+__device__ __forceinline__ float xor_lanes_max(float v) {
+  const f32x2 p = xor_lanes_pair<X>(v);
+  return fmaxf(p.x, p.y);
+}
+template <int X>
+__device__ __forceinline__ float xor_lanes_sum(float v) {
+  const f32x2 p = xor_lanes_pair<X>(v);
+  return p.x + p.y;
+}
+
 // One workgroup = one 16-head tile x a range of stages of 64 gathered
 // positions.  Per stage: the 256 threads dequantise the 64 rows into LDS as
 // fp16; wave w computes S^T for positions 16w..16w+15 (16 MFMA k-steps);
@@ -475,8 +498,8 @@ __global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_e
       z[r] = s_ok[16 * wv + 4 * g + r] ? sacc[r] * a.scale_log2 : -__builtin_huge_valf();
       mx = fmaxf(mx, z[r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor_lanes_max<16>(mx);
+    mx = xor_lanes_max<32>(mx);
     if (g == 0) s_max[wv][n16] = mx;
     __syncthreads();
     const float m_new = fmaxf(m_run, fmaxf(fmaxf(s_max[0][n16], s_max[1][n16]),
@@ -497,8 +520,8 @@ __global__ void __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_e
     *reinterpret_cast<u32x2 *>(s_p + p_offset(0, 1, n16, 16 * wv + 4 * g)) =
         u32x2{__builtin_bit_cast(uint32_t, f16x2{ph[0], ph[1]}),
               __builtin_bit_cast(uint32_t, f16x2{ph[2], ph[3]})};
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = xor_lanes_sum<16>(psum);
+    psum = xor_lanes_sum<32>(psum);
     if (g == 0) s_sum[wv][n16] = psum;
     __syncthreads();
     CSA2_TS(3);
@@ -789,8 +812,8 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
         sl[u] = s_mine[u * 64];
         mx = fmaxf(mx, fmaxf(fmaxf(sl[u][0], sl[u][1]), fmaxf(sl[u][2], sl[u][3])));
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = xor_lanes_max<16>(mx);
+      mx = xor_lanes_max<32>(mx);
       // The reference moves only when the stage's max exceeds it by more
       // than 8 (log2 domain), so P <= 256 (fp16-safe) and the 128
       // accumulators are rescaled only on such jumps (with the exact running
@@ -816,8 +839,8 @@ __global__ void __launch_bounds__(ATT64_THREADS) attend64_kernel(AttendArgs a) {
           pw[u >> 1][2 * (u & 1) + 1] = __builtin_bit_cast(uint32_t, f16x2{pv[2], pv[3]});
         }
       }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
+      psum = xor_lanes_sum<16>(psum);
+      psum = xor_lanes_sum<32>(psum);
       l_run = l_run * corr + psum;
       m_run = m_new;
       if (corr != 1.f) {
