@@ -127,6 +127,26 @@ __device__ __forceinline__ void load_block(BlockRows &r, const uint8_t *__restri
   }
 }
 
+// One level of the score's pairwise tree: v plus the value of lane ^ M.
+// M = 1 and 2 are exact quad permutes (DPP).  For M = 4, 8 and 16 the lower
+// levels have already made every group of M lanes hold one value, so any
+// lane of the partner group serves: the half-row and row mirrors (DPP) and
+// the permlane16 row swap (whose two results are the lane's own value and
+// its partner's, in either order; the sum is the same).  All are lane moves
+// in the vector unit, with no LDS round trip, and each lane adds the same
+// two values as with an exchange by lane ^ M.
+template <int M>
+__device__ __forceinline__ float tree_add(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (M == 16) {
+    const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  } else {
+    constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : M == 4 ? 0x141 : 0x140;   // quad [1,0,3,2], [2,3,0,1]; half-row, row mirror
+    return v + __uint_as_float(CSA2_DPP(u, ctrl, 0xf));
+  }
+}
+
 // Score of one block from its loaded rows; the 16 lanes of a slot call it
 // together (lane16 = i).  cnt: rows present (1..8).  qb: this lane's 32
 // Qbar values (LDS).  RELOAD: as soon as row t is consumed its registers
@@ -183,10 +203,10 @@ __device__ __forceinline__ float block_score(BlockRows &r, int cnt, const float 
     for (int c = 17; c < 32; ++c) g1 = g1 + qb[c] * __fdiv_rn(S[c], fc);
   }
   float v = g0 + g1;                    // tree level 1: groups 2i, 2i+1
-  v = v + __shfl_xor(v, 1);             // level 2
-  v = v + __shfl_xor(v, 2);             // level 3
-  v = v + __shfl_xor(v, 4);             // level 4
-  v = v + __shfl_xor(v, 8);             // level 5
+  v = tree_add<1>(v);                   // level 2
+  v = tree_add<2>(v);                   // level 3
+  v = tree_add<4>(v);                   // level 4
+  v = tree_add<8>(v);                   // level 5
   return v + 0.0f;
 }
 
@@ -259,11 +279,11 @@ __device__ __forceinline__ float block_score32(BlockRows32 &r, int cnt, const fl
     g = qb[0] * __fdiv_rn(S[0], fc);
     for (int c = 1; c < 16; ++c) g = g + qb[64 * (c >> 2) + (c & 3)] * __fdiv_rn(S[c], fc);
   }
-  g = g + __shfl_xor(g, 1);             // tree level 1: groups 2k, 2k+1
-  g = g + __shfl_xor(g, 2);
-  g = g + __shfl_xor(g, 4);
-  g = g + __shfl_xor(g, 8);
-  g = g + __shfl_xor(g, 16);            // level 5
+  g = tree_add<1>(g);                   // tree level 1: groups 2k, 2k+1
+  g = tree_add<2>(g);
+  g = tree_add<4>(g);
+  g = tree_add<8>(g);
+  g = tree_add<16>(g);                  // level 5
   return g + 0.0f;
 }
 
